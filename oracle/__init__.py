@@ -1,0 +1,208 @@
+"""ctypes front end of the binary64 CPU oracle (``moe_oracle.c``).
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the CPU-baseline
+leg of the benchmark are the only users.  The GPU library neither imports nor
+links anything here.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+# ORACLE_LIB points the front end at another build of moe_oracle.c (the
+# mutation tests load deliberately broken copies to show the pins catch them).
+_LIB_PATH = os.environ.get("ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+class _Dims(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("latent", ctypes.c_int32),
+                ("n_experts", ctypes.c_int32), ("expert_inter", ctypes.c_int32),
+                ("shared_inter", ctypes.c_int32), ("top_k", ctypes.c_int32),
+                ("router_is_f32", ctypes.c_int32)]
+
+
+class _Outputs(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("logit", "score", "key", "idx", "weight", "z", "act", "ylat", "ash", "sh",
+                 "up", "out")]
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            from . import build as _b
+            _b.build()
+        L = ctypes.CDLL(_LIB_PATH)
+        vp, i32 = ctypes.c_void_p, ctypes.c_int32
+        L.oracle_e2m1_value.argtypes = [i32]
+        L.oracle_e2m1_value.restype = ctypes.c_double
+        L.oracle_e8m0_value.argtypes = [i32]
+        L.oracle_e8m0_value.restype = ctypes.c_double
+        L.oracle_bf16_value.argtypes = [ctypes.c_uint16]
+        L.oracle_bf16_value.restype = ctypes.c_double
+        L.oracle_bf16_bits_rne.argtypes = [ctypes.c_double]
+        L.oracle_bf16_bits_rne.restype = ctypes.c_uint16
+        L.oracle_bf16_round.argtypes = [ctypes.c_double]
+        L.oracle_bf16_round.restype = ctypes.c_double
+        L.oracle_mxfp4_element.argtypes = [vp, vp, i32]
+        L.oracle_mxfp4_element.restype = ctypes.c_double
+        L.oracle_topk.argtypes = [vp, i32, i32, vp]
+        L.oracle_topk.restype = i32
+        L.oracle_router_scores.argtypes = [ctypes.POINTER(_Dims), i32, vp, vp, vp, vp]
+        L.oracle_router_scores.restype = i32
+        L.oracle_select.argtypes = [ctypes.POINTER(_Dims), i32, vp, vp, vp, vp, vp, vp]
+        L.oracle_select.restype = i32
+        L.oracle_moe_step.argtypes = [ctypes.POINTER(_Dims), i32] + [vp] * 11 + \
+            [i32, vp, ctypes.POINTER(_Outputs)]
+        L.oracle_moe_step.restype = i32
+        _lib = L
+    return _lib
+
+
+def _p(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a: Optional[np.ndarray], dtype) -> Optional[np.ndarray]:
+    return None if a is None else np.ascontiguousarray(a, dtype=dtype)
+
+
+def dims_struct(d) -> _Dims:
+    return _Dims(d.hidden, d.latent, d.n_experts, d.expert_inter, d.shared_inter, d.top_k,
+                 1 if d.router_f32 else 0)
+
+
+# ---- scalar helpers (format definitions) ----
+
+def e2m1_value(code: int) -> float:
+    return lib().oracle_e2m1_value(code)
+
+
+def e8m0_value(byte: int) -> float:
+    return lib().oracle_e8m0_value(byte)
+
+
+def bf16_value(bits: int) -> float:
+    return lib().oracle_bf16_value(bits)
+
+
+def bf16_bits_rne(v: float) -> int:
+    return lib().oracle_bf16_bits_rne(v)
+
+
+def bf16_round(v: float) -> float:
+    return lib().oracle_bf16_round(v)
+
+
+def mxfp4_element(q_row: np.ndarray, s_row: np.ndarray, j: int) -> float:
+    q = _c(q_row, np.uint8)
+    s = _c(s_row, np.uint8)
+    return lib().oracle_mxfp4_element(_p(q), _p(s), j)
+
+
+# ---- routing ----
+
+def topk(key: np.ndarray, k: int) -> np.ndarray:
+    key = _c(key, np.float32)
+    out = np.empty(k, np.int32)
+    if lib().oracle_topk(_p(key), key.size, k, _p(out)) != 0:
+        raise ValueError("oracle_topk: bad arguments")
+    return out
+
+
+def router_scores(dims, x: np.ndarray, router_w: np.ndarray):
+    """(logit, score) for tokens x [B][H]; both binary64 [B][E]."""
+    x = _c(x, np.uint16)
+    B = x.shape[0]
+    rw = _c(router_w, np.float32 if dims.router_f32 else np.uint16)
+    logit = np.empty((B, dims.n_experts))
+    score = np.empty((B, dims.n_experts))
+    ds = dims_struct(dims)
+    if lib().oracle_router_scores(ctypes.byref(ds), B, _p(x), _p(rw), _p(logit), _p(score)):
+        raise RuntimeError("oracle_router_scores failed")
+    return logit, score
+
+
+def select(dims, score: np.ndarray, bias: Optional[np.ndarray], forced_idx=None):
+    """(key f32 [B][E], idx [B][k], weight [B][k]) from scores."""
+    score = _c(score, np.float64)
+    B = score.shape[0]
+    key = np.empty((B, dims.n_experts), np.float32)
+    idx = np.empty((B, dims.top_k), np.int32)
+    w = np.empty((B, dims.top_k))
+    ds = dims_struct(dims)
+    rc = lib().oracle_select(ctypes.byref(ds), B, _p(score), _p(_c(bias, np.float32)),
+                             _p(_c(forced_idx, np.int32)), _p(key), _p(idx), _p(w))
+    if rc:
+        raise RuntimeError("oracle_select failed")
+    return key, idx, w
+
+
+# ---- the whole step ----
+
+_ALL = ("logit", "score", "key", "idx", "weight", "z", "act", "ylat", "ash", "sh", "up", "out")
+
+
+def moe_step(layer, x: np.ndarray, mirror: bool = True, forced_idx=None,
+             want=("idx", "weight", "out")) -> dict:
+    """Run the oracle on tokens x [B][H] (bf16 patterns) of a synth.Layer.
+
+    Returns a dict of the requested results (see oracle_outputs in the C
+    source); `want="all"` returns every intermediate.
+    """
+    d = layer.dims
+    x = _c(np.atleast_2d(x), np.uint16)
+    B = x.shape[0]
+    H, L, E, I, Is, k = d.hidden, d.latent, d.n_experts, d.expert_inter, d.shared_inter, d.top_k
+    shapes = {"logit": ((B, E), np.float64), "score": ((B, E), np.float64),
+              "key": ((B, E), np.float32), "idx": ((B, k), np.int32),
+              "weight": ((B, k), np.float64), "z": ((B, L), np.float64),
+              "act": ((B, k, I), np.float64), "ylat": ((B, L), np.float64),
+              "ash": ((B, Is), np.float64), "sh": ((B, H), np.float64),
+              "up": ((B, H), np.float64), "out": ((B, H), np.float64)}
+    names = _ALL if want == "all" else tuple(want)
+    res = {n: np.empty(*shapes[n]) for n in names}
+    outs = _Outputs(**{n: (_p(res[n]) if n in res else None) for n in _ALL})
+    arrs = [_c(layer.router_w, np.float32 if d.router_f32 else np.uint16),
+            _c(layer.bias, np.float32), _c(layer.lat_down, np.uint16),
+            _c(layer.lat_up, np.uint16), _c(layer.w13_q, np.uint8), _c(layer.w13_s, np.uint8),
+            _c(layer.w2_q, np.uint8), _c(layer.w2_s, np.uint8), _c(layer.sh_w13, np.uint16),
+            _c(layer.sh_w2, np.uint16)]
+    if layer.w13_q.shape[0] != E:
+        raise ValueError("layer was generated without experts")
+    fi = _c(forced_idx, np.int32)
+    ds = dims_struct(d)
+    rc = lib().oracle_moe_step(ctypes.byref(ds), B, _p(x), *[_p(a) for a in arrs],
+                               1 if mirror else 0, _p(fi), ctypes.byref(outs))
+    if rc:
+        raise RuntimeError("oracle_moe_step failed")
+    return res
+
+
+def near_tie_alternatives(key64_row: np.ndarray, k: int, tau: float):
+    """Valid selections for one token whose k-th/(k+1)-th keys lie within tau.
+
+    Experts whose binary64 key is within tau of the boundary key may trade
+    places; every selection of k experts that keeps all experts clearly above
+    the boundary and fills the rest from the near-boundary set is valid.
+    Returns (is_near_tie, list of sorted index arrays).
+    """
+    import itertools
+    order = np.lexsort((np.arange(key64_row.size), -key64_row))
+    kth = key64_row[order[k - 1]]
+    near = [int(e) for e in np.nonzero(np.abs(key64_row - kth) <= tau)[0]]
+    sure = [int(e) for e in order[:k] if key64_row[e] - kth > tau]
+    free = k - len(sure)
+    gap = key64_row[order[k - 1]] - key64_row[order[k]] if k < key64_row.size else np.inf
+    if gap > tau:
+        return False, [np.sort(order[:k]).astype(np.int32)]
+    alts = []
+    for combo in itertools.combinations(sorted(near), free):
+        alts.append(np.sort(np.array(sure + list(combo), np.int32)))
+    return True, alts
