@@ -149,10 +149,16 @@ def select(dims, score: np.ndarray, bias: Optional[np.ndarray], forced_idx=None)
 _ALL = ("logit", "score", "key", "idx", "weight", "z", "act", "ylat", "ash", "sh", "up", "out")
 
 
-def moe_step(layer, x: np.ndarray, mirror: bool = True, forced_idx=None,
+ROUNDING = {"none": 0, "output": 1, "bf16_all": 2}
+
+
+def moe_step(layer, x: np.ndarray, rounding: str = "output", forced_idx=None,
              want=("idx", "weight", "out")) -> dict:
     """Run the oracle on tokens x [B][H] (bf16 patterns) of a synth.Layer.
 
+    rounding: "output" (intermediates binary64, output rounded to bf16, the
+    policy of the GPU library), "bf16_all" (also z, expert activations,
+    combined latent and shared activation rounded to bf16) or "none".
     Returns a dict of the requested results (see oracle_outputs in the C
     source); `want="all"` returns every intermediate.
     """
@@ -179,7 +185,7 @@ def moe_step(layer, x: np.ndarray, mirror: bool = True, forced_idx=None,
     fi = _c(forced_idx, np.int32)
     ds = dims_struct(d)
     rc = lib().oracle_moe_step(ctypes.byref(ds), B, _p(x), *[_p(a) for a in arrs],
-                               1 if mirror else 0, _p(fi), ctypes.byref(outs))
+                               ROUNDING[rounding], _p(fi), ctypes.byref(outs))
     if rc:
         raise RuntimeError("oracle_moe_step failed")
     return res

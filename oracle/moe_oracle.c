@@ -255,20 +255,30 @@ int32_t oracle_select(const oracle_dims *d, int32_t B, const double *score, cons
 /* The whole layer step                                                       */
 /* ------------------------------------------------------------------------- */
 
-/* mirror = 1: round to bf16 where the GPU path stores bf16 (z, expert
- * activation, combined latent, shared activation, output); mirror = 0: keep
- * every intermediate in binary64 ("exact", report only).
+/* Rounding policy (the layer definition fixes only "bf16 output, f32
+ * accumulation"; where intermediates are rounded is an implementation choice):
+ *   ORACLE_ROUND_NONE    = 0: every value stays binary64, output included;
+ *   ORACLE_ROUND_OUTPUT  = 1: intermediates stay binary64, the output is
+ *                             rounded to bf16 (the GPU library keeps its
+ *                             intermediates at f32-grade precision);
+ *   ORACLE_ROUND_BF16_ALL = 2: z, the expert activations, the combined latent,
+ *                             the shared activation and the output are each
+ *                             rounded to bf16 where they are produced.
  * Tokens are independent; each is processed on its own. */
+enum { ORACLE_ROUND_NONE = 0, ORACLE_ROUND_OUTPUT = 1, ORACLE_ROUND_BF16_ALL = 2 };
 int32_t oracle_moe_step(const oracle_dims *d, int32_t B, const uint16_t *x, const void *router_w,
                         const float *bias, const uint16_t *lat_down, const uint16_t *lat_up,
                         const uint8_t *w13_q, const uint8_t *w13_s, const uint8_t *w2_q,
                         const uint8_t *w2_s, const uint16_t *sh_w13, const uint16_t *sh_w2,
-                        int32_t mirror, const int32_t *forced_idx, oracle_outputs *o)
+                        int32_t rounding, const int32_t *forced_idx, oracle_outputs *o)
 {
     const int64_t H = d->hidden, L = d->latent, E = d->n_experts, I = d->expert_inter,
                   Is = d->shared_inter, k = d->top_k;
     if (H < 1 || L < 1 || E < 1 || I < 1 || Is < 1 || k < 1 || k > E || B < 1) return -1;
     if (L % 32 || I % 32) return -1; /* whole MX blocks per row */
+    if (rounding < ORACLE_ROUND_NONE || rounding > ORACLE_ROUND_BF16_ALL) return -1;
+    const int mid = rounding == ORACLE_ROUND_BF16_ALL; /* round intermediates */
+    const int fin = rounding != ORACLE_ROUND_NONE;     /* round the output   */
 
     double *score = malloc(sizeof(double) * E);
     double *logit = malloc(sizeof(double) * E);
@@ -306,7 +316,7 @@ int32_t oracle_moe_step(const oracle_dims *d, int32_t B, const uint16_t *x, cons
         /* Latent down-projection: z = W_ld x. */
         for (int64_t l = 0; l < L; ++l) {
             double v = dot_bf16(lat_down + l * H, xv, H);
-            z[l] = mirror ? oracle_bf16_round(v) : v;
+            z[l] = mid ? oracle_bf16_round(v) : v;
         }
         if (o->z) memcpy(o->z + b * L, z, sizeof(double) * L);
 
@@ -322,7 +332,7 @@ int32_t oracle_moe_step(const oracle_dims *d, int32_t B, const uint16_t *x, cons
                 double u = dot_mxfp4(q13 + (I + i) * (L / 2), s13 + (I + i) * (L / 32), z,
                                      (int32_t)L);
                 double v = g * sigmoid(g) * u; /* silu(gate) * up */
-                a[i] = mirror ? oracle_bf16_round(v) : v;
+                a[i] = mid ? oracle_bf16_round(v) : v;
             }
             if (o->act) memcpy(o->act + (b * k + j) * I, a, sizeof(double) * I);
             const uint8_t *q2 = w2_q + e * L * (I / 2);
@@ -331,7 +341,7 @@ int32_t oracle_moe_step(const oracle_dims *d, int32_t B, const uint16_t *x, cons
                 ye[l] = dot_mxfp4(q2 + l * (I / 2), s2 + l * (I / 32), a, (int32_t)I);
             for (int64_t l = 0; l < L; ++l) ylat[l] += wsel[j] * ye[l];
         }
-        if (mirror)
+        if (mid)
             for (int64_t l = 0; l < L; ++l) ylat[l] = oracle_bf16_round(ylat[l]);
         if (o->ylat) memcpy(o->ylat + b * L, ylat, sizeof(double) * L);
 
@@ -340,7 +350,7 @@ int32_t oracle_moe_step(const oracle_dims *d, int32_t B, const uint16_t *x, cons
             double g = dot_bf16(sh_w13 + i * H, xv, H);
             double u = dot_bf16(sh_w13 + (Is + i) * H, xv, H);
             double v = g * sigmoid(g) * u;
-            as[i] = mirror ? oracle_bf16_round(v) : v;
+            as[i] = mid ? oracle_bf16_round(v) : v;
         }
         if (o->ash) memcpy(o->ash + b * Is, as, sizeof(double) * Is);
         for (int64_t h = 0; h < H; ++h) sh[h] = dot_bf16(sh_w2 + h * Is, as, Is);
@@ -351,7 +361,7 @@ int32_t oracle_moe_step(const oracle_dims *d, int32_t B, const uint16_t *x, cons
             double u = dot_bf16(lat_up + h * L, ylat, L);
             if (o->up) o->up[b * H + h] = u;
             double v = u + sh[h];
-            if (o->out) o->out[b * H + h] = mirror ? oracle_bf16_round(v) : v;
+            if (o->out) o->out[b * H + h] = fin ? oracle_bf16_round(v) : v;
         }
     }
 

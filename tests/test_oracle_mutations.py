@@ -14,7 +14,11 @@ SRC = os.path.join(ROOT, "oracle", "moe_oracle.c")
 MUTATIONS = {
     "nibble order swapped": ("(byte & 0x0F) : (byte >> 4)", "(byte >> 4) : (byte & 0x0F)"),
     "scale block of 16": ("s_row[j / 32]", "s_row[j / 16]"),
-    "activation not rounded": ("a[i] = mirror ? oracle_bf16_round(v) : v;", "a[i] = v;"),
+    "activation not rounded": ("a[i] = mid ? oracle_bf16_round(v) : v;", "a[i] = v;"),
+    "output not rounded": ("fin ? oracle_bf16_round(v) : v", "v"),
+    "intermediates rounded under the output policy": (
+        "const int mid = rounding == ORACLE_ROUND_BF16_ALL;",
+        "const int mid = rounding != ORACLE_ROUND_NONE;"),
     "silu on the up half": ("double v = g * sigmoid(g) * u; /* silu",
                             "double v = u * sigmoid(u) * g; /* silu"),
     "routing weight dropped": ("ylat[l] += wsel[j] * ye[l]", "ylat[l] += ye[l]"),

@@ -71,12 +71,15 @@ def bf16_f64(bits: np.ndarray) -> np.ndarray:
         np.float64)
 
 
-def dense_reference(layer, x, mirror=True, forced_idx=None):
+def dense_reference(layer, x, rounding="output", forced_idx=None):
     """The layer evaluated densely with NumPy: every expert is computed for
-    every token, then masked by the selection and weighted."""
+    every token, then masked by the selection and weighted.  `rounding` as in
+    oracle.moe_step."""
     d = layer.dims
     E, I, k = d.n_experts, d.expert_inter, d.top_k
-    rnd = bf16_round_bruteforce if mirror else (lambda a: a)
+    ident = lambda a: a  # noqa: E731
+    rnd = bf16_round_bruteforce if rounding == "bf16_all" else ident
+    rnd_out = ident if rounding == "none" else bf16_round_bruteforce
     xv = bf16_f64(x)
     rw = layer.router_w.astype(np.float64) if d.router_f32 else bf16_f64(layer.router_w)
     logit = xv @ rw.T
@@ -112,7 +115,7 @@ def dense_reference(layer, x, mirror=True, forced_idx=None):
     ash = rnd(gs / (1.0 + np.exp(-gs)) * us)
     sh = ash @ bf16_f64(layer.sh_w2).T
     up = ylat @ bf16_f64(layer.lat_up).T
-    out = rnd(up + sh)
+    out = rnd_out(up + sh)
     return dict(idx=idx, weight=w, score=score, key=key, z=z, ylat=ylat, ash=ash, sh=sh, up=up,
                 out=out)
 
@@ -287,27 +290,40 @@ def test_router_scores_match_matmul_and_logistic(router_f32):
 # The whole step against the dense NumPy evaluation
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("mirror", [True, False])
+@pytest.mark.parametrize("rounding", ["output", "bf16_all", "none"])
 @pytest.mark.parametrize("recipe_name,B", [("small", 3), ("small_f32router", 2),
                                            ("tiny", 2)])
-def test_step_matches_dense_reference(recipe_name, B, mirror):
+def test_step_matches_dense_reference(recipe_name, B, rounding):
     recipe = {"small": small_recipe(), "small_f32router": small_recipe(router_f32=True, E=12,
                                                                        k=3, bias="none"),
               "tiny": synth.TINY}[recipe_name]
     layer = synth.make_layer(recipe, 7)
     x = synth.make_tokens(layer.dims, 7, B)
-    got = oracle.moe_step(layer, x, mirror=mirror, want="all")
-    ref = dense_reference(layer, x, mirror=mirror)
+    got = oracle.moe_step(layer, x, rounding=rounding, want="all")
+    ref = dense_reference(layer, x, rounding=rounding)
     np.testing.assert_array_equal(got["idx"], ref["idx"])
     np.testing.assert_allclose(got["weight"], ref["weight"], rtol=1e-14)
     for name in ("z", "ylat", "ash", "sh", "up", "out"):
-        if mirror and name in ("z", "ylat", "ash", "out"):
+        rounded = {"bf16_all": ("z", "ylat", "ash", "out"), "output": ("out",),
+                   "none": ()}[rounding]
+        if name in rounded:
             # both sides round the same binary64 value; only a sum-order
             # difference of ~1e-16 could move a value across a rounding edge
             diff = got[name] != ref[name]
             assert diff.mean() < 1e-3, name
         else:
             assert rel_l2(got[name], ref[name]) < 1e-12, name
+
+
+def test_output_policy_rounds_only_the_output():
+    layer = synth.make_layer(small_recipe(), 17)
+    x = synth.make_tokens(layer.dims, 17, 3)
+    got = oracle.moe_step(layer, x, rounding="output", want="all")
+    exact = oracle.moe_step(layer, x, rounding="none", want="all")
+    for name in ("z", "act", "ylat", "ash", "sh", "up"):
+        np.testing.assert_array_equal(got[name], exact[name])
+    np.testing.assert_array_equal(got["out"], bf16_round_bruteforce(exact["out"]))
+    np.testing.assert_array_equal(got["out"], bf16_round_bruteforce(got["up"] + got["sh"]))
 
 
 def test_zero_gate_weights_leave_only_the_shared_expert():
@@ -342,7 +358,7 @@ def test_unit_codes_reduce_experts_to_matmul():
     layer.w13_s[:] = 125
     layer.w2_s[:] = 126
     x = synth.make_tokens(d, 10, 1)
-    got = oracle.moe_step(layer, x, mirror=False, want="all")
+    got = oracle.moe_step(layer, x, rounding="none", want="all")
 
     def signs(q):
         lo, hi = q & 0xF, q >> 4
@@ -364,7 +380,7 @@ def test_unit_codes_reduce_experts_to_matmul():
 def test_k_equal_E_is_a_dense_weighted_moe():
     layer = synth.make_layer(small_recipe(E=4, k=4), 11)
     x = synth.make_tokens(layer.dims, 11, 2)
-    got = oracle.moe_step(layer, x, mirror=False, want="all")
+    got = oracle.moe_step(layer, x, rounding="none", want="all")
     np.testing.assert_array_equal(got["idx"], np.tile(np.arange(4), (2, 1)))
     np.testing.assert_allclose(got["weight"], got["score"] / got["score"].sum(1, keepdims=True),
                                rtol=1e-14)
@@ -377,7 +393,7 @@ def test_identity_latent_projections_give_a_plain_moe():
     layer.lat_down[:] = eye
     layer.lat_up[:] = eye
     x = synth.make_tokens(layer.dims, 12, 2)
-    got = oracle.moe_step(layer, x, mirror=False, want="all")
+    got = oracle.moe_step(layer, x, rounding="none", want="all")
     np.testing.assert_array_equal(got["z"], bf16_f64(x))
     np.testing.assert_allclose(got["out"], got["ylat"] + got["sh"], rtol=1e-15)
 
