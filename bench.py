@@ -1,0 +1,275 @@
+#!/usr/bin/env python3
+"""Benchmark of the sparse latent-MoE decode step on one MI355X.
+
+One step = one pass of the whole layer (router + top-k, latent-down, MXFP4
+experts, combine, shared expert, latent-up) over one batch of synthetic
+tokens, replayed from a HIP graph.  Inputs rotate through R pre-generated
+batches (different routing each step) that are resident in HBM before the
+timed region starts.
+
+Prints ONE JSON line:
+  value        whole-step algorithmic HBM bytes / time (GB/s)
+  ms_per_step  time per layer step (graph replays, K steps between two
+               synchronisations)
+  roofline     the kernel with the largest time, its algorithmic bytes per
+               launch over its average duration (HIP events on the step's
+               stream, recorded inside the replayed graphs), against 8 TB/s
+  cpu_baseline the binary64 CPU oracle on a bounded sample of the same inputs
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE decode layer µs/step + achieved HBM GB/s (% peak) at batch 1/8/64"
+HBM_PEAK_GBS = 8000.0
+
+# name -> (layer recipe, batch, top_k, description)
+WORKLOADS = {
+    "k3_b1": ("k3", 1, 16, "K3-scale layer, batch 1: hidden 7168, latent 2048, 896 MXFP4 "
+              "experts (SwiGLU 2048->2048->2048), top-16, bias N(0,0.1), shared expert 4096"),
+    "k3_zipf_b8": ("k3_zipf", 8, 16, "K3-scale layer, batch 8, Zipf(1.1) expert popularity"),
+    "k3_flat_b64": ("k3_flat", 64, 16, "K3-scale layer, batch 64, near-uniform routing"),
+    "k3_b64": ("k3", 64, 16, "K3-scale layer, batch 64, bias N(0,0.1)"),
+    "k3_tp8_b1": ("k3_tp8", 1, 16, "one TP8 rank's share of the K3 layer, batch 1"),
+    "tiny_b1": ("tiny", 1, 4, "64-expert layer, batch 1"),
+}
+KERNELS_BF16 = ("dense_in", "w13", "w2", "out")
+KERNEL_SYMBOLS = {"dense_in": "k_dense_in", "w13": "k_w13", "w2": "k_w2", "out": "k_out",
+                  "router_f32": "k_router_f32"}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_bytes(d, B, k, D):
+    """Algorithmic HBM bytes of each kernel of one step: weights read once
+    (experts: only the D distinct active ones), activations in and out in the
+    precision they are stored in (bf16 x/out, hi+lo bf16 intermediates, f32
+    scores/keys/weights, i32 ids)."""
+    H, L, E, I, Is = d.hidden, d.latent, d.n_experts, d.expert_inter, d.shared_inter
+    P = B * k
+    router = E * H * (4 if d.router_f32 else 2)
+    expert13 = 2 * I * (L // 2 + L // 32)
+    expert2 = L * (I // 2 + I // 32)
+    b = {
+        "dense_in": (0 if d.router_f32 else router) + L * H * 2 + 2 * Is * H * 2 + B * H * 2
+        + B * L * 4 + B * Is * 4 + (0 if d.router_f32 else B * E * 8 + P * 8),
+        "w13": D * expert13 + B * L * 4 + P * I * 4,
+        "w2": D * expert2 + P * I * 4 + B * L * 4,
+        "out": H * L * 2 + H * Is * 2 + B * L * 4 + B * Is * 4 + B * H * 2,
+    }
+    if d.router_f32:
+        b["router_f32"] = router + B * H * 2 + B * E * 8 + P * 8
+    return b
+
+
+def source_digest():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "sparse_moe_decode_router_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel, workload):
+    """HBM bytes per launch measured with rocprofv3 counters for this kernel
+    source, from profiles/traffic.json; None when absent or stale."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    e = t.get(workload, {}).get(kernel)
+    if not e or e.get("source_digest") != source_digest():
+        return None
+    return e.get("bytes_per_launch")
+
+
+def cpu_baseline(layer, xs, k, bytes_per_step, seconds):
+    """The oracle as it stands, single-threaded, on whole steps of the same
+    inputs until about `seconds` of work has been done."""
+    import oracle
+    oracle.lib()
+    done, t_total = 0, 0.0
+    for x in xs:
+        t0 = time.perf_counter()
+        oracle.moe_step(layer, x, rounding="output")
+        t_total += time.perf_counter() - t0
+        done += 1
+        if t_total >= seconds:
+            break
+    per_step = t_total / done
+    return {"value": bytes_per_step / per_step / 1e9, "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{done} of the {len(xs)} rotating input batches, whole steps "
+                      f"(batch {xs[0].shape[0]}), {per_step:.3f} s per step single-threaded"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="k3_b1", choices=sorted(WORKLOADS))
+    ap.add_argument("--rotate", type=int, default=8, help="distinct input batches cycled")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures the decode step on one GPU only; multi-GPU runs "
+              f"(--gpus {args.gpus}, WORLD_SIZE {world}) are not part of this build.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from sparse_moe_decode_router_amd import binding, synth
+
+    recipe_name, B, k, desc = WORKLOADS[args.workload]
+    recipe = synth.RECIPES[recipe_name]
+    d = recipe.dims
+    seed = synth.TP8_STACK_SEED0 if recipe_name == "k3_tp8" else 0
+    log(f"[bench] generating {args.workload} layer (seed {seed})")
+    t0 = time.time()
+    layer = synth.make_layer(recipe, seed)
+    log(f"[bench] generated in {time.time() - t0:.1f} s; copying to the GPU")
+    torch.cuda.set_device(0)
+    dev = binding.DeviceLayer(layer)
+    ctx = binding.MoEDecode(dev, B, k)
+    R = args.rotate
+    xs = [synth.make_tokens(d, seed, B, draw=r) for r in range(R)]
+    xd = [torch.from_numpy(x.view(np.int16)).cuda() for x in xs]
+    out = torch.empty((B, d.hidden), dtype=torch.int16, device="cuda")
+    idx = torch.empty((B, k), dtype=torch.int32, device="cuda")
+    wts = torch.empty((B, k), dtype=torch.float32, device="cuda")
+
+    # Distinct experts each input actually selects on the GPU.
+    Ds = []
+    for r in range(R):
+        ctx.step(xd[r], k, out, idx, wts)
+        torch.cuda.synchronize()
+        Ds.append(int(np.unique(idx.cpu().numpy()).size))
+    disp = ctx.last_dispatch()
+    names = (("router_f32",) if d.router_f32 else ()) + KERNELS_BF16
+    kb = [kernel_bytes(d, B, k, D) for D in Ds]
+    step_bytes = [sum(b.values()) for b in kb]
+    log(f"[bench] distinct experts per input {Ds}; dispatch {disp}")
+
+    stream = torch.cuda.Stream()
+    graphs = [binding.Graph([ctx], [xd[r]], B, k, [out], [idx], [wts]) for r in range(R)]
+
+    # Pass A: the timed region (graph replays, no timing nodes).
+    for i in range(args.warmup):
+        graphs[i % R].launch(stream)
+    torch.cuda.synchronize()
+    log(f"[bench] timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        graphs[i % R].launch(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = (t1 - t0) * 1e3 / args.steps
+    mean_bytes = sum(step_bytes[i % R] for i in range(args.steps)) / args.steps
+    value = mean_bytes / (ms * 1e-3) / 1e9
+
+    # Pass B: the same replays with HIP events between the kernels, recorded on
+    # the step's stream inside each graph; per-kernel averages over K steps.
+    evs = []
+    for r in range(R):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+        for x in e:
+            x.record(stream)
+        evs.append(e)
+    torch.cuda.synchronize()
+    tgraphs = []
+    for r in range(R):
+        ctx.set_timing_events(evs[r])
+        tgraphs.append(binding.Graph([ctx], [xd[r]], B, k, [out], [idx], [wts]))
+    ctx.set_timing_events(None)
+    for i in range(args.warmup):
+        tgraphs[i % R].launch(stream)
+    torch.cuda.synchronize()
+    sums = {n: 0.0 for n in names}
+    kbytes = {n: 0.0 for n in names}
+    pending = [None] * R
+
+    def collect(r):
+        e = evs[r]
+        e[-1].synchronize()
+        for j, n in enumerate(names):
+            sums[n] += e[j].elapsed_time(e[j + 1])
+            kbytes[n] += kb[r][n]
+
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        r = i % R
+        if pending[r] is not None:
+            collect(r)
+        tgraphs[r].launch(stream)
+        pending[r] = i
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for r in range(R):
+        if pending[r] is not None:
+            collect(r)
+    ms_events_pass = (t1 - t0) * 1e3 / args.steps
+    per_kernel = {}
+    for n in names:
+        avg_ms = sums[n] / args.steps
+        avg_bytes = kbytes[n] / args.steps
+        gbs = avg_bytes / (avg_ms * 1e-3) / 1e9
+        per_kernel[n] = {"symbol": KERNEL_SYMBOLS[n], "us": round(avg_ms * 1e3, 2),
+                         "bytes": int(avg_bytes), "gbs": round(gbs, 1),
+                         "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    dom = max(names, key=lambda n: per_kernel[n]["us"])
+    pk = per_kernel[dom]
+    ex_us = per_kernel["w13"]["us"] + per_kernel["w2"]["us"]
+    ex_bytes = per_kernel["w13"]["bytes"] + per_kernel["w2"]["bytes"]
+    ex_gbs = ex_bytes / (ex_us * 1e-6) / 1e9
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a bounded sample")
+        cpu = cpu_baseline(layer, xs, k, float(np.mean(step_bytes)), args.cpu_seconds)
+
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{args.workload}: {desc}", "batch": B, "top_k": k,
+                   "hidden": d.hidden, "latent": d.latent, "experts": d.n_experts,
+                   "expert_inter": d.expert_inter, "shared_inter": d.shared_inter,
+                   "weights": "MXFP4 experts, bf16 dense", "rotating_inputs": R,
+                   "parallelism": "1 GPU"},
+        "us_per_step": round(ms * 1e3, 2),
+        "tokens_per_s": round(B / (ms * 1e-3), 1),
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "distinct_experts": Ds,
+        "expert_path": {"us": round(ex_us, 2), "gbs": round(ex_gbs, 1),
+                        "pct_hbm_peak": round(100 * ex_gbs / HBM_PEAK_GBS, 2)},
+        "kernels": per_kernel,
+        "ms_per_step_events_pass": round(ms_events_pass, 5),
+        "roofline": {"bound": "hbm", "kernel": pk["symbol"], "achieved": pk["gbs"],
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": pk["frac"],
+                     "traffic": load_traffic(pk["symbol"], args.workload)},
+        "cpu_baseline": cpu,
+        "dispatch": disp,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,174 @@
+// device_common.h - gfx950 device helpers shared by the decode-step kernels:
+// vector types, bf16 rounding and hi/lo splitting, MXFP4 -> bf16 conversion
+// with the E8M0 block scale, the 16x16x32 bf16 MFMA, wave reductions and the
+// agent-scope arrival counters used for split-K fix-ups.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+constexpr int kWavesPerBlock = 4;
+constexpr int kBlock = kWave * kWavesPerBlock;
+constexpr int kKStep = 128;      // K elements one lane group covers per step (4 x 32)
+constexpr int kMaxExperts = 2048;
+constexpr int kMaxBatch = 64;
+constexpr int kMaxTopK = 64;
+constexpr int kKeysPerLane = kMaxExperts / kWave;
+constexpr int kMaxStepsPerChunk = 8;
+
+// Global counter slots (u32) at the head of the workspace.
+enum { G_ROUTER_DONE = 0, G_NEXT_TOKEN = 1, G_TOKENS_DONE = 2, G_COUNT = 64 };
+// Routing metadata header (i32).
+enum { M_N_ACTIVE = 0, M_N_COLS = 1, M_COUNT = 16 };
+
+__device__ __forceinline__ int lane_id() {
+    return (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+}
+
+__device__ __forceinline__ uint32_t uniform(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// f32 -> bf16 bit pattern, round to nearest, ties to even (finite inputs).
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+__device__ __forceinline__ float bf16_val(uint32_t h) { return __uint_as_float(h << 16); }
+
+// v ~= hi + lo with hi = bf16(v), lo = bf16(v - hi); the residual of the pair
+// is below 2^-17 |v|.
+__device__ __forceinline__ void split_hl(float v, uint32_t &hi, uint32_t &lo) {
+    hi = bf16_rne(v);
+    lo = bf16_rne(v - bf16_val(hi));
+}
+
+// Writes four values as hi and lo bf16 halves (8 bytes each).
+__device__ __forceinline__ void store_hl4(uint16_t *hi, uint16_t *lo, f32x4 v) {
+    uint32_t h[4], l[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) split_hl(v[i], h[i], l[i]);
+    *(u32x2 *)hi = (u32x2){h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+    *(u32x2 *)lo = (u32x2){l[0] | (l[1] << 16), l[2] | (l[3] << 16)};
+}
+
+// E8M0 byte -> f32 scale 2^(byte-127) (bytes 1..254).
+__device__ __forceinline__ float e8m0_scale(uint32_t byte) { return __uint_as_float(byte << 23); }
+
+// Eight E2M1 codes (one dword, element 2j in the low nibble of byte j) times
+// a power-of-two scale -> eight bf16, exactly.
+__device__ __forceinline__ bf16x8 fp4x8_to_bf16(uint32_t codes, float scale) {
+    bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 0);
+    bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 1);
+    bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 2);
+    bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 3);
+    return (bf16x8){p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// D(16x16, f32) += A(16x32) B(32x16).  Lane l supplies A row l%16 and B
+// column l%16, eight K values each (lane group l/16 picks which eight); it
+// receives D rows 4*(l/16)+0..3 of column l%16.
+__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 zero4() { return (f32x4){0.f, 0.f, 0.f, 0.f}; }
+
+// Adds the value of the neighbouring column (lane ^ 1): joins the hi and lo
+// column of one token.
+__device__ __forceinline__ f32x4 add_pair_column(f32x4 v) {
+    f32x4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = v[i] + __shfl_xor(v[i], 1);
+    return r;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+    return v;
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+        uint64_t o = __shfl_xor(v, m);
+        v = o > v ? o : v;
+    }
+    return v;
+}
+
+// Exclusive prefix sum over the wave; *total receives the sum of all lanes.
+__device__ __forceinline__ int wave_excl_scan(int v, int *total) {
+    const int lane = lane_id();
+    int inc = v;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        int o = __shfl_up(inc, d);
+        if (lane >= d) inc += o;
+    }
+    *total = __shfl(inc, kWave - 1);
+    return inc - v;
+}
+
+__device__ __forceinline__ void wave_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+}
+
+// One arrival of the whole wave on an agent-scope counter.  Every lane's
+// earlier global stores are released before the increment; the old value is
+// returned to every lane.  The caller issues acquire_agent() before reading
+// what other arrivals wrote.
+__device__ __forceinline__ uint32_t wave_arrive(uint32_t *ctr) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    uint32_t old = 0;
+    if (lane_id() == 0) old = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return uniform(old);
+}
+
+__device__ __forceinline__ void acquire_agent() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
+
+__device__ __forceinline__ uint32_t wave_load_counter(uint32_t *ctr) {
+    uint32_t v = 0;
+    if (lane_id() == 0) v = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return uniform(v);
+}
+
+__device__ __forceinline__ uint32_t wave_fetch_add(uint32_t *ctr, uint32_t v) {
+    uint32_t old = 0;
+    if (lane_id() == 0) old = __hip_atomic_fetch_add(ctr, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return uniform(old);
+}
+
+__device__ __forceinline__ void wave_store_counter(uint32_t *ctr, uint32_t v) {
+    if (lane_id() == 0) __hip_atomic_store(ctr, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Weight streams are read once per step and never written by the step, so
+// they may use non-temporal loads.  Everything the step itself produces is
+// read with ordinary loads after an acquire.
+__device__ __forceinline__ u32x4 ld_weight16(const void *p) {
+    return __builtin_nontemporal_load((const u32x4 *)p);
+}
+__device__ __forceinline__ uint32_t ld_weight4(const void *p) {
+    return __builtin_nontemporal_load((const uint32_t *)p);
+}
+__device__ __forceinline__ u32x4 ld16(const void *p) { return *(const u32x4 *)p; }
+__device__ __forceinline__ f32x4 ldf4(const float *p) { return *(const f32x4 *)p; }
+__device__ __forceinline__ void stf4(float *p, f32x4 v) { *(f32x4 *)p = v; }
+
+__device__ __forceinline__ float sigmoidf_(float t) { return 1.0f / (1.0f + expf(-t)); }
+__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
+
+}  // namespace moe

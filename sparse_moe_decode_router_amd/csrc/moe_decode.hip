@@ -1,0 +1,512 @@
+// moe_decode.hip - host side of the decode-step library: configuration checks,
+// workspace carving, the batch-dependent launch plan and the C ABI declared in
+// include/moe_decode.h.  The kernels live in kernels.h.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "kernels.h"
+#include "moe_decode.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
+int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+// Split of a K range of `nsteps` 128-element steps into equal chunks of
+// `spc` steps (a divisor of nsteps, at most kMaxStepsPerChunk) so that
+// `units_per_split` x splits reaches about `target` wave units.
+struct Split {
+    int s, spc;
+};
+Split choose_split(int units_per_split, int nsteps, int target) {
+    const long long want = std::max<long long>(1, (long long)nsteps * units_per_split / target);
+    int spc = 1;
+    for (int d = 1; d <= std::min(nsteps, kMaxStepsPerChunk); ++d)
+        if (nsteps % d == 0 && d <= want) spc = d;
+    return Split{nsteps / spc, spc};
+}
+
+int units_target() {
+    const char *s = std::getenv("MOE_DECODE_UNITS_TARGET");  // tuning sweeps only
+    int v = s ? std::atoi(s) : 0;
+    return v > 0 ? v : 4096;
+}
+
+int ncols_cap(int E, int B, int k) { return std::min(E, B * k) + cdiv(B * k, 8); }
+
+struct Plan {
+    int n_r2, ncg_in, ncg_out;
+    Split in, out, w13, w2;
+};
+
+Plan make_plan(const moe_decode_config &c, int B, int k) {
+    const int target = units_target();
+    Plan p;
+    p.n_r2 = c.router_dtype == MOE_ROUTER_BF16 ? c.n_experts / 32 : 0;
+    p.ncg_in = cdiv(B, 16);
+    p.ncg_out = cdiv(B, 8);
+    const int n_t2_in = p.n_r2 + c.latent / 32 + c.shared_inter / 16;
+    p.in = choose_split(n_t2_in * p.ncg_in, c.hidden / kKStep, target);
+    p.out = choose_split((c.hidden / 32) * p.ncg_out, (c.latent + c.shared_inter) / kKStep, target);
+    const int cols = std::min(c.n_experts, B * k);  // typical column units
+    p.w13 = choose_split(cols * (c.expert_inter / 16), c.latent / kKStep, target);
+    p.w2 = choose_split(cols * (c.latent / 32), c.expert_inter / kKStep, target);
+    return p;
+}
+
+struct Layout {
+    size_t gctr, meta, ctr_in, ctr_out, ctr13, ctr2, score, key, idx, wsel, act_expert, act_off,
+        cu_expert, cu_p0, cu_n, pair_slot, pair_of_slot, z_hi, z_lo, ash_hi, ash_lo, act_hi,
+        act_lo, ylat_hi, ylat_lo, part_in, part_out, part13, ypart, total;
+    size_t counters_end;  // [0, counters_end) holds every counter: cleared at init
+};
+
+Layout make_layout(const moe_decode_config &c) {
+    const size_t Bm = c.max_batch, km = c.max_top_k, E = c.n_experts, L = c.latent,
+                 I = c.expert_inter, Is = c.shared_inter, H = c.hidden;
+    const size_t P = Bm * km;
+    const size_t n_t2_in = (c.router_dtype == MOE_ROUTER_BF16 ? E / 32 : 0) + L / 32 + Is / 16;
+    const size_t n_t2_out = H / 32;
+    const size_t ncols = (size_t)ncols_cap((int)E, (int)Bm, (int)km);
+    // Largest split any batch / top-k can use, times the pairs it serves.
+    size_t s_in = 1, s_out = 1, p13 = 1, p2 = 1;
+    for (int B = 1; B <= (int)Bm; ++B) {
+        for (int k = 1; k <= (int)km; ++k) {
+            const Plan pl = make_plan(c, B, k);
+            s_in = std::max(s_in, (size_t)pl.in.s);
+            s_out = std::max(s_out, (size_t)pl.out.s);
+            p13 = std::max(p13, (size_t)B * k * pl.w13.s);
+            p2 = std::max(p2, (size_t)B * k * pl.w2.s);
+        }
+    }
+    Layout l;
+    size_t o = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = o;
+        o = align_up(o + bytes);
+        return at;
+    };
+    l.gctr = take(G_COUNT * 4);
+    l.meta = take(M_COUNT * 4);
+    l.ctr_in = take(n_t2_in * (size_t)cdiv((int)Bm, 16) * 4);
+    l.ctr_out = take(n_t2_out * (size_t)cdiv((int)Bm, 8) * 4);
+    l.ctr13 = take(ncols * (I / 16) * 4);
+    l.ctr2 = take((L / 32) * 4);
+    l.counters_end = o;
+    l.score = take(Bm * E * 4);
+    l.key = take(Bm * E * 4);
+    l.idx = take(P * 4);
+    l.wsel = take(P * 4);
+    l.act_expert = take((std::min(E, P) + 1) * 4);
+    l.act_off = take((std::min(E, P) + 1) * 4);
+    l.cu_expert = take(ncols * 4);
+    l.cu_p0 = take(ncols * 4);
+    l.cu_n = take(ncols * 4);
+    l.pair_slot = take(P * 4);
+    l.pair_of_slot = take(P * 4);
+    l.z_hi = take(Bm * L * 2);
+    l.z_lo = take(Bm * L * 2);
+    l.ash_hi = take(Bm * Is * 2);
+    l.ash_lo = take(Bm * Is * 2);
+    l.act_hi = take(P * I * 2);
+    l.act_lo = take(P * I * 2);
+    l.ylat_hi = take(Bm * L * 2);
+    l.ylat_lo = take(Bm * L * 2);
+    l.part_in = take(n_t2_in * s_in * Bm * 32 * 4);
+    l.part_out = take(n_t2_out * s_out * Bm * 32 * 4);
+    l.part13 = take(p13 * (I / 16) * 32 * 4);
+    l.ypart = take(p2 * L * 4);
+    l.total = o;
+    return l;
+}
+
+typedef void (*StepKernel)(const StepArgs);
+#define MOE_SPC_TABLE(K) {nullptr, K<1>, K<2>, K<3>, K<4>, K<5>, K<6>, K<7>, K<8>}
+const StepKernel kDenseIn[] = MOE_SPC_TABLE(k_dense_in);
+const StepKernel kW13[] = MOE_SPC_TABLE(k_w13);
+const StepKernel kW2[] = MOE_SPC_TABLE(k_w2);
+const StepKernel kOut[] = MOE_SPC_TABLE(k_out);
+#undef MOE_SPC_TABLE
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+}  // namespace
+
+struct moe_decode_ctx {
+    moe_decode_config cfg;
+    moe_decode_weights w;
+    char *ws;
+    size_t ws_bytes;
+    Layout lay;
+    int device;
+    int32_t last_hip;
+    moe_decode_dispatch_info last;
+    hipEvent_t events[8];  // timing events (caller-owned), n_events = 0: off
+    int32_t n_events;
+};
+
+struct moe_decode_graph {
+    hipGraph_t graph;
+    hipGraphExec_t exec;
+};
+
+namespace {
+
+moe_status hip_fail(moe_decode_ctx *ctx, hipError_t e) {
+    if (ctx) ctx->last_hip = (int32_t)e;
+    return MOE_ERR_HIP;
+}
+
+StepArgs base_args(const moe_decode_ctx *ctx) {
+    const moe_decode_config &c = ctx->cfg;
+    const Layout &l = ctx->lay;
+    char *ws = ctx->ws;
+    StepArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.H = c.hidden;
+    a.L = c.latent;
+    a.E = c.n_experts;
+    a.I = c.expert_inter;
+    a.Is = c.shared_inter;
+    a.Bm = c.max_batch;
+    a.km = c.max_top_k;
+    a.ncg_in_cap = cdiv(c.max_batch, 16);
+    a.ncg_out_cap = cdiv(c.max_batch, 8);
+    a.ncols_cap = ncols_cap(c.n_experts, c.max_batch, c.max_top_k);
+    const moe_decode_weights &w = ctx->w;
+    if (c.router_dtype == MOE_ROUTER_BF16)
+        a.router_w = (const uint16_t *)w.router_w;
+    else
+        a.router_w32 = (const float *)w.router_w;
+    a.bias = w.router_bias;
+    a.lat_down = w.lat_down;
+    a.lat_up = w.lat_up;
+    a.w13_q = w.w13_q;
+    a.w13_s = w.w13_s;
+    a.w2_q = w.w2_q;
+    a.w2_s = w.w2_s;
+    a.sh_w13 = w.sh_w13;
+    a.sh_w2 = w.sh_w2;
+    a.gctr = (uint32_t *)(ws + l.gctr);
+    a.meta = (int32_t *)(ws + l.meta);
+    a.ctr_in = (uint32_t *)(ws + l.ctr_in);
+    a.ctr_out = (uint32_t *)(ws + l.ctr_out);
+    a.ctr13 = (uint32_t *)(ws + l.ctr13);
+    a.ctr2 = (uint32_t *)(ws + l.ctr2);
+    a.score = (float *)(ws + l.score);
+    a.key = (float *)(ws + l.key);
+    a.idx = (int32_t *)(ws + l.idx);
+    a.wsel = (float *)(ws + l.wsel);
+    a.act_expert = (int32_t *)(ws + l.act_expert);
+    a.act_off = (int32_t *)(ws + l.act_off);
+    a.cu_expert = (int32_t *)(ws + l.cu_expert);
+    a.cu_p0 = (int32_t *)(ws + l.cu_p0);
+    a.cu_n = (int32_t *)(ws + l.cu_n);
+    a.pair_slot = (int32_t *)(ws + l.pair_slot);
+    a.pair_of_slot = (int32_t *)(ws + l.pair_of_slot);
+    a.z_hi = (uint16_t *)(ws + l.z_hi);
+    a.z_lo = (uint16_t *)(ws + l.z_lo);
+    a.ash_hi = (uint16_t *)(ws + l.ash_hi);
+    a.ash_lo = (uint16_t *)(ws + l.ash_lo);
+    a.act_hi = (uint16_t *)(ws + l.act_hi);
+    a.act_lo = (uint16_t *)(ws + l.act_lo);
+    a.ylat_hi = (uint16_t *)(ws + l.ylat_hi);
+    a.ylat_lo = (uint16_t *)(ws + l.ylat_lo);
+    a.part_in = (float *)(ws + l.part_in);
+    a.part_out = (float *)(ws + l.part_out);
+    a.part13 = (float *)(ws + l.part13);
+    a.ypart = (float *)(ws + l.ypart);
+    return a;
+}
+
+int grid_for(long long units, long long cap_blocks) {
+    long long blocks = (units + kWavesPerBlock - 1) / kWavesPerBlock;
+    return (int)std::max(1LL, std::min(blocks, cap_blocks));
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_decode_validate_config(const moe_decode_config *c) {
+    if (!c) return MOE_ERR_INVALID_ARG;
+    if (c->hidden <= 0 || c->latent <= 0 || c->n_experts <= 0 || c->expert_inter <= 0 ||
+        c->shared_inter <= 0 || c->max_batch <= 0 || c->max_top_k <= 0)
+        return MOE_ERR_INVALID_ARG;
+    if (c->router_dtype != MOE_ROUTER_BF16 && c->router_dtype != MOE_ROUTER_F32)
+        return MOE_ERR_INVALID_ARG;
+    if (c->max_top_k > c->n_experts) return MOE_ERR_INVALID_ARG;
+    if (c->max_batch > kMaxBatch || c->max_top_k > kMaxTopK) return MOE_ERR_UNSUPPORTED;
+    if (c->hidden % kKStep || c->latent % kKStep || c->expert_inter % kKStep ||
+        c->shared_inter % kKStep)
+        return MOE_ERR_UNSUPPORTED;
+    if (c->n_experts % 32 || c->n_experts > kMaxExperts) return MOE_ERR_UNSUPPORTED;
+    // Offsets are formed in 32-bit ints where they index one token or pair.
+    if ((long long)c->hidden * c->shared_inter > (1LL << 31) ||
+        (long long)c->n_experts * 2 * c->expert_inter > (1LL << 31))
+        return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+size_t moe_decode_workspace_size(const moe_decode_config *c) {
+    if (moe_decode_validate_config(c) != MOE_OK) return 0;
+    return make_layout(*c).total;
+}
+
+const char *moe_decode_status_string(moe_status s) {
+    switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported shape or device";
+    case MOE_ERR_HIP: return "HIP runtime error";
+    case MOE_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
+    }
+    return "unknown status";
+}
+
+int32_t moe_decode_last_hip_error(const moe_decode_ctx *ctx) { return ctx ? ctx->last_hip : 0; }
+
+moe_status moe_decode_init(const moe_decode_config *cfg, const moe_decode_weights *w,
+                           void *workspace, size_t workspace_bytes, moe_decode_ctx **out) {
+    if (!out) return MOE_ERR_INVALID_ARG;
+    *out = nullptr;
+    moe_status st = moe_decode_validate_config(cfg);
+    if (st != MOE_OK) return st;
+    if (!w) return MOE_ERR_INVALID_ARG;
+    const void *req[] = {w->router_w, w->lat_down, w->lat_up, w->w13_q, w->w13_s,
+                         w->w2_q,     w->w2_s,     w->sh_w13, w->sh_w2};
+    for (const void *p : req)
+        if (!p || !aligned16(p)) return MOE_ERR_INVALID_ARG;
+    if (w->router_bias && !aligned16(w->router_bias)) return MOE_ERR_INVALID_ARG;
+    const Layout lay = make_layout(*cfg);
+    if (!workspace || ((uintptr_t)workspace & (kAlign - 1)) || workspace_bytes < lay.total)
+        return MOE_ERR_WORKSPACE;
+
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return MOE_ERR_UNSUPPORTED;
+
+    moe_decode_ctx *ctx = new (std::nothrow) moe_decode_ctx();
+    if (!ctx) return MOE_ERR_HIP;
+    ctx->cfg = *cfg;
+    ctx->w = *w;
+    ctx->ws = (char *)workspace;
+    ctx->ws_bytes = workspace_bytes;
+    ctx->lay = lay;
+    ctx->device = dev;
+    ctx->last_hip = 0;
+    ctx->n_events = 0;
+    std::memset(&ctx->last, 0, sizeof ctx->last);
+
+    // Every counter starts at zero; the step returns them to zero itself.
+    const size_t nwords = lay.counters_end / 4;
+    hipLaunchKernelGGL(k_fill_u32, dim3(std::min<size_t>(1024, (nwords + 255) / 256)), dim3(256),
+                       0, nullptr, (uint32_t *)ctx->ws, nwords, 0u);
+    e = hipGetLastError();
+    if (e == hipSuccess) e = hipStreamSynchronize(nullptr);
+    if (e != hipSuccess) {
+        delete ctx;
+        return MOE_ERR_HIP;
+    }
+    *out = ctx;
+    return MOE_OK;
+}
+
+moe_status moe_decode_step(moe_decode_ctx *ctx, const uint16_t *x, int32_t batch, int32_t top_k,
+                           uint16_t *out, int32_t *topk_idx, float *topk_w, moe_stream_t stream) {
+    if (!ctx || !x || !out) return MOE_ERR_INVALID_ARG;
+    const moe_decode_config &c = ctx->cfg;
+    if (batch < 1 || batch > c.max_batch || top_k < 1 || top_k > c.max_top_k)
+        return MOE_ERR_INVALID_ARG;
+    if (!aligned16(x) || ((uintptr_t)out & 7u) || ((uintptr_t)topk_idx & 3u) ||
+        ((uintptr_t)topk_w & 3u))
+        return MOE_ERR_INVALID_ARG;
+    hipStream_t s = (hipStream_t)stream;
+    const Plan pl = make_plan(c, batch, top_k);
+    StepArgs a = base_args(ctx);
+    a.B = batch;
+    a.k = top_k;
+    a.x = x;
+    a.out = out;
+    a.user_idx = topk_idx;
+    a.user_w = topk_w;
+    a.n_r2 = pl.n_r2;
+    a.router_target = c.router_dtype == MOE_ROUTER_BF16 ? pl.n_r2 * pl.ncg_in : c.n_experts;
+    a.s_in = pl.in.s;
+    a.spc_in = pl.in.spc;
+    a.s_out = pl.out.s;
+    a.spc_out = pl.out.spc;
+    a.s13 = pl.w13.s;
+    a.spc13 = pl.w13.spc;
+    a.s2 = pl.w2.s;
+    a.spc2 = pl.w2.spc;
+
+    const int n_t2_in = pl.n_r2 + c.latent / 32 + c.shared_inter / 16;
+    const long long units_in = (long long)n_t2_in * pl.ncg_in * pl.in.s;
+    const long long units_out = (long long)(c.hidden / 32) * pl.ncg_out * pl.out.s;
+    const long long cols = ncols_cap(c.n_experts, batch, top_k);
+    const long long units_13 = cols * (c.expert_inter / 16) * pl.w13.s;
+    const long long units_2 = cols * (c.latent / 32) * pl.w2.s;
+    const long long cap = 8192;  // blocks; larger grids loop over their units
+
+    moe_decode_dispatch_info &d = ctx->last;
+    d.batch = batch;
+    d.top_k = top_k;
+    d.col_tiles = pl.ncg_in;
+    d.split_in = pl.in.s;
+    d.split_out = pl.out.s;
+    d.split_w13 = pl.w13.s;
+    d.split_w2 = pl.w2.s;
+    d.grid_in = grid_for(units_in, cap);
+    d.grid_w13 = grid_for(units_13, cap);
+    d.grid_w2 = grid_for(units_2, cap);
+    d.grid_out = grid_for(units_out, cap);
+    d.router_f32 = c.router_dtype == MOE_ROUTER_F32;
+    d.n_kernels = 4 + d.router_f32;
+
+    const bool timed = ctx->n_events == d.n_kernels + 1;
+    int ev = 0;
+    auto mark = [&]() {
+        if (timed) (void)hipEventRecord(ctx->events[ev++], s);
+    };
+    mark();
+    if (d.router_f32) {
+        hipLaunchKernelGGL(k_router_f32, dim3(grid_for(c.n_experts, cap)), dim3(kBlock), 0, s, a);
+        mark();
+    }
+    hipLaunchKernelGGL(kDenseIn[pl.in.spc], dim3(d.grid_in), dim3(kBlock), 0, s, a);
+    mark();
+    hipLaunchKernelGGL(kW13[pl.w13.spc], dim3(d.grid_w13), dim3(kBlock), 0, s, a);
+    mark();
+    hipLaunchKernelGGL(kW2[pl.w2.spc], dim3(d.grid_w2), dim3(kBlock), 0, s, a);
+    mark();
+    hipLaunchKernelGGL(kOut[pl.out.spc], dim3(d.grid_out), dim3(kBlock), 0, s, a);
+    mark();
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(ctx, e);
+    return MOE_OK;
+}
+
+moe_status moe_decode_destroy(moe_decode_ctx *ctx) {
+    if (!ctx) return MOE_ERR_INVALID_ARG;
+    delete ctx;
+    return MOE_OK;
+}
+
+moe_status moe_decode_graph_create(moe_decode_ctx *const *ctxs, int32_t n_layers,
+                                   const uint16_t *const *x, int32_t batch, int32_t top_k,
+                                   uint16_t *const *out, int32_t *const *topk_idx,
+                                   float *const *topk_w, moe_decode_graph **graph) {
+    if (!ctxs || n_layers < 1 || !x || !out || !graph) return MOE_ERR_INVALID_ARG;
+    *graph = nullptr;
+    for (int i = 0; i < n_layers; ++i) {
+        const moe_decode_ctx *c = ctxs[i];
+        if (!c || !x[i] || !out[i] || batch < 1 || batch > c->cfg.max_batch || top_k < 1 ||
+            top_k > c->cfg.max_top_k)
+            return MOE_ERR_INVALID_ARG;
+    }
+    hipStream_t cs = nullptr;
+    hipError_t e = hipStreamCreateWithFlags(&cs, hipStreamNonBlocking);
+    if (e != hipSuccess) return hip_fail(ctxs[0], e);
+    moe_status st = MOE_OK;
+    hipGraph_t g = nullptr;
+    e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
+    if (e == hipSuccess) {
+        for (int i = 0; i < n_layers && st == MOE_OK; ++i)
+            st = moe_decode_step(ctxs[i], x[i], batch, top_k, out[i],
+                                 topk_idx ? topk_idx[i] : nullptr, topk_w ? topk_w[i] : nullptr,
+                                 (moe_stream_t)cs);
+        const hipError_t e2 = hipStreamEndCapture(cs, &g);
+        if (e == hipSuccess) e = e2;
+    }
+    hipGraphExec_t ex = nullptr;
+    if (e == hipSuccess && st == MOE_OK) e = hipGraphInstantiate(&ex, g, nullptr, nullptr, 0);
+    hipStreamDestroy(cs);
+    if (st != MOE_OK || e != hipSuccess) {
+        if (g) hipGraphDestroy(g);
+        return st != MOE_OK ? st : hip_fail(ctxs[0], e);
+    }
+    moe_decode_graph *gr = new (std::nothrow) moe_decode_graph();
+    if (!gr) {
+        hipGraphExecDestroy(ex);
+        hipGraphDestroy(g);
+        return MOE_ERR_HIP;
+    }
+    gr->graph = g;
+    gr->exec = ex;
+    *graph = gr;
+    return MOE_OK;
+}
+
+moe_status moe_decode_graph_launch(moe_decode_graph *graph, moe_stream_t stream) {
+    if (!graph) return MOE_ERR_INVALID_ARG;
+    return hipGraphLaunch(graph->exec, (hipStream_t)stream) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+moe_status moe_decode_graph_destroy(moe_decode_graph *graph) {
+    if (!graph) return MOE_ERR_INVALID_ARG;
+    hipGraphExecDestroy(graph->exec);
+    hipGraphDestroy(graph->graph);
+    delete graph;
+    return MOE_OK;
+}
+
+moe_status moe_decode_last_dispatch(const moe_decode_ctx *ctx, moe_decode_dispatch_info *info) {
+    if (!ctx || !info) return MOE_ERR_INVALID_ARG;
+    *info = ctx->last;
+    return MOE_OK;
+}
+
+moe_status moe_decode_set_timing_events(moe_decode_ctx *ctx, void *const *events, int32_t n) {
+    if (!ctx || n < 0) return MOE_ERR_INVALID_ARG;
+    const int32_t want = 4 + (ctx->cfg.router_dtype == MOE_ROUTER_F32 ? 1 : 0) + 1;
+    if (n == 0) {
+        ctx->n_events = 0;
+        return MOE_OK;
+    }
+    if (n != want || !events) return MOE_ERR_INVALID_ARG;
+    for (int i = 0; i < n; ++i) {
+        if (!events[i]) return MOE_ERR_INVALID_ARG;
+        ctx->events[i] = (hipEvent_t)events[i];
+    }
+    ctx->n_events = n;
+    return MOE_OK;
+}
+
+moe_status moe_decode_debug_export(moe_decode_ctx *ctx, int32_t batch, int32_t top_k,
+                                   const moe_decode_debug *dbg, moe_stream_t stream) {
+    if (!ctx || !dbg || batch < 1 || batch > ctx->cfg.max_batch || top_k < 1 ||
+        top_k > ctx->cfg.max_top_k)
+        return MOE_ERR_INVALID_ARG;
+    StepArgs a = base_args(ctx);
+    a.B = batch;
+    a.k = top_k;
+    const DebugArgs d{dbg->score, dbg->key, dbg->z, dbg->act, dbg->ylat, dbg->ash, dbg->n_active};
+    hipLaunchKernelGGL(k_debug_export, dim3(256), dim3(256), 0, (hipStream_t)stream, a, d);
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? MOE_OK : hip_fail(ctx, e);
+}
+
+moe_status moe_decode_debug_dequant(const uint8_t *q, const uint8_t *s, int64_t n, float *out,
+                                    moe_stream_t stream) {
+    if (!q || !s || !out || n <= 0 || n % 32 || ((uintptr_t)q & 3u)) return MOE_ERR_INVALID_ARG;
+    const int64_t threads = n / 8;
+    hipLaunchKernelGGL(k_dequant, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
+                       (hipStream_t)stream, q, s, n, out);
+    return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,104 @@
+"""Helpers of the GPU parity tests: run the HIP path through the C ABI and
+compare it with the CPU oracle on the same seeded inputs.
+
+Acceptance (per token):
+  * selected experts: the same set as the oracle's, except at a near tie (the
+    binary64 keys of the k-th and (k+1)-th experts within TAU), where the GPU
+    may pick any equally valid set; the GPU's selection is then the one the
+    oracle is re-run with;
+  * weights: |w_gpu - w_oracle| <= 1e-5;
+  * output: relative L2 error over the batch <= 2e-3 against the oracle with
+    intermediates in binary64 and the output rounded to bf16 once.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+from sparse_moe_decode_router_amd import binding, synth
+
+TAU = 1e-5            # near-tie width on binary64 keys
+REL_L2_GATE = 2e-3    # output tolerance of the layer definition
+W_TOL = 1e-5
+
+
+def bf16_f64(bits) -> np.ndarray:
+    b = np.asarray(bits).view(np.uint16) if np.asarray(bits).dtype == np.int16 else \
+        np.asarray(bits, np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def to_dev_tokens(x: np.ndarray):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).cuda()
+
+
+def rel_l2(a, b) -> float:
+    a, b = np.asarray(a, np.float64), np.asarray(b, np.float64)
+    nb = np.linalg.norm(b)
+    return float(np.linalg.norm(a - b) / (nb if nb > 0 else 1.0))
+
+
+def oracle_keys(layer, x) -> np.ndarray:
+    """Binary64 selection keys s + bias of the oracle."""
+    _, score = oracle.router_scores(layer.dims, x, layer.router_w)
+    bias = 0.0 if layer.bias is None else layer.bias.astype(np.float64)
+    return score + bias
+
+
+def check_selection(layer, x, gpu_idx, k, tau=TAU):
+    """Asserts the GPU selection is the oracle's (or a valid near-tie
+    alternative).  Returns the number of near-tie tokens."""
+    key64 = oracle_keys(layer, x)
+    d = layer.dims
+    dims_k = synth.LayerDims(d.hidden, d.latent, d.n_experts, d.expert_inter, d.shared_inter, k,
+                             d.router_f32)
+    _, score = oracle.router_scores(layer.dims, x, layer.router_w)
+    _, o_idx, _ = oracle.select(dims_k, score, layer.bias)
+    near = 0
+    for b in range(x.shape[0]):
+        g = np.sort(gpu_idx[b])
+        assert np.all(np.diff(g) > 0), f"token {b}: repeated expert {gpu_idx[b]}"
+        assert np.array_equal(g, gpu_idx[b]), f"token {b}: ids not ascending {gpu_idx[b]}"
+        if np.array_equal(g, o_idx[b]):
+            continue
+        is_near, alts = oracle.near_tie_alternatives(key64[b], k, tau)
+        assert is_near, (f"token {b}: GPU experts {g} != oracle {o_idx[b]} without a near tie")
+        assert any(np.array_equal(g, a) for a in alts), f"token {b}: {g} not a valid tie choice"
+        near += 1
+    return near
+
+
+def with_k(layer, k):
+    """The same layer with another top-k."""
+    import dataclasses
+    return dataclasses.replace(layer, dims=dataclasses.replace(layer.dims, top_k=k))
+
+
+def check_step(layer, x, top_k, out, idx, w, sample=None, gate=REL_L2_GATE):
+    """Full parity check of one GPU step (numpy arrays from the device).
+    `sample`: token indices the oracle evaluates end to end (None = all);
+    selection is checked for every token.  Returns a dict of measured errors."""
+    B = x.shape[0]
+    near = check_selection(layer, x, idx, top_k)
+    toks = np.arange(B) if sample is None else np.asarray(sample)
+    lk = with_k(layer, top_k)
+    ref = oracle.moe_step(lk, x[toks], rounding="output", forced_idx=idx[toks],
+                          want=("idx", "weight", "out"))
+    np.testing.assert_array_equal(ref["idx"], idx[toks])
+    werr = float(np.max(np.abs(ref["weight"] - w[toks].astype(np.float64))))
+    assert werr <= W_TOL, f"weights differ by {werr}"
+    got = bf16_f64(out[toks])
+    err = rel_l2(got, ref["out"])
+    per_tok = [rel_l2(got[i], ref["out"][i]) for i in range(len(toks))]
+    assert err <= gate, f"relative L2 error {err} > {gate} (per token max {max(per_tok)})"
+    return {"rel_l2": err, "max_token_rel_l2": max(per_tok), "w_err": werr, "near_ties": near}
+
+
+def run(ctx: binding.MoEDecode, x: np.ndarray, top_k: int):
+    """One eager step; returns numpy (out uint16, idx, w)."""
+    import torch
+    xd = to_dev_tokens(x)
+    out, idx, w = ctx.step(xd, top_k)
+    torch.cuda.synchronize()
+    return (out.cpu().numpy().view(np.uint16), idx.cpu().numpy(), w.cpu().numpy())
