@@ -12,8 +12,8 @@ Prints ONE JSON line:
   ms_per_step  time per layer step (graph replays, K steps between two
                synchronisations)
   roofline     the kernel with the largest time, its algorithmic bytes per
-               launch over its average duration (HIP events on the step's
-               stream, recorded inside the replayed graphs), against 8 TB/s
+               launch over its average duration (HIP events recorded between
+               the kernels on the step's stream), against 8 TB/s
   cpu_baseline the binary64 CPU oracle on a bounded sample of the same inputs
 """
 import argparse
@@ -184,8 +184,20 @@ def main():
     mean_bytes = sum(step_bytes[i % R] for i in range(args.steps)) / args.steps
     value = mean_bytes / (ms * 1e-3) / 1e9
 
-    # Pass B: the same replays with HIP events between the kernels, recorded on
-    # the step's stream inside each graph; per-kernel averages over K steps.
+    # Eager steps (four launches each, no graph), for comparison.
+    for i in range(args.warmup):
+        ctx.step(xd[i % R], k, out, idx, wts, stream=stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ctx.step(xd[i % R], k, out, idx, wts, stream=stream)
+    torch.cuda.synchronize()
+    ms_eager = (time.perf_counter() - t0) * 1e3 / args.steps
+
+    # Pass B: per-kernel durations from HIP events recorded between the
+    # kernels on the step's stream (eager steps; event-record nodes inside a
+    # replayed graph do not time its kernels on this runtime).  R rotating
+    # event sets, each read back before it is reused.
     evs = []
     for r in range(R):
         e = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
@@ -193,17 +205,9 @@ def main():
             x.record(stream)
         evs.append(e)
     torch.cuda.synchronize()
-    tgraphs = []
-    for r in range(R):
-        ctx.set_timing_events(evs[r])
-        tgraphs.append(binding.Graph([ctx], [xd[r]], B, k, [out], [idx], [wts]))
-    ctx.set_timing_events(None)
-    for i in range(args.warmup):
-        tgraphs[i % R].launch(stream)
-    torch.cuda.synchronize()
     sums = {n: 0.0 for n in names}
     kbytes = {n: 0.0 for n in names}
-    pending = [None] * R
+    pending = [False] * R
 
     def collect(r):
         e = evs[r]
@@ -215,14 +219,16 @@ def main():
     t0 = time.perf_counter()
     for i in range(args.steps):
         r = i % R
-        if pending[r] is not None:
+        if pending[r]:
             collect(r)
-        tgraphs[r].launch(stream)
-        pending[r] = i
+        ctx.set_timing_events(evs[r])
+        ctx.step(xd[r], k, out, idx, wts, stream=stream)
+        pending[r] = True
+    ctx.set_timing_events(None)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     for r in range(R):
-        if pending[r] is not None:
+        if pending[r]:
             collect(r)
     ms_events_pass = (t1 - t0) * 1e3 / args.steps
     per_kernel = {}
@@ -262,6 +268,7 @@ def main():
                         "pct_hbm_peak": round(100 * ex_gbs / HBM_PEAK_GBS, 2)},
         "kernels": per_kernel,
         "ms_per_step_events_pass": round(ms_events_pass, 5),
+        "ms_per_step_eager": round(ms_eager, 5),
         "roofline": {"bound": "hbm", "kernel": pk["symbol"], "achieved": pk["gbs"],
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": pk["frac"],
                      "traffic": load_traffic(pk["symbol"], args.workload)},

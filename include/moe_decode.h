@@ -89,9 +89,10 @@ typedef enum {
 
 enum { MOE_ROUTER_BF16 = 0, MOE_ROUTER_F32 = 1 };
 
-/* Layer dimensions, all in elements.  Supported: H, L, I, Is multiples of 128;
- * E a multiple of 32 and at most 2048; 1 <= max_batch <= 64;
- * 1 <= max_top_k <= min(E, 64). */
+/* Layer dimensions, all in elements.  Supported: H, L, I, Is multiples of 128
+ * such that each of H, L, I and L + Is is 128 * KW * S with KW in {1, 2, 4, 8}
+ * and S <= 8 (at most 8192 elements); E a multiple of 32 and at most 1024;
+ * 1 <= max_batch <= 64; 1 <= max_top_k <= min(E, 64). */
 typedef struct {
     int32_t hidden;       /* H  */
     int32_t latent;       /* L  */
@@ -167,11 +168,11 @@ moe_status moe_decode_graph_destroy(moe_decode_graph *graph);
  * choices), for tests that check a batch reaches the intended code path. */
 typedef struct {
     int32_t batch, top_k;
-    int32_t col_tiles;     /* 16-token column tiles of the dense kernels (1..4) */
-    int32_t split_in;      /* K splits of the router / latent-down / shared gate-up kernel */
-    int32_t split_out;     /* K splits of the latent-up + shared-down kernel */
-    int32_t split_w13;     /* K splits of the expert gate/up kernel */
-    int32_t split_w2;      /* K splits of the expert down kernel */
+    int32_t col_tiles;     /* 16-token column groups of the router / latent-down kernel */
+    int32_t split_in;      /* waves of a workgroup splitting K: router / latent-down / shared gate-up */
+    int32_t split_out;     /* ... latent-up + shared-down */
+    int32_t split_w13;     /* ... expert gate/up */
+    int32_t split_w2;      /* ... expert down */
     int32_t grid_in, grid_w13, grid_w2, grid_out; /* workgroups launched */
     int32_t router_f32;    /* 1 when the f32 router kernel ran */
     int32_t n_kernels;     /* kernels launched by the step */

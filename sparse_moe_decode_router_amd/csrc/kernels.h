@@ -6,27 +6,29 @@
 // router):
 //   k_dense_in : router logits, latent-down z = W_ld x and shared gate/up
 //                (all contract over the hidden size H against x); epilogues:
-//                sigmoid + bias keys, z as hi/lo bf16, shared SwiGLU.  The
-//                router tiles come first and the top-k + routing metadata run
-//                inside this kernel while the latent and shared rows stream.
+//                sigmoid + bias keys, z, shared SwiGLU.  The router tiles come
+//                first and the top-k + routing metadata run inside this kernel
+//                while the latent and shared rows stream.
 //   k_w13      : active experts' MXFP4 gate/up rows, fused dequantisation,
-//                SwiGLU epilogue -> expert activation a (hi/lo bf16).
-//   k_w2       : active experts' MXFP4 down rows; the last arrival for a
-//                32-row latent tile forms the weighted combine ylat.
+//                SwiGLU epilogue -> expert activation a.
+//   k_w2       : active experts' MXFP4 down rows; each result is weighted and
+//                added into the latent combine ylat.
 //   k_out      : latent-up W_lu ylat plus shared-down S2 ash, one bf16 RNE.
 //
-// Work decomposition.  A unit is one wave: 32 weight rows (two 16-row MFMA
-// tiles) x one K chunk x one column group of tokens.  Units are split along K
-// so that there are several thousand of them (256 CUs, 8 XCDs); each unit
-// writes an f32 partial and arrives on a per-tile counter, and the last
-// arrival sums the partials in chunk order (deterministic) and runs the
-// epilogue.  No wave waits for another.
+// Work decomposition.  A workgroup is 8 waves.  It covers RW row groups of
+// 32 weight rows (two 16-row MFMA tiles) for one group of token columns; the
+// KW = 8 / RW waves of a row group split the reduction dimension K into equal
+// slices of SPC 128-element steps and their partial tiles are summed through
+// LDS in slice order.  No wave of the hot loops synchronises with another
+// workgroup; cross-workgroup communication is limited to the routing (one
+// release per router tile and per token) and the f32 atomic adds of the
+// expert combine.
 //
 // Operands.  x is bf16 and enters the MFMA as is (16 tokens per column group).
-// f32 intermediates (z, a, ylat, ash) are stored as hi + lo bf16 and enter as
-// two adjacent columns of the same MFMA (8 tokens per column group); the two
-// column sums are added afterwards, which keeps f32-grade precision at the cost
-// of one MFMA per K-slice.
+// The f32 intermediates z, a, ylat and ash are split when they are loaded into
+// hi = bf16(v) and lo = bf16(v - hi); hi and lo occupy two adjacent columns of
+// the same MFMA (8 tokens per column group) and the two column sums are added
+// afterwards, which keeps f32-grade precision at one MFMA per K slice.
 //
 // K layout within one 128-element step: lane group g = lane/16 owns the 32
 // consecutive elements [32g, 32g+32) of the step, one MX block for MXFP4 rows
@@ -41,8 +43,11 @@
 
 namespace moe {
 
+constexpr int kWG = 8;              // waves per workgroup of the step kernels
+constexpr int kWGThreads = kWG * kWave;
+
 // ---------------------------------------------------------------------------
-// Dense bf16 rows x bf16 tokens (router, latent-down, shared gate/up)
+// Operand loads
 // ---------------------------------------------------------------------------
 
 __device__ __forceinline__ void load_rows_bf16(const uint16_t *A0, const uint16_t *A1, int s,
@@ -56,10 +61,11 @@ __device__ __forceinline__ void load_rows_bf16(const uint16_t *A0, const uint16_
     }
 }
 
-// Column operand of one step.  Lanes without a token read a valid row (the
-// caller points them at one) and drop the value, so no load sits under a
-// lane-dependent branch.
-__device__ __forceinline__ void load_cols(const uint16_t *X, bool valid, int s, u32x4 (&rb)[4]) {
+// bf16 column operand of one step (x).  Lanes without a token read a valid
+// row (the caller points them at one) and drop the value, so no load sits
+// under a lane-dependent branch.
+__device__ __forceinline__ void load_cols_bf16(const uint16_t *X, bool valid, int s,
+                                               u32x4 (&rb)[4]) {
     const uint16_t *p = X + (size_t)s * kKStep;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -68,101 +74,180 @@ __device__ __forceinline__ void load_cols(const uint16_t *X, bool valid, int s, 
     }
 }
 
-// acc0/acc1 += rows A0/A1 (16 each) . columns X over the SPC steps from s0,
-// with the next step's loads in flight while the current step's MFMAs run.
-template <int SPC>
-__device__ __forceinline__ void dense_chunk(const uint16_t *A0, const uint16_t *A1,
-                                            const uint16_t *X, bool valid, int s0, f32x4 &acc0,
-                                            f32x4 &acc1) {
-    u32x4 ra[2][8], rb[2][4];
-    load_rows_bf16(A0, A1, s0, ra[0]);
-    load_cols(X, valid, s0, rb[0]);
+// f32 column operand of one step, delivered as the hi (part 0) or lo (part 1)
+// bf16 half of each value.
+__device__ __forceinline__ uint32_t pack_part(float a, float b, int part) {
+    uint32_t ha, la, hb, lb;
+    split_hl(a, ha, la);
+    split_hl(b, hb, lb);
+    return part ? (la | (lb << 16)) : (ha | (hb << 16));
+}
+
+__device__ __forceinline__ void load_cols_f32(const float *X, bool valid, int part, int s,
+                                              u32x4 (&rb)[4]) {
+    const float *p = X + (size_t)s * kKStep;
+    f32x4 v[8];
 #pragma unroll
-    for (int q = 0; q < SPC; ++q) {
-        if (q + 1 < SPC) {
-            load_rows_bf16(A0, A1, s0 + q + 1, ra[(q + 1) & 1]);
-            load_cols(X, valid, s0 + q + 1, rb[(q + 1) & 1]);
-        }
+    for (int j = 0; j < 8; ++j) v[j] = ldf4(p + 4 * j);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const bf16x8 b = as_bf16x8(rb[q & 1][j]);
-            acc0 = mfma(as_bf16x8(ra[q & 1][j]), b, acc0);
-            acc1 = mfma(as_bf16x8(ra[q & 1][4 + j]), b, acc1);
-        }
+    for (int j = 0; j < 4; ++j) {
+        const f32x4 a = v[2 * j], b = v[2 * j + 1];
+        const u32x4 w = {pack_part(a[0], a[1], part), pack_part(a[2], a[3], part),
+                         pack_part(b[0], b[1], part), pack_part(b[2], b[3], part)};
+        rb[j] = valid ? w : (u32x4){0u, 0u, 0u, 0u};
     }
 }
 
-// Same for the output kernel: K runs over [0, L) against lat_up and ylat,
-// then over [0, Is) against sh_w2 and ash.  Step s < Ls selects the first pair.
+// ---------------------------------------------------------------------------
+// Chunk loops (SPC steps, compile-time, straight-line)
+// ---------------------------------------------------------------------------
+
+// The loops below issue every load of a group of steps before the first MFMA
+// that consumes one, and keep the scheduler from moving them apart: left
+// alone, the compiler recycles the operand registers between the loads of a
+// step and serialises several memory round trips per step.
+__device__ __forceinline__ void fence_schedule() { __builtin_amdgcn_sched_barrier(0); }
+
+__device__ __forceinline__ void mfma_step(const u32x4 (&ra)[8], const u32x4 (&rb)[4], f32x4 &acc0,
+                                          f32x4 &acc1) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const bf16x8 b = as_bf16x8(rb[j]);
+        acc0 = mfma(as_bf16x8(ra[j]), b, acc0);
+        acc1 = mfma(as_bf16x8(ra[4 + j]), b, acc1);
+    }
+}
+
+// acc0/acc1 += bf16 rows A0/A1 (16 each) . bf16 columns X over steps
+// [s0, s1), one step (8 KB of weights per wave) in flight at a time.
+__device__ __forceinline__ void dense_chunk_x(const uint16_t *A0, const uint16_t *A1,
+                                              const uint16_t *X, bool valid, int s0, int s1,
+                                              f32x4 &acc0, f32x4 &acc1) {
+#pragma unroll 1
+    for (int s = s0; s < s1; ++s) {
+        u32x4 ra[8], rb[4];
+        load_rows_bf16(A0, A1, s, ra);
+        load_cols_bf16(X, valid, s, rb);
+        fence_schedule();
+        mfma_step(ra, rb, acc0, acc1);
+    }
+}
+
+// Output kernel: K runs over [0, L) against lat_up and ylat, then over
+// [0, Is) against sh_w2 and ash; step s < Ls selects the first pair.
 struct TwoSource {
-    const uint16_t *A0a, *A1a, *Xa;  // K in [0, L)
-    const uint16_t *A0b, *A1b, *Xb;  // K in [0, Is)
-    int Ls;                          // L / 128
+    const uint16_t *A0a, *A1a;
+    const float *Xa;  // K in [0, L)
+    const uint16_t *A0b, *A1b;
+    const float *Xb;  // K in [0, Is)
+    int Ls;           // L / 128
 };
 
-__device__ __forceinline__ void load_two(const TwoSource &t, bool valid, int s, u32x4 (&ra)[8],
-                                         u32x4 (&rb)[4]) {
+__device__ __forceinline__ void load_two(const TwoSource &t, bool valid, int part, int s,
+                                         u32x4 (&ra)[8], u32x4 (&rb)[4]) {
     const bool first = s < t.Ls;
     const int ss = first ? s : s - t.Ls;
     load_rows_bf16(first ? t.A0a : t.A0b, first ? t.A1a : t.A1b, ss, ra);
-    load_cols(first ? t.Xa : t.Xb, valid, ss, rb);
+    load_cols_f32(first ? t.Xa : t.Xb, valid, part, ss, rb);
 }
 
-template <int SPC>
-__device__ __forceinline__ void out_chunk(const TwoSource &t, bool valid, int s0, f32x4 &acc0,
-                                          f32x4 &acc1) {
-    u32x4 ra[2][8], rb[2][4];
-    load_two(t, valid, s0, ra[0], rb[0]);
-#pragma unroll
-    for (int q = 0; q < SPC; ++q) {
-        if (q + 1 < SPC) load_two(t, valid, s0 + q + 1, ra[(q + 1) & 1], rb[(q + 1) & 1]);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const bf16x8 b = as_bf16x8(rb[q & 1][j]);
-            acc0 = mfma(as_bf16x8(ra[q & 1][j]), b, acc0);
-            acc1 = mfma(as_bf16x8(ra[q & 1][4 + j]), b, acc1);
-        }
+__device__ __forceinline__ void dense_chunk_out(const TwoSource &t, bool valid, int part, int s0,
+                                                int s1, f32x4 &acc0, f32x4 &acc1) {
+#pragma unroll 1
+    for (int s = s0; s < s1; ++s) {
+        u32x4 ra[8], rb[4];
+        load_two(t, valid, part, s, ra, rb);
+        fence_schedule();
+        mfma_step(ra, rb, acc0, acc1);
     }
 }
 
-// ---------------------------------------------------------------------------
-// MXFP4 expert rows x hi/lo token columns
-// ---------------------------------------------------------------------------
-
-// acc0/acc1 += MXFP4 rows (q0,sc0)/(q1,sc1) . columns X over the SPC steps
-// from s0.  All code and scale loads of the chunk (2 x SPC x 16 code bytes
-// and 2 x SPC scale dwords per lane) are issued first; the column operand is
-// fetched one step ahead.  q0/q1 point at the lane's 16-byte slice of step 0,
-// sc0/sc1 at the row's scale bytes (byte 4s+g is lane group g's block).
+// acc0/acc1 += MXFP4 rows (q0,sc0)/(q1,sc1) . f32 columns X (hi/lo) over the
+// SPC steps from s0, in groups of two steps whose code, scale and column
+// loads are all issued before the group's MFMAs.  q0/q1 point at the lane's
+// 16-byte slice of step 0, sc0/sc1 at the row's scale bytes (byte 4s+g is
+// lane group g's block).
 template <int SPC>
 __device__ __forceinline__ void fp4_chunk(const uint8_t *q0, const uint8_t *sc0,
-                                          const uint8_t *q1, const uint8_t *sc1,
-                                          const uint16_t *X, bool valid, int g, int s0,
-                                          f32x4 &acc0, f32x4 &acc1) {
-    u32x4 c0[SPC], c1[SPC];
-    uint32_t e0[SPC], e1[SPC];
-    u32x4 rb[2][4];
-    load_cols(X, valid, s0, rb[0]);
-#pragma unroll
-    for (int q = 0; q < SPC; ++q) {
-        c0[q] = ld_weight16(q0 + (size_t)(s0 + q) * 64);
-        c1[q] = ld_weight16(q1 + (size_t)(s0 + q) * 64);
-        e0[q] = ld_weight4(sc0 + (size_t)(s0 + q) * 4);
-        e1[q] = ld_weight4(sc1 + (size_t)(s0 + q) * 4);
-    }
+                                          const uint8_t *q1, const uint8_t *sc1, const float *X,
+                                          bool valid, int part, int g, int s0, f32x4 &acc0,
+                                          f32x4 &acc1) {
     const int sh = 8 * g;
 #pragma unroll
-    for (int q = 0; q < SPC; ++q) {
-        if (q + 1 < SPC) load_cols(X, valid, s0 + q + 1, rb[(q + 1) & 1]);
-        const float f0 = e8m0_scale((e0[q] >> sh) & 0xFFu);
-        const float f1 = e8m0_scale((e1[q] >> sh) & 0xFFu);
+    for (int q0s = 0; q0s < SPC; q0s += 2) {
+        constexpr int G = 2;
+        u32x4 c0[G], c1[G], rb[G][4];
+        uint32_t e0[G], e1[G];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const bf16x8 b = as_bf16x8(rb[q & 1][j]);
-            acc0 = mfma(fp4x8_to_bf16(c0[q][j], f0), b, acc0);
-            acc1 = mfma(fp4x8_to_bf16(c1[q][j], f1), b, acc1);
+        for (int q = 0; q < G; ++q) {
+            if (q0s + q >= SPC) break;
+            const int s = s0 + q0s + q;
+            c0[q] = ld_weight16(q0 + (size_t)s * 64);
+            c1[q] = ld_weight16(q1 + (size_t)s * 64);
+            e0[q] = ld_weight4(sc0 + (size_t)s * 4);
+            e1[q] = ld_weight4(sc1 + (size_t)s * 4);
+        }
+#pragma unroll
+        for (int q = 0; q < G; ++q) {
+            if (q0s + q >= SPC) break;
+            load_cols_f32(X, valid, part, s0 + q0s + q, rb[q]);
+        }
+        fence_schedule();
+#pragma unroll
+        for (int q = 0; q < G; ++q) {
+            if (q0s + q >= SPC) break;
+            const float f0 = e8m0_scale((e0[q] >> sh) & 0xFFu);
+            const float f1 = e8m0_scale((e1[q] >> sh) & 0xFFu);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const bf16x8 b = as_bf16x8(rb[q][j]);
+                acc0 = mfma(fp4x8_to_bf16(c0[q][j], f0), b, acc0);
+                acc1 = mfma(fp4x8_to_bf16(c1[q][j], f1), b, acc1);
+            }
         }
     }
+}
+
+// ---------------------------------------------------------------------------
+// Workgroup split-K reduction
+// ---------------------------------------------------------------------------
+
+// Waves w = rg*KW + kw.  Each writes its two partial tiles to LDS; after the
+// barrier the wave with kw == 0 of each row group sums its group's KW slices
+// in slice order and returns true (the leader).  The caller issues the
+// barrier that ends the unit before LDS is reused.
+__device__ __forceinline__ bool reduce_k(float *s_red, int wave, int kw, int KW, f32x4 &acc0,
+                                         f32x4 &acc1) {
+    const int lane = lane_id();
+    float *mine = s_red + (wave * kWave + lane) * 8;
+    stf4(mine, acc0);
+    stf4(mine + 4, acc1);
+    __syncthreads();
+    if (kw != 0) return false;
+    if (KW > 1) {
+        acc0 = zero4();
+        acc1 = zero4();
+        for (int j = 0; j < KW; ++j) {
+            const float *p = s_red + ((wave + j) * kWave + lane) * 8;
+            acc0 += ldf4(p);
+            acc1 += ldf4(p + 4);
+        }
+    }
+    return true;
+}
+
+struct Role {
+    int wave, KW, RW, rg, kw;
+};
+
+__device__ __forceinline__ Role role_of(int KW) {
+    Role r;
+    r.wave = wave_index();
+    r.KW = KW;
+    r.RW = kWG / KW;
+    r.rg = r.wave / KW;
+    r.kw = r.wave % KW;
+    return r;
 }
 
 // ---------------------------------------------------------------------------
@@ -171,9 +256,12 @@ __device__ __forceinline__ void fp4_chunk(const uint8_t *q0, const uint8_t *sc0,
 
 __global__ void __launch_bounds__(kBlock) k_router_f32(const StepArgs a) {
     __shared__ unsigned long long s_mask[kMaxExperts];
+    __shared__ float s_keys[kWavesPerBlock][kMaxExperts];
+    const int wave = wave_index();
+    float *my_keys = s_keys[wave];
     const int lane = lane_id();
     const int nwaves = gridDim.x * kWavesPerBlock;
-    for (int e = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6); e < a.E; e += nwaves) {
+    for (int e = blockIdx.x * kWavesPerBlock + wave; e < a.E; e += nwaves) {
         const float *row = a.router_w32 + (size_t)e * a.H;
         for (int b = 0; b < a.B; ++b) {
             const uint16_t *xb = a.x + (size_t)b * a.H;
@@ -187,9 +275,9 @@ __global__ void __launch_bounds__(kBlock) k_router_f32(const StepArgs a) {
             }
         }
         if (wave_arrive(&a.gctr[G_ROUTER_DONE]) == (uint32_t)a.router_target - 1u)
-            topk_loop(a, s_mask);
+            topk_loop(a, s_mask, my_keys);
         else
-            maybe_join_topk(a, s_mask);
+            maybe_join_topk(a, s_mask, my_keys);
     }
 }
 
@@ -197,31 +285,41 @@ __global__ void __launch_bounds__(kBlock) k_router_f32(const StepArgs a) {
 // Kernel 1: router + latent-down + shared gate/up over x.
 // ---------------------------------------------------------------------------
 
-template <int SPC>
-__global__ void __launch_bounds__(kBlock) k_dense_in(const StepArgs a) {
+__global__ void __launch_bounds__(kWGThreads) __attribute__((amdgpu_waves_per_eu(4)))
+k_dense_in(const StepArgs a) {
     __shared__ unsigned long long s_mask[kMaxExperts];
+    __shared__ float s_keys[kWG][kMaxExperts];
+    __shared__ float s_red[kWG * kWave * 8];
     const int lane = lane_id(), n = lane & 15, g = lane >> 4;
+    const Role ro = role_of(a.kw_in);
+    float *my_keys = s_keys[ro.wave];
+    // The latent combine accumulates into ylat with atomics later in the step.
+    for (int i = (blockIdx.x * kWGThreads + threadIdx.x) * 4; i < a.B * a.L;
+         i += gridDim.x * kWGThreads * 4)
+        stf4(a.ylat + i, zero4());
     const int n_l2 = a.L >> 5, n_s2 = a.Is >> 4;
     const int n_t2 = a.n_r2 + n_l2 + n_s2;
     const int ncg = (a.B + 15) >> 4;
-    const int total = n_t2 * ncg * a.s_in;
-    const int nwaves = gridDim.x * kWavesPerBlock;
-    for (int u = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6); u < total; u += nwaves) {
-        const int c = u % a.s_in, r = u / a.s_in, cg = r % ncg, t2 = r / ncg;
-        const int s0 = c * SPC;
+    const int tgroups = (n_t2 + ro.RW - 1) / ro.RW;
+    const int units = tgroups * ncg;
+    for (int u = blockIdx.x; u < units; u += gridDim.x) {
+        const int cg = u % ncg;
+        const int t2 = (u / ncg) * ro.RW + ro.rg;
+        const bool active = t2 < n_t2;
+        const int tt = active ? t2 : 0;
         int kind;
         const uint16_t *A0, *A1;
-        if (t2 < a.n_r2) {
+        if (tt < a.n_r2) {
             kind = 0;
-            A0 = a.router_w + (size_t)(32 * t2 + n) * a.H;
+            A0 = a.router_w + (size_t)(32 * tt + n) * a.H;
             A1 = A0 + (size_t)16 * a.H;
-        } else if (t2 < a.n_r2 + n_l2) {
+        } else if (tt < a.n_r2 + n_l2) {
             kind = 1;
-            A0 = a.lat_down + (size_t)(32 * (t2 - a.n_r2) + n) * a.H;
+            A0 = a.lat_down + (size_t)(32 * (tt - a.n_r2) + n) * a.H;
             A1 = A0 + (size_t)16 * a.H;
         } else {
             kind = 2;
-            const int pt = t2 - a.n_r2 - n_l2;
+            const int pt = tt - a.n_r2 - n_l2;
             A0 = a.sh_w13 + (size_t)(16 * pt + n) * a.H;
             A1 = a.sh_w13 + (size_t)(a.Is + 16 * pt + n) * a.H;
         }
@@ -229,34 +327,13 @@ __global__ void __launch_bounds__(kBlock) k_dense_in(const StepArgs a) {
         const bool valid = b < a.B;
         const uint16_t *X = a.x + (size_t)(valid ? b : 0) * a.H + 32 * g;
         f32x4 acc0 = zero4(), acc1 = zero4();
-        dense_chunk<SPC>(A0 + 32 * g, A1 + 32 * g, X, valid, s0, acc0, acc1);
-
-        bool finish = true;
-        if (a.s_in > 1) {
-            float *mine = a.part_in + ((size_t)(t2 * a.s_in + c) * a.Bm + b) * 32 + 4 * g;
-            if (valid) {
-                stf4(mine, acc0);
-                stf4(mine + 16, acc1);
-            }
-            uint32_t *ctr = a.ctr_in + t2 * a.ncg_in_cap + cg;
-            finish = wave_arrive(ctr) == (uint32_t)(a.s_in - 1);
-            if (finish) {
-                acquire_agent();
-                wave_store_counter(ctr, 0u);
-                acc0 = zero4();
-                acc1 = zero4();
-                if (valid) {
-                    const float *p = a.part_in + ((size_t)t2 * a.s_in * a.Bm + b) * 32 + 4 * g;
-                    for (int cc = 0; cc < a.s_in; ++cc, p += (size_t)a.Bm * 32) {
-                        acc0 += ldf4(p);
-                        acc1 += ldf4(p + 16);
-                    }
-                }
-            }
-        }
-        if (finish) {
+        if (active)
+            dense_chunk_x(A0 + 32 * g, A1 + 32 * g, X, valid, ro.kw * a.spc_in,
+                          (ro.kw + 1) * a.spc_in, acc0, acc1);
+        const bool leader = reduce_k(s_red, ro.wave, ro.kw, ro.KW, acc0, acc1);
+        if (leader && active) {
             if (kind == 0) {
-                const int e = 32 * t2 + 4 * g;
+                const int e = 32 * tt + 4 * g;
                 if (valid) {
                     f32x4 s0v, s1v;
 #pragma unroll
@@ -273,29 +350,25 @@ __global__ void __launch_bounds__(kBlock) k_dense_in(const StepArgs a) {
                     stf4(kr, s0v + b0);
                     stf4(kr + 16, s1v + b1);
                 }
-                if (wave_arrive(&a.gctr[G_ROUTER_DONE]) == (uint32_t)a.router_target - 1u) {
-                    topk_loop(a, s_mask);
-                    continue;
-                }
+                if (wave_arrive(&a.gctr[G_ROUTER_DONE]) == (uint32_t)a.router_target - 1u)
+                    topk_loop(a, s_mask, my_keys);
             } else if (kind == 1) {
-                const int l = 32 * (t2 - a.n_r2) + 4 * g;
                 if (valid) {
-                    const size_t o = (size_t)b * a.L + l;
-                    store_hl4(a.z_hi + o, a.z_lo + o, acc0);
-                    store_hl4(a.z_hi + o + 16, a.z_lo + o + 16, acc1);
+                    float *zr = a.z + (size_t)b * a.L + 32 * (tt - a.n_r2) + 4 * g;
+                    stf4(zr, acc0);
+                    stf4(zr + 16, acc1);
                 }
             } else {
-                const int i0 = 16 * (t2 - a.n_r2 - n_l2) + 4 * g;
                 if (valid) {
                     f32x4 v;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) v[i] = silu_mul(acc0[i], acc1[i]);
-                    const size_t o = (size_t)b * a.Is + i0;
-                    store_hl4(a.ash_hi + o, a.ash_lo + o, v);
+                    stf4(a.ash + (size_t)b * a.Is + 16 * (tt - a.n_r2 - n_l2) + 4 * g, v);
                 }
             }
         }
-        if (a.router_target > 0 && a.n_r2 > 0) maybe_join_topk(a, s_mask);
+        __syncthreads();
+        if (a.n_r2 > 0) maybe_join_topk(a, s_mask, my_keys);
     }
 }
 
@@ -303,62 +376,44 @@ __global__ void __launch_bounds__(kBlock) k_dense_in(const StepArgs a) {
 // Kernel 2: expert gate/up (MXFP4) + SwiGLU.
 // ---------------------------------------------------------------------------
 
-__device__ __forceinline__ void swiglu_store(const StepArgs &a, int p, int row0, f32x4 vg,
-                                             f32x4 vu) {
-    f32x4 v;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = silu_mul(vg[i], vu[i]);
-    const size_t o = (size_t)p * a.I + row0;
-    store_hl4(a.act_hi + o, a.act_lo + o, v);
-}
-
 template <int SPC>
-__global__ void __launch_bounds__(kBlock) k_w13(const StepArgs a) {
+__global__ void __launch_bounds__(kWGThreads) k_w13(const StepArgs a) {
+    __shared__ float s_red[kWG * kWave * 8];
     const int lane = lane_id(), n = lane & 15, g = lane >> 4;
     const int col = n >> 1, part = n & 1;
-    const int NC = a.meta[M_N_COLS];
+    const Role ro = role_of(a.kw13);
+    const int NC = min(a.meta[M_N_COLS], a.ncols_cap);  // never beyond the lists
     const int PT = a.I >> 4;
-    const int total = NC * PT * a.s13;
-    const int nwaves = gridDim.x * kWavesPerBlock;
+    const int ptg = (PT + ro.RW - 1) / ro.RW;
+    const int units = NC * ptg;
     const size_t qrow = a.L / 2, srow = a.L / 32;
-    for (int u = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6); u < total; u += nwaves) {
-        const int c = u % a.s13, r = u / a.s13, pt = r % PT, cu = r / PT;
+    for (int u = blockIdx.x; u < units; u += gridDim.x) {
+        const int cu = u / ptg;
+        const int pt = (u % ptg) * ro.RW + ro.rg;
+        const bool active = pt < PT;
         const int e = a.cu_expert[cu], p0 = a.cu_p0[cu], nt = a.cu_n[cu];
-        const int s0 = c * SPC;
-        const size_t rg = (size_t)e * 2 * a.I + 16 * pt + n, ru = rg + a.I;
         const bool valid = col < nt;
-        const int p = p0 + col;
-        const int tok = valid ? a.pair_slot[p] / a.k : 0;
-        const uint16_t *X = (part ? a.z_lo : a.z_hi) + (size_t)tok * a.L + 32 * g;
+        const int p = p0 + (valid ? col : 0);
+        const int tok = a.pair_slot[p] / a.k;
+        const float *X = a.z + (size_t)tok * a.L + 32 * g;
+        const size_t rg = (size_t)e * 2 * a.I + 16 * (active ? pt : 0) + n, ru = rg + a.I;
         f32x4 accg = zero4(), accu = zero4();
-        fp4_chunk<SPC>(a.w13_q + rg * qrow + 16 * g, a.w13_s + rg * srow,
-                       a.w13_q + ru * qrow + 16 * g, a.w13_s + ru * srow, X, valid, g, s0, accg,
-                       accu);
-        accg = add_pair_column(accg);
-        accu = add_pair_column(accu);
-        const bool writer = valid && part == 0;
-        if (a.s13 == 1) {
-            if (writer) swiglu_store(a, p, 16 * pt + 4 * g, accg, accu);
-            continue;
-        }
-        float *mine = a.part13 + (((size_t)p * PT + pt) * a.s13 + c) * 32 + 4 * g;
-        if (writer) {
-            stf4(mine, accg);
-            stf4(mine + 16, accu);
-        }
-        uint32_t *ctr = a.ctr13 + (size_t)cu * PT + pt;
-        if (wave_arrive(ctr) != (uint32_t)(a.s13 - 1)) continue;
-        acquire_agent();
-        wave_store_counter(ctr, 0u);
-        if (writer) {
-            const float *q = a.part13 + ((size_t)p * PT + pt) * a.s13 * 32 + 4 * g;
-            f32x4 vg = zero4(), vu = zero4();
-            for (int cc = 0; cc < a.s13; ++cc, q += 32) {
-                vg += ldf4(q);
-                vu += ldf4(q + 16);
+        if (active)
+            fp4_chunk<SPC>(a.w13_q + rg * qrow + 16 * g, a.w13_s + rg * srow,
+                           a.w13_q + ru * qrow + 16 * g, a.w13_s + ru * srow, X, valid, part, g,
+                           ro.kw * SPC, accg, accu);
+        const bool leader = reduce_k(s_red, ro.wave, ro.kw, ro.KW, accg, accu);
+        if (leader && active) {
+            accg = add_pair_column(accg);
+            accu = add_pair_column(accu);
+            if (valid && part == 0) {
+                f32x4 v;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) v[i] = silu_mul(accg[i], accu[i]);
+                stf4(a.act + (size_t)p * a.I + 16 * pt + 4 * g, v);
             }
-            swiglu_store(a, p, 16 * pt + 4 * g, vg, vu);
         }
+        __syncthreads();
     }
 }
 
@@ -366,61 +421,47 @@ __global__ void __launch_bounds__(kBlock) k_w13(const StepArgs a) {
 // Kernel 3: expert down (MXFP4) + weighted combine in latent space.
 // ---------------------------------------------------------------------------
 
-// ylat for rows [r0, r0+32) of every token: sum over the token's experts in
-// ascending id of w * (sum of the K-chunk partials in chunk order).
-__device__ __noinline__ void combine_latent_tile(const StepArgs &a, int r0) {
-    const int lane = lane_id();
-    for (int it = lane; it < a.B * 8; it += kWave) {
-        const int b = it >> 3, q = it & 7;
-        f32x4 acc = zero4();
-        for (int j = 0; j < a.k; ++j) {
-            const int slot = b * a.k + j;
-            const int p = a.pair_of_slot[slot];
-            const float w = a.wsel[slot];
-            const float *src = a.ypart + (size_t)p * a.s2 * a.L + r0 + 4 * q;
-            f32x4 t = zero4();
-            for (int cc = 0; cc < a.s2; ++cc, src += a.L) t += ldf4(src);
-            acc += w * t;
-        }
-        const size_t o = (size_t)b * a.L + r0 + 4 * q;
-        store_hl4(a.ylat_hi + o, a.ylat_lo + o, acc);
-    }
-}
-
 template <int SPC>
-__global__ void __launch_bounds__(kBlock) k_w2(const StepArgs a) {
+__global__ void __launch_bounds__(kWGThreads) k_w2(const StepArgs a) {
+    __shared__ float s_red[kWG * kWave * 8];
     const int lane = lane_id(), n = lane & 15, g = lane >> 4;
     const int col = n >> 1, part = n & 1;
-    const int NC = a.meta[M_N_COLS];
+    const Role ro = role_of(a.kw2);
+    const int NC = min(a.meta[M_N_COLS], a.ncols_cap);  // never beyond the lists
     const int LT = a.L >> 5;
-    const int total = NC * LT * a.s2;
-    const int nwaves = gridDim.x * kWavesPerBlock;
+    const int ltg = (LT + ro.RW - 1) / ro.RW;
+    const int units = NC * ltg;
     const size_t qrow = a.I / 2, srow = a.I / 32;
-    const uint32_t target = (uint32_t)(NC * a.s2);
-    for (int u = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6); u < total; u += nwaves) {
-        const int c = u % a.s2, r = u / a.s2, lt = r % LT, cu = r / LT;
+    for (int u = blockIdx.x; u < units; u += gridDim.x) {
+        const int cu = u / ltg;
+        const int lt = (u % ltg) * ro.RW + ro.rg;
+        const bool active = lt < LT;
         const int e = a.cu_expert[cu], p0 = a.cu_p0[cu], nt = a.cu_n[cu];
-        const int s0 = c * SPC;
-        const size_t r0 = (size_t)e * a.L + 32 * lt + n, r1 = r0 + 16;
         const bool valid = col < nt;
         const int p = p0 + (valid ? col : 0);
-        const uint16_t *X = (part ? a.act_lo : a.act_hi) + (size_t)p * a.I + 32 * g;
+        const float *X = a.act + (size_t)p * a.I + 32 * g;
+        const size_t r0 = (size_t)e * a.L + 32 * (active ? lt : 0) + n, r1 = r0 + 16;
         f32x4 acc0 = zero4(), acc1 = zero4();
-        fp4_chunk<SPC>(a.w2_q + r0 * qrow + 16 * g, a.w2_s + r0 * srow,
-                       a.w2_q + r1 * qrow + 16 * g, a.w2_s + r1 * srow, X, valid, g, s0, acc0,
-                       acc1);
-        acc0 = add_pair_column(acc0);
-        acc1 = add_pair_column(acc1);
-        if (valid && part == 0) {
-            float *mine = a.ypart + ((size_t)p * a.s2 + c) * a.L + 32 * lt + 4 * g;
-            stf4(mine, acc0);
-            stf4(mine + 16, acc1);
+        if (active)
+            fp4_chunk<SPC>(a.w2_q + r0 * qrow + 16 * g, a.w2_s + r0 * srow,
+                           a.w2_q + r1 * qrow + 16 * g, a.w2_s + r1 * srow, X, valid, part, g,
+                           ro.kw * SPC, acc0, acc1);
+        const bool leader = reduce_k(s_red, ro.wave, ro.kw, ro.KW, acc0, acc1);
+        if (leader && active) {
+            acc0 = add_pair_column(acc0);
+            acc1 = add_pair_column(acc1);
+            if (valid && part == 0) {
+                const int slot = a.pair_slot[p];
+                const float w = a.wsel[slot];
+                float *dst = a.ylat + (size_t)(slot / a.k) * a.L + 32 * lt + 4 * g;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    unsafeAtomicAdd(dst + i, w * acc0[i]);
+                    unsafeAtomicAdd(dst + 16 + i, w * acc1[i]);
+                }
+            }
         }
-        uint32_t *ctr = a.ctr2 + lt;
-        if (wave_arrive(ctr) != target - 1u) continue;
-        acquire_agent();
-        wave_store_counter(ctr, 0u);
-        combine_latent_tile(a, 32 * lt);
+        __syncthreads();
     }
 }
 
@@ -433,61 +474,50 @@ __device__ __forceinline__ void store_out4(uint16_t *dst, f32x4 v) {
                             bf16_rne(v[2]) | (bf16_rne(v[3]) << 16)};
 }
 
-template <int SPC>
-__global__ void __launch_bounds__(kBlock) k_out(const StepArgs a) {
+__global__ void __launch_bounds__(kWGThreads) __attribute__((amdgpu_waves_per_eu(4)))
+k_out(const StepArgs a) {
+    __shared__ float s_red[kWG * kWave * 8];
     // The routing counters of the dense input kernel are cleared here, where
     // no wave of the step can touch them any more.
     if (blockIdx.x == 0 && threadIdx.x < 3) a.gctr[threadIdx.x] = 0u;
     const int lane = lane_id(), n = lane & 15, g = lane >> 4;
     const int col = n >> 1, part = n & 1;
+    const Role ro = role_of(a.kw_out);
     const int ncg = (a.B + 7) >> 3;
     const int n_t2 = a.H >> 5;
-    const int total = n_t2 * ncg * a.s_out;
-    const int nwaves = gridDim.x * kWavesPerBlock;
-    for (int u = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6); u < total; u += nwaves) {
-        const int c = u % a.s_out, r = u / a.s_out, cg = r % ncg, t2 = r / ncg;
-        const int s0 = c * SPC;
+    const int tgroups = (n_t2 + ro.RW - 1) / ro.RW;
+    const int units = tgroups * ncg;
+    for (int u = blockIdx.x; u < units; u += gridDim.x) {
+        const int cg = u % ncg;
+        const int t2 = (u / ncg) * ro.RW + ro.rg;
+        const bool active = t2 < n_t2;
         const int b = 8 * cg + col;
         const bool valid = b < a.B;
         const int bb = valid ? b : 0;
-        const size_t h0 = 32 * (size_t)t2 + n;
+        const size_t h0 = 32 * (size_t)(active ? t2 : 0) + n;
         TwoSource t;
         t.A0a = a.lat_up + h0 * a.L + 32 * g;
         t.A1a = t.A0a + (size_t)16 * a.L;
-        t.Xa = (part ? a.ylat_lo : a.ylat_hi) + (size_t)bb * a.L + 32 * g;
+        t.Xa = a.ylat + (size_t)bb * a.L + 32 * g;
         t.A0b = a.sh_w2 + h0 * a.Is + 32 * g;
         t.A1b = t.A0b + (size_t)16 * a.Is;
-        t.Xb = (part ? a.ash_lo : a.ash_hi) + (size_t)bb * a.Is + 32 * g;
+        t.Xb = a.ash + (size_t)bb * a.Is + 32 * g;
         t.Ls = a.L / kKStep;
         f32x4 acc0 = zero4(), acc1 = zero4();
-        out_chunk<SPC>(t, valid, s0, acc0, acc1);
-        acc0 = add_pair_column(acc0);
-        acc1 = add_pair_column(acc1);
-        const bool writer = valid && part == 0;
-        if (a.s_out > 1) {
-            float *mine = a.part_out + ((size_t)(t2 * a.s_out + c) * a.Bm + bb) * 32 + 4 * g;
-            if (writer) {
-                stf4(mine, acc0);
-                stf4(mine + 16, acc1);
-            }
-            uint32_t *ctr = a.ctr_out + t2 * a.ncg_out_cap + cg;
-            if (wave_arrive(ctr) != (uint32_t)(a.s_out - 1)) continue;
-            acquire_agent();
-            wave_store_counter(ctr, 0u);
-            if (!writer) continue;
-            acc0 = zero4();
-            acc1 = zero4();
-            const float *p = a.part_out + ((size_t)t2 * a.s_out * a.Bm + bb) * 32 + 4 * g;
-            for (int cc = 0; cc < a.s_out; ++cc, p += (size_t)a.Bm * 32) {
-                acc0 += ldf4(p);
-                acc1 += ldf4(p + 16);
+        if (active)
+            dense_chunk_out(t, valid, part, ro.kw * a.spc_out, (ro.kw + 1) * a.spc_out, acc0,
+                            acc1);
+        const bool leader = reduce_k(s_red, ro.wave, ro.kw, ro.KW, acc0, acc1);
+        if (leader && active) {
+            acc0 = add_pair_column(acc0);
+            acc1 = add_pair_column(acc1);
+            if (valid && part == 0) {
+                uint16_t *o = a.out + (size_t)b * a.H + 32 * t2 + 4 * g;
+                store_out4(o, acc0);
+                store_out4(o + 16, acc1);
             }
         }
-        if (writer) {
-            uint16_t *o = a.out + (size_t)b * a.H + 32 * t2 + 4 * g;
-            store_out4(o, acc0);
-            store_out4(o + 16, acc1);
-        }
+        __syncthreads();
     }
 }
 
@@ -516,10 +546,6 @@ struct DebugArgs {
     int32_t *n_active;
 };
 
-__device__ __forceinline__ float hl_val(const uint16_t *hi, const uint16_t *lo, size_t i) {
-    return bf16_val(hi[i]) + bf16_val(lo[i]);
-}
-
 __global__ void k_debug_export(const StepArgs a, const DebugArgs d) {
     const size_t tid = blockIdx.x * (size_t)blockDim.x + threadIdx.x;
     const size_t stride = (size_t)gridDim.x * blockDim.x;
@@ -530,16 +556,15 @@ __global__ void k_debug_export(const StepArgs a, const DebugArgs d) {
         if (d.key) d.key[i] = a.key[i];
     }
     for (size_t i = tid; i < nL; i += stride) {
-        if (d.z) d.z[i] = hl_val(a.z_hi, a.z_lo, i);
-        if (d.ylat) d.ylat[i] = hl_val(a.ylat_hi, a.ylat_lo, i);
+        if (d.z) d.z[i] = a.z[i];
+        if (d.ylat) d.ylat[i] = a.ylat[i];
     }
     for (size_t i = tid; i < nS; i += stride)
-        if (d.ash) d.ash[i] = hl_val(a.ash_hi, a.ash_lo, i);
+        if (d.ash) d.ash[i] = a.ash[i];
     for (size_t i = tid; i < nA; i += stride) {
         if (!d.act) break;
-        const size_t slot = i / a.I, col = i % a.I;
-        const size_t p = (size_t)a.pair_of_slot[slot];
-        d.act[i] = hl_val(a.act_hi, a.act_lo, p * a.I + col);
+        const size_t slot = i / a.I, c = i % a.I;
+        d.act[i] = a.act[(size_t)a.pair_of_slot[slot] * a.I + c];
     }
     if (tid == 0 && d.n_active) d.n_active[0] = a.meta[M_N_ACTIVE];
 }

@@ -21,24 +21,16 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
 int cdiv(int a, int b) { return (a + b - 1) / b; }
 
-// Split of a K range of `nsteps` 128-element steps into equal chunks of
-// `spc` steps (a divisor of nsteps, at most kMaxStepsPerChunk) so that
-// `units_per_split` x splits reaches about `target` wave units.
+// K split of one kernel: KW waves of a workgroup share the K range of a row
+// group, each taking SPC consecutive 128-element steps (KW * SPC = K / 128,
+// KW in {8, 4, 2, 1}, SPC <= kMaxStepsPerChunk); the largest KW is chosen.
 struct Split {
-    int s, spc;
+    int kw, spc;
 };
-Split choose_split(int units_per_split, int nsteps, int target) {
-    const long long want = std::max<long long>(1, (long long)nsteps * units_per_split / target);
-    int spc = 1;
-    for (int d = 1; d <= std::min(nsteps, kMaxStepsPerChunk); ++d)
-        if (nsteps % d == 0 && d <= want) spc = d;
-    return Split{nsteps / spc, spc};
-}
-
-int units_target() {
-    const char *s = std::getenv("MOE_DECODE_UNITS_TARGET");  // tuning sweeps only
-    int v = s ? std::atoi(s) : 0;
-    return v > 0 ? v : 4096;
+Split choose_split(int nsteps) {
+    for (int kw = kWG; kw >= 1; kw /= 2)
+        if (nsteps % kw == 0 && nsteps / kw <= kMaxStepsPerChunk) return Split{kw, nsteps / kw};
+    return Split{0, 0};
 }
 
 int ncols_cap(int E, int B, int k) { return std::min(E, B * k) + cdiv(B * k, 8); }
@@ -46,48 +38,38 @@ int ncols_cap(int E, int B, int k) { return std::min(E, B * k) + cdiv(B * k, 8);
 struct Plan {
     int n_r2, ncg_in, ncg_out;
     Split in, out, w13, w2;
+    long long units_in, units_out, units_13, units_2;
 };
 
 Plan make_plan(const moe_decode_config &c, int B, int k) {
-    const int target = units_target();
     Plan p;
     p.n_r2 = c.router_dtype == MOE_ROUTER_BF16 ? c.n_experts / 32 : 0;
     p.ncg_in = cdiv(B, 16);
     p.ncg_out = cdiv(B, 8);
+    p.in = choose_split(c.hidden / kKStep);
+    p.out = choose_split((c.latent + c.shared_inter) / kKStep);
+    p.w13 = choose_split(c.latent / kKStep);
+    p.w2 = choose_split(c.expert_inter / kKStep);
     const int n_t2_in = p.n_r2 + c.latent / 32 + c.shared_inter / 16;
-    p.in = choose_split(n_t2_in * p.ncg_in, c.hidden / kKStep, target);
-    p.out = choose_split((c.hidden / 32) * p.ncg_out, (c.latent + c.shared_inter) / kKStep, target);
-    const int cols = std::min(c.n_experts, B * k);  // typical column units
-    p.w13 = choose_split(cols * (c.expert_inter / 16), c.latent / kKStep, target);
-    p.w2 = choose_split(cols * (c.latent / 32), c.expert_inter / kKStep, target);
+    const long long cols = ncols_cap(c.n_experts, B, k);
+    p.units_in = (long long)cdiv(n_t2_in, kWG / p.in.kw) * p.ncg_in;
+    p.units_out = (long long)cdiv(c.hidden / 32, kWG / p.out.kw) * p.ncg_out;
+    p.units_13 = cols * cdiv(c.expert_inter / 16, kWG / p.w13.kw);
+    p.units_2 = cols * cdiv(c.latent / 32, kWG / p.w2.kw);
     return p;
 }
 
 struct Layout {
-    size_t gctr, meta, ctr_in, ctr_out, ctr13, ctr2, score, key, idx, wsel, act_expert, act_off,
-        cu_expert, cu_p0, cu_n, pair_slot, pair_of_slot, z_hi, z_lo, ash_hi, ash_lo, act_hi,
-        act_lo, ylat_hi, ylat_lo, part_in, part_out, part13, ypart, total;
+    size_t gctr, meta, score, key, idx, wsel, act_expert, act_off, cu_expert, cu_p0, cu_n,
+        pair_slot, pair_of_slot, z, ash, act, ylat, total;
     size_t counters_end;  // [0, counters_end) holds every counter: cleared at init
 };
 
 Layout make_layout(const moe_decode_config &c) {
     const size_t Bm = c.max_batch, km = c.max_top_k, E = c.n_experts, L = c.latent,
-                 I = c.expert_inter, Is = c.shared_inter, H = c.hidden;
+                 I = c.expert_inter, Is = c.shared_inter;
     const size_t P = Bm * km;
-    const size_t n_t2_in = (c.router_dtype == MOE_ROUTER_BF16 ? E / 32 : 0) + L / 32 + Is / 16;
-    const size_t n_t2_out = H / 32;
     const size_t ncols = (size_t)ncols_cap((int)E, (int)Bm, (int)km);
-    // Largest split any batch / top-k can use, times the pairs it serves.
-    size_t s_in = 1, s_out = 1, p13 = 1, p2 = 1;
-    for (int B = 1; B <= (int)Bm; ++B) {
-        for (int k = 1; k <= (int)km; ++k) {
-            const Plan pl = make_plan(c, B, k);
-            s_in = std::max(s_in, (size_t)pl.in.s);
-            s_out = std::max(s_out, (size_t)pl.out.s);
-            p13 = std::max(p13, (size_t)B * k * pl.w13.s);
-            p2 = std::max(p2, (size_t)B * k * pl.w2.s);
-        }
-    }
     Layout l;
     size_t o = 0;
     auto take = [&](size_t bytes) {
@@ -97,10 +79,6 @@ Layout make_layout(const moe_decode_config &c) {
     };
     l.gctr = take(G_COUNT * 4);
     l.meta = take(M_COUNT * 4);
-    l.ctr_in = take(n_t2_in * (size_t)cdiv((int)Bm, 16) * 4);
-    l.ctr_out = take(n_t2_out * (size_t)cdiv((int)Bm, 8) * 4);
-    l.ctr13 = take(ncols * (I / 16) * 4);
-    l.ctr2 = take((L / 32) * 4);
     l.counters_end = o;
     l.score = take(Bm * E * 4);
     l.key = take(Bm * E * 4);
@@ -113,28 +91,18 @@ Layout make_layout(const moe_decode_config &c) {
     l.cu_n = take(ncols * 4);
     l.pair_slot = take(P * 4);
     l.pair_of_slot = take(P * 4);
-    l.z_hi = take(Bm * L * 2);
-    l.z_lo = take(Bm * L * 2);
-    l.ash_hi = take(Bm * Is * 2);
-    l.ash_lo = take(Bm * Is * 2);
-    l.act_hi = take(P * I * 2);
-    l.act_lo = take(P * I * 2);
-    l.ylat_hi = take(Bm * L * 2);
-    l.ylat_lo = take(Bm * L * 2);
-    l.part_in = take(n_t2_in * s_in * Bm * 32 * 4);
-    l.part_out = take(n_t2_out * s_out * Bm * 32 * 4);
-    l.part13 = take(p13 * (I / 16) * 32 * 4);
-    l.ypart = take(p2 * L * 4);
+    l.z = take(Bm * L * 4);
+    l.ash = take(Bm * Is * 4);
+    l.act = take(P * I * 4);
+    l.ylat = take(Bm * L * 4);
     l.total = o;
     return l;
 }
 
 typedef void (*StepKernel)(const StepArgs);
 #define MOE_SPC_TABLE(K) {nullptr, K<1>, K<2>, K<3>, K<4>, K<5>, K<6>, K<7>, K<8>}
-const StepKernel kDenseIn[] = MOE_SPC_TABLE(k_dense_in);
 const StepKernel kW13[] = MOE_SPC_TABLE(k_w13);
 const StepKernel kW2[] = MOE_SPC_TABLE(k_w2);
-const StepKernel kOut[] = MOE_SPC_TABLE(k_out);
 #undef MOE_SPC_TABLE
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
@@ -179,8 +147,6 @@ StepArgs base_args(const moe_decode_ctx *ctx) {
     a.Is = c.shared_inter;
     a.Bm = c.max_batch;
     a.km = c.max_top_k;
-    a.ncg_in_cap = cdiv(c.max_batch, 16);
-    a.ncg_out_cap = cdiv(c.max_batch, 8);
     a.ncols_cap = ncols_cap(c.n_experts, c.max_batch, c.max_top_k);
     const moe_decode_weights &w = ctx->w;
     if (c.router_dtype == MOE_ROUTER_BF16)
@@ -198,10 +164,6 @@ StepArgs base_args(const moe_decode_ctx *ctx) {
     a.sh_w2 = w.sh_w2;
     a.gctr = (uint32_t *)(ws + l.gctr);
     a.meta = (int32_t *)(ws + l.meta);
-    a.ctr_in = (uint32_t *)(ws + l.ctr_in);
-    a.ctr_out = (uint32_t *)(ws + l.ctr_out);
-    a.ctr13 = (uint32_t *)(ws + l.ctr13);
-    a.ctr2 = (uint32_t *)(ws + l.ctr2);
     a.score = (float *)(ws + l.score);
     a.key = (float *)(ws + l.key);
     a.idx = (int32_t *)(ws + l.idx);
@@ -213,24 +175,15 @@ StepArgs base_args(const moe_decode_ctx *ctx) {
     a.cu_n = (int32_t *)(ws + l.cu_n);
     a.pair_slot = (int32_t *)(ws + l.pair_slot);
     a.pair_of_slot = (int32_t *)(ws + l.pair_of_slot);
-    a.z_hi = (uint16_t *)(ws + l.z_hi);
-    a.z_lo = (uint16_t *)(ws + l.z_lo);
-    a.ash_hi = (uint16_t *)(ws + l.ash_hi);
-    a.ash_lo = (uint16_t *)(ws + l.ash_lo);
-    a.act_hi = (uint16_t *)(ws + l.act_hi);
-    a.act_lo = (uint16_t *)(ws + l.act_lo);
-    a.ylat_hi = (uint16_t *)(ws + l.ylat_hi);
-    a.ylat_lo = (uint16_t *)(ws + l.ylat_lo);
-    a.part_in = (float *)(ws + l.part_in);
-    a.part_out = (float *)(ws + l.part_out);
-    a.part13 = (float *)(ws + l.part13);
-    a.ypart = (float *)(ws + l.ypart);
+    a.z = (float *)(ws + l.z);
+    a.ash = (float *)(ws + l.ash);
+    a.act = (float *)(ws + l.act);
+    a.ylat = (float *)(ws + l.ylat);
     return a;
 }
 
 int grid_for(long long units, long long cap_blocks) {
-    long long blocks = (units + kWavesPerBlock - 1) / kWavesPerBlock;
-    return (int)std::max(1LL, std::min(blocks, cap_blocks));
+    return (int)std::max(1LL, std::min(units, cap_blocks));
 }
 
 }  // namespace
@@ -250,6 +203,10 @@ moe_status moe_decode_validate_config(const moe_decode_config *c) {
         c->shared_inter % kKStep)
         return MOE_ERR_UNSUPPORTED;
     if (c->n_experts % 32 || c->n_experts > kMaxExperts) return MOE_ERR_UNSUPPORTED;
+    // Every reduction length must split into KW x SPC steps (see choose_split).
+    const int ks[4] = {c->hidden, c->latent, c->expert_inter, c->latent + c->shared_inter};
+    for (int K : ks)
+        if (choose_split(K / kKStep).kw == 0) return MOE_ERR_UNSUPPORTED;
     // Offsets are formed in 32-bit ints where they index one token or pair.
     if ((long long)c->hidden * c->shared_inter > (1LL << 31) ||
         (long long)c->n_experts * 2 * c->expert_inter > (1LL << 31))
@@ -345,35 +302,26 @@ moe_status moe_decode_step(moe_decode_ctx *ctx, const uint16_t *x, int32_t batch
     a.user_w = topk_w;
     a.n_r2 = pl.n_r2;
     a.router_target = c.router_dtype == MOE_ROUTER_BF16 ? pl.n_r2 * pl.ncg_in : c.n_experts;
-    a.s_in = pl.in.s;
+    a.kw_in = pl.in.kw;
+    a.kw_out = pl.out.kw;
+    a.kw13 = pl.w13.kw;
+    a.kw2 = pl.w2.kw;
     a.spc_in = pl.in.spc;
-    a.s_out = pl.out.s;
     a.spc_out = pl.out.spc;
-    a.s13 = pl.w13.s;
-    a.spc13 = pl.w13.spc;
-    a.s2 = pl.w2.s;
-    a.spc2 = pl.w2.spc;
-
-    const int n_t2_in = pl.n_r2 + c.latent / 32 + c.shared_inter / 16;
-    const long long units_in = (long long)n_t2_in * pl.ncg_in * pl.in.s;
-    const long long units_out = (long long)(c.hidden / 32) * pl.ncg_out * pl.out.s;
-    const long long cols = ncols_cap(c.n_experts, batch, top_k);
-    const long long units_13 = cols * (c.expert_inter / 16) * pl.w13.s;
-    const long long units_2 = cols * (c.latent / 32) * pl.w2.s;
-    const long long cap = 8192;  // blocks; larger grids loop over their units
+    const long long cap = 65535;  // workgroups; larger unit counts loop
 
     moe_decode_dispatch_info &d = ctx->last;
     d.batch = batch;
     d.top_k = top_k;
     d.col_tiles = pl.ncg_in;
-    d.split_in = pl.in.s;
-    d.split_out = pl.out.s;
-    d.split_w13 = pl.w13.s;
-    d.split_w2 = pl.w2.s;
-    d.grid_in = grid_for(units_in, cap);
-    d.grid_w13 = grid_for(units_13, cap);
-    d.grid_w2 = grid_for(units_2, cap);
-    d.grid_out = grid_for(units_out, cap);
+    d.split_in = pl.in.kw;
+    d.split_out = pl.out.kw;
+    d.split_w13 = pl.w13.kw;
+    d.split_w2 = pl.w2.kw;
+    d.grid_in = grid_for(pl.units_in, cap);
+    d.grid_w13 = grid_for(pl.units_13, cap);
+    d.grid_w2 = grid_for(pl.units_2, cap);
+    d.grid_out = grid_for(pl.units_out, cap);
     d.router_f32 = c.router_dtype == MOE_ROUTER_F32;
     d.n_kernels = 4 + d.router_f32;
 
@@ -384,16 +332,17 @@ moe_status moe_decode_step(moe_decode_ctx *ctx, const uint16_t *x, int32_t batch
     };
     mark();
     if (d.router_f32) {
-        hipLaunchKernelGGL(k_router_f32, dim3(grid_for(c.n_experts, cap)), dim3(kBlock), 0, s, a);
+        hipLaunchKernelGGL(k_router_f32, dim3(cdiv(c.n_experts, kWavesPerBlock)), dim3(kBlock), 0,
+                           s, a);
         mark();
     }
-    hipLaunchKernelGGL(kDenseIn[pl.in.spc], dim3(d.grid_in), dim3(kBlock), 0, s, a);
+    hipLaunchKernelGGL(k_dense_in, dim3(d.grid_in), dim3(kWGThreads), 0, s, a);
     mark();
-    hipLaunchKernelGGL(kW13[pl.w13.spc], dim3(d.grid_w13), dim3(kBlock), 0, s, a);
+    hipLaunchKernelGGL(kW13[pl.w13.spc], dim3(d.grid_w13), dim3(kWGThreads), 0, s, a);
     mark();
-    hipLaunchKernelGGL(kW2[pl.w2.spc], dim3(d.grid_w2), dim3(kBlock), 0, s, a);
+    hipLaunchKernelGGL(kW2[pl.w2.spc], dim3(d.grid_w2), dim3(kWGThreads), 0, s, a);
     mark();
-    hipLaunchKernelGGL(kOut[pl.out.spc], dim3(d.grid_out), dim3(kBlock), 0, s, a);
+    hipLaunchKernelGGL(k_out, dim3(d.grid_out), dim3(kWGThreads), 0, s, a);
     mark();
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(ctx, e);

@@ -26,32 +26,27 @@ __device__ __forceinline__ uint64_t pack_key(float key, int e) {
     return ((uint64_t)ord << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
 }
 
-// Top-k of one token, by one wave.  Lane l holds the keys of experts
-// l, l+64, ...; k rounds of a wave-wide maximum pick the experts in key order;
-// they are then written in ascending id with weights s_e / sum(s).
-__device__ __noinline__ void topk_token(const StepArgs &a, int b) {
+// Top-k of one token, by one wave.  The token's keys are staged in the
+// wave's LDS buffer; lane l owns experts l, l+64, ...; k rounds of a
+// wave-wide maximum pick the experts in key order; they are then written in
+// ascending id with weights s_e / sum(s).
+__device__ __forceinline__ void topk_token(const StepArgs &a, int b, float *s_keys) {
     const int lane = lane_id();
     const int E = a.E, k = a.k;
     const float *keyrow = a.key + (size_t)b * E;
+    for (int e = lane; e < E; e += kWave) s_keys[e] = keyrow[e];
+    wave_sync();
     const int nk = (E + kWave - 1) / kWave;
-    float kv[kKeysPerLane];
     uint32_t avail = 0;
-#pragma unroll
-    for (int i = 0; i < kKeysPerLane; ++i) {
-        const int e = lane + kWave * i;
-        const bool ok = i < nk && e < E;
-        kv[i] = ok ? keyrow[e] : 0.f;
-        avail |= ok ? (1u << i) : 0u;
-    }
+    for (int i = 0; i < nk; ++i) avail |= (lane + kWave * i < E) ? (1u << i) : 0u;
     // First maximum of this lane's available keys in ascending id, packed.
     auto local_best = [&]() {
         float bk = 0.f;
         int bi = -1;
-#pragma unroll
-        for (int i = 0; i < kKeysPerLane; ++i) {
-            if (i >= nk) break;
-            const bool take = ((avail >> i) & 1u) && (bi < 0 || kv[i] > bk);
-            bk = take ? kv[i] : bk;
+        for (int i = 0; i < nk; ++i) {
+            const float v = s_keys[lane + kWave * i];
+            const bool take = ((avail >> i) & 1u) && (bi < 0 || v > bk);
+            bk = take ? v : bk;
             bi = take ? i : bi;
         }
         return bi < 0 ? (uint64_t)0 : pack_key(bk, lane + kWave * bi);
@@ -79,13 +74,14 @@ __device__ __noinline__ void topk_token(const StepArgs &a, int b) {
         if (a.user_idx) a.user_idx[o] = mine;
         if (a.user_w) a.user_w[o] = w;
     }
+    wave_sync();
 }
 
 // Routing metadata from idx [B][k], by one wave, with an LDS bit mask of the
 // tokens of each expert.  Active experts are listed in ascending id; the pairs
 // of an expert in ascending token; each expert's pairs are cut into column
 // units of at most 8 tokens (16 MFMA columns: hi and lo of each token).
-__device__ __noinline__ void build_meta(const StepArgs &a, unsigned long long *s_mask) {
+__device__ __forceinline__ void build_meta(const StepArgs &a, unsigned long long *s_mask) {
     const int lane = lane_id();
     const int B = a.B, k = a.k, E = a.E;
     for (int e = lane; e < E; e += kWave) s_mask[e] = 0ull;
@@ -140,13 +136,16 @@ __device__ __noinline__ void build_meta(const StepArgs &a, unsigned long long *s
 }
 
 // Claims tokens until none is left; the wave that finishes the last token
-// builds the metadata.  Called only once the router is complete.
-__device__ __noinline__ void topk_loop(const StepArgs &a, unsigned long long *s_mask) {
+// builds the metadata.  Called only once the router is complete.  s_keys is
+// the calling wave's own LDS buffer of kMaxExperts floats.
+__device__ __forceinline__ void topk_loop(const StepArgs &a, unsigned long long *s_mask,
+                                       float *s_keys) {
     acquire_agent();
-    for (;;) {
+    // Claims are unique, so one wave can never claim more than B tokens.
+    for (int it = 0; it < a.B; ++it) {
         const uint32_t t = wave_fetch_add(&a.gctr[G_NEXT_TOKEN], 1u);
         if (t >= (uint32_t)a.B) break;
-        topk_token(a, (int)t);
+        topk_token(a, (int)t, s_keys);
         if (wave_arrive(&a.gctr[G_TOKENS_DONE]) == (uint32_t)a.B - 1u) {
             acquire_agent();
             build_meta(a, s_mask);
@@ -156,10 +155,11 @@ __device__ __noinline__ void topk_loop(const StepArgs &a, unsigned long long *s_
 
 // A wave that finished a tile helps with the top-k when the router is
 // complete and tokens are still unclaimed.
-__device__ __forceinline__ void maybe_join_topk(const StepArgs &a, unsigned long long *s_mask) {
+__device__ __forceinline__ void maybe_join_topk(const StepArgs &a, unsigned long long *s_mask,
+                                                float *s_keys) {
     if (wave_load_counter(&a.gctr[G_ROUTER_DONE]) != (uint32_t)a.router_target) return;
     if (wave_load_counter(&a.gctr[G_NEXT_TOKEN]) >= (uint32_t)a.B) return;
-    topk_loop(a, s_mask);
+    topk_loop(a, s_mask, s_keys);
 }
 
 }  // namespace moe

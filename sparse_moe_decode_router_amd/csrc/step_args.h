@@ -12,14 +12,12 @@ struct StepArgs {
     int32_t H, L, E, I, Is;   // hidden, latent, experts, expert inter., shared inter.
     int32_t B, k;             // tokens and experts per token of this step
     int32_t Bm, km;           // capacities (context max_batch / max_top_k)
-    // Launch plan.
+    // Launch plan: waves of a workgroup that split K in each kernel (the
+    // rest of the 8 waves take further row groups).
     int32_t n_r2;             // 32-row router tiles computed by the dense input kernel
     int32_t router_target;    // arrivals on G_ROUTER_DONE that complete the router
-    int32_t s_in, spc_in;     // K splits / steps per split: router + latent-down + shared gate/up
-    int32_t s_out, spc_out;   // latent-up + shared-down
-    int32_t s13, spc13;       // expert gate/up
-    int32_t s2, spc2;         // expert down
-    int32_t ncg_in_cap, ncg_out_cap;  // column-group strides of the dense counters
+    int32_t kw_in, kw_out, kw13, kw2;
+    int32_t spc_in, spc_out;  // 128-element steps per wave in the dense kernels
     int32_t ncols_cap;        // capacity of the expert column-unit list
     // Weights (borrowed).
     const uint16_t *router_w;
@@ -34,14 +32,13 @@ struct StepArgs {
     int32_t *user_idx;
     float *user_w;
     // Workspace.
-    uint32_t *gctr, *ctr_in, *ctr_out, *ctr13, *ctr2;
+    uint32_t *gctr;
     int32_t *meta;
     float *score, *key;
     int32_t *idx;
     float *wsel;
     int32_t *act_expert, *act_off, *cu_expert, *cu_p0, *cu_n, *pair_slot, *pair_of_slot;
-    uint16_t *z_hi, *z_lo, *ash_hi, *ash_lo, *act_hi, *act_lo, *ylat_hi, *ylat_lo;
-    float *part_in, *part_out, *part13, *ypart;
+    float *z, *ash, *act, *ylat;  // f32 intermediates
 };
 
 }  // namespace moe

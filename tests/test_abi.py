@@ -62,7 +62,8 @@ def validate(c):
     (dict(expert_inter=2000), binding.MOE_ERR_UNSUPPORTED),
     (dict(shared_inter=100), binding.MOE_ERR_UNSUPPORTED),
     (dict(n_experts=900), binding.MOE_ERR_UNSUPPORTED),
-    (dict(n_experts=4096), binding.MOE_ERR_UNSUPPORTED),
+    (dict(n_experts=1056), binding.MOE_ERR_UNSUPPORTED),
+    (dict(n_experts=1024), binding.MOE_OK),
     (dict(router_dtype=2), binding.MOE_ERR_INVALID_ARG),
     (dict(hidden=-128), binding.MOE_ERR_INVALID_ARG),
 ])

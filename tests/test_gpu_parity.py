@@ -180,18 +180,30 @@ def test_all_experts_selected():
     check_step(layer, x, 32, out, idx, w)
 
 
-def test_repeated_steps_are_bitwise_identical(small_layer, small_ctx):
+def assert_same_step(a, b):
+    """Two runs of one step: identical expert ids and weights; outputs equal
+    up to the order of the f32 atomic adds of the expert combine, which can
+    move a bf16 output to its neighbour (one unit in the last place)."""
+    np.testing.assert_array_equal(a[1], b[1])
+    np.testing.assert_array_equal(a[2], b[2])
+    da, db = a[0].astype(np.int32), b[0].astype(np.int32)
+    same_sign = (da >> 15) == (db >> 15)
+    assert np.all(same_sign | (da == db) | ((da & 0x7FFF) == 0) | ((db & 0x7FFF) == 0))
+    assert np.max(np.abs((da & 0x7FFF) - (db & 0x7FFF))) <= 1
+    assert np.mean(da != db) < 1e-2
+
+
+def test_repeated_steps_agree(small_layer, small_ctx):
     x = synth.make_tokens(small_layer.dims, 11, 24)
     a = run(small_ctx, x, 6)
     for _ in range(3):
-        b = run(small_ctx, x, 6)
-        for u, v in zip(a, b):
-            np.testing.assert_array_equal(u, v)
+        assert_same_step(a, run(small_ctx, x, 6))
 
 
 def test_graph_replays_match_eager_and_track_new_inputs(small_layer):
-    """Captured graph = eager bit for bit; replays with a changed input (the
-    same device buffer) give the new input's result, not a stale one."""
+    """A captured two-layer graph gives the eager result; replays with a
+    changed input (the same device buffer) give the new input's result, not
+    a stale one; eager work runs between replays."""
     import torch
     ctxs = [make_ctx(small_layer, 8, 6) for _ in range(2)]
     B, k = 8, 6
@@ -215,9 +227,9 @@ def test_graph_replays_match_eager_and_track_new_inputs(small_layer):
         g.launch(stream)
         stream.synchronize()
         for layer_i in range(2):
-            np.testing.assert_array_equal(outs[layer_i].cpu().numpy().view(np.uint16), want[0])
-            np.testing.assert_array_equal(idxs[layer_i].cpu().numpy(), want[1])
-            np.testing.assert_array_equal(ws[layer_i].cpu().numpy(), want[2])
+            got = (outs[layer_i].cpu().numpy().view(np.uint16), idxs[layer_i].cpu().numpy(),
+                   ws[layer_i].cpu().numpy())
+            assert_same_step(got, want)
         run(ctxs[1], x2, k)        # eager work between replays
     g.close()
 
