@@ -50,17 +50,6 @@ constexpr int kWGThreads = kWG * kWave;
 // Operand loads
 // ---------------------------------------------------------------------------
 
-__device__ __forceinline__ void load_rows_bf16(const uint16_t *A0, const uint16_t *A1, int s,
-                                               u32x4 (&ra)[8]) {
-    const uint16_t *p0 = A0 + (size_t)s * kKStep;
-    const uint16_t *p1 = A1 + (size_t)s * kKStep;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        ra[j] = ld_weight16(p0 + 8 * j);
-        ra[4 + j] = ld_weight16(p1 + 8 * j);
-    }
-}
-
 // bf16 column operand of one step (x).  Lanes without a token read a valid
 // row (the caller points them at one) and drop the value, so no load sits
 // under a lane-dependent branch.
@@ -108,57 +97,79 @@ __device__ __forceinline__ void load_cols_f32(const float *X, bool valid, int pa
 // step and serialises several memory round trips per step.
 __device__ __forceinline__ void fence_schedule() { __builtin_amdgcn_sched_barrier(0); }
 
-__device__ __forceinline__ void mfma_step(const u32x4 (&ra)[8], const u32x4 (&rb)[4], f32x4 &acc0,
-                                          f32x4 &acc1) {
+// One 16-row bf16 tile: lane (r = l%16, g = l/16) loads row r's 64 bytes at
+// elements [32g, 32g+32) of step s.
+__device__ __forceinline__ void load_tile_bf16(const uint16_t *A, int s, u32x4 (&ra)[4]) {
+    const uint16_t *p = A + (size_t)s * kKStep;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const bf16x8 b = as_bf16x8(rb[j]);
-        acc0 = mfma(as_bf16x8(ra[j]), b, acc0);
-        acc1 = mfma(as_bf16x8(ra[4 + j]), b, acc1);
-    }
+    for (int j = 0; j < 4; ++j) ra[j] = ld_weight16(p + 8 * j);
 }
 
-// acc0/acc1 += bf16 rows A0/A1 (16 each) . bf16 columns X over steps
-// [s0, s1), one step (8 KB of weights per wave) in flight at a time.
-__device__ __forceinline__ void dense_chunk_x(const uint16_t *A0, const uint16_t *A1,
-                                              const uint16_t *X, bool valid, int s0, int s1,
-                                              f32x4 &acc0, f32x4 &acc1) {
+__device__ __forceinline__ void mfma_tile(const u32x4 (&ra)[4], const u32x4 (&rb)[4], f32x4 &acc) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc = mfma(as_bf16x8(ra[j]), as_bf16x8(rb[j]), acc);
+}
+
+// acc += bf16 tile A . bf16 columns X over steps [s0, s1), two steps (8 KB of
+// weights per wave) in flight at a time.
+__device__ __forceinline__ void dense_chunk_x(const uint16_t *A, const uint16_t *X, bool valid,
+                                              int s0, int s1, f32x4 &acc) {
+    int s = s0;
 #pragma unroll 1
-    for (int s = s0; s < s1; ++s) {
-        u32x4 ra[8], rb[4];
-        load_rows_bf16(A0, A1, s, ra);
-        load_cols_bf16(X, valid, s, rb);
+    for (; s + 1 < s1; s += 2) {
+        u32x4 ra0[4], rb0[4], ra1[4], rb1[4];
+        load_tile_bf16(A, s, ra0);
+        load_tile_bf16(A, s + 1, ra1);
+        load_cols_bf16(X, valid, s, rb0);
+        load_cols_bf16(X, valid, s + 1, rb1);
         fence_schedule();
-        mfma_step(ra, rb, acc0, acc1);
+        mfma_tile(ra0, rb0, acc);
+        mfma_tile(ra1, rb1, acc);
+    }
+    if (s < s1) {
+        u32x4 ra0[4], rb0[4];
+        load_tile_bf16(A, s, ra0);
+        load_cols_bf16(X, valid, s, rb0);
+        fence_schedule();
+        mfma_tile(ra0, rb0, acc);
     }
 }
 
 // Output kernel: K runs over [0, L) against lat_up and ylat, then over
 // [0, Is) against sh_w2 and ash; step s < Ls selects the first pair.
 struct TwoSource {
-    const uint16_t *A0a, *A1a;
+    const uint16_t *Aa;
     const float *Xa;  // K in [0, L)
-    const uint16_t *A0b, *A1b;
+    const uint16_t *Ab;
     const float *Xb;  // K in [0, Is)
     int Ls;           // L / 128
 };
 
 __device__ __forceinline__ void load_two(const TwoSource &t, bool valid, int part, int s,
-                                         u32x4 (&ra)[8], u32x4 (&rb)[4]) {
+                                         u32x4 (&ra)[4], u32x4 (&rb)[4]) {
     const bool first = s < t.Ls;
     const int ss = first ? s : s - t.Ls;
-    load_rows_bf16(first ? t.A0a : t.A0b, first ? t.A1a : t.A1b, ss, ra);
+    load_tile_bf16(first ? t.Aa : t.Ab, ss, ra);
     load_cols_f32(first ? t.Xa : t.Xb, valid, part, ss, rb);
 }
 
 __device__ __forceinline__ void dense_chunk_out(const TwoSource &t, bool valid, int part, int s0,
-                                                int s1, f32x4 &acc0, f32x4 &acc1) {
+                                                int s1, f32x4 &acc) {
+    int s = s0;
 #pragma unroll 1
-    for (int s = s0; s < s1; ++s) {
-        u32x4 ra[8], rb[4];
-        load_two(t, valid, part, s, ra, rb);
+    for (; s + 1 < s1; s += 2) {
+        u32x4 ra0[4], rb0[4], ra1[4], rb1[4];
+        load_two(t, valid, part, s, ra0, rb0);
+        load_two(t, valid, part, s + 1, ra1, rb1);
         fence_schedule();
-        mfma_step(ra, rb, acc0, acc1);
+        mfma_tile(ra0, rb0, acc);
+        mfma_tile(ra1, rb1, acc);
+    }
+    if (s < s1) {
+        u32x4 ra0[4], rb0[4];
+        load_two(t, valid, part, s, ra0, rb0);
+        fence_schedule();
+        mfma_tile(ra0, rb0, acc);
     }
 }
 
@@ -236,6 +247,19 @@ __device__ __forceinline__ bool reduce_k(float *s_red, int wave, int kw, int KW,
     return true;
 }
 
+// Single-tile form of reduce_k.
+__device__ __forceinline__ bool reduce_k1(float *s_red, int wave, int kw, int KW, f32x4 &acc) {
+    const int lane = lane_id();
+    stf4(s_red + (wave * kWave + lane) * 4, acc);
+    __syncthreads();
+    if (kw != 0) return false;
+    if (KW > 1) {
+        acc = zero4();
+        for (int j = 0; j < KW; ++j) acc += ldf4(s_red + ((wave + j) * kWave + lane) * 4);
+    }
+    return true;
+}
+
 struct Role {
     int wave, KW, RW, rg, kw;
 };
@@ -256,9 +280,7 @@ __device__ __forceinline__ Role role_of(int KW) {
 
 __global__ void __launch_bounds__(kBlock) k_router_f32(const StepArgs a) {
     __shared__ unsigned long long s_mask[kMaxExperts];
-    __shared__ float s_keys[kWavesPerBlock][kMaxExperts];
     const int wave = wave_index();
-    float *my_keys = s_keys[wave];
     const int lane = lane_id();
     const int nwaves = gridDim.x * kWavesPerBlock;
     for (int e = blockIdx.x * kWavesPerBlock + wave; e < a.E; e += nwaves) {
@@ -275,9 +297,9 @@ __global__ void __launch_bounds__(kBlock) k_router_f32(const StepArgs a) {
             }
         }
         if (wave_arrive(&a.gctr[G_ROUTER_DONE]) == (uint32_t)a.router_target - 1u)
-            topk_loop(a, s_mask, my_keys);
+            topk_loop(a, s_mask);
         else
-            maybe_join_topk(a, s_mask, my_keys);
+            maybe_join_topk(a, s_mask);
     }
 }
 
@@ -285,90 +307,78 @@ __global__ void __launch_bounds__(kBlock) k_router_f32(const StepArgs a) {
 // Kernel 1: router + latent-down + shared gate/up over x.
 // ---------------------------------------------------------------------------
 
+// Tiles of 16 rows, in this order: router (E/16), latent-down (L/16), shared
+// (Is/8: gate rows 8p..8p+7 and up rows 8p..8p+7 in one tile, so SwiGLU pairs
+// D rows i and 8+i, held by lanes l and l+32).
 __global__ void __launch_bounds__(kWGThreads) __attribute__((amdgpu_waves_per_eu(4)))
 k_dense_in(const StepArgs a) {
     __shared__ unsigned long long s_mask[kMaxExperts];
-    __shared__ float s_keys[kWG][kMaxExperts];
-    __shared__ float s_red[kWG * kWave * 8];
+    __shared__ float s_red[kWG * kWave * 4];
     const int lane = lane_id(), n = lane & 15, g = lane >> 4;
     const Role ro = role_of(a.kw_in);
-    float *my_keys = s_keys[ro.wave];
     // The latent combine accumulates into ylat with atomics later in the step.
     for (int i = (blockIdx.x * kWGThreads + threadIdx.x) * 4; i < a.B * a.L;
          i += gridDim.x * kWGThreads * 4)
         stf4(a.ylat + i, zero4());
-    const int n_l2 = a.L >> 5, n_s2 = a.Is >> 4;
-    const int n_t2 = a.n_r2 + n_l2 + n_s2;
+    const int n_rt = a.n_r16, n_lt = a.L >> 4, n_st = a.Is >> 3;
+    const int n_t = n_rt + n_lt + n_st;
     const int ncg = (a.B + 15) >> 4;
-    const int tgroups = (n_t2 + ro.RW - 1) / ro.RW;
+    const int tgroups = (n_t + ro.RW - 1) / ro.RW;
     const int units = tgroups * ncg;
     for (int u = blockIdx.x; u < units; u += gridDim.x) {
         const int cg = u % ncg;
-        const int t2 = (u / ncg) * ro.RW + ro.rg;
-        const bool active = t2 < n_t2;
-        const int tt = active ? t2 : 0;
+        const int t = (u / ncg) * ro.RW + ro.rg;
+        const bool active = t < n_t;
+        const int tt = active ? t : 0;
         int kind;
-        const uint16_t *A0, *A1;
-        if (tt < a.n_r2) {
+        const uint16_t *A;
+        if (tt < n_rt) {
             kind = 0;
-            A0 = a.router_w + (size_t)(32 * tt + n) * a.H;
-            A1 = A0 + (size_t)16 * a.H;
-        } else if (tt < a.n_r2 + n_l2) {
+            A = a.router_w + (size_t)(16 * tt + n) * a.H;
+        } else if (tt < n_rt + n_lt) {
             kind = 1;
-            A0 = a.lat_down + (size_t)(32 * (tt - a.n_r2) + n) * a.H;
-            A1 = A0 + (size_t)16 * a.H;
+            A = a.lat_down + (size_t)(16 * (tt - n_rt) + n) * a.H;
         } else {
             kind = 2;
-            const int pt = tt - a.n_r2 - n_l2;
-            A0 = a.sh_w13 + (size_t)(16 * pt + n) * a.H;
-            A1 = a.sh_w13 + (size_t)(a.Is + 16 * pt + n) * a.H;
+            const int p = tt - n_rt - n_lt;
+            A = a.sh_w13 + (size_t)((n < 8 ? 0 : a.Is) + 8 * p + (n & 7)) * a.H;
         }
         const int b = 16 * cg + n;
         const bool valid = b < a.B;
         const uint16_t *X = a.x + (size_t)(valid ? b : 0) * a.H + 32 * g;
-        f32x4 acc0 = zero4(), acc1 = zero4();
+        f32x4 acc = zero4();
         if (active)
-            dense_chunk_x(A0 + 32 * g, A1 + 32 * g, X, valid, ro.kw * a.spc_in,
-                          (ro.kw + 1) * a.spc_in, acc0, acc1);
-        const bool leader = reduce_k(s_red, ro.wave, ro.kw, ro.KW, acc0, acc1);
+            dense_chunk_x(A + 32 * g, X, valid, ro.kw * a.spc_in, (ro.kw + 1) * a.spc_in, acc);
+        const bool leader = reduce_k1(s_red, ro.wave, ro.kw, ro.KW, acc);
         if (leader && active) {
             if (kind == 0) {
-                const int e = 32 * tt + 4 * g;
+                const int e = 16 * tt + 4 * g;
                 if (valid) {
-                    f32x4 s0v, s1v;
+                    f32x4 sv;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        s0v[i] = sigmoidf_(acc0[i]);
-                        s1v[i] = sigmoidf_(acc1[i]);
-                    }
-                    const f32x4 b0 = a.bias ? ldf4(a.bias + e) : zero4();
-                    const f32x4 b1 = a.bias ? ldf4(a.bias + e + 16) : zero4();
-                    float *sr = a.score + (size_t)b * a.E + e;
-                    float *kr = a.key + (size_t)b * a.E + e;
-                    stf4(sr, s0v);
-                    stf4(sr + 16, s1v);
-                    stf4(kr, s0v + b0);
-                    stf4(kr + 16, s1v + b1);
+                    for (int i = 0; i < 4; ++i) sv[i] = sigmoidf_(acc[i]);
+                    const f32x4 bv = a.bias ? ldf4(a.bias + e) : zero4();
+                    stf4(a.score + (size_t)b * a.E + e, sv);
+                    stf4(a.key + (size_t)b * a.E + e, sv + bv);
                 }
                 if (wave_arrive(&a.gctr[G_ROUTER_DONE]) == (uint32_t)a.router_target - 1u)
-                    topk_loop(a, s_mask, my_keys);
+                    topk_loop(a, s_mask);
             } else if (kind == 1) {
-                if (valid) {
-                    float *zr = a.z + (size_t)b * a.L + 32 * (tt - a.n_r2) + 4 * g;
-                    stf4(zr, acc0);
-                    stf4(zr + 16, acc1);
-                }
+                if (valid) stf4(a.z + (size_t)b * a.L + 16 * (tt - n_rt) + 4 * g, acc);
             } else {
-                if (valid) {
+                f32x4 up;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) up[i] = __shfl_xor(acc[i], 32);
+                if (valid && g < 2) {
                     f32x4 v;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) v[i] = silu_mul(acc0[i], acc1[i]);
-                    stf4(a.ash + (size_t)b * a.Is + 16 * (tt - a.n_r2 - n_l2) + 4 * g, v);
+                    for (int i = 0; i < 4; ++i) v[i] = silu_mul(acc[i], up[i]);
+                    stf4(a.ash + (size_t)b * a.Is + 8 * (tt - n_rt - n_lt) + 4 * g, v);
                 }
             }
         }
         __syncthreads();
-        if (a.n_r2 > 0) maybe_join_topk(a, s_mask, my_keys);
+        if (n_rt > 0) maybe_join_topk(a, s_mask);
     }
 }
 
@@ -476,7 +486,7 @@ __device__ __forceinline__ void store_out4(uint16_t *dst, f32x4 v) {
 
 __global__ void __launch_bounds__(kWGThreads) __attribute__((amdgpu_waves_per_eu(4)))
 k_out(const StepArgs a) {
-    __shared__ float s_red[kWG * kWave * 8];
+    __shared__ float s_red[kWG * kWave * 4];
     // The routing counters of the dense input kernel are cleared here, where
     // no wave of the step can touch them any more.
     if (blockIdx.x == 0 && threadIdx.x < 3) a.gctr[threadIdx.x] = 0u;
@@ -484,38 +494,30 @@ k_out(const StepArgs a) {
     const int col = n >> 1, part = n & 1;
     const Role ro = role_of(a.kw_out);
     const int ncg = (a.B + 7) >> 3;
-    const int n_t2 = a.H >> 5;
-    const int tgroups = (n_t2 + ro.RW - 1) / ro.RW;
+    const int n_t = a.H >> 4;
+    const int tgroups = (n_t + ro.RW - 1) / ro.RW;
     const int units = tgroups * ncg;
     for (int u = blockIdx.x; u < units; u += gridDim.x) {
         const int cg = u % ncg;
-        const int t2 = (u / ncg) * ro.RW + ro.rg;
-        const bool active = t2 < n_t2;
+        const int t = (u / ncg) * ro.RW + ro.rg;
+        const bool active = t < n_t;
         const int b = 8 * cg + col;
         const bool valid = b < a.B;
         const int bb = valid ? b : 0;
-        const size_t h0 = 32 * (size_t)(active ? t2 : 0) + n;
-        TwoSource t;
-        t.A0a = a.lat_up + h0 * a.L + 32 * g;
-        t.A1a = t.A0a + (size_t)16 * a.L;
-        t.Xa = a.ylat + (size_t)bb * a.L + 32 * g;
-        t.A0b = a.sh_w2 + h0 * a.Is + 32 * g;
-        t.A1b = t.A0b + (size_t)16 * a.Is;
-        t.Xb = a.ash + (size_t)bb * a.Is + 32 * g;
-        t.Ls = a.L / kKStep;
-        f32x4 acc0 = zero4(), acc1 = zero4();
+        const size_t h = 16 * (size_t)(active ? t : 0) + n;
+        TwoSource ts;
+        ts.Aa = a.lat_up + h * a.L + 32 * g;
+        ts.Xa = a.ylat + (size_t)bb * a.L + 32 * g;
+        ts.Ab = a.sh_w2 + h * a.Is + 32 * g;
+        ts.Xb = a.ash + (size_t)bb * a.Is + 32 * g;
+        ts.Ls = a.L / kKStep;
+        f32x4 acc = zero4();
         if (active)
-            dense_chunk_out(t, valid, part, ro.kw * a.spc_out, (ro.kw + 1) * a.spc_out, acc0,
-                            acc1);
-        const bool leader = reduce_k(s_red, ro.wave, ro.kw, ro.KW, acc0, acc1);
+            dense_chunk_out(ts, valid, part, ro.kw * a.spc_out, (ro.kw + 1) * a.spc_out, acc);
+        const bool leader = reduce_k1(s_red, ro.wave, ro.kw, ro.KW, acc);
         if (leader && active) {
-            acc0 = add_pair_column(acc0);
-            acc1 = add_pair_column(acc1);
-            if (valid && part == 0) {
-                uint16_t *o = a.out + (size_t)b * a.H + 32 * t2 + 4 * g;
-                store_out4(o, acc0);
-                store_out4(o + 16, acc1);
-            }
+            acc = add_pair_column(acc);
+            if (valid && part == 0) store_out4(a.out + (size_t)b * a.H + 16 * t + 4 * g, acc);
         }
         __syncthreads();
     }

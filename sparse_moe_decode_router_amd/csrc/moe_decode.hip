@@ -36,24 +36,26 @@ Split choose_split(int nsteps) {
 int ncols_cap(int E, int B, int k) { return std::min(E, B * k) + cdiv(B * k, 8); }
 
 struct Plan {
-    int n_r2, ncg_in, ncg_out;
+    int n_r16, ncg_in, ncg_out;
     Split in, out, w13, w2;
     long long units_in, units_out, units_13, units_2;
 };
 
 Plan make_plan(const moe_decode_config &c, int B, int k) {
     Plan p;
-    p.n_r2 = c.router_dtype == MOE_ROUTER_BF16 ? c.n_experts / 32 : 0;
+    p.n_r16 = c.router_dtype == MOE_ROUTER_BF16 ? c.n_experts / 16 : 0;
     p.ncg_in = cdiv(B, 16);
     p.ncg_out = cdiv(B, 8);
     p.in = choose_split(c.hidden / kKStep);
     p.out = choose_split((c.latent + c.shared_inter) / kKStep);
     p.w13 = choose_split(c.latent / kKStep);
     p.w2 = choose_split(c.expert_inter / kKStep);
-    const int n_t2_in = p.n_r2 + c.latent / 32 + c.shared_inter / 16;
+    // Dense kernels work on 16-row tiles: router, latent-down, then shared
+    // tiles of 8 gate + 8 up rows.
+    const int n_t_in = p.n_r16 + c.latent / 16 + c.shared_inter / 8;
     const long long cols = ncols_cap(c.n_experts, B, k);
-    p.units_in = (long long)cdiv(n_t2_in, kWG / p.in.kw) * p.ncg_in;
-    p.units_out = (long long)cdiv(c.hidden / 32, kWG / p.out.kw) * p.ncg_out;
+    p.units_in = (long long)cdiv(n_t_in, kWG / p.in.kw) * p.ncg_in;
+    p.units_out = (long long)cdiv(c.hidden / 16, kWG / p.out.kw) * p.ncg_out;
     p.units_13 = cols * cdiv(c.expert_inter / 16, kWG / p.w13.kw);
     p.units_2 = cols * cdiv(c.latent / 32, kWG / p.w2.kw);
     return p;
@@ -300,8 +302,8 @@ moe_status moe_decode_step(moe_decode_ctx *ctx, const uint16_t *x, int32_t batch
     a.out = out;
     a.user_idx = topk_idx;
     a.user_w = topk_w;
-    a.n_r2 = pl.n_r2;
-    a.router_target = c.router_dtype == MOE_ROUTER_BF16 ? pl.n_r2 * pl.ncg_in : c.n_experts;
+    a.n_r16 = pl.n_r16;
+    a.router_target = c.router_dtype == MOE_ROUTER_BF16 ? pl.n_r16 * pl.ncg_in : c.n_experts;
     a.kw_in = pl.in.kw;
     a.kw_out = pl.out.kw;
     a.kw13 = pl.w13.kw;

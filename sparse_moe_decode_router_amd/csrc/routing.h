@@ -11,7 +11,9 @@
 // The work runs inside the kernel that produces the router scores: the wave
 // whose arrival completes the router starts claiming tokens, and any wave that
 // finishes a tile afterwards joins it; the wave that completes the last token
-// builds the metadata.  No wave ever waits on another.
+// builds the metadata.  No wave ever waits on another.  Wave-wide reductions
+// and scans use DPP row operations and scalar lane reads, so one top-16 of
+// 896 costs a few thousand cycles of one wave.
 #pragma once
 
 #include "device_common.h"
@@ -19,62 +21,131 @@
 
 namespace moe {
 
-// Orders (key, id) pairs: larger key first, then lower id, as one u64 maximum.
-__device__ __forceinline__ uint64_t pack_key(float key, int e) {
-    const uint32_t u = __float_as_uint(key);
-    const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-    return ((uint64_t)ord << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
+constexpr int kKeysPerLane = kMaxExperts / kWave;  // 16
+
+// DPP controls (GFX9 encoding).
+enum : int {
+    kQuadSwap1 = 0xB1,   // quad_perm [1,0,3,2]
+    kQuadSwap2 = 0x4E,   // quad_perm [2,3,0,1]
+    kRowShr1 = 0x111,
+    kRowShr2 = 0x112,
+    kRowShr4 = 0x114,
+    kRowShr8 = 0x118,
+    kRowMirror = 0x140,
+    kRowHalfMirror = 0x141,
+    kRowBcast15 = 0x142,
+    kRowBcast31 = 0x143,
+};
+
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROWS, 0xF, false);
 }
 
-// Top-k of one token, by one wave.  The token's keys are staged in the
-// wave's LDS buffer; lane l owns experts l, l+64, ...; k rounds of a
-// wave-wide maximum pick the experts in key order; they are then written in
-// ascending id with weights s_e / sum(s).
-__device__ __forceinline__ void topk_token(const StepArgs &a, int b, float *s_keys) {
+__device__ __forceinline__ uint32_t readlane(uint32_t v, int l) {
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, l);
+}
+
+// Wave-wide maximum / minimum of a u32, as a scalar.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = max(v, dpp<kQuadSwap1>(v));
+    v = max(v, dpp<kQuadSwap2>(v));
+    v = max(v, dpp<kRowHalfMirror>(v));
+    v = max(v, dpp<kRowMirror>(v));
+    return max(max(readlane(v, 0), readlane(v, 16)), max(readlane(v, 32), readlane(v, 48)));
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) { return ~wave_max_u32(~v); }
+
+// Inclusive prefix sum over the wave (lane order).
+__device__ __forceinline__ int wave_incl_scan(int v) {
+    uint32_t u = (uint32_t)v;
+    u += dpp<kRowShr1>(u);
+    u += dpp<kRowShr2>(u);
+    u += dpp<kRowShr4>(u);
+    u += dpp<kRowShr8>(u);
+    u += dpp<kRowBcast15, 0xA>(u);
+    u += dpp<kRowBcast31, 0xC>(u);
+    return (int)u;
+}
+
+// Orders f32 keys as u32 (larger key -> larger u32; 0 never occurs for a
+// finite key, so 0 marks "no candidate").
+__device__ __forceinline__ uint32_t orderable(float key) {
+    const uint32_t u = __float_as_uint(key);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Top-k of one token, by one wave.  Lane l owns experts l, l+64, ... and
+// keeps its best remaining (key, lowest id) as a candidate.  Each round takes
+// the wave-wide largest candidate key (equal keys: the lowest expert id), the
+// winning lane advances its candidate, and the selection is recorded in lane
+// r (round r) together with its rank among the selected ids.  Selected ids
+// are written in ascending order with weights s_e / sum(s); the sum is taken
+// in selection order.
+__device__ __forceinline__ void topk_token(const StepArgs &a, int b) {
     const int lane = lane_id();
     const int E = a.E, k = a.k;
     const float *keyrow = a.key + (size_t)b * E;
-    for (int e = lane; e < E; e += kWave) s_keys[e] = keyrow[e];
-    wave_sync();
+    const float *srow = a.score + (size_t)b * E;
     const int nk = (E + kWave - 1) / kWave;
+    uint32_t ok[kKeysPerLane];
     uint32_t avail = 0;
-    for (int i = 0; i < nk; ++i) avail |= (lane + kWave * i < E) ? (1u << i) : 0u;
-    // First maximum of this lane's available keys in ascending id, packed.
-    auto local_best = [&]() {
-        float bk = 0.f;
-        int bi = -1;
-        for (int i = 0; i < nk; ++i) {
-            const float v = s_keys[lane + kWave * i];
-            const bool take = ((avail >> i) & 1u) && (bi < 0 || v > bk);
-            bk = take ? v : bk;
-            bi = take ? i : bi;
+#pragma unroll
+    for (int i = 0; i < kKeysPerLane; ++i) {
+        const int e = lane + kWave * i;
+        const bool in = i < nk && e < E;
+        ok[i] = in ? orderable(keyrow[in ? e : 0]) : 0u;
+        avail |= in ? (1u << i) : 0u;
+    }
+    auto candidate = [&](uint32_t &ck, int &ci) {
+        ck = 0;
+        ci = 0;
+#pragma unroll
+        for (int i = 0; i < kKeysPerLane; ++i) {
+            const bool take = ((avail >> i) & 1u) && ok[i] > ck;  // strict: lowest i on ties
+            ck = take ? ok[i] : ck;
+            ci = take ? i : ci;
         }
-        return bi < 0 ? (uint64_t)0 : pack_key(bk, lane + kWave * bi);
     };
-    uint64_t best = local_best();
-    int mine = 0x7FFFFFFF;
+    uint32_t ck;
+    int ci;
+    candidate(ck, ci);
+    int mine = 0, rank = 0;
+    float s_mine = 0.f, total = 0.f;
     for (int r = 0; r < k; ++r) {
-        const uint64_t w = wave_max_u64(best);
-        const int e = (int)(0xFFFFFFFFu - (uint32_t)w);
-        if (lane == r) mine = e;
-        if ((e & (kWave - 1)) == lane) {
-            avail &= ~(1u << (e >> 6));
-            best = local_best();
+        const uint32_t m = wave_max_u32(ck);
+        const unsigned long long tied = __ballot(ck == m);
+        int wl = (int)__ffsll((long long)tied) - 1;
+        if (__popcll(tied) > 1) {  // equal keys in several lanes: lowest expert id wins
+            const uint32_t id = (ck == m) ? (uint32_t)(lane + kWave * ci) : 0xFFFFFFFFu;
+            wl = (int)(wave_min_u32(id) & (kWave - 1));
+        }
+        const int e = (int)readlane((uint32_t)(wl + kWave * ci), wl);
+        const float s = srow[e];  // same address in every lane: one load
+        total += s;
+        // Ranks: earlier selections above e move up; the new one counts the
+        // earlier selections below it.
+        const bool earlier = lane < r;
+        rank += (earlier && mine > e) ? 1 : 0;
+        const unsigned long long below = __ballot(earlier && mine < e);
+        if (lane == r) {
+            mine = e;
+            s_mine = s;
+            rank = __popcll(below);
+        }
+        if (lane == wl) {
+            avail &= ~(1u << ci);
+            candidate(ck, ci);
         }
     }
-    int rank = 0;
-    for (int r = 0; r < k; ++r) rank += __shfl(mine, r) < mine ? 1 : 0;
-    const float s = lane < k ? a.score[(size_t)b * E + mine] : 0.f;
-    const float total = wave_sum(s);
     if (lane < k) {
-        const float w = s / total;
+        const float w = s_mine / total;
         const int o = b * k + rank;
         a.idx[o] = mine;
         a.wsel[o] = w;
         if (a.user_idx) a.user_idx[o] = mine;
         if (a.user_w) a.user_w[o] = w;
     }
-    wave_sync();
 }
 
 // Routing metadata from idx [B][k], by one wave, with an LDS bit mask of the
@@ -97,10 +168,11 @@ __device__ __forceinline__ void build_meta(const StepArgs &a, unsigned long long
         np += n;
         nc += (n + 7) >> 3;
     }
-    int D, P, NC;
-    int ai = wave_excl_scan(na, &D);
-    int pi = wave_excl_scan(np, &P);
-    int ci = wave_excl_scan(nc, &NC);
+    const int ia = wave_incl_scan(na), ip = wave_incl_scan(np), ic = wave_incl_scan(nc);
+    const int D = (int)readlane((uint32_t)ia, kWave - 1);
+    const int P = (int)readlane((uint32_t)ip, kWave - 1);
+    const int NC = (int)readlane((uint32_t)ic, kWave - 1);
+    int ai = ia - na, pi = ip - np, ci = ic - nc;
     for (int e = e0; e < e1; ++e) {
         unsigned long long m = s_mask[e];
         const int n = __popcll(m);
@@ -136,16 +208,14 @@ __device__ __forceinline__ void build_meta(const StepArgs &a, unsigned long long
 }
 
 // Claims tokens until none is left; the wave that finishes the last token
-// builds the metadata.  Called only once the router is complete.  s_keys is
-// the calling wave's own LDS buffer of kMaxExperts floats.
-__device__ __forceinline__ void topk_loop(const StepArgs &a, unsigned long long *s_mask,
-                                       float *s_keys) {
+// builds the metadata.  Called only once the router is complete.
+__device__ __forceinline__ void topk_loop(const StepArgs &a, unsigned long long *s_mask) {
     acquire_agent();
     // Claims are unique, so one wave can never claim more than B tokens.
     for (int it = 0; it < a.B; ++it) {
         const uint32_t t = wave_fetch_add(&a.gctr[G_NEXT_TOKEN], 1u);
         if (t >= (uint32_t)a.B) break;
-        topk_token(a, (int)t, s_keys);
+        topk_token(a, (int)t);
         if (wave_arrive(&a.gctr[G_TOKENS_DONE]) == (uint32_t)a.B - 1u) {
             acquire_agent();
             build_meta(a, s_mask);
@@ -155,11 +225,10 @@ __device__ __forceinline__ void topk_loop(const StepArgs &a, unsigned long long 
 
 // A wave that finished a tile helps with the top-k when the router is
 // complete and tokens are still unclaimed.
-__device__ __forceinline__ void maybe_join_topk(const StepArgs &a, unsigned long long *s_mask,
-                                                float *s_keys) {
+__device__ __forceinline__ void maybe_join_topk(const StepArgs &a, unsigned long long *s_mask) {
     if (wave_load_counter(&a.gctr[G_ROUTER_DONE]) != (uint32_t)a.router_target) return;
     if (wave_load_counter(&a.gctr[G_NEXT_TOKEN]) >= (uint32_t)a.B) return;
-    topk_loop(a, s_mask, s_keys);
+    topk_loop(a, s_mask);
 }
 
 }  // namespace moe

@@ -14,7 +14,7 @@ struct StepArgs {
     int32_t Bm, km;           // capacities (context max_batch / max_top_k)
     // Launch plan: waves of a workgroup that split K in each kernel (the
     // rest of the 8 waves take further row groups).
-    int32_t n_r2;             // 32-row router tiles computed by the dense input kernel
+    int32_t n_r16;            // 16-row router tiles computed by the dense input kernel
     int32_t router_target;    // arrivals on G_ROUTER_DONE that complete the router
     int32_t kw_in, kw_out, kw13, kw2;
     int32_t spc_in, spc_out;  // 128-element steps per wave in the dense kernels

@@ -182,15 +182,19 @@ def test_all_experts_selected():
 
 def assert_same_step(a, b):
     """Two runs of one step: identical expert ids and weights; outputs equal
-    up to the order of the f32 atomic adds of the expert combine, which can
-    move a bf16 output to its neighbour (one unit in the last place)."""
+    up to the order of the f32 atomic adds of the expert combine.  A different
+    order moves each latent value by a few f32 rounding steps (about
+    k * 2^-24 relative); after the latent-up contraction that is far below
+    2^-16 of the row's rms, plus the one bf16 step a value near a rounding
+    boundary can take.  Outputs that cancel to almost zero can differ by more
+    bf16 steps of their own, never by more than this absolute bound."""
     np.testing.assert_array_equal(a[1], b[1])
     np.testing.assert_array_equal(a[2], b[2])
-    da, db = a[0].astype(np.int32), b[0].astype(np.int32)
-    same_sign = (da >> 15) == (db >> 15)
-    assert np.all(same_sign | (da == db) | ((da & 0x7FFF) == 0) | ((db & 0x7FFF) == 0))
-    assert np.max(np.abs((da & 0x7FFF) - (db & 0x7FFF))) <= 1
-    assert np.mean(da != db) < 1e-2
+    fa, fb = bf16_f64(a[0]), bf16_f64(b[0])
+    rms = np.sqrt(np.mean(fa * fa, axis=1, keepdims=True))
+    ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(fa), np.abs(fb)) + 1e-300)) - 7)
+    assert np.all(np.abs(fa - fb) <= np.maximum(ulp, rms * 2.0 ** -16))
+    assert np.mean(a[0] != b[0]) < 1e-2
 
 
 def test_repeated_steps_agree(small_layer, small_ctx):
