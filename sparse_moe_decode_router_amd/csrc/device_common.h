@@ -28,6 +28,9 @@ constexpr int kMaxStepsPerChunk = 8;
 enum { G_ROUTER_DONE = 0, G_NEXT_TOKEN = 1, G_TOKENS_DONE = 2, G_COUNT = 64 };
 // Routing metadata header (i32).
 enum { M_N_ACTIVE = 0, M_N_COLS = 1, M_COUNT = 16 };
+// Column-unit record (i32 words): expert, pair count (<= 8), first pair index,
+// then the token and the routing weight (f32 bits) of each pair.
+enum { R_EXPERT = 0, R_COUNT = 1, R_PAIR0 = 2, R_TOKEN = 8, R_WEIGHT = 16, kRecWords = 32 };
 
 __device__ __forceinline__ int lane_id() {
     return (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));

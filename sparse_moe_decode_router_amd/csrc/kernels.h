@@ -173,81 +173,14 @@ __device__ __forceinline__ void dense_chunk_out(const TwoSource &t, bool valid, 
     }
 }
 
-// acc0/acc1 += MXFP4 rows (q0,sc0)/(q1,sc1) . f32 columns X (hi/lo) over the
-// SPC steps from s0, in groups of two steps whose code, scale and column
-// loads are all issued before the group's MFMAs.  q0/q1 point at the lane's
-// 16-byte slice of step 0, sc0/sc1 at the row's scale bytes (byte 4s+g is
-// lane group g's block).
-template <int SPC>
-__device__ __forceinline__ void fp4_chunk(const uint8_t *q0, const uint8_t *sc0,
-                                          const uint8_t *q1, const uint8_t *sc1, const float *X,
-                                          bool valid, int part, int g, int s0, f32x4 &acc0,
-                                          f32x4 &acc1) {
-    const int sh = 8 * g;
-#pragma unroll
-    for (int q0s = 0; q0s < SPC; q0s += 2) {
-        constexpr int G = 2;
-        u32x4 c0[G], c1[G], rb[G][4];
-        uint32_t e0[G], e1[G];
-#pragma unroll
-        for (int q = 0; q < G; ++q) {
-            if (q0s + q >= SPC) break;
-            const int s = s0 + q0s + q;
-            c0[q] = ld_weight16(q0 + (size_t)s * 64);
-            c1[q] = ld_weight16(q1 + (size_t)s * 64);
-            e0[q] = ld_weight4(sc0 + (size_t)s * 4);
-            e1[q] = ld_weight4(sc1 + (size_t)s * 4);
-        }
-#pragma unroll
-        for (int q = 0; q < G; ++q) {
-            if (q0s + q >= SPC) break;
-            load_cols_f32(X, valid, part, s0 + q0s + q, rb[q]);
-        }
-        fence_schedule();
-#pragma unroll
-        for (int q = 0; q < G; ++q) {
-            if (q0s + q >= SPC) break;
-            const float f0 = e8m0_scale((e0[q] >> sh) & 0xFFu);
-            const float f1 = e8m0_scale((e1[q] >> sh) & 0xFFu);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const bf16x8 b = as_bf16x8(rb[q][j]);
-                acc0 = mfma(fp4x8_to_bf16(c0[q][j], f0), b, acc0);
-                acc1 = mfma(fp4x8_to_bf16(c1[q][j], f1), b, acc1);
-            }
-        }
-    }
-}
-
 // ---------------------------------------------------------------------------
 // Workgroup split-K reduction
 // ---------------------------------------------------------------------------
 
-// Waves w = rg*KW + kw.  Each writes its two partial tiles to LDS; after the
+// Waves w = rg*KW + kw.  Each writes its partial tile to LDS; after the
 // barrier the wave with kw == 0 of each row group sums its group's KW slices
 // in slice order and returns true (the leader).  The caller issues the
 // barrier that ends the unit before LDS is reused.
-__device__ __forceinline__ bool reduce_k(float *s_red, int wave, int kw, int KW, f32x4 &acc0,
-                                         f32x4 &acc1) {
-    const int lane = lane_id();
-    float *mine = s_red + (wave * kWave + lane) * 8;
-    stf4(mine, acc0);
-    stf4(mine + 4, acc1);
-    __syncthreads();
-    if (kw != 0) return false;
-    if (KW > 1) {
-        acc0 = zero4();
-        acc1 = zero4();
-        for (int j = 0; j < KW; ++j) {
-            const float *p = s_red + ((wave + j) * kWave + lane) * 8;
-            acc0 += ldf4(p);
-            acc1 += ldf4(p + 4);
-        }
-    }
-    return true;
-}
-
-// Single-tile form of reduce_k.
 __device__ __forceinline__ bool reduce_k1(float *s_red, int wave, int kw, int KW, f32x4 &acc) {
     const int lane = lane_id();
     stf4(s_red + (wave * kWave + lane) * 4, acc);
@@ -364,7 +297,10 @@ k_dense_in(const StepArgs a) {
                 if (wave_arrive(&a.gctr[G_ROUTER_DONE]) == (uint32_t)a.router_target - 1u)
                     topk_loop(a, s_mask);
             } else if (kind == 1) {
-                if (valid) stf4(a.z + (size_t)b * a.L + 16 * (tt - n_rt) + 4 * g, acc);
+                if (valid) {
+                    uint16_t *dst = a.zhl + (size_t)b * 2 * a.L + 16 * (tt - n_rt) + 4 * g;
+                    store_hl4(dst, dst + a.L, acc);
+                }
             } else {
                 f32x4 up;
 #pragma unroll
@@ -383,47 +319,152 @@ k_dense_in(const StepArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Expert kernels (2 and 3): shared structure
+// ---------------------------------------------------------------------------
+//
+// A workgroup serves one column unit (one expert, up to 8 of its tokens) and
+// 8 row tiles of that expert, one per wave; each wave runs the whole
+// reduction length K of its tile, so no partial sums cross waves.  K is taken
+// in chunks of S steps (S <= 16, 2048 elements).  Per chunk a wave issues all
+// of its MXFP4 code and scale loads at once (S x 16 B of codes per lane), the
+// workgroup copies the unit's activation rows for the chunk straight from
+// global memory into LDS, and the MFMAs run once everything has landed.  The
+// only round trips a workgroup waits on are its unit record, then one chunk
+// of weights.
+
+// LDS image of a unit's activation operand for one chunk: row n = 2j + part
+// (pair j's hi or lo values), 16 S chunks of 16 bytes (8 bf16) per row; chunk
+// q of row n is stored at position q ^ n of its row (n < 16 flips only the
+// low four bits of q, so a chunk stays in its 16-chunk block), which puts the
+// 16 rows of one MFMA operand read on distinct LDS banks.
+template <int S>
+struct Stage {
+    static constexpr int kRowChunks = 16 * S;
+    static constexpr int kChunks = 16 * kRowChunks;  // 16 rows
+};
+
+// Wave-cooperative copy of rows 0 .. 2 nt - 1 of the operand for K range
+// [k0, k0 + 128 S): source row (j, part) starts at src + row_of(j) * 2 K +
+// part * K + k0 (elements).  Every wave takes every 8th 64-chunk block; each
+// lane moves one 16-byte chunk with a direct global -> LDS load, which lands
+// at the block base + 16 * lane.
+template <int S, typename RowOf>
+__device__ __forceinline__ void stage_operand(uint16_t *s_b, const uint16_t *src, int K, int k0,
+                                              int nt, RowOf row_of) {
+    const int lane = lane_id(), wave = wave_index();
+    const int total = 2 * nt * Stage<S>::kRowChunks;
+    for (int c0 = 64 * wave; c0 < total; c0 += 64 * kWG) {
+        const int c = c0 + lane;
+        const int n = c / Stage<S>::kRowChunks, st = c % Stage<S>::kRowChunks;
+        const int q = st ^ (n & 15);
+        const int j = n >> 1, part = n & 1;
+        const uint16_t *g = src + ((size_t)row_of(j) * 2 + part) * K + k0 + 8 * q;
+        if (c < total) __builtin_amdgcn_global_load_lds(g, s_b + 8 * c0, 16, 0, 0);
+    }
+}
+
+// Operand of MFMA jj at step s for lane (row n_eff, lane group g).
+template <int S>
+__device__ __forceinline__ bf16x8 stage_read(const uint16_t *s_b, int n_eff, int g, int s, int jj) {
+    const int q = 16 * s + ((4 * g + jj) ^ n_eff);
+    return as_bf16x8(*(const u32x4 *)(s_b + 8 * (n_eff * Stage<S>::kRowChunks + q)));
+}
+
+__device__ __forceinline__ void wait_all_loads() {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0); expcnt and lgkmcnt unconstrained
+}
+
+// One chunk of one MXFP4 tile row per lane: codes (16 B per step: lane
+// group g's 32-element block) and the step's four scale bytes.
+template <int S>
+struct Fp4Chunk {
+    u32x4 code[S];
+    uint32_t scale[S];
+};
+
+template <int S>
+__device__ __forceinline__ void load_fp4_chunk(const uint8_t *q, const uint8_t *sc, int step0,
+                                               Fp4Chunk<S> &w) {
+#pragma unroll
+    for (int s = 0; s < S; ++s) w.code[s] = ld_weight16(q + (size_t)(step0 + s) * 64);
+    if constexpr (S % 4 == 0) {
+#pragma unroll
+        for (int m = 0; m < S / 4; ++m) {
+            const u32x4 v = ld_weight16(sc + (size_t)(step0 + 4 * m) * 4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) w.scale[4 * m + i] = v[i];
+        }
+    } else {
+#pragma unroll
+        for (int s = 0; s < S; ++s) w.scale[s] = ld_weight4(sc + (size_t)(step0 + s) * 4);
+    }
+}
+
+template <int S>
+__device__ __forceinline__ void mfma_fp4_chunk(const Fp4Chunk<S> &w, const uint16_t *s_b,
+                                               int n_eff, int g, f32x4 &acc) {
+    const int sh = 8 * g;
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+        const float f = e8m0_scale((w.scale[s] >> sh) & 0xFFu);
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+            acc = mfma(fp4x8_to_bf16(w.code[s][jj], f), stage_read<S>(s_b, n_eff, g, s, jj), acc);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Kernel 2: expert gate/up (MXFP4) + SwiGLU.
 // ---------------------------------------------------------------------------
 
-template <int SPC>
-__global__ void __launch_bounds__(kWGThreads) k_w13(const StepArgs a) {
-    __shared__ float s_red[kWG * kWave * 8];
-    const int lane = lane_id(), n = lane & 15, g = lane >> 4;
-    const int col = n >> 1, part = n & 1;
-    const Role ro = role_of(a.kw13);
-    const int NC = min(a.meta[M_N_COLS], a.ncols_cap);  // never beyond the lists
-    const int PT = a.I >> 4;
-    const int ptg = (PT + ro.RW - 1) / ro.RW;
-    const int units = NC * ptg;
+// Tile t of expert e: gate rows 8t .. 8t+7 (MFMA rows 0-7) and up rows
+// I + 8t .. I + 8t + 7 (MFMA rows 8-15), so lanes l and l + 32 hold a gate and
+// its up value.  Output: the activation of each pair as hi/lo bf16 rows.
+template <int S>
+__global__ void __launch_bounds__(kWGThreads) __attribute__((amdgpu_waves_per_eu(4)))
+k_w13(const StepArgs a) {
+    __shared__ __attribute__((aligned(16))) uint16_t s_b[8 * Stage<S>::kChunks];
+    const int lane = lane_id(), n = lane & 15, g = lane >> 4, wave = wave_index();
+    const int j = n >> 1, part = n & 1;
+    const int NC = min(a.meta[M_N_COLS], a.ncols_cap);  // never beyond the records
+    const int OT = a.I >> 3;
+    const int TG = (OT + kWG - 1) / kWG;
+    const int nchunk = a.L / (kKStep * S);
     const size_t qrow = a.L / 2, srow = a.L / 32;
-    for (int u = blockIdx.x; u < units; u += gridDim.x) {
-        const int cu = u / ptg;
-        const int pt = (u % ptg) * ro.RW + ro.rg;
-        const bool active = pt < PT;
-        const int e = a.cu_expert[cu], p0 = a.cu_p0[cu], nt = a.cu_n[cu];
-        const bool valid = col < nt;
-        const int p = p0 + (valid ? col : 0);
-        const int tok = a.pair_slot[p] / a.k;
-        const float *X = a.z + (size_t)tok * a.L + 32 * g;
-        const size_t rg = (size_t)e * 2 * a.I + 16 * (active ? pt : 0) + n, ru = rg + a.I;
-        f32x4 accg = zero4(), accu = zero4();
-        if (active)
-            fp4_chunk<SPC>(a.w13_q + rg * qrow + 16 * g, a.w13_s + rg * srow,
-                           a.w13_q + ru * qrow + 16 * g, a.w13_s + ru * srow, X, valid, part, g,
-                           ro.kw * SPC, accg, accu);
-        const bool leader = reduce_k(s_red, ro.wave, ro.kw, ro.KW, accg, accu);
-        if (leader && active) {
-            accg = add_pair_column(accg);
-            accu = add_pair_column(accu);
-            if (valid && part == 0) {
-                f32x4 v;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) v[i] = silu_mul(accg[i], accu[i]);
-                stf4(a.act + (size_t)p * a.I + 16 * pt + 4 * g, v);
-            }
+    for (int u = blockIdx.x; u < NC * TG; u += gridDim.x) {
+        const int c = u / TG;
+        const int t = (u % TG) * kWG + wave;
+        const bool active = t < OT;
+        const int recw = a.cu_rec[c * kRecWords + (lane & 31)];
+        const int e = (int)readlane((uint32_t)recw, R_EXPERT);
+        const int nt = (int)readlane((uint32_t)recw, R_COUNT);
+        const int p0 = (int)readlane((uint32_t)recw, R_PAIR0);
+        const int n_eff = j < nt ? n : part;
+        const size_t r = (size_t)e * 2 * a.I + (n < 8 ? 0 : a.I) + 8 * (active ? t : 0) + (n & 7);
+        const uint8_t *qp = a.w13_q + r * qrow + 16 * g;
+        const uint8_t *sp = a.w13_s + r * srow;
+        f32x4 acc = zero4();
+        for (int ch = 0; ch < nchunk; ++ch) {
+            Fp4Chunk<S> w;
+            if (active) load_fp4_chunk<S>(qp, sp, ch * S, w);
+            stage_operand<S>(s_b, a.zhl, a.L, ch * S * kKStep, nt,
+                             [&](int jj) { return __shfl(recw, R_TOKEN + jj); });
+            wait_all_loads();
+            __syncthreads();
+            if (active) mfma_fp4_chunk<S>(w, s_b, n_eff, g, acc);
+            __syncthreads();
         }
-        __syncthreads();
+        acc = add_pair_column(acc);
+        f32x4 up;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) up[i] = __shfl_xor(acc[i], 32);
+        if (active && j < nt && part == 0 && g < 2) {
+            f32x4 v;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] = silu_mul(acc[i], up[i]);
+            uint16_t *dst = a.acthl + (size_t)(p0 + j) * 2 * a.I + 8 * t + 4 * g;
+            store_hl4(dst, dst + a.I, v);
+        }
     }
 }
 
@@ -431,47 +472,51 @@ __global__ void __launch_bounds__(kWGThreads) k_w13(const StepArgs a) {
 // Kernel 3: expert down (MXFP4) + weighted combine in latent space.
 // ---------------------------------------------------------------------------
 
-template <int SPC>
-__global__ void __launch_bounds__(kWGThreads) k_w2(const StepArgs a) {
-    __shared__ float s_red[kWG * kWave * 8];
-    const int lane = lane_id(), n = lane & 15, g = lane >> 4;
-    const int col = n >> 1, part = n & 1;
-    const Role ro = role_of(a.kw2);
-    const int NC = min(a.meta[M_N_COLS], a.ncols_cap);  // never beyond the lists
-    const int LT = a.L >> 5;
-    const int ltg = (LT + ro.RW - 1) / ro.RW;
-    const int units = NC * ltg;
+// Tile t of expert e: latent rows 16t .. 16t+15; the routing weight of each
+// pair scales its column before the f32 atomic add into ylat.
+template <int S>
+__global__ void __launch_bounds__(kWGThreads) __attribute__((amdgpu_waves_per_eu(4)))
+k_w2(const StepArgs a) {
+    __shared__ __attribute__((aligned(16))) uint16_t s_b[8 * Stage<S>::kChunks];
+    const int lane = lane_id(), n = lane & 15, g = lane >> 4, wave = wave_index();
+    const int j = n >> 1, part = n & 1;
+    const int NC = min(a.meta[M_N_COLS], a.ncols_cap);  // never beyond the records
+    const int OT = a.L >> 4;
+    const int TG = (OT + kWG - 1) / kWG;
+    const int nchunk = a.I / (kKStep * S);
     const size_t qrow = a.I / 2, srow = a.I / 32;
-    for (int u = blockIdx.x; u < units; u += gridDim.x) {
-        const int cu = u / ltg;
-        const int lt = (u % ltg) * ro.RW + ro.rg;
-        const bool active = lt < LT;
-        const int e = a.cu_expert[cu], p0 = a.cu_p0[cu], nt = a.cu_n[cu];
-        const bool valid = col < nt;
-        const int p = p0 + (valid ? col : 0);
-        const float *X = a.act + (size_t)p * a.I + 32 * g;
-        const size_t r0 = (size_t)e * a.L + 32 * (active ? lt : 0) + n, r1 = r0 + 16;
-        f32x4 acc0 = zero4(), acc1 = zero4();
-        if (active)
-            fp4_chunk<SPC>(a.w2_q + r0 * qrow + 16 * g, a.w2_s + r0 * srow,
-                           a.w2_q + r1 * qrow + 16 * g, a.w2_s + r1 * srow, X, valid, part, g,
-                           ro.kw * SPC, acc0, acc1);
-        const bool leader = reduce_k(s_red, ro.wave, ro.kw, ro.KW, acc0, acc1);
-        if (leader && active) {
-            acc0 = add_pair_column(acc0);
-            acc1 = add_pair_column(acc1);
-            if (valid && part == 0) {
-                const int slot = a.pair_slot[p];
-                const float w = a.wsel[slot];
-                float *dst = a.ylat + (size_t)(slot / a.k) * a.L + 32 * lt + 4 * g;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    unsafeAtomicAdd(dst + i, w * acc0[i]);
-                    unsafeAtomicAdd(dst + 16 + i, w * acc1[i]);
-                }
-            }
+    for (int u = blockIdx.x; u < NC * TG; u += gridDim.x) {
+        const int c = u / TG;
+        const int t = (u % TG) * kWG + wave;
+        const bool active = t < OT;
+        const int recw = a.cu_rec[c * kRecWords + (lane & 31)];
+        const int e = (int)readlane((uint32_t)recw, R_EXPERT);
+        const int nt = (int)readlane((uint32_t)recw, R_COUNT);
+        const int p0 = (int)readlane((uint32_t)recw, R_PAIR0);
+        const int jc = j < nt ? j : 0;
+        const int tok_j = __shfl(recw, R_TOKEN + jc);
+        const float w_j = __int_as_float(__shfl(recw, R_WEIGHT + jc));
+        const int n_eff = j < nt ? n : part;
+        const size_t r = (size_t)e * a.L + 16 * (active ? t : 0) + n;
+        const uint8_t *qp = a.w2_q + r * qrow + 16 * g;
+        const uint8_t *sp = a.w2_s + r * srow;
+        f32x4 acc = zero4();
+        for (int ch = 0; ch < nchunk; ++ch) {
+            Fp4Chunk<S> w;
+            if (active) load_fp4_chunk<S>(qp, sp, ch * S, w);
+            stage_operand<S>(s_b, a.acthl, a.I, ch * S * kKStep, nt,
+                             [&](int jj) { return p0 + jj; });
+            wait_all_loads();
+            __syncthreads();
+            if (active) mfma_fp4_chunk<S>(w, s_b, n_eff, g, acc);
+            __syncthreads();
         }
-        __syncthreads();
+        acc = add_pair_column(acc);
+        if (active && j < nt && part == 0) {
+            float *dst = a.ylat + (size_t)tok_j * a.L + 16 * t + 4 * g;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) unsafeAtomicAdd(dst + i, w_j * acc[i]);
+        }
     }
 }
 
@@ -558,7 +603,9 @@ __global__ void k_debug_export(const StepArgs a, const DebugArgs d) {
         if (d.key) d.key[i] = a.key[i];
     }
     for (size_t i = tid; i < nL; i += stride) {
-        if (d.z) d.z[i] = a.z[i];
+        const size_t b = i / a.L, c = i % a.L;
+        const uint16_t *zr = a.zhl + b * 2 * a.L;
+        if (d.z) d.z[i] = bf16_val(zr[c]) + bf16_val(zr[a.L + c]);
         if (d.ylat) d.ylat[i] = a.ylat[i];
     }
     for (size_t i = tid; i < nS; i += stride)
@@ -566,7 +613,8 @@ __global__ void k_debug_export(const StepArgs a, const DebugArgs d) {
     for (size_t i = tid; i < nA; i += stride) {
         if (!d.act) break;
         const size_t slot = i / a.I, c = i % a.I;
-        d.act[i] = a.act[(size_t)a.pair_of_slot[slot] * a.I + c];
+        const uint16_t *ar = a.acthl + (size_t)a.pair_of_slot[slot] * 2 * a.I;
+        d.act[i] = bf16_val(ar[c]) + bf16_val(ar[a.I + c]);
     }
     if (tid == 0 && d.n_active) d.n_active[0] = a.meta[M_N_ACTIVE];
 }

@@ -35,9 +35,18 @@ Split choose_split(int nsteps) {
 
 int ncols_cap(int E, int B, int k) { return std::min(E, B * k) + cdiv(B * k, 8); }
 
+// Steps per staged chunk of the expert kernels: the largest divisor of
+// K / 128 that is at most 16.
+int expert_chunk(int nsteps) {
+    for (int s = 16; s >= 1; --s)
+        if (nsteps % s == 0) return s;
+    return 1;
+}
+
 struct Plan {
     int n_r16, ncg_in, ncg_out;
-    Split in, out, w13, w2;
+    Split in, out;
+    int s13, s2;
     long long units_in, units_out, units_13, units_2;
 };
 
@@ -48,22 +57,24 @@ Plan make_plan(const moe_decode_config &c, int B, int k) {
     p.ncg_out = cdiv(B, 8);
     p.in = choose_split(c.hidden / kKStep);
     p.out = choose_split((c.latent + c.shared_inter) / kKStep);
-    p.w13 = choose_split(c.latent / kKStep);
-    p.w2 = choose_split(c.expert_inter / kKStep);
+    p.s13 = expert_chunk(c.latent / kKStep);
+    p.s2 = expert_chunk(c.expert_inter / kKStep);
     // Dense kernels work on 16-row tiles: router, latent-down, then shared
     // tiles of 8 gate + 8 up rows.
     const int n_t_in = p.n_r16 + c.latent / 16 + c.shared_inter / 8;
     const long long cols = ncols_cap(c.n_experts, B, k);
     p.units_in = (long long)cdiv(n_t_in, kWG / p.in.kw) * p.ncg_in;
     p.units_out = (long long)cdiv(c.hidden / 16, kWG / p.out.kw) * p.ncg_out;
-    p.units_13 = cols * cdiv(c.expert_inter / 16, kWG / p.w13.kw);
-    p.units_2 = cols * cdiv(c.latent / 32, kWG / p.w2.kw);
+    // Expert kernels: 8 row tiles per workgroup (8 gate + 8 up rows, or 16
+    // latent rows, per tile).
+    p.units_13 = cols * cdiv(c.expert_inter / 8, kWG);
+    p.units_2 = cols * cdiv(c.latent / 16, kWG);
     return p;
 }
 
 struct Layout {
-    size_t gctr, meta, score, key, idx, wsel, act_expert, act_off, cu_expert, cu_p0, cu_n,
-        pair_slot, pair_of_slot, z, ash, act, ylat, total;
+    size_t gctr, meta, score, key, idx, wsel, act_expert, act_off, cu_rec, pair_slot,
+        pair_of_slot, zhl, ash, acthl, ylat, total;
     size_t counters_end;  // [0, counters_end) holds every counter: cleared at init
 };
 
@@ -88,21 +99,21 @@ Layout make_layout(const moe_decode_config &c) {
     l.wsel = take(P * 4);
     l.act_expert = take((std::min(E, P) + 1) * 4);
     l.act_off = take((std::min(E, P) + 1) * 4);
-    l.cu_expert = take(ncols * 4);
-    l.cu_p0 = take(ncols * 4);
-    l.cu_n = take(ncols * 4);
+    l.cu_rec = take(ncols * kRecWords * 4);
     l.pair_slot = take(P * 4);
     l.pair_of_slot = take(P * 4);
-    l.z = take(Bm * L * 4);
+    l.zhl = take(Bm * 2 * L * 2);
     l.ash = take(Bm * Is * 4);
-    l.act = take(P * I * 4);
+    l.acthl = take(P * 2 * I * 2);
     l.ylat = take(Bm * L * 4);
     l.total = o;
     return l;
 }
 
 typedef void (*StepKernel)(const StepArgs);
-#define MOE_SPC_TABLE(K) {nullptr, K<1>, K<2>, K<3>, K<4>, K<5>, K<6>, K<7>, K<8>}
+#define MOE_SPC_TABLE(K)                                                                      \
+    {nullptr, K<1>, K<2>,  K<3>,  K<4>,  K<5>,  K<6>,  K<7>, K<8>,                                \
+     K<9>,    K<10>, K<11>, K<12>, K<13>, K<14>, K<15>, K<16>}
 const StepKernel kW13[] = MOE_SPC_TABLE(k_w13);
 const StepKernel kW2[] = MOE_SPC_TABLE(k_w2);
 #undef MOE_SPC_TABLE
@@ -172,14 +183,12 @@ StepArgs base_args(const moe_decode_ctx *ctx) {
     a.wsel = (float *)(ws + l.wsel);
     a.act_expert = (int32_t *)(ws + l.act_expert);
     a.act_off = (int32_t *)(ws + l.act_off);
-    a.cu_expert = (int32_t *)(ws + l.cu_expert);
-    a.cu_p0 = (int32_t *)(ws + l.cu_p0);
-    a.cu_n = (int32_t *)(ws + l.cu_n);
+    a.cu_rec = (int32_t *)(ws + l.cu_rec);
     a.pair_slot = (int32_t *)(ws + l.pair_slot);
     a.pair_of_slot = (int32_t *)(ws + l.pair_of_slot);
-    a.z = (float *)(ws + l.z);
+    a.zhl = (uint16_t *)(ws + l.zhl);
     a.ash = (float *)(ws + l.ash);
-    a.act = (float *)(ws + l.act);
+    a.acthl = (uint16_t *)(ws + l.acthl);
     a.ylat = (float *)(ws + l.ylat);
     return a;
 }
@@ -205,8 +214,9 @@ moe_status moe_decode_validate_config(const moe_decode_config *c) {
         c->shared_inter % kKStep)
         return MOE_ERR_UNSUPPORTED;
     if (c->n_experts % 32 || c->n_experts > kMaxExperts) return MOE_ERR_UNSUPPORTED;
-    // Every reduction length must split into KW x SPC steps (see choose_split).
-    const int ks[4] = {c->hidden, c->latent, c->expert_inter, c->latent + c->shared_inter};
+    // The dense reduction lengths must split into KW x SPC steps (see
+    // choose_split); the expert kernels take any multiple of 128.
+    const int ks[2] = {c->hidden, c->latent + c->shared_inter};
     for (int K : ks)
         if (choose_split(K / kKStep).kw == 0) return MOE_ERR_UNSUPPORTED;
     // Offsets are formed in 32-bit ints where they index one token or pair.
@@ -306,8 +316,6 @@ moe_status moe_decode_step(moe_decode_ctx *ctx, const uint16_t *x, int32_t batch
     a.router_target = c.router_dtype == MOE_ROUTER_BF16 ? pl.n_r16 * pl.ncg_in : c.n_experts;
     a.kw_in = pl.in.kw;
     a.kw_out = pl.out.kw;
-    a.kw13 = pl.w13.kw;
-    a.kw2 = pl.w2.kw;
     a.spc_in = pl.in.spc;
     a.spc_out = pl.out.spc;
     const long long cap = 65535;  // workgroups; larger unit counts loop
@@ -318,8 +326,8 @@ moe_status moe_decode_step(moe_decode_ctx *ctx, const uint16_t *x, int32_t batch
     d.col_tiles = pl.ncg_in;
     d.split_in = pl.in.kw;
     d.split_out = pl.out.kw;
-    d.split_w13 = pl.w13.kw;
-    d.split_w2 = pl.w2.kw;
+    d.split_w13 = 1;
+    d.split_w2 = 1;
     d.grid_in = grid_for(pl.units_in, cap);
     d.grid_w13 = grid_for(pl.units_13, cap);
     d.grid_w2 = grid_for(pl.units_2, cap);
@@ -340,9 +348,9 @@ moe_status moe_decode_step(moe_decode_ctx *ctx, const uint16_t *x, int32_t batch
     }
     hipLaunchKernelGGL(k_dense_in, dim3(d.grid_in), dim3(kWGThreads), 0, s, a);
     mark();
-    hipLaunchKernelGGL(kW13[pl.w13.spc], dim3(d.grid_w13), dim3(kWGThreads), 0, s, a);
+    hipLaunchKernelGGL(kW13[pl.s13], dim3(d.grid_w13), dim3(kWGThreads), 0, s, a);
     mark();
-    hipLaunchKernelGGL(kW2[pl.w2.spc], dim3(d.grid_w2), dim3(kWGThreads), 0, s, a);
+    hipLaunchKernelGGL(kW2[pl.s2], dim3(d.grid_w2), dim3(kWGThreads), 0, s, a);
     mark();
     hipLaunchKernelGGL(k_out, dim3(d.grid_out), dim3(kWGThreads), 0, s, a);
     mark();

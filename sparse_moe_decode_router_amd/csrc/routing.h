@@ -151,7 +151,10 @@ __device__ __forceinline__ void topk_token(const StepArgs &a, int b) {
 // Routing metadata from idx [B][k], by one wave, with an LDS bit mask of the
 // tokens of each expert.  Active experts are listed in ascending id; the pairs
 // of an expert in ascending token; each expert's pairs are cut into column
-// units of at most 8 tokens (16 MFMA columns: hi and lo of each token).
+// units of at most 8 tokens (16 MFMA columns: hi and lo of each token).  A
+// unit's record holds everything its workgroups need, so that they read it in
+// one round trip: expert, pair count, first pair, and per pair the token and
+// the routing weight.
 __device__ __forceinline__ void build_meta(const StepArgs &a, unsigned long long *s_mask) {
     const int lane = lane_id();
     const int B = a.B, k = a.k, E = a.E;
@@ -179,11 +182,6 @@ __device__ __forceinline__ void build_meta(const StepArgs &a, unsigned long long
         if (!n) continue;
         a.act_expert[ai] = e;
         a.act_off[ai] = pi;
-        for (int q = 0; q < n; q += 8, ++ci) {
-            a.cu_expert[ci] = e;
-            a.cu_p0[ci] = pi + q;
-            a.cu_n[ci] = min(8, n - q);
-        }
         for (int r = 0; m; ++r) {
             const int b = __ffsll((long long)m) - 1;
             m &= m - 1;
@@ -196,7 +194,16 @@ __device__ __forceinline__ void build_meta(const StepArgs &a, unsigned long long
             const int slot = b * k + lo;
             a.pair_slot[pi + r] = slot;
             a.pair_of_slot[slot] = pi + r;
+            int32_t *rec = a.cu_rec + (size_t)(ci + (r >> 3)) * kRecWords;
+            if ((r & 7) == 0) {
+                rec[R_EXPERT] = e;
+                rec[R_COUNT] = min(8, n - r);
+                rec[R_PAIR0] = pi + r;
+            }
+            rec[R_TOKEN + (r & 7)] = b;
+            rec[R_WEIGHT + (r & 7)] = __float_as_int(a.wsel[slot]);
         }
+        ci += (n + 7) >> 3;
         ++ai;
         pi += n;
     }

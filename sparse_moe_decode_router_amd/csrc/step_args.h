@@ -16,7 +16,7 @@ struct StepArgs {
     // rest of the 8 waves take further row groups).
     int32_t n_r16;            // 16-row router tiles computed by the dense input kernel
     int32_t router_target;    // arrivals on G_ROUTER_DONE that complete the router
-    int32_t kw_in, kw_out, kw13, kw2;
+    int32_t kw_in, kw_out;
     int32_t spc_in, spc_out;  // 128-element steps per wave in the dense kernels
     int32_t ncols_cap;        // capacity of the expert column-unit list
     // Weights (borrowed).
@@ -37,8 +37,11 @@ struct StepArgs {
     float *score, *key;
     int32_t *idx;
     float *wsel;
-    int32_t *act_expert, *act_off, *cu_expert, *cu_p0, *cu_n, *pair_slot, *pair_of_slot;
-    float *z, *ash, *act, *ylat;  // f32 intermediates
+    int32_t *act_expert, *act_off, *cu_rec, *pair_slot, *pair_of_slot;
+    // Expert operands as bf16 hi/lo row pairs: zhl [B][2][L], acthl [pair][2][I]
+    // (row 0: hi = bf16(v), row 1: lo = bf16(v - hi)).
+    uint16_t *zhl, *acthl;
+    float *ash, *ylat;  // f32 intermediates
 };
 
 }  // namespace moe
