@@ -370,10 +370,6 @@ __device__ __forceinline__ bf16x8 stage_read(const uint16_t *s_b, int n_eff, int
     return as_bf16x8(*(const u32x4 *)(s_b + 8 * (n_eff * Stage<S>::kRowChunks + q)));
 }
 
-__device__ __forceinline__ void wait_all_loads() {
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0); expcnt and lgkmcnt unconstrained
-}
-
 // One chunk of one MXFP4 tile row per lane: codes (16 B per step: lane
 // group g's 32-element block) and the step's four scale bytes.
 template <int S>
@@ -382,34 +378,71 @@ struct Fp4Chunk {
     uint32_t scale[S];
 };
 
+// Scale bytes of the chunk (four per step, lane group g uses byte g).  The
+// compiler may merge these loads, so they are issued before the staging
+// copies, where their number does not matter.
 template <int S>
-__device__ __forceinline__ void load_fp4_chunk(const uint8_t *q, const uint8_t *sc, int step0,
-                                               Fp4Chunk<S> &w) {
-#pragma unroll
-    for (int s = 0; s < S; ++s) w.code[s] = ld_weight16(q + (size_t)(step0 + s) * 64);
+__device__ __forceinline__ void load_fp4_scales(const uint8_t *sc, Fp4Chunk<S> &w) {
     if constexpr (S % 4 == 0) {
 #pragma unroll
         for (int m = 0; m < S / 4; ++m) {
-            const u32x4 v = ld_weight16(sc + (size_t)(step0 + 4 * m) * 4);
+            const u32x4 v = ld_weight16(sc + 16 * m);
 #pragma unroll
             for (int i = 0; i < 4; ++i) w.scale[4 * m + i] = v[i];
         }
     } else {
 #pragma unroll
-        for (int s = 0; s < S; ++s) w.scale[s] = ld_weight4(sc + (size_t)(step0 + s) * 4);
+        for (int s = 0; s < S; ++s) w.scale[s] = ld_weight4(sc + 4 * s);
     }
 }
 
+// Codes of the chunk: S loads of 16 bytes, 64 bytes apart (never merged).
+// Issued after the staging copies, in step order, so that step s waits only
+// for the loads up to its own.
+template <int S>
+__device__ __forceinline__ void load_fp4_codes(const uint8_t *q, Fp4Chunk<S> &w) {
+#pragma unroll
+    for (int s = 0; s < S; ++s) w.code[s] = ld_weight16(q + 64 * s);
+}
+
+// Waits until this wave's staging copies have landed while the S code loads
+// issued after them may still be in flight: vector memory loads complete in
+// issue order.
+template <int S>
+__device__ __forceinline__ void wait_staging() {
+    static_assert(S <= 63, "vmcnt field");
+    // s_waitcnt: vmcnt in bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8].
+    __builtin_amdgcn_s_waitcnt((S & 15) | ((S >> 4) << 14) | 0x0F70);
+}
+
+// Workgroup barrier after wait_staging: LDS holds every wave's copy once all
+// waves pass it.  A plain barrier, without the memory fence of
+// __syncthreads, which would also wait for the weight loads still in flight.
+__device__ __forceinline__ void staged_barrier() {
+    fence_schedule();
+    __builtin_amdgcn_s_barrier();
+    fence_schedule();
+}
+
+// The MFMAs of one chunk; the activation operand of step s + 1 is read from
+// LDS while step s multiplies.  The compiler waits for each step's weight
+// registers just before their first use.
 template <int S>
 __device__ __forceinline__ void mfma_fp4_chunk(const Fp4Chunk<S> &w, const uint16_t *s_b,
                                                int n_eff, int g, f32x4 &acc) {
     const int sh = 8 * g;
+    bf16x8 b[2][4];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) b[0][jj] = stage_read<S>(s_b, n_eff, g, 0, jj);
 #pragma unroll
     for (int s = 0; s < S; ++s) {
+        if (s + 1 < S) {
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) b[(s + 1) & 1][jj] = stage_read<S>(s_b, n_eff, g, s + 1, jj);
+        }
         const float f = e8m0_scale((w.scale[s] >> sh) & 0xFFu);
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj)
-            acc = mfma(fp4x8_to_bf16(w.code[s][jj], f), stage_read<S>(s_b, n_eff, g, s, jj), acc);
+        for (int jj = 0; jj < 4; ++jj) acc = mfma(fp4x8_to_bf16(w.code[s][jj], f), b[s & 1][jj], acc);
     }
 }
 
@@ -445,13 +478,21 @@ k_w13(const StepArgs a) {
         const uint8_t *sp = a.w13_s + r * srow;
         f32x4 acc = zero4();
         for (int ch = 0; ch < nchunk; ++ch) {
+            // Every wave loads and multiplies (a wave past the last tile
+            // reads tile 0 again and drops its result), which keeps the
+            // load sequence free of branches: the compiler then waits for
+            // each step's own loads only.
             Fp4Chunk<S> w;
-            if (active) load_fp4_chunk<S>(qp, sp, ch * S, w);
+            load_fp4_scales<S>(sp + (size_t)ch * S * 4, w);
+            fence_schedule();
             stage_operand<S>(s_b, a.zhl, a.L, ch * S * kKStep, nt,
                              [&](int jj) { return __shfl(recw, R_TOKEN + jj); });
-            wait_all_loads();
-            __syncthreads();
-            if (active) mfma_fp4_chunk<S>(w, s_b, n_eff, g, acc);
+            fence_schedule();
+            load_fp4_codes<S>(qp + (size_t)ch * S * 64, w);
+            fence_schedule();
+            wait_staging<S>();
+            staged_barrier();
+            mfma_fp4_chunk<S>(w, s_b, n_eff, g, acc);
             __syncthreads();
         }
         acc = add_pair_column(acc);
@@ -502,13 +543,21 @@ k_w2(const StepArgs a) {
         const uint8_t *sp = a.w2_s + r * srow;
         f32x4 acc = zero4();
         for (int ch = 0; ch < nchunk; ++ch) {
+            // Every wave loads and multiplies (a wave past the last tile
+            // reads tile 0 again and drops its result), which keeps the
+            // load sequence free of branches: the compiler then waits for
+            // each step's own loads only.
             Fp4Chunk<S> w;
-            if (active) load_fp4_chunk<S>(qp, sp, ch * S, w);
+            load_fp4_scales<S>(sp + (size_t)ch * S * 4, w);
+            fence_schedule();
             stage_operand<S>(s_b, a.acthl, a.I, ch * S * kKStep, nt,
                              [&](int jj) { return p0 + jj; });
-            wait_all_loads();
-            __syncthreads();
-            if (active) mfma_fp4_chunk<S>(w, s_b, n_eff, g, acc);
+            fence_schedule();
+            load_fp4_codes<S>(qp + (size_t)ch * S * 64, w);
+            fence_schedule();
+            wait_staging<S>();
+            staged_barrier();
+            mfma_fp4_chunk<S>(w, s_b, n_eff, g, acc);
             __syncthreads();
         }
         acc = add_pair_column(acc);
