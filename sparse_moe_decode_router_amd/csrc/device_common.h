@@ -25,7 +25,7 @@ constexpr int kMaxTopK = 64;
 constexpr int kMaxStepsPerChunk = 8;
 
 // Global counter slots (u32) at the head of the workspace.
-enum { G_ROUTER_DONE = 0, G_NEXT_TOKEN = 1, G_TOKENS_DONE = 2, G_COUNT = 64 };
+enum { G_ROUTER_DONE = 0, G_COUNT = 64 };
 // Routing metadata header (i32).
 enum { M_N_ACTIVE = 0, M_N_COLS = 1, M_COUNT = 16 };
 // Column-unit record (i32 words): expert, pair count (<= 8), first pair index,

@@ -212,11 +212,11 @@ __device__ __forceinline__ Role role_of(int KW) {
 // ---------------------------------------------------------------------------
 
 __global__ void __launch_bounds__(kBlock) k_router_f32(const StepArgs a) {
-    __shared__ unsigned long long s_mask[kMaxExperts];
+    __shared__ RouteLds s_route;
+    __shared__ int s_last;
     const int wave = wave_index();
     const int lane = lane_id();
-    const int nwaves = gridDim.x * kWavesPerBlock;
-    for (int e = blockIdx.x * kWavesPerBlock + wave; e < a.E; e += nwaves) {
+    for (int e = blockIdx.x * kWavesPerBlock + wave; e < a.E; e += gridDim.x * kWavesPerBlock) {
         const float *row = a.router_w32 + (size_t)e * a.H;
         for (int b = 0; b < a.B; ++b) {
             const uint16_t *xb = a.x + (size_t)b * a.H;
@@ -229,11 +229,15 @@ __global__ void __launch_bounds__(kBlock) k_router_f32(const StepArgs a) {
                 a.key[(size_t)b * a.E + e] = s + (a.bias ? a.bias[e] : 0.f);
             }
         }
-        if (wave_arrive(&a.gctr[G_ROUTER_DONE]) == (uint32_t)a.router_target - 1u)
-            topk_loop(a, s_mask);
-        else
-            maybe_join_topk(a, s_mask);
     }
+    // One arrival per workgroup, once all of its waves have stored.
+    __syncthreads();
+    if (wave == 0) {
+        const bool last = wave_arrive(&a.gctr[G_ROUTER_DONE]) == (uint32_t)a.router_target - 1u;
+        if (lane == 0) s_last = last;
+    }
+    __syncthreads();
+    if (s_last) route_step(a, s_route, kWavesPerBlock);
 }
 
 // ---------------------------------------------------------------------------
@@ -245,10 +249,12 @@ __global__ void __launch_bounds__(kBlock) k_router_f32(const StepArgs a) {
 // D rows i and 8+i, held by lanes l and l+32).
 __global__ void __launch_bounds__(kWGThreads) __attribute__((amdgpu_waves_per_eu(4)))
 k_dense_in(const StepArgs a) {
-    __shared__ unsigned long long s_mask[kMaxExperts];
+    __shared__ RouteLds s_route;
     __shared__ float s_red[kWG * kWave * 4];
+    __shared__ int s_last;
     const int lane = lane_id(), n = lane & 15, g = lane >> 4;
     const Role ro = role_of(a.kw_in);
+    if (threadIdx.x == 0) s_last = 0;
     // The latent combine accumulates into ylat with atomics later in the step.
     for (int i = (blockIdx.x * kWGThreads + threadIdx.x) * 4; i < a.B * a.L;
          i += gridDim.x * kWGThreads * 4)
@@ -294,8 +300,9 @@ k_dense_in(const StepArgs a) {
                     stf4(a.score + (size_t)b * a.E + e, sv);
                     stf4(a.key + (size_t)b * a.E + e, sv + bv);
                 }
-                if (wave_arrive(&a.gctr[G_ROUTER_DONE]) == (uint32_t)a.router_target - 1u)
-                    topk_loop(a, s_mask);
+                if (wave_arrive(&a.gctr[G_ROUTER_DONE]) == (uint32_t)a.router_target - 1u &&
+                    lane == 0)
+                    s_last = 1;
             } else if (kind == 1) {
                 if (valid) {
                     uint16_t *dst = a.zhl + (size_t)b * 2 * a.L + 16 * (tt - n_rt) + 4 * g;
@@ -314,7 +321,11 @@ k_dense_in(const StepArgs a) {
             }
         }
         __syncthreads();
-        if (n_rt > 0) maybe_join_topk(a, s_mask);
+        if (s_last) {  // this workgroup completed the router: route the step
+            route_step(a, s_route, kWG);
+            __syncthreads();
+            if (threadIdx.x == 0) s_last = 0;
+        }
     }
 }
 
@@ -581,9 +592,9 @@ __device__ __forceinline__ void store_out4(uint16_t *dst, f32x4 v) {
 __global__ void __launch_bounds__(kWGThreads) __attribute__((amdgpu_waves_per_eu(4)))
 k_out(const StepArgs a) {
     __shared__ float s_red[kWG * kWave * 4];
-    // The routing counters of the dense input kernel are cleared here, where
-    // no wave of the step can touch them any more.
-    if (blockIdx.x == 0 && threadIdx.x < 3) a.gctr[threadIdx.x] = 0u;
+    // The router counter of the dense input kernel is cleared here, where no
+    // wave of the step can touch it any more.
+    if (blockIdx.x == 0 && threadIdx.x == 0) a.gctr[G_ROUTER_DONE] = 0u;
     const int lane = lane_id(), n = lane & 15, g = lane >> 4;
     const int col = n >> 1, part = n & 1;
     const Role ro = role_of(a.kw_out);

@@ -313,7 +313,10 @@ moe_status moe_decode_step(moe_decode_ctx *ctx, const uint16_t *x, int32_t batch
     a.user_idx = topk_idx;
     a.user_w = topk_w;
     a.n_r16 = pl.n_r16;
-    a.router_target = c.router_dtype == MOE_ROUTER_BF16 ? pl.n_r16 * pl.ncg_in : c.n_experts;
+    // Arrivals that complete the router: one per router unit of the dense
+    // input kernel, or one per workgroup of the f32 router kernel.
+    a.router_target = c.router_dtype == MOE_ROUTER_BF16 ? pl.n_r16 * pl.ncg_in
+                                                        : cdiv(c.n_experts, kWavesPerBlock);
     a.kw_in = pl.in.kw;
     a.kw_out = pl.out.kw;
     a.spc_in = pl.in.spc;

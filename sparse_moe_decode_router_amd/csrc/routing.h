@@ -8,12 +8,13 @@
 // active per token; sigmoid scores, the bias on the key only and the
 // renormalisation are readings of the layer definition).
 //
-// The work runs inside the kernel that produces the router scores: the wave
-// whose arrival completes the router starts claiming tokens, and any wave that
-// finishes a tile afterwards joins it; the wave that completes the last token
-// builds the metadata.  No wave ever waits on another.  Wave-wide reductions
-// and scans use DPP row operations and scalar lane reads, so one top-16 of
-// 896 costs a few thousand cycles of one wave.
+// The work runs inside the kernel that produces the router scores: every
+// router tile ends with an arrival on one agent-scope counter, and the
+// workgroup whose arrival completes the router runs the whole routing with
+// all of its waves (tokens split by wave), hands the selections over in LDS
+// and builds the metadata; no other workgroup waits or polls.  Wave-wide
+// reductions and scans use DPP row operations and scalar lane reads, and the
+// selection rounds touch no memory.
 #pragma once
 
 #include "device_common.h"
@@ -75,41 +76,57 @@ __device__ __forceinline__ uint32_t orderable(float key) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// LDS of the routing workgroup: the selections of every token, the token
+// masks of the experts and per-expert offsets.
+struct RouteLds {
+    int16_t idx[kMaxBatch * kMaxTopK];
+    float w[kMaxBatch * kMaxTopK];
+    unsigned long long mask[kMaxExperts];
+    int off[kMaxExperts];
+    int unit[kMaxExperts];
+};
+
 // Top-k of one token, by one wave.  Lane l owns experts l, l+64, ... and
-// keeps its best remaining (key, lowest id) as a candidate.  Each round takes
-// the wave-wide largest candidate key (equal keys: the lowest expert id), the
-// winning lane advances its candidate, and the selection is recorded in lane
-// r (round r) together with its rank among the selected ids.  Selected ids
-// are written in ascending order with weights s_e / sum(s); the sum is taken
-// in selection order.
-__device__ __forceinline__ void topk_token(const StepArgs &a, int b) {
+// keeps their keys and scores in registers, plus its best remaining (key,
+// lowest id) as a candidate.  Each round takes the wave-wide largest
+// candidate key (equal keys: the lowest expert id), the winning lane advances
+// its candidate, and the selection is recorded in lane r (round r) together
+// with its rank among the selected ids.  Selected ids are written in
+// ascending order with weights s_e / sum(s); the sum is taken in selection
+// order.  No memory access happens inside the rounds.
+__device__ __forceinline__ void topk_token(const StepArgs &a, int b, RouteLds &lds) {
     const int lane = lane_id();
     const int E = a.E, k = a.k;
     const float *keyrow = a.key + (size_t)b * E;
     const float *srow = a.score + (size_t)b * E;
     const int nk = (E + kWave - 1) / kWave;
     uint32_t ok[kKeysPerLane];
+    float os[kKeysPerLane];
     uint32_t avail = 0;
 #pragma unroll
     for (int i = 0; i < kKeysPerLane; ++i) {
         const int e = lane + kWave * i;
         const bool in = i < nk && e < E;
         ok[i] = in ? orderable(keyrow[in ? e : 0]) : 0u;
+        os[i] = in ? srow[in ? e : 0] : 0.f;
         avail |= in ? (1u << i) : 0u;
     }
-    auto candidate = [&](uint32_t &ck, int &ci) {
+    uint32_t ck;
+    int ci;
+    float cs;
+    auto candidate = [&]() {
         ck = 0;
         ci = 0;
+        cs = 0.f;
 #pragma unroll
         for (int i = 0; i < kKeysPerLane; ++i) {
             const bool take = ((avail >> i) & 1u) && ok[i] > ck;  // strict: lowest i on ties
             ck = take ? ok[i] : ck;
             ci = take ? i : ci;
+            cs = take ? os[i] : cs;
         }
     };
-    uint32_t ck;
-    int ci;
-    candidate(ck, ci);
+    candidate();
     int mine = 0, rank = 0;
     float s_mine = 0.f, total = 0.f;
     for (int r = 0; r < k; ++r) {
@@ -120,8 +137,8 @@ __device__ __forceinline__ void topk_token(const StepArgs &a, int b) {
             const uint32_t id = (ck == m) ? (uint32_t)(lane + kWave * ci) : 0xFFFFFFFFu;
             wl = (int)(wave_min_u32(id) & (kWave - 1));
         }
-        const int e = (int)readlane((uint32_t)(wl + kWave * ci), wl);
-        const float s = srow[e];  // same address in every lane: one load
+        const int e = (int)readlane((uint32_t)(lane + kWave * ci), wl);
+        const float s = __uint_as_float(readlane(__float_as_uint(cs), wl));
         total += s;
         // Ranks: earlier selections above e move up; the new one counts the
         // earlier selections below it.
@@ -135,12 +152,14 @@ __device__ __forceinline__ void topk_token(const StepArgs &a, int b) {
         }
         if (lane == wl) {
             avail &= ~(1u << ci);
-            candidate(ck, ci);
+            candidate();
         }
     }
     if (lane < k) {
         const float w = s_mine / total;
         const int o = b * k + rank;
+        lds.idx[o] = (int16_t)mine;
+        lds.w[o] = w;
         a.idx[o] = mine;
         a.wsel[o] = w;
         if (a.user_idx) a.user_idx[o] = mine;
@@ -154,19 +173,21 @@ __device__ __forceinline__ void topk_token(const StepArgs &a, int b) {
 // units of at most 8 tokens (16 MFMA columns: hi and lo of each token).  A
 // unit's record holds everything its workgroups need, so that they read it in
 // one round trip: expert, pair count, first pair, and per pair the token and
-// the routing weight.
-__device__ __forceinline__ void build_meta(const StepArgs &a, unsigned long long *s_mask) {
+// the routing weight.  A pair's place follows from the bit mask alone (its
+// token's rank among the expert's tokens), so the pairs are placed in
+// parallel.
+__device__ __forceinline__ void build_meta(const StepArgs &a, RouteLds &lds) {
     const int lane = lane_id();
     const int B = a.B, k = a.k, E = a.E;
-    for (int e = lane; e < E; e += kWave) s_mask[e] = 0ull;
+    for (int e = lane; e < E; e += kWave) lds.mask[e] = 0ull;
     wave_sync();
-    for (int p = lane; p < B * k; p += kWave) atomicOr(&s_mask[a.idx[p]], 1ull << (p / k));
+    for (int p = lane; p < B * k; p += kWave) atomicOr(&lds.mask[lds.idx[p]], 1ull << (p / k));
     wave_sync();
     const int C = (E + kWave - 1) / kWave;
     const int e0 = lane * C, e1 = min(E, e0 + C);
     int na = 0, np = 0, nc = 0;
     for (int e = e0; e < e1; ++e) {
-        const int n = __popcll(s_mask[e]);
+        const int n = __popcll(lds.mask[e]);
         na += n ? 1 : 0;
         np += n;
         nc += (n + 7) >> 3;
@@ -177,35 +198,31 @@ __device__ __forceinline__ void build_meta(const StepArgs &a, unsigned long long
     const int NC = (int)readlane((uint32_t)ic, kWave - 1);
     int ai = ia - na, pi = ip - np, ci = ic - nc;
     for (int e = e0; e < e1; ++e) {
-        unsigned long long m = s_mask[e];
-        const int n = __popcll(m);
+        const int n = __popcll(lds.mask[e]);
+        lds.off[e] = pi;
+        lds.unit[e] = ci;
         if (!n) continue;
         a.act_expert[ai] = e;
         a.act_off[ai] = pi;
-        for (int r = 0; m; ++r) {
-            const int b = __ffsll((long long)m) - 1;
-            m &= m - 1;
-            const int *row = a.idx + b * k;  // ascending ids
-            int lo = 0, hi = k - 1;
-            while (lo < hi) {
-                const int mid = (lo + hi) >> 1;
-                if (row[mid] < e) lo = mid + 1; else hi = mid;
-            }
-            const int slot = b * k + lo;
-            a.pair_slot[pi + r] = slot;
-            a.pair_of_slot[slot] = pi + r;
-            int32_t *rec = a.cu_rec + (size_t)(ci + (r >> 3)) * kRecWords;
-            if ((r & 7) == 0) {
-                rec[R_EXPERT] = e;
-                rec[R_COUNT] = min(8, n - r);
-                rec[R_PAIR0] = pi + r;
-            }
-            rec[R_TOKEN + (r & 7)] = b;
-            rec[R_WEIGHT + (r & 7)] = __float_as_int(a.wsel[slot]);
+        for (int r = 0; r < n; r += 8, ++ci) {
+            int32_t *rec = a.cu_rec + (size_t)ci * kRecWords;
+            rec[R_EXPERT] = e;
+            rec[R_COUNT] = min(8, n - r);
+            rec[R_PAIR0] = pi + r;
         }
-        ci += (n + 7) >> 3;
         ++ai;
         pi += n;
+    }
+    wave_sync();
+    for (int p = lane; p < B * k; p += kWave) {
+        const int e = lds.idx[p], b = p / k;
+        const int r = __popcll(lds.mask[e] & ((1ull << b) - 1ull));
+        const int pos = lds.off[e] + r;
+        a.pair_slot[pos] = p;
+        a.pair_of_slot[p] = pos;
+        int32_t *rec = a.cu_rec + (size_t)(lds.unit[e] + (r >> 3)) * kRecWords;
+        rec[R_TOKEN + (r & 7)] = b;
+        rec[R_WEIGHT + (r & 7)] = __float_as_int(lds.w[p]);
     }
     if (lane == 0) {
         a.meta[M_N_ACTIVE] = D;
@@ -214,28 +231,14 @@ __device__ __forceinline__ void build_meta(const StepArgs &a, unsigned long long
     }
 }
 
-// Claims tokens until none is left; the wave that finishes the last token
-// builds the metadata.  Called only once the router is complete.
-__device__ __forceinline__ void topk_loop(const StepArgs &a, unsigned long long *s_mask) {
-    acquire_agent();
-    // Claims are unique, so one wave can never claim more than B tokens.
-    for (int it = 0; it < a.B; ++it) {
-        const uint32_t t = wave_fetch_add(&a.gctr[G_NEXT_TOKEN], 1u);
-        if (t >= (uint32_t)a.B) break;
-        topk_token(a, (int)t);
-        if (wave_arrive(&a.gctr[G_TOKENS_DONE]) == (uint32_t)a.B - 1u) {
-            acquire_agent();
-            build_meta(a, s_mask);
-        }
-    }
-}
-
-// A wave that finished a tile helps with the top-k when the router is
-// complete and tokens are still unclaimed.
-__device__ __forceinline__ void maybe_join_topk(const StepArgs &a, unsigned long long *s_mask) {
-    if (wave_load_counter(&a.gctr[G_ROUTER_DONE]) != (uint32_t)a.router_target) return;
-    if (wave_load_counter(&a.gctr[G_NEXT_TOKEN]) >= (uint32_t)a.B) return;
-    topk_loop(a, s_mask);
+// The whole routing of the step, by every wave of the workgroup whose router
+// arrival completed the router (all waves call it, after a workgroup
+// barrier).  Tokens are split across the waves; the selections meet in LDS.
+__device__ __forceinline__ void route_step(const StepArgs &a, RouteLds &lds, int nwaves) {
+    acquire_agent();  // every router tile's scores and keys
+    for (int b = wave_index(); b < a.B; b += nwaves) topk_token(a, b, lds);
+    __syncthreads();
+    if (wave_index() == 0) build_meta(a, lds);
 }
 
 }  // namespace moe
