@@ -194,13 +194,12 @@ def main():
     torch.cuda.synchronize()
     ms_eager = (time.perf_counter() - t0) * 1e3 / args.steps
 
-    # Pass B: per-kernel durations from HIP events recorded between the
-    # kernels on the step's stream (eager steps; event-record nodes inside a
-    # replayed graph do not time its kernels on this runtime).  R rotating
-    # event sets, each read back before it is reused.
+    # Pass B: per-kernel durations from HIP events attached to each kernel's
+    # dispatch (start and stop of the kernel itself) on eager steps; R
+    # rotating event sets, each read back before it is reused.
     evs = []
     for r in range(R):
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2 * len(names))]
         for x in e:
             x.record(stream)
         evs.append(e)
@@ -213,7 +212,7 @@ def main():
         e = evs[r]
         e[-1].synchronize()
         for j, n in enumerate(names):
-            sums[n] += e[j].elapsed_time(e[j + 1])
+            sums[n] += e[2 * j].elapsed_time(e[2 * j + 1])
             kbytes[n] += kb[r][n]
 
     t0 = time.perf_counter()

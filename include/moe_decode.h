@@ -179,12 +179,13 @@ typedef struct {
 } moe_decode_dispatch_info;
 moe_status moe_decode_last_dispatch(const moe_decode_ctx *ctx, moe_decode_dispatch_info *info);
 
-/* Per-kernel timing.  With events set (n = the step's kernel count + 1, see
+/* Per-kernel timing.  With events set (n = 2 x the step's kernel count, see
  * moe_decode_dispatch_info.n_kernels; HIP event handles owned by the caller),
- * every later step records events[0] on its stream before its first kernel and
- * events[i+1] after kernel i; a step captured into a graph records them on
- * each replay.  n = 0 (events may be NULL) switches recording off.  Returns
- * MOE_ERR_INVALID_ARG when n does not match the step's kernel count. */
+ * every later eager step launches kernel i with events[2i] and events[2i+1]
+ * attached to its dispatch (hipExtLaunchKernel), so that their elapsed time is
+ * the kernel's own execution time, as a kernel trace reports it.  n = 0
+ * (events may be NULL) switches timing off.  Returns MOE_ERR_INVALID_ARG when
+ * n does not match the step's kernel count. */
 moe_status moe_decode_set_timing_events(moe_decode_ctx *ctx, void *const *events, int32_t n);
 
 /* Copies the intermediates of the last step out of the workspace as f32

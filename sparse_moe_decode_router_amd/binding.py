@@ -223,7 +223,8 @@ class MoEDecode:
 
     def set_timing_events(self, events) -> None:
         """torch.cuda.Event(enable_timing=True) objects (already recorded once,
-        so their handles exist), one per kernel plus one; None switches off."""
+        so their handles exist), a start and a stop event per kernel of the
+        step, attached to the kernels' dispatches; None switches off."""
         if not events:
             _check(lib().moe_decode_set_timing_events(self.handle, None, 0), "timing events")
             return

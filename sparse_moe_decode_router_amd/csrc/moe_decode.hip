@@ -1,6 +1,7 @@
 // moe_decode.hip - host side of the decode-step library: configuration checks,
 // workspace carving, the batch-dependent launch plan and the C ABI declared in
 // include/moe_decode.h.  The kernels live in kernels.h.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -131,7 +132,7 @@ struct moe_decode_ctx {
     int device;
     int32_t last_hip;
     moe_decode_dispatch_info last;
-    hipEvent_t events[8];  // timing events (caller-owned), n_events = 0: off
+    hipEvent_t events[10];  // timing events (caller-owned), n_events = 0: off
     int32_t n_events;
 };
 
@@ -338,25 +339,21 @@ moe_status moe_decode_step(moe_decode_ctx *ctx, const uint16_t *x, int32_t batch
     d.router_f32 = c.router_dtype == MOE_ROUTER_F32;
     d.n_kernels = 4 + d.router_f32;
 
-    const bool timed = ctx->n_events == d.n_kernels + 1;
-    int ev = 0;
-    auto mark = [&]() {
-        if (timed) (void)hipEventRecord(ctx->events[ev++], s);
+    const bool timed = ctx->n_events == 2 * d.n_kernels;
+    int ki = 0;
+    auto launch = [&](StepKernel kernel, unsigned grid, unsigned threads) {
+        if (timed)
+            hipExtLaunchKernelGGL(kernel, dim3(grid), dim3(threads), 0, s, ctx->events[2 * ki],
+                                  ctx->events[2 * ki + 1], 0, a);
+        else
+            hipLaunchKernelGGL(kernel, dim3(grid), dim3(threads), 0, s, a);
+        ++ki;
     };
-    mark();
-    if (d.router_f32) {
-        hipLaunchKernelGGL(k_router_f32, dim3(cdiv(c.n_experts, kWavesPerBlock)), dim3(kBlock), 0,
-                           s, a);
-        mark();
-    }
-    hipLaunchKernelGGL(k_dense_in, dim3(d.grid_in), dim3(kWGThreads), 0, s, a);
-    mark();
-    hipLaunchKernelGGL(kW13[pl.s13], dim3(d.grid_w13), dim3(kWGThreads), 0, s, a);
-    mark();
-    hipLaunchKernelGGL(kW2[pl.s2], dim3(d.grid_w2), dim3(kWGThreads), 0, s, a);
-    mark();
-    hipLaunchKernelGGL(k_out, dim3(d.grid_out), dim3(kWGThreads), 0, s, a);
-    mark();
+    if (d.router_f32) launch(k_router_f32, cdiv(c.n_experts, kWavesPerBlock), kBlock);
+    launch(k_dense_in, d.grid_in, kWGThreads);
+    launch(kW13[pl.s13], d.grid_w13, kWGThreads);
+    launch(kW2[pl.s2], d.grid_w2, kWGThreads);
+    launch(k_out, d.grid_out, kWGThreads);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(ctx, e);
     return MOE_OK;
@@ -434,7 +431,7 @@ moe_status moe_decode_last_dispatch(const moe_decode_ctx *ctx, moe_decode_dispat
 
 moe_status moe_decode_set_timing_events(moe_decode_ctx *ctx, void *const *events, int32_t n) {
     if (!ctx || n < 0) return MOE_ERR_INVALID_ARG;
-    const int32_t want = 4 + (ctx->cfg.router_dtype == MOE_ROUTER_F32 ? 1 : 0) + 1;
+    const int32_t want = 2 * (4 + (ctx->cfg.router_dtype == MOE_ROUTER_F32 ? 1 : 0));
     if (n == 0) {
         ctx->n_events = 0;
         return MOE_OK;

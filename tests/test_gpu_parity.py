@@ -238,6 +238,33 @@ def test_graph_replays_match_eager_and_track_new_inputs(small_layer):
     g.close()
 
 
+def test_timing_events_time_each_kernel(small_layer, small_ctx):
+    """Events attached to the dispatches: one positive duration per kernel,
+    together no longer than the step; a wrong event count is refused."""
+    import torch
+    x = synth.make_tokens(small_layer.dims, 15, 4)
+    run(small_ctx, x, 6)
+    n = small_ctx.last_dispatch()["n_kernels"]
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n)]
+    for e in evs:
+        e.record()
+    torch.cuda.synchronize()
+    small_ctx.set_timing_events(evs)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    run(small_ctx, x, 6)
+    t1.record()
+    torch.cuda.synchronize()
+    small_ctx.set_timing_events(None)
+    d = [evs[2 * i].elapsed_time(evs[2 * i + 1]) for i in range(n)]
+    log("  kernel ms", d, "step ms", t0.elapsed_time(t1))
+    assert all(v > 0 for v in d)
+    assert sum(d) <= t0.elapsed_time(t1)
+    with pytest.raises(binding.MoEError):
+        small_ctx.set_timing_events(evs[:-1])
+
+
 def test_dispatch_follows_the_batch(small_layer, small_ctx):
     for B, cg in ((1, 1), (16, 1), (17, 2), (64, 4)):
         x = synth.make_tokens(small_layer.dims, 14, B)
