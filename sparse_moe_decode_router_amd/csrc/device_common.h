@@ -128,30 +128,38 @@ __device__ __forceinline__ void wave_sync() {
     __builtin_amdgcn_wave_barrier();
 }
 
-// Wave-level counter operations.  Every lane takes part (lane 0 contributes
-// the value, the others zero), so no atomic sits under a lane-dependent
-// branch, and the result is read from lane 0 into a scalar register: the
-// control flow that follows stays uniform across the wave.
+// Publication without cache maintenance.  Data that one workgroup publishes
+// to another through a counter is written with agent-scope atomic stores
+// (they go through to the agent's point of coherence instead of staying in
+// this XCD's L2) and read with agent-scope atomic loads (which do not hit a
+// stale line in the reader's caches).  An arrival then only has to wait until
+// the wave's own stores have completed before it increments the counter: no
+// L2 write-back (release fence) on the writer side, no invalidation
+// (acquire fence) on the reader side.
+__device__ __forceinline__ void store_agent(float *p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_agent(const float *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
-// One arrival of the whole wave on an agent-scope counter.  Every lane's
-// earlier global stores are released before the increment; the old value is
-// returned.  The caller issues acquire_agent() before reading what other
-// arrivals wrote.
+// Waits for every vector memory access of the wave (stores included).
+__device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Wave-wide fetch-add on an agent-scope counter: lane 0 adds v (the other
+// lanes add zero, so the atomic sits under no lane-dependent branch) and the
+// old value is returned as a scalar.
 __device__ __forceinline__ uint32_t wave_fetch_add(uint32_t *ctr, uint32_t v) {
     const uint32_t add = lane_id() == 0 ? v : 0u;
     const uint32_t old = __hip_atomic_fetch_add(ctr, add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return uniform(old);
 }
 
-__device__ __forceinline__ uint32_t wave_arrive(uint32_t *ctr) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+// One arrival of the whole wave on an agent-scope counter after its
+// agent-scope stores (see above) have completed; returns the old value.
+__device__ __forceinline__ uint32_t wave_publish(uint32_t *ctr) {
+    wait_vm_all();
     return wave_fetch_add(ctr, 1u);
-}
-
-__device__ __forceinline__ void acquire_agent() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
-
-__device__ __forceinline__ uint32_t wave_load_counter(uint32_t *ctr) {
-    return uniform(__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
 }
 
 // Index of the calling wave in its workgroup, as a scalar.

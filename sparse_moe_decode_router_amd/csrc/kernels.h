@@ -225,19 +225,21 @@ __global__ void __launch_bounds__(kBlock) k_router_f32(const StepArgs a) {
             acc = wave_sum(acc);
             if (lane == 0) {
                 const float s = sigmoidf_(acc);
-                a.score[(size_t)b * a.E + e] = s;
-                a.key[(size_t)b * a.E + e] = s + (a.bias ? a.bias[e] : 0.f);
+                store_agent(a.score + (size_t)b * kMaxExperts + e, s);
+                store_agent(a.key + (size_t)b * kMaxExperts + e, s + (a.bias ? a.bias[e] : 0.f));
             }
         }
     }
-    // One arrival per workgroup, once all of its waves have stored.
+    // One arrival per workgroup, once the stores of all of its waves have
+    // completed.
+    wait_vm_all();
     __syncthreads();
     if (wave == 0) {
-        const bool last = wave_arrive(&a.gctr[G_ROUTER_DONE]) == (uint32_t)a.router_target - 1u;
+        const bool last = wave_publish(&a.gctr[G_ROUTER_DONE]) == (uint32_t)a.router_target - 1u;
         if (lane == 0) s_last = last;
     }
     __syncthreads();
-    if (s_last) route_step(a, s_route, kWavesPerBlock);
+    if (s_last) route_step(route_args(a), &s_route, kWavesPerBlock);
 }
 
 // ---------------------------------------------------------------------------
@@ -293,14 +295,15 @@ k_dense_in(const StepArgs a) {
             if (kind == 0) {
                 const int e = 16 * tt + 4 * g;
                 if (valid) {
-                    f32x4 sv;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) sv[i] = sigmoidf_(acc[i]);
                     const f32x4 bv = a.bias ? ldf4(a.bias + e) : zero4();
-                    stf4(a.score + (size_t)b * a.E + e, sv);
-                    stf4(a.key + (size_t)b * a.E + e, sv + bv);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float sv = sigmoidf_(acc[i]);
+                        store_agent(a.score + (size_t)b * kMaxExperts + e + i, sv);
+                        store_agent(a.key + (size_t)b * kMaxExperts + e + i, sv + bv[i]);
+                    }
                 }
-                if (wave_arrive(&a.gctr[G_ROUTER_DONE]) == (uint32_t)a.router_target - 1u &&
+                if (wave_publish(&a.gctr[G_ROUTER_DONE]) == (uint32_t)a.router_target - 1u &&
                     lane == 0)
                     s_last = 1;
             } else if (kind == 1) {
@@ -322,7 +325,7 @@ k_dense_in(const StepArgs a) {
         }
         __syncthreads();
         if (s_last) {  // this workgroup completed the router: route the step
-            route_step(a, s_route, kWG);
+            route_step(route_args(a), &s_route, kWG);
             __syncthreads();
             if (threadIdx.x == 0) s_last = 0;
         }
@@ -659,8 +662,9 @@ __global__ void k_debug_export(const StepArgs a, const DebugArgs d) {
     const size_t nE = (size_t)a.B * a.E, nL = (size_t)a.B * a.L, nS = (size_t)a.B * a.Is;
     const size_t nA = (size_t)a.B * a.k * a.I;
     for (size_t i = tid; i < nE; i += stride) {
-        if (d.score) d.score[i] = a.score[i];
-        if (d.key) d.key[i] = a.key[i];
+        const size_t j = (i / a.E) * kMaxExperts + i % a.E;
+        if (d.score) d.score[i] = a.score[j];
+        if (d.key) d.key[i] = a.key[j];
     }
     for (size_t i = tid; i < nL; i += stride) {
         const size_t b = i / a.L, c = i % a.L;

@@ -94,8 +94,10 @@ Layout make_layout(const moe_decode_config &c) {
     l.gctr = take(G_COUNT * 4);
     l.meta = take(M_COUNT * 4);
     l.counters_end = o;
-    l.score = take(Bm * E * 4);
-    l.key = take(Bm * E * 4);
+    // Score and key rows are padded to kMaxExperts: the routing reads a whole
+    // row with one base address (entries past E are never used).
+    l.score = take(Bm * kMaxExperts * 4);
+    l.key = take(Bm * kMaxExperts * 4);
     l.idx = take(P * 4);
     l.wsel = take(P * 4);
     l.act_expert = take((std::min(E, P) + 1) * 4);

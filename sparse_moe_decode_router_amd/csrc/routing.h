@@ -76,70 +76,128 @@ __device__ __forceinline__ uint32_t orderable(float key) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+constexpr int kMaxRouteWaves = 8;
+
+// What the routing reads and writes.
+struct RouteArgs {
+    int32_t B, k, E;
+    const float *score, *key;
+    int32_t *idx;
+    float *wsel;
+    int32_t *user_idx;
+    float *user_w;
+    int32_t *meta, *act_expert, *act_off, *cu_rec, *pair_slot, *pair_of_slot;
+};
+
+__device__ __forceinline__ RouteArgs route_args(const StepArgs &a) {
+    RouteArgs r;
+    r.B = a.B;
+    r.k = a.k;
+    r.E = a.E;
+    r.score = a.score;
+    r.key = a.key;
+    r.idx = a.idx;
+    r.wsel = a.wsel;
+    r.user_idx = a.user_idx;
+    r.user_w = a.user_w;
+    r.meta = a.meta;
+    r.act_expert = a.act_expert;
+    r.act_off = a.act_off;
+    r.cu_rec = a.cu_rec;
+    r.pair_slot = a.pair_slot;
+    r.pair_of_slot = a.pair_of_slot;
+    return r;
+}
+
 // LDS of the routing workgroup: the selections of every token, the token
-// masks of the experts and per-expert offsets.
+// masks of the experts, per-expert offsets and per-wave scan totals.
 struct RouteLds {
     int16_t idx[kMaxBatch * kMaxTopK];
     float w[kMaxBatch * kMaxTopK];
     unsigned long long mask[kMaxExperts];
     int off[kMaxExperts];
     int unit[kMaxExperts];
+    int wsum[kMaxRouteWaves][4];
 };
 
-// Top-k of one token, by one wave.  Lane l owns experts l, l+64, ... and
-// keeps their keys and scores in registers, plus its best remaining (key,
-// lowest id) as a candidate.  Each round takes the wave-wide largest
-// candidate key (equal keys: the lowest expert id), the winning lane advances
-// its candidate, and the selection is recorded in lane r (round r) together
-// with its rank among the selected ids.  Selected ids are written in
-// ascending order with weights s_e / sum(s); the sum is taken in selection
-// order.  No memory access happens inside the rounds.
-__device__ __forceinline__ void topk_token(const StepArgs &a, int b, RouteLds &lds) {
-    const int lane = lane_id();
-    const int E = a.E, k = a.k;
-    const float *keyrow = a.key + (size_t)b * E;
-    const float *srow = a.score + (size_t)b * E;
-    const int nk = (E + kWave - 1) / kWave;
-    uint32_t ok[kKeysPerLane];
-    float os[kKeysPerLane];
-    uint32_t avail = 0;
+// Best remaining experts of one lane, best first: orderable keys (0: none)
+// and slots (expert = lane + 64 * slot).
+constexpr int kList = 4;
+struct LaneList {
+    uint32_t k[kList];
+    int i[kList];
+};
+
+// The lane's kList best experts among those that come after (after_k,
+// after_i) in selection order: larger key first, equal keys by lower slot
+// (= lower expert id).  Branch-free insertion over the lane's slots.
+__device__ __forceinline__ void fill_list(LaneList &L, const uint32_t (&ok)[kKeysPerLane],
+                                          uint32_t after_k, int after_i) {
+#pragma unroll
+    for (int j = 0; j < kList; ++j) {
+        L.k[j] = 0u;
+        L.i[j] = 0;
+    }
 #pragma unroll
     for (int i = 0; i < kKeysPerLane; ++i) {
-        const int e = lane + kWave * i;
-        const bool in = i < nk && e < E;
-        ok[i] = in ? orderable(keyrow[in ? e : 0]) : 0u;
-        os[i] = in ? srow[in ? e : 0] : 0.f;
-        avail |= in ? (1u << i) : 0u;
-    }
-    uint32_t ck;
-    int ci;
-    float cs;
-    auto candidate = [&]() {
-        ck = 0;
-        ci = 0;
-        cs = 0.f;
+        const uint32_t v = ok[i];
+        const bool elig = v != 0u && (v < after_k || (v == after_k && i > after_i));
+        const uint32_t w = elig ? v : 0u;
+        bool gt[kList];
 #pragma unroll
-        for (int i = 0; i < kKeysPerLane; ++i) {
-            const bool take = ((avail >> i) & 1u) && ok[i] > ck;  // strict: lowest i on ties
-            ck = take ? ok[i] : ck;
-            ci = take ? i : ci;
-            cs = take ? os[i] : cs;
+        for (int j = 0; j < kList; ++j) gt[j] = w > L.k[j];  // strict: a later slot goes after
+#pragma unroll
+        for (int j = kList - 1; j >= 1; --j) {
+            L.k[j] = gt[j - 1] ? L.k[j - 1] : (gt[j] ? w : L.k[j]);
+            L.i[j] = gt[j - 1] ? L.i[j - 1] : (gt[j] ? i : L.i[j]);
         }
-    };
-    candidate();
+        L.k[0] = gt[0] ? w : L.k[0];
+        L.i[0] = gt[0] ? i : L.i[0];
+    }
+}
+
+// Top-k of one token, by one wave.  Lane l owns experts l, l+64, ... and
+// keeps their keys in registers and a short list of its best remaining ones.
+// Each round takes the wave-wide largest list head (equal keys: the lowest
+// expert id), the winning lane pops its head (and refills its list after
+// kList pops), and the selection is recorded in lane r (round r) together
+// with its rank among the selected ids.  Then lane r fetches the score of
+// its selection; the sum of the selected scores is taken in selection order
+// and the ids are written in ascending order with weights s_e / sum(s).
+// Scores and keys are read with agent-scope loads: they were published by
+// other workgroups.
+__device__ __forceinline__ void topk_token(const RouteArgs &a, int b, RouteLds &lds) {
+    const int lane = lane_id();
+    const int E = a.E, k = a.k;
+    const float *keyrow = a.key + (size_t)b * kMaxExperts;  // rows padded to kMaxExperts
+    const float *srow = a.score + (size_t)b * kMaxExperts;
+    const int nk = (E + kWave - 1) / kWave;
+    // All loads first, then their uses: the compiler keeps atomic loads in
+    // program order, so a use between two of them would serialise the round
+    // trips.
+    uint32_t ok[kKeysPerLane];
+#pragma unroll
+    for (int i = 0; i < kKeysPerLane; ++i) ok[i] = __float_as_uint(load_agent(keyrow + lane + kWave * i));
+#pragma unroll
+    for (int i = 0; i < kKeysPerLane; ++i) {
+        const bool in = i < nk && lane + kWave * i < E;
+        ok[i] = in ? orderable(__uint_as_float(ok[i])) : 0u;
+    }
+    LaneList L;
+    fill_list(L, ok, 0xFFFFFFFFu, -1);
+    int npop = 0;
     int mine = 0, rank = 0;
-    float s_mine = 0.f, total = 0.f;
     for (int r = 0; r < k; ++r) {
+        const uint32_t ck = L.k[0];
+        const int cid = lane + kWave * L.i[0];
         const uint32_t m = wave_max_u32(ck);
         const unsigned long long tied = __ballot(ck == m);
         int wl = (int)__ffsll((long long)tied) - 1;
         if (__popcll(tied) > 1) {  // equal keys in several lanes: lowest expert id wins
-            const uint32_t id = (ck == m) ? (uint32_t)(lane + kWave * ci) : 0xFFFFFFFFu;
+            const uint32_t id = (ck == m) ? (uint32_t)cid : 0xFFFFFFFFu;
             wl = (int)(wave_min_u32(id) & (kWave - 1));
         }
-        const int e = (int)readlane((uint32_t)(lane + kWave * ci), wl);
-        const float s = __uint_as_float(readlane(__float_as_uint(cs), wl));
-        total += s;
+        const int e = (int)readlane((uint32_t)cid, wl);
         // Ranks: earlier selections above e move up; the new one counts the
         // earlier selections below it.
         const bool earlier = lane < r;
@@ -147,14 +205,26 @@ __device__ __forceinline__ void topk_token(const StepArgs &a, int b, RouteLds &l
         const unsigned long long below = __ballot(earlier && mine < e);
         if (lane == r) {
             mine = e;
-            s_mine = s;
             rank = __popcll(below);
         }
         if (lane == wl) {
-            avail &= ~(1u << ci);
-            candidate();
+            const uint32_t pk = L.k[0];
+            const int pi = L.i[0];
+#pragma unroll
+            for (int j = 0; j + 1 < kList; ++j) {
+                L.k[j] = L.k[j + 1];
+                L.i[j] = L.i[j + 1];
+            }
+            L.k[kList - 1] = 0u;
+            if (++npop == kList) {
+                fill_list(L, ok, pk, pi);
+                npop = 0;
+            }
         }
     }
+    const float s_mine = lane < k ? load_agent(srow + mine) : 0.f;
+    float total = 0.f;
+    for (int r = 0; r < k; ++r) total += __uint_as_float(readlane(__float_as_uint(s_mine), r));
     if (lane < k) {
         const float w = s_mine / total;
         const int o = b * k + rank;
@@ -167,24 +237,25 @@ __device__ __forceinline__ void topk_token(const StepArgs &a, int b, RouteLds &l
     }
 }
 
-// Routing metadata from idx [B][k], by one wave, with an LDS bit mask of the
-// tokens of each expert.  Active experts are listed in ascending id; the pairs
-// of an expert in ascending token; each expert's pairs are cut into column
-// units of at most 8 tokens (16 MFMA columns: hi and lo of each token).  A
-// unit's record holds everything its workgroups need, so that they read it in
-// one round trip: expert, pair count, first pair, and per pair the token and
-// the routing weight.  A pair's place follows from the bit mask alone (its
-// token's rank among the expert's tokens), so the pairs are placed in
-// parallel.
-__device__ __forceinline__ void build_meta(const StepArgs &a, RouteLds &lds) {
-    const int lane = lane_id();
-    const int B = a.B, k = a.k, E = a.E;
-    for (int e = lane; e < E; e += kWave) lds.mask[e] = 0ull;
-    wave_sync();
-    for (int p = lane; p < B * k; p += kWave) atomicOr(&lds.mask[lds.idx[p]], 1ull << (p / k));
-    wave_sync();
-    const int C = (E + kWave - 1) / kWave;
-    const int e0 = lane * C, e1 = min(E, e0 + C);
+// Routing metadata from the selections in LDS, by all nw waves of the routing
+// workgroup.  Active experts are listed in ascending id; the pairs of an
+// expert in ascending token; each expert's pairs are cut into column units of
+// at most 8 tokens (16 MFMA columns: hi and lo of each token).  A unit's
+// record holds everything its workgroups need, so that they read it in one
+// round trip: expert, pair count, first pair, and per pair the token and the
+// routing weight.  A pair's place follows from the token mask of its expert
+// (the token's rank among the expert's tokens), so pairs are placed in
+// parallel; expert offsets come from a two-level scan (lanes, then waves).
+__device__ __forceinline__ void build_meta(const RouteArgs &a, RouteLds &lds, int nw) {
+    const int lane = lane_id(), wave = wave_index();
+    const int tid = threadIdx.x, nt = nw * kWave;
+    const int B = a.B, k = a.k, E = a.E, P = B * k;
+    for (int e = tid; e < E; e += nt) lds.mask[e] = 0ull;
+    __syncthreads();
+    for (int p = tid; p < P; p += nt) atomicOr(&lds.mask[lds.idx[p]], 1ull << (p / k));
+    __syncthreads();
+    const int C = (E + nt - 1) / nt;
+    const int e0 = min(E, tid * C), e1 = min(E, e0 + C);
     int na = 0, np = 0, nc = 0;
     for (int e = e0; e < e1; ++e) {
         const int n = __popcll(lds.mask[e]);
@@ -193,10 +264,25 @@ __device__ __forceinline__ void build_meta(const StepArgs &a, RouteLds &lds) {
         nc += (n + 7) >> 3;
     }
     const int ia = wave_incl_scan(na), ip = wave_incl_scan(np), ic = wave_incl_scan(nc);
-    const int D = (int)readlane((uint32_t)ia, kWave - 1);
-    const int P = (int)readlane((uint32_t)ip, kWave - 1);
-    const int NC = (int)readlane((uint32_t)ic, kWave - 1);
-    int ai = ia - na, pi = ip - np, ci = ic - nc;
+    if (lane == kWave - 1) {
+        lds.wsum[wave][0] = ia;
+        lds.wsum[wave][1] = ip;
+        lds.wsum[wave][2] = ic;
+    }
+    __syncthreads();
+    int ba = 0, bp = 0, bc = 0, D = 0, PT = 0, NC = 0;
+    for (int w = 0; w < nw; ++w) {
+        const int xa = lds.wsum[w][0], xp = lds.wsum[w][1], xc = lds.wsum[w][2];
+        if (w < wave) {
+            ba += xa;
+            bp += xp;
+            bc += xc;
+        }
+        D += xa;
+        PT += xp;
+        NC += xc;
+    }
+    int ai = ba + ia - na, pi = bp + ip - np, ci = bc + ic - nc;
     for (int e = e0; e < e1; ++e) {
         const int n = __popcll(lds.mask[e]);
         lds.off[e] = pi;
@@ -213,8 +299,8 @@ __device__ __forceinline__ void build_meta(const StepArgs &a, RouteLds &lds) {
         ++ai;
         pi += n;
     }
-    wave_sync();
-    for (int p = lane; p < B * k; p += kWave) {
+    __syncthreads();
+    for (int p = tid; p < P; p += nt) {
         const int e = lds.idx[p], b = p / k;
         const int r = __popcll(lds.mask[e] & ((1ull << b) - 1ull));
         const int pos = lds.off[e] + r;
@@ -224,21 +310,20 @@ __device__ __forceinline__ void build_meta(const StepArgs &a, RouteLds &lds) {
         rec[R_TOKEN + (r & 7)] = b;
         rec[R_WEIGHT + (r & 7)] = __float_as_int(lds.w[p]);
     }
-    if (lane == 0) {
+    if (tid == 0) {
         a.meta[M_N_ACTIVE] = D;
         a.meta[M_N_COLS] = NC;
-        a.act_off[D] = P;
+        a.act_off[D] = PT;
     }
 }
 
 // The whole routing of the step, by every wave of the workgroup whose router
 // arrival completed the router (all waves call it, after a workgroup
 // barrier).  Tokens are split across the waves; the selections meet in LDS.
-__device__ __forceinline__ void route_step(const StepArgs &a, RouteLds &lds, int nwaves) {
-    acquire_agent();  // every router tile's scores and keys
-    for (int b = wave_index(); b < a.B; b += nwaves) topk_token(a, b, lds);
+__device__ __forceinline__ void route_step(const RouteArgs &a, RouteLds *lds, int nwaves) {
+    for (int b = wave_index(); b < a.B; b += nwaves) topk_token(a, b, *lds);
     __syncthreads();
-    if (wave_index() == 0) build_meta(a, lds);
+    build_meta(a, *lds, nwaves);
 }
 
 }  // namespace moe
