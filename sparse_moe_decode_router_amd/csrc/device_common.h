@@ -46,20 +46,27 @@ __device__ __forceinline__ uint32_t bf16_rne(float f) {
 }
 __device__ __forceinline__ float bf16_val(uint32_t h) { return __uint_as_float(h << 16); }
 
-// v ~= hi + lo with hi = bf16(v), lo = bf16(v - hi); the residual of the pair
-// is below 2^-17 |v|.
-__device__ __forceinline__ void split_hl(float v, uint32_t &hi, uint32_t &lo) {
-    hi = bf16_rne(v);
-    lo = bf16_rne(v - bf16_val(hi));
+// Two f32 -> two bf16 (low half: a), round to nearest even, with the
+// packed conversion instruction.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16x2_rne(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
+}
+
+// (a, b) ~= hi + lo with hi = bf16(v), lo = bf16(v - hi) per value; the
+// residual of the pair is below 2^-17 |v|.  Both halves as packed bf16 pairs.
+__device__ __forceinline__ void split_hl2(float a, float b, uint32_t &hi, uint32_t &lo) {
+    hi = bf16x2_rne(a, b);
+    lo = bf16x2_rne(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xFFFF0000u));
 }
 
 // Writes four values as hi and lo bf16 halves (8 bytes each).
 __device__ __forceinline__ void store_hl4(uint16_t *hi, uint16_t *lo, f32x4 v) {
-    uint32_t h[4], l[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) split_hl(v[i], h[i], l[i]);
-    *(u32x2 *)hi = (u32x2){h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
-    *(u32x2 *)lo = (u32x2){l[0] | (l[1] << 16), l[2] | (l[3] << 16)};
+    uint32_t h0, l0, h1, l1;
+    split_hl2(v[0], v[1], h0, l0);
+    split_hl2(v[2], v[3], h1, l1);
+    *(u32x2 *)hi = (u32x2){h0, h1};
+    *(u32x2 *)lo = (u32x2){l0, l1};
 }
 
 // E8M0 byte -> f32 scale 2^(byte-127) (bytes 1..254).

@@ -25,8 +25,9 @@
 // expert combine.
 //
 // Operands.  x is bf16 and enters the MFMA as is (16 tokens per column group).
-// The f32 intermediates z, a, ylat and ash are split when they are loaded into
-// hi = bf16(v) and lo = bf16(v - hi); hi and lo occupy two adjacent columns of
+// The f32 intermediates z, a, ylat and ash are carried as hi = bf16(v) and
+// lo = bf16(v - hi) (z, a and ash stored that way by their producers, ylat
+// split while it is loaded); hi and lo occupy two adjacent columns of
 // the same MFMA (8 tokens per column group) and the two column sums are added
 // afterwards, which keeps f32-grade precision at one MFMA per K slice.
 //
@@ -66,10 +67,9 @@ __device__ __forceinline__ void load_cols_bf16(const uint16_t *X, bool valid, in
 // f32 column operand of one step, delivered as the hi (part 0) or lo (part 1)
 // bf16 half of each value.
 __device__ __forceinline__ uint32_t pack_part(float a, float b, int part) {
-    uint32_t ha, la, hb, lb;
-    split_hl(a, ha, la);
-    split_hl(b, hb, lb);
-    return part ? (la | (lb << 16)) : (ha | (hb << 16));
+    uint32_t h, l;
+    split_hl2(a, b, h, l);
+    return part ? l : h;
 }
 
 __device__ __forceinline__ void load_cols_f32(const float *X, bool valid, int part, int s,
@@ -135,22 +135,27 @@ __device__ __forceinline__ void dense_chunk_x(const uint16_t *A, const uint16_t 
     }
 }
 
-// Output kernel: K runs over [0, L) against lat_up and ylat, then over
-// [0, Is) against sh_w2 and ash; step s < Ls selects the first pair.
+// Output kernel: K runs over [0, L) against lat_up and ylat (f32, split into
+// hi/lo while loading), then over [0, Is) against sh_w2 and the shared
+// activation (already stored as hi/lo bf16 rows); step s < Ls selects the
+// first pair.
 struct TwoSource {
     const uint16_t *Aa;
     const float *Xa;  // K in [0, L)
     const uint16_t *Ab;
-    const float *Xb;  // K in [0, Is)
-    int Ls;           // L / 128
+    const uint16_t *Xb;  // K in [0, Is): the lane's hi or lo row
+    int Ls;              // L / 128
 };
 
 __device__ __forceinline__ void load_two(const TwoSource &t, bool valid, int part, int s,
                                          u32x4 (&ra)[4], u32x4 (&rb)[4]) {
-    const bool first = s < t.Ls;
-    const int ss = first ? s : s - t.Ls;
-    load_tile_bf16(first ? t.Aa : t.Ab, ss, ra);
-    load_cols_f32(first ? t.Xa : t.Xb, valid, part, ss, rb);
+    if (s < t.Ls) {
+        load_tile_bf16(t.Aa, s, ra);
+        load_cols_f32(t.Xa, valid, part, s, rb);
+    } else {
+        load_tile_bf16(t.Ab, s - t.Ls, ra);
+        load_cols_bf16(t.Xb, valid, s - t.Ls, rb);
+    }
 }
 
 __device__ __forceinline__ void dense_chunk_out(const TwoSource &t, bool valid, int part, int s0,
@@ -319,7 +324,8 @@ k_dense_in(const StepArgs a) {
                     f32x4 v;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) v[i] = silu_mul(acc[i], up[i]);
-                    stf4(a.ash + (size_t)b * a.Is + 8 * (tt - n_rt - n_lt) + 4 * g, v);
+                    uint16_t *dst = a.ashhl + (size_t)b * 2 * a.Is + 8 * (tt - n_rt - n_lt) + 4 * g;
+                    store_hl4(dst, dst + a.Is, v);
                 }
             }
         }
@@ -392,9 +398,7 @@ struct Fp4Chunk {
     uint32_t scale[S];
 };
 
-// Scale bytes of the chunk (four per step, lane group g uses byte g).  The
-// compiler may merge these loads, so they are issued before the staging
-// copies, where their number does not matter.
+// Scale bytes of the chunk (four per step, lane group g uses byte g).
 template <int S>
 __device__ __forceinline__ void load_fp4_scales(const uint8_t *sc, Fp4Chunk<S> &w) {
     if constexpr (S % 4 == 0) {
@@ -410,23 +414,34 @@ __device__ __forceinline__ void load_fp4_scales(const uint8_t *sc, Fp4Chunk<S> &
     }
 }
 
-// Codes of the chunk: S loads of 16 bytes, 64 bytes apart (never merged).
-// Issued after the staging copies, in step order, so that step s waits only
-// for the loads up to its own.
+// Codes of the chunk: S loads of 16 bytes, 64 bytes apart (never merged),
+// issued in step order, so that step s waits only for the loads up to its
+// own.
 template <int S>
 __device__ __forceinline__ void load_fp4_codes(const uint8_t *q, Fp4Chunk<S> &w) {
 #pragma unroll
     for (int s = 0; s < S; ++s) w.code[s] = ld_weight16(q + 64 * s);
 }
 
-// Waits until this wave's staging copies have landed while the S code loads
+// Number of weight loads of a chunk that may still be in flight when the
+// staging copies have landed.  For S % 4 == 0 the scales are S / 4 loads of 16
+// bytes (never merged) issued after the copies together with the codes;
+// otherwise they are issued before the copies (the compiler may merge 4-byte
+// loads, so their count is not fixed) and only the S code loads follow.
+template <int S>
+constexpr int loads_after_staging() {
+    return S % 4 == 0 ? S + S / 4 : S;
+}
+
+// Waits until this wave's staging copies have landed while the weight loads
 // issued after them may still be in flight: vector memory loads complete in
 // issue order.
 template <int S>
 __device__ __forceinline__ void wait_staging() {
-    static_assert(S <= 63, "vmcnt field");
+    constexpr int n = loads_after_staging<S>();
+    static_assert(n <= 63, "vmcnt field");
     // s_waitcnt: vmcnt in bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8].
-    __builtin_amdgcn_s_waitcnt((S & 15) | ((S >> 4) << 14) | 0x0F70);
+    __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | 0x0F70);
 }
 
 // Workgroup barrier after wait_staging: LDS holds every wave's copy once all
@@ -478,6 +493,7 @@ k_w13(const StepArgs a) {
     const int TG = (OT + kWG - 1) / kWG;
     const int nchunk = a.L / (kKStep * S);
     const size_t qrow = a.L / 2, srow = a.L / 32;
+    bool reuse = false;  // s_b holds a previous chunk
     for (int u = blockIdx.x; u < NC * TG; u += gridDim.x) {
         const int c = u / TG;
         const int t = (u % TG) * kWG + wave;
@@ -495,19 +511,22 @@ k_w13(const StepArgs a) {
             // Every wave loads and multiplies (a wave past the last tile
             // reads tile 0 again and drops its result), which keeps the
             // load sequence free of branches: the compiler then waits for
-            // each step's own loads only.
+            // each step's own loads only.  The staging copies go first, so
+            // that the barrier below waits for them alone.
+            if (reuse) __syncthreads();  // every wave is done with s_b
+            reuse = true;
             Fp4Chunk<S> w;
-            load_fp4_scales<S>(sp + (size_t)ch * S * 4, w);
+            if constexpr (S % 4 != 0) load_fp4_scales<S>(sp + (size_t)ch * S * 4, w);
             fence_schedule();
             stage_operand<S>(s_b, a.zhl, a.L, ch * S * kKStep, nt,
                              [&](int jj) { return __shfl(recw, R_TOKEN + jj); });
             fence_schedule();
+            if constexpr (S % 4 == 0) load_fp4_scales<S>(sp + (size_t)ch * S * 4, w);
             load_fp4_codes<S>(qp + (size_t)ch * S * 64, w);
             fence_schedule();
             wait_staging<S>();
             staged_barrier();
             mfma_fp4_chunk<S>(w, s_b, n_eff, g, acc);
-            __syncthreads();
         }
         acc = add_pair_column(acc);
         f32x4 up;
@@ -540,6 +559,7 @@ k_w2(const StepArgs a) {
     const int TG = (OT + kWG - 1) / kWG;
     const int nchunk = a.I / (kKStep * S);
     const size_t qrow = a.I / 2, srow = a.I / 32;
+    bool reuse = false;  // s_b holds a previous chunk
     for (int u = blockIdx.x; u < NC * TG; u += gridDim.x) {
         const int c = u / TG;
         const int t = (u % TG) * kWG + wave;
@@ -560,19 +580,22 @@ k_w2(const StepArgs a) {
             // Every wave loads and multiplies (a wave past the last tile
             // reads tile 0 again and drops its result), which keeps the
             // load sequence free of branches: the compiler then waits for
-            // each step's own loads only.
+            // each step's own loads only.  The staging copies go first, so
+            // that the barrier below waits for them alone.
+            if (reuse) __syncthreads();  // every wave is done with s_b
+            reuse = true;
             Fp4Chunk<S> w;
-            load_fp4_scales<S>(sp + (size_t)ch * S * 4, w);
+            if constexpr (S % 4 != 0) load_fp4_scales<S>(sp + (size_t)ch * S * 4, w);
             fence_schedule();
             stage_operand<S>(s_b, a.acthl, a.I, ch * S * kKStep, nt,
                              [&](int jj) { return p0 + jj; });
             fence_schedule();
+            if constexpr (S % 4 == 0) load_fp4_scales<S>(sp + (size_t)ch * S * 4, w);
             load_fp4_codes<S>(qp + (size_t)ch * S * 64, w);
             fence_schedule();
             wait_staging<S>();
             staged_barrier();
             mfma_fp4_chunk<S>(w, s_b, n_eff, g, acc);
-            __syncthreads();
         }
         acc = add_pair_column(acc);
         if (active && j < nt && part == 0) {
@@ -587,11 +610,9 @@ k_w2(const StepArgs a) {
 // Kernel 4: latent-up + shared-down, bf16 output.
 // ---------------------------------------------------------------------------
 
-__device__ __forceinline__ void store_out4(uint16_t *dst, f32x4 v) {
-    *(u32x2 *)dst = (u32x2){bf16_rne(v[0]) | (bf16_rne(v[1]) << 16),
-                            bf16_rne(v[2]) | (bf16_rne(v[3]) << 16)};
-}
-
+// Output tiles cover RT = out_rows <= 16 rows (MFMA rows past RT repeat the
+// tile's last row and are dropped), chosen so that the tiles split evenly
+// over the compute units.
 __global__ void __launch_bounds__(kWGThreads) __attribute__((amdgpu_waves_per_eu(4)))
 k_out(const StepArgs a) {
     __shared__ float s_red[kWG * kWave * 4];
@@ -601,8 +622,9 @@ k_out(const StepArgs a) {
     const int lane = lane_id(), n = lane & 15, g = lane >> 4;
     const int col = n >> 1, part = n & 1;
     const Role ro = role_of(a.kw_out);
+    const int RT = a.out_rows;
     const int ncg = (a.B + 7) >> 3;
-    const int n_t = a.H >> 4;
+    const int n_t = (a.H + RT - 1) / RT;
     const int tgroups = (n_t + ro.RW - 1) / ro.RW;
     const int units = tgroups * ncg;
     for (int u = blockIdx.x; u < units; u += gridDim.x) {
@@ -612,12 +634,13 @@ k_out(const StepArgs a) {
         const int b = 8 * cg + col;
         const bool valid = b < a.B;
         const int bb = valid ? b : 0;
-        const size_t h = 16 * (size_t)(active ? t : 0) + n;
+        const int h0 = RT * (active ? t : 0);
+        const size_t h = min(h0 + min(n, RT - 1), a.H - 1);
         TwoSource ts;
         ts.Aa = a.lat_up + h * a.L + 32 * g;
         ts.Xa = a.ylat + (size_t)bb * a.L + 32 * g;
         ts.Ab = a.sh_w2 + h * a.Is + 32 * g;
-        ts.Xb = a.ash + (size_t)bb * a.Is + 32 * g;
+        ts.Xb = a.ashhl + ((size_t)bb * 2 + part) * a.Is + 32 * g;
         ts.Ls = a.L / kKStep;
         f32x4 acc = zero4();
         if (active)
@@ -625,7 +648,14 @@ k_out(const StepArgs a) {
         const bool leader = reduce_k1(s_red, ro.wave, ro.kw, ro.KW, acc);
         if (leader && active) {
             acc = add_pair_column(acc);
-            if (valid && part == 0) store_out4(a.out + (size_t)b * a.H + 16 * t + 4 * g, acc);
+            if (valid && part == 0) {
+                uint16_t *dst = a.out + (size_t)b * a.H;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = 4 * g + i;
+                    if (r < RT && h0 + r < a.H) dst[h0 + r] = (uint16_t)bf16_rne(acc[i]);
+                }
+            }
         }
         __syncthreads();
     }
@@ -672,8 +702,11 @@ __global__ void k_debug_export(const StepArgs a, const DebugArgs d) {
         if (d.z) d.z[i] = bf16_val(zr[c]) + bf16_val(zr[a.L + c]);
         if (d.ylat) d.ylat[i] = a.ylat[i];
     }
-    for (size_t i = tid; i < nS; i += stride)
-        if (d.ash) d.ash[i] = a.ash[i];
+    for (size_t i = tid; i < nS; i += stride) {
+        const size_t b = i / a.Is, c = i % a.Is;
+        const uint16_t *r = a.ashhl + b * 2 * a.Is;
+        if (d.ash) d.ash[i] = bf16_val(r[c]) + bf16_val(r[a.Is + c]);
+    }
     for (size_t i = tid; i < nA; i += stride) {
         if (!d.act) break;
         const size_t slot = i / a.I, c = i % a.I;

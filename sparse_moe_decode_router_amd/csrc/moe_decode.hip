@@ -44,8 +44,17 @@ int expert_chunk(int nsteps) {
     return 1;
 }
 
+// Rows per output tile: 16, unless that gives more tiles than the 256
+// compute units of MI355X take at once; then the hidden rows are split into
+// 2 x 256 tiles (two workgroups per compute unit) of at most 16 rows, so that
+// every unit gets the same share.
+int out_tile_rows(int H) {
+    if (cdiv(H, 16) <= 256) return 16;
+    return std::min(16, cdiv(H, 2 * 256));
+}
+
 struct Plan {
-    int n_r16, ncg_in, ncg_out;
+    int n_r16, ncg_in, ncg_out, out_rows;
     Split in, out;
     int s13, s2;
     long long units_in, units_out, units_13, units_2;
@@ -65,7 +74,8 @@ Plan make_plan(const moe_decode_config &c, int B, int k) {
     const int n_t_in = p.n_r16 + c.latent / 16 + c.shared_inter / 8;
     const long long cols = ncols_cap(c.n_experts, B, k);
     p.units_in = (long long)cdiv(n_t_in, kWG / p.in.kw) * p.ncg_in;
-    p.units_out = (long long)cdiv(c.hidden / 16, kWG / p.out.kw) * p.ncg_out;
+    p.out_rows = out_tile_rows(c.hidden);
+    p.units_out = (long long)cdiv(cdiv(c.hidden, p.out_rows), kWG / p.out.kw) * p.ncg_out;
     // Expert kernels: 8 row tiles per workgroup (8 gate + 8 up rows, or 16
     // latent rows, per tile).
     p.units_13 = cols * cdiv(c.expert_inter / 8, kWG);
@@ -75,7 +85,7 @@ Plan make_plan(const moe_decode_config &c, int B, int k) {
 
 struct Layout {
     size_t gctr, meta, score, key, idx, wsel, act_expert, act_off, cu_rec, pair_slot,
-        pair_of_slot, zhl, ash, acthl, ylat, total;
+        pair_of_slot, zhl, ashhl, acthl, ylat, total;
     size_t counters_end;  // [0, counters_end) holds every counter: cleared at init
 };
 
@@ -106,7 +116,7 @@ Layout make_layout(const moe_decode_config &c) {
     l.pair_slot = take(P * 4);
     l.pair_of_slot = take(P * 4);
     l.zhl = take(Bm * 2 * L * 2);
-    l.ash = take(Bm * Is * 4);
+    l.ashhl = take(Bm * 2 * Is * 2);
     l.acthl = take(P * 2 * I * 2);
     l.ylat = take(Bm * L * 4);
     l.total = o;
@@ -190,7 +200,7 @@ StepArgs base_args(const moe_decode_ctx *ctx) {
     a.pair_slot = (int32_t *)(ws + l.pair_slot);
     a.pair_of_slot = (int32_t *)(ws + l.pair_of_slot);
     a.zhl = (uint16_t *)(ws + l.zhl);
-    a.ash = (float *)(ws + l.ash);
+    a.ashhl = (uint16_t *)(ws + l.ashhl);
     a.acthl = (uint16_t *)(ws + l.acthl);
     a.ylat = (float *)(ws + l.ylat);
     return a;
@@ -322,6 +332,7 @@ moe_status moe_decode_step(moe_decode_ctx *ctx, const uint16_t *x, int32_t batch
                                                         : cdiv(c.n_experts, kWavesPerBlock);
     a.kw_in = pl.in.kw;
     a.kw_out = pl.out.kw;
+    a.out_rows = pl.out_rows;
     a.spc_in = pl.in.spc;
     a.spc_out = pl.out.spc;
     const long long cap = 65535;  // workgroups; larger unit counts loop

@@ -19,6 +19,7 @@ struct StepArgs {
     int32_t kw_in, kw_out;
     int32_t spc_in, spc_out;  // 128-element steps per wave in the dense kernels
     int32_t ncols_cap;        // capacity of the expert column-unit list
+    int32_t out_rows;         // rows per output tile (<= 16)
     // Weights (borrowed).
     const uint16_t *router_w;
     const float *router_w32;
@@ -38,10 +39,10 @@ struct StepArgs {
     int32_t *idx;
     float *wsel;
     int32_t *act_expert, *act_off, *cu_rec, *pair_slot, *pair_of_slot;
-    // Expert operands as bf16 hi/lo row pairs: zhl [B][2][L], acthl [pair][2][I]
-    // (row 0: hi = bf16(v), row 1: lo = bf16(v - hi)).
-    uint16_t *zhl, *acthl;
-    float *ash, *ylat;  // f32 intermediates
+    // Intermediates as bf16 hi/lo row pairs: zhl [B][2][L], acthl [pair][2][I],
+    // ashhl [B][2][Is] (row 0: hi = bf16(v), row 1: lo = bf16(v - hi)).
+    uint16_t *zhl, *acthl, *ashhl;
+    float *ylat;  // f32 latent combine (atomic adds)
 };
 
 }  // namespace moe
