@@ -10,11 +10,14 @@ timed region starts.
 Prints ONE JSON line:
   value        whole-step algorithmic HBM bytes / time (GB/s)
   ms_per_step  time per layer step (graph replays, K steps between two
-               synchronisations)
+               synchronisations); p10/p50/p90 from events between replays
   roofline     the kernel with the largest time, its algorithmic bytes per
-               launch over its average duration (HIP events recorded between
-               the kernels on the step's stream), against 8 TB/s
+               launch over its average duration (HIP events attached to each
+               kernel's dispatch on eager steps), against 8 TB/s
   cpu_baseline the binary64 CPU oracle on a bounded sample of the same inputs
+  batch_sweep  the same K3 weights at batch 2, 8 (Zipf routing), 64
+               (near-uniform routing) and 64 (the batch-1 bias)
+With --workload c4_x8: eight TP8-share layers in one graph, batch 1..64.
 """
 import argparse
 import hashlib
@@ -114,15 +117,215 @@ def cpu_baseline(layer, xs, k, bytes_per_step, seconds):
                       f"(batch {xs[0].shape[0]}), {per_step:.3f} s per step single-threaded"}
 
 
+def pct(v, q):
+    import numpy as np
+    return float(np.percentile(np.asarray(v), q))
+
+
+def measure(dev, d, B, k, xs, steps, warmup, names):
+    """One configuration: graph replays (wall clock over `steps` replays, then
+    per-replay events for percentiles) and eager steps with events attached to
+    each kernel's dispatch (per-kernel durations).  Inputs rotate through xs."""
+    import numpy as np
+    import torch
+
+    from sparse_moe_decode_router_amd import binding
+
+    ctx = binding.MoEDecode(dev, B, k)
+    R = len(xs)
+    xd = [torch.from_numpy(x.view(np.int16)).cuda() for x in xs]
+    out = torch.empty((B, d.hidden), dtype=torch.int16, device="cuda")
+    idx = torch.empty((B, k), dtype=torch.int32, device="cuda")
+    wts = torch.empty((B, k), dtype=torch.float32, device="cuda")
+    # Distinct experts each input actually selects on the GPU.
+    Ds = []
+    for r in range(R):
+        ctx.step(xd[r], k, out, idx, wts)
+        torch.cuda.synchronize()
+        Ds.append(int(np.unique(idx.cpu().numpy()).size))
+    disp = ctx.last_dispatch()
+    kb = [kernel_bytes(d, B, k, D) for D in Ds]
+    step_bytes = [sum(b.values()) for b in kb]
+
+    stream = torch.cuda.Stream()
+    graphs = [binding.Graph([ctx], [xd[r]], B, k, [out], [idx], [wts]) for r in range(R)]
+    # Timed region: back-to-back replays between two synchronisations.
+    for i in range(warmup):
+        graphs[i % R].launch(stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        graphs[i % R].launch(stream)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    mean_bytes = sum(step_bytes[i % R] for i in range(steps)) / steps
+    # Per-replay spread: an event between consecutive replays.
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    evs[0].record(stream)
+    for i in range(steps):
+        graphs[i % R].launch(stream)
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per = [evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(steps)]
+
+    # Eager steps (launches without a graph), for comparison.
+    for i in range(warmup):
+        ctx.step(xd[i % R], k, out, idx, wts, stream=stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ctx.step(xd[i % R], k, out, idx, wts, stream=stream)
+    torch.cuda.synchronize()
+    ms_eager = (time.perf_counter() - t0) * 1e3 / steps
+
+    # Per-kernel durations: events attached to each kernel's dispatch (start
+    # and stop of the kernel itself) on eager steps; one event set per
+    # rotating input, read back before it is reused.
+    kev = []
+    for r in range(R):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2 * len(names))]
+        for x in e:
+            x.record(stream)
+        kev.append(e)
+    torch.cuda.synchronize()
+    sums = {n: 0.0 for n in names}
+    kbytes = {n: 0.0 for n in names}
+    pending = [False] * R
+
+    def collect(r):
+        e = kev[r]
+        e[-1].synchronize()
+        for j, n in enumerate(names):
+            sums[n] += e[2 * j].elapsed_time(e[2 * j + 1])
+            kbytes[n] += kb[r][n]
+
+    for i in range(steps):
+        r = i % R
+        if pending[r]:
+            collect(r)
+        ctx.set_timing_events(kev[r])
+        ctx.step(xd[r], k, out, idx, wts, stream=stream)
+        pending[r] = True
+    ctx.set_timing_events(None)
+    torch.cuda.synchronize()
+    for r in range(R):
+        if pending[r]:
+            collect(r)
+    per_kernel = {}
+    for n in names:
+        avg_ms = sums[n] / steps
+        avg_bytes = kbytes[n] / steps
+        gbs = avg_bytes / (avg_ms * 1e-3) / 1e9
+        per_kernel[n] = {"symbol": KERNEL_SYMBOLS[n], "us": round(avg_ms * 1e3, 2),
+                         "bytes": int(avg_bytes), "gbs": round(gbs, 1),
+                         "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    ex_us = per_kernel["w13"]["us"] + per_kernel["w2"]["us"]
+    ex_bytes = per_kernel["w13"]["bytes"] + per_kernel["w2"]["bytes"]
+    ex_gbs = ex_bytes / (ex_us * 1e-6) / 1e9
+    for g in graphs:
+        g.close()
+    ctx.close()
+    return {
+        "ms": ms, "value": mean_bytes / (ms * 1e-3) / 1e9, "ms_eager": ms_eager,
+        "us_p10": pct(per, 10), "us_p50": pct(per, 50), "us_p90": pct(per, 90),
+        "Ds": Ds, "step_bytes": step_bytes, "per_kernel": per_kernel, "dispatch": disp,
+        "expert_path": {"us": round(ex_us, 2), "gbs": round(ex_gbs, 1),
+                        "pct_hbm_peak": round(100 * ex_gbs / HBM_PEAK_GBS, 2)},
+    }
+
+
+def summary(name, B, m):
+    return {"workload": name, "batch": B, "us_per_step": round(m["ms"] * 1e3, 2),
+            "us_p10": round(m["us_p10"], 2), "us_p50": round(m["us_p50"], 2),
+            "us_p90": round(m["us_p90"], 2), "tokens_per_s": round(B / (m["ms"] * 1e-3), 1),
+            "gbs": round(m["value"], 1), "pct_hbm_peak": round(100 * m["value"] / HBM_PEAK_GBS, 2),
+            "distinct_experts_mean": round(sum(m["Ds"]) / len(m["Ds"]), 1),
+            "expert_path": m["expert_path"]}
+
+
+# Batch sweep on the K3 layer's weights (the bias alone changes): name ->
+# (bias recipe, batch).
+SWEEP = (("k3_b2", "k3", 2), ("k3_zipf_b8", "k3_zipf", 8), ("k3_flat_b64", "k3_flat", 64),
+         ("k3_b64", "k3", 64))
+
+
+def run_c4(args):
+    """Eight TP8-share layers (own seeds, own inputs) captured in one graph,
+    swept over the batch; value = algorithmic bytes of the eight layers over
+    the time of one graph replay at batch 1."""
+    import numpy as np
+    import torch
+
+    from sparse_moe_decode_router_amd import binding, synth
+
+    recipe = synth.K3_TP8
+    d = recipe.dims
+    n_layers, k = 8, 16
+    layers = []
+    for l in range(n_layers):
+        log(f"[bench] generating C4 layer {l}")
+        layers.append(synth.make_layer(recipe, synth.TP8_STACK_SEED0 + l))
+    devs = [binding.DeviceLayer(la) for la in layers]
+    stream = torch.cuda.Stream()
+    results = []
+    for B in (1, 2, 4, 8, 16, 32, 64):
+        ctxs = [binding.MoEDecode(dv, B, k) for dv in devs]
+        R = 4
+        xd = [[torch.from_numpy(synth.make_tokens(d, synth.TP8_STACK_SEED0 + l, B, draw=r)
+                                .view(np.int16)).cuda() for l in range(n_layers)] for r in range(R)]
+        outs = [torch.empty((B, d.hidden), dtype=torch.int16, device="cuda") for _ in range(n_layers)]
+        idxs = [torch.empty((B, k), dtype=torch.int32, device="cuda") for _ in range(n_layers)]
+        wts = [torch.empty((B, k), dtype=torch.float32, device="cuda") for _ in range(n_layers)]
+        graphs = [binding.Graph(ctxs, xd[r], B, k, outs, idxs, wts) for r in range(R)]
+        Ds = []
+        for r in range(R):
+            graphs[r].launch(stream)
+            torch.cuda.synchronize()
+            Ds.append([int(np.unique(i.cpu().numpy()).size) for i in idxs])
+        step_bytes = [sum(sum(kernel_bytes(d, B, k, D).values()) for D in ds) for ds in Ds]
+        for i in range(args.warmup):
+            graphs[i % R].launch(stream)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            graphs[i % R].launch(stream)
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        mean_bytes = sum(step_bytes[i % R] for i in range(args.steps)) / args.steps
+        results.append({"batch": B, "us_per_8_layers": round(ms * 1e3, 2),
+                        "us_per_layer": round(ms * 1e3 / n_layers, 2),
+                        "tokens_per_s": round(B / (ms * 1e-3), 1),
+                        "gbs": round(mean_bytes / (ms * 1e-3) / 1e9, 1),
+                        "distinct_experts_mean": round(float(np.mean(Ds)), 1)})
+        log(f"[bench] C4 B={B}: {results[-1]}")
+        for g in graphs:
+            g.close()
+        for c in ctxs:
+            c.close()
+    r1 = results[0]
+    line = {
+        "metric": METRIC, "value": r1["gbs"], "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(r1["us_per_8_layers"] / 1e3, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "c4_x8: eight TP8-share layers (hidden 7168, latent 2048, 896 "
+                   "MXFP4 experts of inter 256, top-16, shared 512) in one HIP graph, batch 1",
+                   "batch": 1, "layers": n_layers, "parallelism": "1 GPU"},
+        "batch_sweep": results, "roofline": None, "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="k3_b1", choices=sorted(WORKLOADS))
-    ap.add_argument("--rotate", type=int, default=8, help="distinct input batches cycled")
+    ap.add_argument("--workload", default="k3_b1", choices=sorted(WORKLOADS) + ["c4_x8"])
+    ap.add_argument("--rotate", type=int, default=32, help="distinct input batches cycled")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the batch sweep of the K3 layer")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -137,6 +340,11 @@ def main():
 
     from sparse_moe_decode_router_amd import binding, synth
 
+    torch.cuda.set_device(0)
+    if args.workload == "c4_x8":
+        run_c4(args)
+        return
+
     recipe_name, B, k, desc = WORKLOADS[args.workload]
     recipe = synth.RECIPES[recipe_name]
     d = recipe.dims
@@ -145,134 +353,58 @@ def main():
     t0 = time.time()
     layer = synth.make_layer(recipe, seed)
     log(f"[bench] generated in {time.time() - t0:.1f} s; copying to the GPU")
-    torch.cuda.set_device(0)
     dev = binding.DeviceLayer(layer)
-    ctx = binding.MoEDecode(dev, B, k)
-    R = args.rotate
-    xs = [synth.make_tokens(d, seed, B, draw=r) for r in range(R)]
-    xd = [torch.from_numpy(x.view(np.int16)).cuda() for x in xs]
-    out = torch.empty((B, d.hidden), dtype=torch.int16, device="cuda")
-    idx = torch.empty((B, k), dtype=torch.int32, device="cuda")
-    wts = torch.empty((B, k), dtype=torch.float32, device="cuda")
-
-    # Distinct experts each input actually selects on the GPU.
-    Ds = []
-    for r in range(R):
-        ctx.step(xd[r], k, out, idx, wts)
-        torch.cuda.synchronize()
-        Ds.append(int(np.unique(idx.cpu().numpy()).size))
-    disp = ctx.last_dispatch()
     names = (("router_f32",) if d.router_f32 else ()) + KERNELS_BF16
-    kb = [kernel_bytes(d, B, k, D) for D in Ds]
-    step_bytes = [sum(b.values()) for b in kb]
-    log(f"[bench] distinct experts per input {Ds}; dispatch {disp}")
-
-    stream = torch.cuda.Stream()
-    graphs = [binding.Graph([ctx], [xd[r]], B, k, [out], [idx], [wts]) for r in range(R)]
-
-    # Pass A: the timed region (graph replays, no timing nodes).
-    for i in range(args.warmup):
-        graphs[i % R].launch(stream)
-    torch.cuda.synchronize()
-    log(f"[bench] timing {args.steps} steps")
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        graphs[i % R].launch(stream)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms = (t1 - t0) * 1e3 / args.steps
-    mean_bytes = sum(step_bytes[i % R] for i in range(args.steps)) / args.steps
-    value = mean_bytes / (ms * 1e-3) / 1e9
-
-    # Eager steps (four launches each, no graph), for comparison.
-    for i in range(args.warmup):
-        ctx.step(xd[i % R], k, out, idx, wts, stream=stream)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        ctx.step(xd[i % R], k, out, idx, wts, stream=stream)
-    torch.cuda.synchronize()
-    ms_eager = (time.perf_counter() - t0) * 1e3 / args.steps
-
-    # Pass B: per-kernel durations from HIP events attached to each kernel's
-    # dispatch (start and stop of the kernel itself) on eager steps; R
-    # rotating event sets, each read back before it is reused.
-    evs = []
-    for r in range(R):
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(2 * len(names))]
-        for x in e:
-            x.record(stream)
-        evs.append(e)
-    torch.cuda.synchronize()
-    sums = {n: 0.0 for n in names}
-    kbytes = {n: 0.0 for n in names}
-    pending = [False] * R
-
-    def collect(r):
-        e = evs[r]
-        e[-1].synchronize()
-        for j, n in enumerate(names):
-            sums[n] += e[2 * j].elapsed_time(e[2 * j + 1])
-            kbytes[n] += kb[r][n]
-
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        r = i % R
-        if pending[r]:
-            collect(r)
-        ctx.set_timing_events(evs[r])
-        ctx.step(xd[r], k, out, idx, wts, stream=stream)
-        pending[r] = True
-    ctx.set_timing_events(None)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    for r in range(R):
-        if pending[r]:
-            collect(r)
-    ms_events_pass = (t1 - t0) * 1e3 / args.steps
-    per_kernel = {}
-    for n in names:
-        avg_ms = sums[n] / args.steps
-        avg_bytes = kbytes[n] / args.steps
-        gbs = avg_bytes / (avg_ms * 1e-3) / 1e9
-        per_kernel[n] = {"symbol": KERNEL_SYMBOLS[n], "us": round(avg_ms * 1e3, 2),
-                         "bytes": int(avg_bytes), "gbs": round(gbs, 1),
-                         "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    xs = [synth.make_tokens(d, seed, B, draw=r) for r in range(args.rotate)]
+    log(f"[bench] timing {args.workload}: {args.steps} steps")
+    m = measure(dev, d, B, k, xs, args.steps, args.warmup, names)
+    log(f"[bench] distinct experts per input {m['Ds']}; dispatch {m['dispatch']}")
+    per_kernel = m["per_kernel"]
     dom = max(names, key=lambda n: per_kernel[n]["us"])
     pk = per_kernel[dom]
-    ex_us = per_kernel["w13"]["us"] + per_kernel["w2"]["us"]
-    ex_bytes = per_kernel["w13"]["bytes"] + per_kernel["w2"]["bytes"]
-    ex_gbs = ex_bytes / (ex_us * 1e-6) / 1e9
+
+    sweep = None
+    if not args.no_sweep and recipe_name == "k3" and B == 1:
+        sweep = [summary(args.workload, B, m)]
+        for name, bias_recipe, Bs in SWEEP:
+            bias = synth.make_bias(synth.RECIPES[bias_recipe], 0)
+            xs_s = [synth.make_tokens(d, 0, Bs, draw=r) for r in range(args.rotate)]
+            log(f"[bench] sweep {name}")
+            ms_ = measure(dev.with_bias(bias), d, Bs, k, xs_s, max(50, args.steps // 2),
+                          args.warmup, names)
+            sweep.append(summary(name, Bs, ms_))
 
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
-        cpu = cpu_baseline(layer, xs, k, float(np.mean(step_bytes)), args.cpu_seconds)
+        cpu = cpu_baseline(layer, xs, k, float(np.mean(m["step_bytes"])), args.cpu_seconds)
 
+    ms = m["ms"]
     line = {
-        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "metric": METRIC, "value": round(m["value"], 1), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": f"{args.workload}: {desc}", "batch": B, "top_k": k,
                    "hidden": d.hidden, "latent": d.latent, "experts": d.n_experts,
                    "expert_inter": d.expert_inter, "shared_inter": d.shared_inter,
-                   "weights": "MXFP4 experts, bf16 dense", "rotating_inputs": R,
+                   "weights": "MXFP4 experts, bf16 dense", "rotating_inputs": args.rotate,
                    "parallelism": "1 GPU"},
         "us_per_step": round(ms * 1e3, 2),
+        "us_p10": round(m["us_p10"], 2), "us_p50": round(m["us_p50"], 2),
+        "us_p90": round(m["us_p90"], 2),
         "tokens_per_s": round(B / (ms * 1e-3), 1),
-        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
-        "distinct_experts": Ds,
-        "expert_path": {"us": round(ex_us, 2), "gbs": round(ex_gbs, 1),
-                        "pct_hbm_peak": round(100 * ex_gbs / HBM_PEAK_GBS, 2)},
+        "pct_hbm_peak": round(100 * m["value"] / HBM_PEAK_GBS, 2),
+        "distinct_experts": m["Ds"],
+        "expert_path": m["expert_path"],
         "kernels": per_kernel,
-        "ms_per_step_events_pass": round(ms_events_pass, 5),
-        "ms_per_step_eager": round(ms_eager, 5),
+        "ms_per_step_eager": round(m["ms_eager"], 5),
         "roofline": {"bound": "hbm", "kernel": pk["symbol"], "achieved": pk["gbs"],
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": pk["frac"],
                      "traffic": load_traffic(pk["symbol"], args.workload)},
         "cpu_baseline": cpu,
-        "dispatch": disp,
+        "batch_sweep": sweep,
+        "dispatch": m["dispatch"],
     }
     print(json.dumps(line), flush=True)
 

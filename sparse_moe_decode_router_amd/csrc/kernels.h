@@ -46,6 +46,7 @@ namespace moe {
 
 constexpr int kWG = 8;              // waves per workgroup of the step kernels
 constexpr int kWGThreads = kWG * kWave;
+constexpr int kXcds = 8;            // XCDs of MI355X; workgroup i runs on XCD i % 8
 
 // ---------------------------------------------------------------------------
 // Operand loads
@@ -202,6 +203,21 @@ struct Role {
     int wave, KW, RW, rg, kw;
 };
 
+// Dense kernels with several column groups (token groups) read the same
+// weight tile once per group.  Unit u runs on XCD u % 8 (workgroups are
+// dealt to the eight XCDs in turn), so the groups of one tile group get units
+// u = 8 (ncg q' + cg) + x: the same XCD x, issued back to back, and the
+// repeated reads hit that XCD's L2.  Units past the last tile group idle.
+__device__ __forceinline__ int dense_units(int n_t, int RW, int ncg) {
+    const int tgroups = (n_t + RW - 1) / RW;
+    return ((tgroups + kXcds - 1) / kXcds) * kXcds * ncg;
+}
+__device__ __forceinline__ void dense_unit(int u, int ncg, int &cg, int &tg) {
+    const int x = u % kXcds, q = u / kXcds;
+    cg = q % ncg;
+    tg = (q / ncg) * kXcds + x;
+}
+
 __device__ __forceinline__ Role role_of(int KW) {
     Role r;
     r.wave = wave_index();
@@ -269,11 +285,11 @@ k_dense_in(const StepArgs a) {
     const int n_rt = a.n_r16, n_lt = a.L >> 4, n_st = a.Is >> 3;
     const int n_t = n_rt + n_lt + n_st;
     const int ncg = (a.B + 15) >> 4;
-    const int tgroups = (n_t + ro.RW - 1) / ro.RW;
-    const int units = tgroups * ncg;
+    const int units = dense_units(n_t, ro.RW, ncg);
     for (int u = blockIdx.x; u < units; u += gridDim.x) {
-        const int cg = u % ncg;
-        const int t = (u / ncg) * ro.RW + ro.rg;
+        int cg, tg;
+        dense_unit(u, ncg, cg, tg);
+        const int t = tg * ro.RW + ro.rg;
         const bool active = t < n_t;
         const int tt = active ? t : 0;
         int kind;
@@ -625,11 +641,11 @@ k_out(const StepArgs a) {
     const int RT = a.out_rows;
     const int ncg = (a.B + 7) >> 3;
     const int n_t = (a.H + RT - 1) / RT;
-    const int tgroups = (n_t + ro.RW - 1) / ro.RW;
-    const int units = tgroups * ncg;
+    const int units = dense_units(n_t, ro.RW, ncg);
     for (int u = blockIdx.x; u < units; u += gridDim.x) {
-        const int cg = u % ncg;
-        const int t = (u / ncg) * ro.RW + ro.rg;
+        int cg, tg;
+        dense_unit(u, ncg, cg, tg);
+        const int t = tg * ro.RW + ro.rg;
         const bool active = t < n_t;
         const int b = 8 * cg + col;
         const bool valid = b < a.B;

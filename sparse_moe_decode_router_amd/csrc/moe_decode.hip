@@ -53,6 +53,12 @@ int out_tile_rows(int H) {
     return std::min(16, cdiv(H, 2 * 256));
 }
 
+// Unit count of a dense kernel (tile groups padded to a multiple of the XCD
+// count, times the column groups); matches dense_units() in the kernels.
+long long dense_units_host(int n_t, int RW, int ncg) {
+    return (long long)cdiv(cdiv(n_t, RW), kXcds) * kXcds * ncg;
+}
+
 struct Plan {
     int n_r16, ncg_in, ncg_out, out_rows;
     Split in, out;
@@ -73,9 +79,9 @@ Plan make_plan(const moe_decode_config &c, int B, int k) {
     // tiles of 8 gate + 8 up rows.
     const int n_t_in = p.n_r16 + c.latent / 16 + c.shared_inter / 8;
     const long long cols = ncols_cap(c.n_experts, B, k);
-    p.units_in = (long long)cdiv(n_t_in, kWG / p.in.kw) * p.ncg_in;
+    p.units_in = dense_units_host(n_t_in, kWG / p.in.kw, p.ncg_in);
     p.out_rows = out_tile_rows(c.hidden);
-    p.units_out = (long long)cdiv(cdiv(c.hidden, p.out_rows), kWG / p.out.kw) * p.ncg_out;
+    p.units_out = dense_units_host(cdiv(c.hidden, p.out_rows), kWG / p.out.kw, p.ncg_out);
     // Expert kernels: 8 row tiles per workgroup (8 gate + 8 up rows, or 16
     // latent rows, per tile).
     p.units_13 = cols * cdiv(c.expert_inter / 8, kWG);
@@ -335,7 +341,7 @@ moe_status moe_decode_step(moe_decode_ctx *ctx, const uint16_t *x, int32_t batch
     a.out_rows = pl.out_rows;
     a.spc_in = pl.in.spc;
     a.spc_out = pl.out.spc;
-    const long long cap = 65535;  // workgroups; larger unit counts loop
+    const long long cap = 65528;  // workgroups (a multiple of the XCD count); more units loop
 
     moe_decode_dispatch_info &d = ctx->last;
     d.batch = batch;

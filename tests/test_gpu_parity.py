@@ -329,3 +329,35 @@ def test_k3_tp8_share_layer():
         out, idx, w = run(ctx, x, 16)
         r = check_step(layer, x, 16, out, idx, w, sample=sample)
         log("  ", r)
+
+
+def test_c4_eight_layer_graph():
+    """Eight TP8-share layers (own seeds and inputs) captured in one HIP graph,
+    the configuration the stacked benchmark replays: every layer's replayed
+    result equals its eager step, and the first and last layers match the
+    oracle on sampled tokens."""
+    import torch
+    n_layers, B, k = 8, 4, 16
+    layers = [synth.make_layer(synth.K3_TP8, synth.TP8_STACK_SEED0 + l) for l in range(n_layers)]
+    ctxs = [make_ctx(la, B, k) for la in layers]
+    xs = [synth.make_tokens(la.dims, synth.TP8_STACK_SEED0 + l, B) for l, la in enumerate(layers)]
+    xd = [to_dev_tokens(x) for x in xs]
+    H = layers[0].dims.hidden
+    outs = [torch.empty((B, H), dtype=torch.int16, device="cuda") for _ in range(n_layers)]
+    idxs = [torch.empty((B, k), dtype=torch.int32, device="cuda") for _ in range(n_layers)]
+    ws = [torch.empty((B, k), dtype=torch.float32, device="cuda") for _ in range(n_layers)]
+    g = binding.Graph(ctxs, xd, B, k, outs, idxs, ws)
+    stream = torch.cuda.Stream()
+    for rep in range(2):
+        g.launch(stream)
+        stream.synchronize()
+        for l in range(n_layers):
+            got = (outs[l].cpu().numpy().view(np.uint16), idxs[l].cpu().numpy(),
+                   ws[l].cpu().numpy())
+            want = run(ctxs[l], xs[l], k)
+            assert_same_step(got, want)
+    for l in (0, n_layers - 1):
+        out, idx, w = run(ctxs[l], xs[l], k)
+        r = check_step(layers[l], xs[l], k, out, idx, w, sample=[0, B - 1])
+        log(f"  C4 layer {l}:", r)
+    g.close()
