@@ -11,9 +11,12 @@ Prints ONE JSON line:
   value        whole-step algorithmic HBM bytes / time (GB/s)
   ms_per_step  time per layer step (graph replays, K steps between two
                synchronisations); p10/p50/p90 from events between replays
-  roofline     the kernel with the largest time, its algorithmic bytes per
-               launch over its average duration (HIP events attached to each
-               kernel's dispatch on eager steps), against 8 TB/s
+  roofline     the kernel with the largest time of the four launches, its
+               algorithmic bytes per launch over its average duration (HIP
+               events attached to each kernel's dispatch on eager steps),
+               against 8 TB/s
+  expert_path  k_w13 + k_w2: the routed-expert kernels alone
+  fused        the same inputs run as one persistent launch (opt-in mode)
   cpu_baseline the binary64 CPU oracle on a bounded sample of the same inputs
   batch_sweep  the same K3 weights at batch 2, 8 (Zipf routing), 64
                (near-uniform routing) and 64 (the batch-1 bias)
@@ -44,7 +47,7 @@ WORKLOADS = {
 }
 KERNELS_BF16 = ("dense_in", "w13", "w2", "out")
 KERNEL_SYMBOLS = {"dense_in": "k_dense_in", "w13": "k_w13", "w2": "k_w2", "out": "k_out",
-                  "router_f32": "k_router_f32"}
+                  "router_f32": "k_router_f32", "step": "k_step"}
 
 
 def log(*a):
@@ -122,16 +125,18 @@ def pct(v, q):
     return float(np.percentile(np.asarray(v), q))
 
 
-def measure(dev, d, B, k, xs, steps, warmup, names):
-    """One configuration: graph replays (wall clock over `steps` replays, then
-    per-replay events for percentiles) and eager steps with events attached to
-    each kernel's dispatch (per-kernel durations).  Inputs rotate through xs."""
+def measure(dev, d, B, k, xs, steps, warmup, mode):
+    """One configuration in one execution mode: graph replays (wall clock over
+    `steps` replays, then per-replay events for percentiles) and eager steps
+    with events attached to each kernel's dispatch (per-kernel durations; the
+    fused step is one kernel).  Inputs rotate through xs."""
     import numpy as np
     import torch
 
     from sparse_moe_decode_router_amd import binding
 
     ctx = binding.MoEDecode(dev, B, k)
+    ctx.set_mode(mode)
     R = len(xs)
     xd = [torch.from_numpy(x.view(np.int16)).cuda() for x in xs]
     out = torch.empty((B, d.hidden), dtype=torch.int16, device="cuda")
@@ -144,8 +149,15 @@ def measure(dev, d, B, k, xs, steps, warmup, names):
         torch.cuda.synchronize()
         Ds.append(int(np.unique(idx.cpu().numpy()).size))
     disp = ctx.last_dispatch()
-    kb = [kernel_bytes(d, B, k, D) for D in Ds]
+    fused = bool(disp["fused"])
+    if fused:
+        names = ("step",)
+        kb = [{"step": sum(kernel_bytes(d, B, k, D).values())} for D in Ds]
+    else:
+        names = (("router_f32",) if d.router_f32 else ()) + KERNELS_BF16
+        kb = [kernel_bytes(d, B, k, D) for D in Ds]
     step_bytes = [sum(b.values()) for b in kb]
+    assert ctx.read_flags() == 0
 
     stream = torch.cuda.Stream()
     graphs = [binding.Graph([ctx], [xd[r]], B, k, [out], [idx], [wts]) for r in range(R)]
@@ -219,9 +231,15 @@ def measure(dev, d, B, k, xs, steps, warmup, names):
         per_kernel[n] = {"symbol": KERNEL_SYMBOLS[n], "us": round(avg_ms * 1e3, 2),
                          "bytes": int(avg_bytes), "gbs": round(gbs, 1),
                          "frac": round(gbs / HBM_PEAK_GBS, 4)}
-    ex_us = per_kernel["w13"]["us"] + per_kernel["w2"]["us"]
-    ex_bytes = per_kernel["w13"]["bytes"] + per_kernel["w2"]["bytes"]
-    ex_gbs = ex_bytes / (ex_us * 1e-6) / 1e9
+    expert = None
+    if not fused:
+        ex_us = per_kernel["w13"]["us"] + per_kernel["w2"]["us"]
+        ex_bytes = per_kernel["w13"]["bytes"] + per_kernel["w2"]["bytes"]
+        ex_gbs = ex_bytes / (ex_us * 1e-6) / 1e9
+        expert = {"us": round(ex_us, 2), "gbs": round(ex_gbs, 1),
+                  "pct_hbm_peak": round(100 * ex_gbs / HBM_PEAK_GBS, 2),
+                  "from": "k_w13 + k_w2 of the four-launch step"}
+    assert ctx.read_flags() == 0, "a bounded wait of the fused step ran out"
     for g in graphs:
         g.close()
     ctx.close()
@@ -229,18 +247,20 @@ def measure(dev, d, B, k, xs, steps, warmup, names):
         "ms": ms, "value": mean_bytes / (ms * 1e-3) / 1e9, "ms_eager": ms_eager,
         "us_p10": pct(per, 10), "us_p50": pct(per, 50), "us_p90": pct(per, 90),
         "Ds": Ds, "step_bytes": step_bytes, "per_kernel": per_kernel, "dispatch": disp,
-        "expert_path": {"us": round(ex_us, 2), "gbs": round(ex_gbs, 1),
-                        "pct_hbm_peak": round(100 * ex_gbs / HBM_PEAK_GBS, 2)},
+        "names": names, "expert_path": expert,
     }
 
 
-def summary(name, B, m):
+def summary(name, B, m, mf):
+    """Four-launch figures of one configuration, with the persistent fused
+    step's time beside them."""
     return {"workload": name, "batch": B, "us_per_step": round(m["ms"] * 1e3, 2),
             "us_p10": round(m["us_p10"], 2), "us_p50": round(m["us_p50"], 2),
             "us_p90": round(m["us_p90"], 2), "tokens_per_s": round(B / (m["ms"] * 1e-3), 1),
             "gbs": round(m["value"], 1), "pct_hbm_peak": round(100 * m["value"] / HBM_PEAK_GBS, 2),
             "distinct_experts_mean": round(sum(m["Ds"]) / len(m["Ds"]), 1),
-            "expert_path": m["expert_path"]}
+            "expert_path": m["expert_path"],
+            "fused_us_per_step": round(mf["ms"] * 1e3, 2)}
 
 
 # Batch sweep on the K3 layer's weights (the bias alone changes): name ->
@@ -268,6 +288,16 @@ def run_c4(args):
     devs = [binding.DeviceLayer(la) for la in layers]
     stream = torch.cuda.Stream()
     results = []
+    def replay_ms(graphs, R):
+        for i in range(args.warmup):
+            graphs[i % R].launch(stream)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            graphs[i % R].launch(stream)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / args.steps
+
     for B in (1, 2, 4, 8, 16, 32, 64):
         ctxs = [binding.MoEDecode(dv, B, k) for dv in devs]
         R = 4
@@ -283,20 +313,21 @@ def run_c4(args):
             torch.cuda.synchronize()
             Ds.append([int(np.unique(i.cpu().numpy()).size) for i in idxs])
         step_bytes = [sum(sum(kernel_bytes(d, B, k, D).values()) for D in ds) for ds in Ds]
-        for i in range(args.warmup):
-            graphs[i % R].launch(stream)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for i in range(args.steps):
-            graphs[i % R].launch(stream)
-        torch.cuda.synchronize()
-        ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        ms = replay_ms(graphs, R)
         mean_bytes = sum(step_bytes[i % R] for i in range(args.steps)) / args.steps
+        for g in graphs:
+            g.close()
+        for c in ctxs:
+            c.set_mode(binding.MODE_FUSED)
+        graphs = [binding.Graph(ctxs, xd[r], B, k, outs, idxs, wts) for r in range(R)]
+        msf = replay_ms(graphs, R)
+        assert all(c.read_flags() == 0 for c in ctxs), "a bounded wait of the fused step ran out"
         results.append({"batch": B, "us_per_8_layers": round(ms * 1e3, 2),
                         "us_per_layer": round(ms * 1e3 / n_layers, 2),
                         "tokens_per_s": round(B / (ms * 1e-3), 1),
                         "gbs": round(mean_bytes / (ms * 1e-3) / 1e9, 1),
-                        "distinct_experts_mean": round(float(np.mean(Ds)), 1)})
+                        "distinct_experts_mean": round(float(np.mean(Ds)), 1),
+                        "fused_us_per_layer": round(msf * 1e3 / n_layers, 2)})
         log(f"[bench] C4 B={B}: {results[-1]}")
         for g in graphs:
             g.close()
@@ -354,25 +385,28 @@ def main():
     layer = synth.make_layer(recipe, seed)
     log(f"[bench] generated in {time.time() - t0:.1f} s; copying to the GPU")
     dev = binding.DeviceLayer(layer)
-    names = (("router_f32",) if d.router_f32 else ()) + KERNELS_BF16
     xs = [synth.make_tokens(d, seed, B, draw=r) for r in range(args.rotate)]
     log(f"[bench] timing {args.workload}: {args.steps} steps")
-    m = measure(dev, d, B, k, xs, args.steps, args.warmup, names)
+    m = measure(dev, d, B, k, xs, args.steps, args.warmup, binding.MODE_FOUR_LAUNCHES)
     log(f"[bench] distinct experts per input {m['Ds']}; dispatch {m['dispatch']}")
+    log("[bench] the same inputs as one persistent launch")
+    mf = measure(dev, d, B, k, xs, args.steps, args.warmup, binding.MODE_FUSED)
     per_kernel = m["per_kernel"]
-    dom = max(names, key=lambda n: per_kernel[n]["us"])
+    dom = max(m["names"], key=lambda n: per_kernel[n]["us"])
     pk = per_kernel[dom]
 
     sweep = None
     if not args.no_sweep and recipe_name == "k3" and B == 1:
-        sweep = [summary(args.workload, B, m)]
+        sweep = [summary(args.workload, B, m, mf)]
         for name, bias_recipe, Bs in SWEEP:
             bias = synth.make_bias(synth.RECIPES[bias_recipe], 0)
             xs_s = [synth.make_tokens(d, 0, Bs, draw=r) for r in range(args.rotate)]
+            n_s = max(50, args.steps // 2)
             log(f"[bench] sweep {name}")
-            ms_ = measure(dev.with_bias(bias), d, Bs, k, xs_s, max(50, args.steps // 2),
-                          args.warmup, names)
-            sweep.append(summary(name, Bs, ms_))
+            dvb = dev.with_bias(bias)
+            ms_ = measure(dvb, d, Bs, k, xs_s, n_s, args.warmup, binding.MODE_FOUR_LAUNCHES)
+            msf = measure(dvb, d, Bs, k, xs_s, n_s, args.warmup, binding.MODE_FUSED)
+            sweep.append(summary(name, Bs, ms_, msf))
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -399,6 +433,8 @@ def main():
         "expert_path": m["expert_path"],
         "kernels": per_kernel,
         "ms_per_step_eager": round(m["ms_eager"], 5),
+        "fused": {"us_per_step": round(mf["ms"] * 1e3, 2),
+                  "gbs": round(mf["value"], 1), "kernels": mf["per_kernel"]},
         "roofline": {"bound": "hbm", "kernel": pk["symbol"], "achieved": pk["gbs"],
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": pk["frac"],
                      "traffic": load_traffic(pk["symbol"], args.workload)},

@@ -37,7 +37,7 @@ class DispatchInfo(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("batch", "top_k", "col_tiles", "split_in", "split_out", "split_w13",
                  "split_w2", "grid_in", "grid_w13", "grid_w2", "grid_out", "router_f32",
-                 "n_kernels")]
+                 "n_kernels", "fused", "grid_step")]
 
 
 class Debug(ctypes.Structure):
@@ -45,11 +45,14 @@ class Debug(ctypes.Structure):
                 ("score", "key", "z", "act", "ylat", "ash", "n_active")]
 
 
+MODE_FUSED, MODE_FOUR_LAUNCHES = 0, 1
+
 EXPORTED = ("moe_decode_validate_config", "moe_decode_workspace_size", "moe_decode_init",
             "moe_decode_step", "moe_decode_destroy", "moe_decode_status_string",
             "moe_decode_last_hip_error", "moe_decode_graph_create", "moe_decode_graph_launch",
             "moe_decode_graph_destroy", "moe_decode_last_dispatch", "moe_decode_debug_export",
-            "moe_decode_debug_dequant", "moe_decode_set_timing_events")
+            "moe_decode_debug_dequant", "moe_decode_set_timing_events", "moe_decode_set_mode",
+            "moe_decode_read_flags")
 
 
 class MoEError(RuntimeError):
@@ -97,6 +100,10 @@ def lib() -> ctypes.CDLL:
     L.moe_decode_debug_dequant.restype = i32
     L.moe_decode_set_timing_events.argtypes = [vp, ctypes.POINTER(vp), i32]
     L.moe_decode_set_timing_events.restype = i32
+    L.moe_decode_set_mode.argtypes = [vp, i32]
+    L.moe_decode_set_mode.restype = i32
+    L.moe_decode_read_flags.argtypes = [vp, ctypes.POINTER(ctypes.c_uint32)]
+    L.moe_decode_read_flags.restype = i32
     _lib = L
     return L
 
@@ -230,6 +237,17 @@ class MoEDecode:
             return
         arr = (ctypes.c_void_p * len(events))(*[e.cuda_event for e in events])
         _check(lib().moe_decode_set_timing_events(self.handle, arr, len(events)), "timing events")
+
+    def set_mode(self, mode: int) -> None:
+        """MODE_FUSED (one persistent launch where the shape has one) or
+        MODE_FOUR_LAUNCHES."""
+        _check(lib().moe_decode_set_mode(self.handle, mode), "set_mode")
+
+    def read_flags(self) -> int:
+        """Sticky fault flags of the context's fused steps (0: none)."""
+        v = ctypes.c_uint32(0)
+        _check(lib().moe_decode_read_flags(self.handle, ctypes.byref(v)), "read_flags")
+        return int(v.value)
 
     def last_dispatch(self) -> dict:
         info = DispatchInfo()

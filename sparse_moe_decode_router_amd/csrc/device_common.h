@@ -25,7 +25,25 @@ constexpr int kMaxTopK = 64;
 constexpr int kMaxStepsPerChunk = 8;
 
 // Global counter slots (u32) at the head of the workspace.
-enum { G_ROUTER_DONE = 0, G_COUNT = 64 };
+// Counter slots (u32 word indices into the counter area).  G_ROUTER_DONE:
+// router arrivals.  The fused step also uses: the unit queue (G_WORK),
+// workgroups that left it (G_EXIT), the routing published (G_ROUTED),
+// latent-down / shared gate/up / shared-down / down units done, and a sticky
+// error flag (a bounded wait ran out).  Counters sit 256 bytes apart: atomics
+// and polls on one line from many workgroups serialise at the memory side.
+constexpr int kCtrStride = 64;
+enum {
+    G_ROUTER_DONE = 0,
+    G_WORK = 1 * kCtrStride,
+    G_EXIT = 2 * kCtrStride,
+    G_ROUTED = 3 * kCtrStride,
+    G_LATENT = 4 * kCtrStride,
+    G_SHARED = 5 * kCtrStride,
+    G_SHDOWN = 6 * kCtrStride,
+    G_W2 = 7 * kCtrStride,
+    G_ERROR = 8 * kCtrStride,
+    G_COUNT = 9 * kCtrStride
+};
 // Routing metadata header (i32).
 enum { M_N_ACTIVE = 0, M_N_COLS = 1, M_COUNT = 16 };
 // Column-unit record (i32 words): expert, pair count (<= 8), first pair index,
@@ -60,13 +78,23 @@ __device__ __forceinline__ void split_hl2(float a, float b, uint32_t &hi, uint32
     lo = bf16x2_rne(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xFFFF0000u));
 }
 
-// Writes four values as hi and lo bf16 halves (8 bytes each).
+// Writes four values as hi and lo bf16 halves (8 bytes each).  Coh: with
+// agent-scope stores, for rows that other workgroups of the same launch read
+// (the fused step); otherwise plain stores, which a later launch reads.
+template <bool Coh>
 __device__ __forceinline__ void store_hl4(uint16_t *hi, uint16_t *lo, f32x4 v) {
     uint32_t h0, l0, h1, l1;
     split_hl2(v[0], v[1], h0, l0);
     split_hl2(v[2], v[3], h1, l1);
-    *(u32x2 *)hi = (u32x2){h0, h1};
-    *(u32x2 *)lo = (u32x2){l0, l1};
+    const uint64_t hv = (uint64_t)h0 | ((uint64_t)h1 << 32);
+    const uint64_t lv = (uint64_t)l0 | ((uint64_t)l1 << 32);
+    if constexpr (Coh) {
+        __hip_atomic_store((uint64_t *)hi, hv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store((uint64_t *)lo, lv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+        *(uint64_t *)hi = hv;
+        *(uint64_t *)lo = lv;
+    }
 }
 
 // E8M0 byte -> f32 scale 2^(byte-127) (bytes 1..254).
@@ -148,6 +176,34 @@ __device__ __forceinline__ void store_agent(float *p, float v) {
 }
 __device__ __forceinline__ float load_agent(const float *p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_agent(int32_t *p, int32_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int32_t load_agent(const int32_t *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t load_agent(const uint32_t *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// 16-byte loads through a buffer resource over [base, base + 2 GiB).  Coh:
+// with the sc1 cache policy (as agent-scope atomic loads use), which reads
+// the agent's coherent copy, for operands another workgroup of the same
+// launch wrote; otherwise a plain load.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kCohAux = 16;  // cache policy bits: sc1
+template <bool Coh>
+constexpr int cache_aux() {
+    return Coh ? kCohAux : 0;
+}
+__device__ __forceinline__ rsrc_t buf_rsrc(const void *base) {
+    return __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, 0x7FFFFFFF, 0x00020000);
+}
+template <bool Coh>
+__device__ __forceinline__ u32x4 buf_ld16(rsrc_t r, uint32_t byte_off) {
+    return __builtin_bit_cast(u32x4,
+                              __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, cache_aux<Coh>()));
 }
 
 // Waits for every vector memory access of the wave (stores included).

@@ -2,34 +2,38 @@
 //
 // Every contraction of the step is an HBM-bound matrix-vector / small-matrix
 // product: weight rows are the 16-row A operand of v_mfma_f32_16x16x32_bf16,
-// tokens are its 16 B columns.  The step is four launches (five with an f32
-// router):
-//   k_dense_in : router logits, latent-down z = W_ld x and shared gate/up
-//                (all contract over the hidden size H against x); epilogues:
-//                sigmoid + bias keys, z, shared SwiGLU.  The router tiles come
-//                first and the top-k + routing metadata run inside this kernel
-//                while the latent and shared rows stream.
-//   k_w13      : active experts' MXFP4 gate/up rows, fused dequantisation,
-//                SwiGLU epilogue -> expert activation a.
-//   k_w2       : active experts' MXFP4 down rows; each result is weighted and
-//                added into the latent combine ylat.
-//   k_out      : latent-up W_lu ylat plus shared-down S2 ash, one bf16 RNE.
+// tokens are its 16 B columns.  The step's work comes in units, each run by
+// one workgroup of 8 waves:
+//   dense-in : router rows, latent-down rows z = W_ld x, shared gate/up rows
+//              (all against x); epilogues: sigmoid + bias keys, z, shared
+//              SwiGLU; the router units also drive the routing (top-k and
+//              the expert lists);
+//   w13      : an active expert's MXFP4 gate/up rows for <= 8 of its tokens,
+//              SwiGLU -> expert activation a;
+//   w2       : an active expert's MXFP4 down rows; weighted, f32 atomic adds
+//              into the latent combine ylat;
+//   output   : latent-up rows against ylat and shared-down rows against ash,
+//              one bf16 rounding.
+// The units run either as four launches (k_dense_in, k_w13, k_w2, k_out; an
+// f32 router adds k_router_f32) or as one persistent launch (k_step) whose
+// workgroups take units from a queue in dependency order and wait on
+// completion counters instead of kernel boundaries.
 //
-// Work decomposition.  A workgroup is 8 waves.  It covers RW row groups of
-// 32 weight rows (two 16-row MFMA tiles) for one group of token columns; the
-// KW = 8 / RW waves of a row group split the reduction dimension K into equal
-// slices of SPC 128-element steps and their partial tiles are summed through
-// LDS in slice order.  No wave of the hot loops synchronises with another
-// workgroup; cross-workgroup communication is limited to the routing (one
-// release per router tile and per token) and the f32 atomic adds of the
-// expert combine.
+// Dense units: RW row groups of 16 rows; the KW = 8 / RW waves of a row group
+// split K into equal slices of SPC 128-element steps and sum their partial
+// tiles through LDS in slice order.  Expert units: every wave runs the whole
+// K of its tile, with the unit's activation rows staged in LDS.
 //
 // Operands.  x is bf16 and enters the MFMA as is (16 tokens per column group).
 // The f32 intermediates z, a, ylat and ash are carried as hi = bf16(v) and
 // lo = bf16(v - hi) (z, a and ash stored that way by their producers, ylat
 // split while it is loaded); hi and lo occupy two adjacent columns of
 // the same MFMA (8 tokens per column group) and the two column sums are added
-// afterwards, which keeps f32-grade precision at one MFMA per K slice.
+// afterwards, which keeps f32-grade precision at one MFMA per K slice.  Data
+// one unit hands to another (scores, keys, z, a, ash, the shared-down sums,
+// the expert records) is written with agent-scope stores and read with
+// coherent (sc1) loads, so that it is visible across XCDs without cache
+// maintenance.
 //
 // K layout within one 128-element step: lane group g = lane/16 owns the 32
 // consecutive elements [32g, 32g+32) of the step, one MX block for MXFP4 rows
@@ -73,12 +77,28 @@ __device__ __forceinline__ uint32_t pack_part(float a, float b, int part) {
     return part ? l : h;
 }
 
-__device__ __forceinline__ void load_cols_f32(const float *X, bool valid, int part, int s,
+// Column operands an earlier unit wrote, read through a buffer resource
+// (Coh: coherent loads, the writer being a unit of the same launch): `off` is
+// the byte offset of the lane's row plus its 32-element slot.  bf16 rows (hi
+// or lo) as they are; f32 values split into the lane's half.
+template <bool Coh>
+__device__ __forceinline__ void buf_cols_bf16(rsrc_t r, uint32_t off, bool valid, int s,
                                               u32x4 (&rb)[4]) {
-    const float *p = X + (size_t)s * kKStep;
+    const uint32_t o = off + (uint32_t)s * kKStep * 2;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const u32x4 v = buf_ld16<Coh>(r, o + 16 * j);
+        rb[j] = valid ? v : (u32x4){0u, 0u, 0u, 0u};
+    }
+}
+
+template <bool Coh>
+__device__ __forceinline__ void buf_cols_f32(rsrc_t r, uint32_t off, bool valid, int part, int s,
+                                             u32x4 (&rb)[4]) {
+    const uint32_t o = off + (uint32_t)s * kKStep * 4;
     f32x4 v[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = ldf4(p + 4 * j);
+    for (int j = 0; j < 8; ++j) v[j] = __builtin_bit_cast(f32x4, buf_ld16<Coh>(r, o + 16 * j));
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const f32x4 a = v[2 * j], b = v[2 * j + 1];
@@ -136,44 +156,45 @@ __device__ __forceinline__ void dense_chunk_x(const uint16_t *A, const uint16_t 
     }
 }
 
-// Output kernel: K runs over [0, L) against lat_up and ylat (f32, split into
-// hi/lo while loading), then over [0, Is) against sh_w2 and the shared
-// activation (already stored as hi/lo bf16 rows); step s < Ls selects the
-// first pair.
+// Output units: K steps s < Ls run against lat_up and ylat (f32, split into
+// hi/lo while loading), the rest against sh_w2 and the shared activation
+// (hi/lo bf16 rows).
 struct TwoSource {
-    const uint16_t *Aa;
-    const float *Xa;  // K in [0, L)
-    const uint16_t *Ab;
-    const uint16_t *Xb;  // K in [0, Is): the lane's hi or lo row
-    int Ls;              // L / 128
+    const uint16_t *Aa;  // lane's lat_up row + its 32-element slot
+    const uint16_t *Ab;  // lane's sh_w2 row + slot
+    rsrc_t Ra, Rb;       // ylat, ashhl
+    uint32_t Oa, Ob;     // byte offsets of the lane's column row + slot
+    int Ls;              // steps against the first source
 };
 
+template <bool Coh>
 __device__ __forceinline__ void load_two(const TwoSource &t, bool valid, int part, int s,
                                          u32x4 (&ra)[4], u32x4 (&rb)[4]) {
     if (s < t.Ls) {
         load_tile_bf16(t.Aa, s, ra);
-        load_cols_f32(t.Xa, valid, part, s, rb);
+        buf_cols_f32<Coh>(t.Ra, t.Oa, valid, part, s, rb);
     } else {
         load_tile_bf16(t.Ab, s - t.Ls, ra);
-        load_cols_bf16(t.Xb, valid, s - t.Ls, rb);
+        buf_cols_bf16<Coh>(t.Rb, t.Ob, valid, s - t.Ls, rb);
     }
 }
 
+template <bool Coh>
 __device__ __forceinline__ void dense_chunk_out(const TwoSource &t, bool valid, int part, int s0,
                                                 int s1, f32x4 &acc) {
     int s = s0;
 #pragma unroll 1
     for (; s + 1 < s1; s += 2) {
         u32x4 ra0[4], rb0[4], ra1[4], rb1[4];
-        load_two(t, valid, part, s, ra0, rb0);
-        load_two(t, valid, part, s + 1, ra1, rb1);
+        load_two<Coh>(t, valid, part, s, ra0, rb0);
+        load_two<Coh>(t, valid, part, s + 1, ra1, rb1);
         fence_schedule();
         mfma_tile(ra0, rb0, acc);
         mfma_tile(ra1, rb1, acc);
     }
     if (s < s1) {
         u32x4 ra0[4], rb0[4];
-        load_two(t, valid, part, s, ra0, rb0);
+        load_two<Coh>(t, valid, part, s, ra0, rb0);
         fence_schedule();
         mfma_tile(ra0, rb0, acc);
     }
@@ -229,144 +250,93 @@ __device__ __forceinline__ Role role_of(int KW) {
 }
 
 // ---------------------------------------------------------------------------
-// Kernel 0 (f32 router only): logits, scores and keys with plain f32 FMAs.
+// Dense-in unit: one tile group of one kind for one column group of tokens.
 // ---------------------------------------------------------------------------
 
-__global__ void __launch_bounds__(kBlock) k_router_f32(const StepArgs a) {
-    __shared__ RouteLds s_route;
-    __shared__ int s_last;
-    const int wave = wave_index();
-    const int lane = lane_id();
-    for (int e = blockIdx.x * kWavesPerBlock + wave; e < a.E; e += gridDim.x * kWavesPerBlock) {
-        const float *row = a.router_w32 + (size_t)e * a.H;
-        for (int b = 0; b < a.B; ++b) {
-            const uint16_t *xb = a.x + (size_t)b * a.H;
-            float acc = 0.f;
-            for (int h = lane; h < a.H; h += kWave) acc = fmaf(row[h], bf16_val(xb[h]), acc);
-            acc = wave_sum(acc);
-            if (lane == 0) {
-                const float s = sigmoidf_(acc);
-                store_agent(a.score + (size_t)b * kMaxExperts + e, s);
-                store_agent(a.key + (size_t)b * kMaxExperts + e, s + (a.bias ? a.bias[e] : 0.f));
-            }
-        }
-    }
-    // One arrival per workgroup, once the stores of all of its waves have
-    // completed.
-    wait_vm_all();
-    __syncthreads();
-    if (wave == 0) {
-        const bool last = wave_publish(&a.gctr[G_ROUTER_DONE]) == (uint32_t)a.router_target - 1u;
-        if (lane == 0) s_last = last;
-    }
-    __syncthreads();
-    if (s_last) route_step(route_args(a), &s_route, kWavesPerBlock);
-}
+enum { KIND_ROUTER = 0, KIND_LATENT = 1, KIND_SHARED = 2 };
 
-// ---------------------------------------------------------------------------
-// Kernel 1: router + latent-down + shared gate/up over x.
-// ---------------------------------------------------------------------------
+// Valid rows of a router tile and of a latent-down tile (a.router_rows,
+// a.latent_rows <= 16).  The fused step uses short tiles, which finish the
+// router and z early (each unit streams only these rows; MFMA rows past them
+// repeat the last row, an L1 hit, and are dropped), so that the routing and
+// the expert units that wait for it start sooner; the four-launch step uses
+// 16-row tiles (fewer units).
 
-// Tiles of 16 rows, in this order: router (E/16), latent-down (L/16), shared
-// (Is/8: gate rows 8p..8p+7 and up rows 8p..8p+7 in one tile, so SwiGLU pairs
-// D rows i and 8+i, held by lanes l and l+32).
-__global__ void __launch_bounds__(kWGThreads) __attribute__((amdgpu_waves_per_eu(4)))
-k_dense_in(const StepArgs a) {
-    __shared__ RouteLds s_route;
-    __shared__ float s_red[kWG * kWave * 4];
-    __shared__ int s_last;
+// Tiles: router rows RR t.., latent-down rows RL t.., shared tiles of 8 gate
+// rows 8t.. and the 8 matching up rows (so SwiGLU pairs D rows i and 8+i,
+// held by lanes l and l+32).  t is the tile index within its kind.  The
+// leader wave of a router tile arrives on the router counter; the arrival
+// that completes the router sets *s_last (LDS) for its workgroup.  Ends with
+// a workgroup barrier.  Coh: the z and shared-activation rows are read by
+// other units of the same launch (the fused step).
+template <bool Coh>
+__device__ __forceinline__ void dense_in_tile(const StepArgs &a, const Role &ro, int kind, int t,
+                                              bool active, int cg, float *s_red, int *s_last) {
     const int lane = lane_id(), n = lane & 15, g = lane >> 4;
-    const Role ro = role_of(a.kw_in);
-    if (threadIdx.x == 0) s_last = 0;
-    // The latent combine accumulates into ylat with atomics later in the step.
-    for (int i = (blockIdx.x * kWGThreads + threadIdx.x) * 4; i < a.B * a.L;
-         i += gridDim.x * kWGThreads * 4)
-        stf4(a.ylat + i, zero4());
-    const int n_rt = a.n_r16, n_lt = a.L >> 4, n_st = a.Is >> 3;
-    const int n_t = n_rt + n_lt + n_st;
-    const int ncg = (a.B + 15) >> 4;
-    const int units = dense_units(n_t, ro.RW, ncg);
-    for (int u = blockIdx.x; u < units; u += gridDim.x) {
-        int cg, tg;
-        dense_unit(u, ncg, cg, tg);
-        const int t = tg * ro.RW + ro.rg;
-        const bool active = t < n_t;
-        const int tt = active ? t : 0;
-        int kind;
-        const uint16_t *A;
-        if (tt < n_rt) {
-            kind = 0;
-            A = a.router_w + (size_t)(16 * tt + n) * a.H;
-        } else if (tt < n_rt + n_lt) {
-            kind = 1;
-            A = a.lat_down + (size_t)(16 * (tt - n_rt) + n) * a.H;
-        } else {
-            kind = 2;
-            const int p = tt - n_rt - n_lt;
-            A = a.sh_w13 + (size_t)((n < 8 ? 0 : a.Is) + 8 * p + (n & 7)) * a.H;
-        }
-        const int b = 16 * cg + n;
-        const bool valid = b < a.B;
-        const uint16_t *X = a.x + (size_t)(valid ? b : 0) * a.H + 32 * g;
-        f32x4 acc = zero4();
-        if (active)
-            dense_chunk_x(A + 32 * g, X, valid, ro.kw * a.spc_in, (ro.kw + 1) * a.spc_in, acc);
-        const bool leader = reduce_k1(s_red, ro.wave, ro.kw, ro.KW, acc);
-        if (leader && active) {
-            if (kind == 0) {
-                const int e = 16 * tt + 4 * g;
-                if (valid) {
-                    const f32x4 bv = a.bias ? ldf4(a.bias + e) : zero4();
+    const int tt = active ? t : 0;
+    const uint16_t *A;
+    const int RR = a.router_rows, RL = a.latent_rows;
+    if (kind == KIND_ROUTER)
+        A = a.router_w + (size_t)(RR * tt + min(n, RR - 1)) * a.H;
+    else if (kind == KIND_LATENT)
+        A = a.lat_down + (size_t)(RL * tt + min(n, RL - 1)) * a.H;
+    else
+        A = a.sh_w13 + (size_t)((n < 8 ? 0 : a.Is) + 8 * tt + (n & 7)) * a.H;
+    const int b = 16 * cg + n;
+    const bool valid = b < a.B;
+    const uint16_t *X = a.x + (size_t)(valid ? b : 0) * a.H + 32 * g;
+    f32x4 acc = zero4();
+    if (active) dense_chunk_x(A + 32 * g, X, valid, ro.kw * a.spc_in, (ro.kw + 1) * a.spc_in, acc);
+    const bool leader = reduce_k1(s_red, ro.wave, ro.kw, ro.KW, acc);
+    if (leader && active) {
+        if (kind == KIND_ROUTER) {
+            const int e = RR * tt + 4 * g;
+            if (valid && 4 * g < RR) {
+                const f32x4 bv = a.bias ? ldf4(a.bias + e) : zero4();
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const float sv = sigmoidf_(acc[i]);
-                        store_agent(a.score + (size_t)b * kMaxExperts + e + i, sv);
-                        store_agent(a.key + (size_t)b * kMaxExperts + e + i, sv + bv[i]);
-                    }
-                }
-                if (wave_publish(&a.gctr[G_ROUTER_DONE]) == (uint32_t)a.router_target - 1u &&
-                    lane == 0)
-                    s_last = 1;
-            } else if (kind == 1) {
-                if (valid) {
-                    uint16_t *dst = a.zhl + (size_t)b * 2 * a.L + 16 * (tt - n_rt) + 4 * g;
-                    store_hl4(dst, dst + a.L, acc);
-                }
-            } else {
-                f32x4 up;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) up[i] = __shfl_xor(acc[i], 32);
-                if (valid && g < 2) {
-                    f32x4 v;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) v[i] = silu_mul(acc[i], up[i]);
-                    uint16_t *dst = a.ashhl + (size_t)b * 2 * a.Is + 8 * (tt - n_rt - n_lt) + 4 * g;
-                    store_hl4(dst, dst + a.Is, v);
+                for (int i = 0; i < 4; ++i) {
+                    const float sv = sigmoidf_(acc[i]);
+                    store_agent(a.score + (size_t)b * kMaxExperts + e + i, sv);
+                    store_agent(a.key + (size_t)b * kMaxExperts + e + i, sv + bv[i]);
                 }
             }
-        }
-        __syncthreads();
-        if (s_last) {  // this workgroup completed the router: route the step
-            route_step(route_args(a), &s_route, kWG);
-            __syncthreads();
-            if (threadIdx.x == 0) s_last = 0;
+            if (wave_publish(&a.gctr[G_ROUTER_DONE]) == (uint32_t)a.router_target - 1u &&
+                lane == 0)
+                *s_last = 1;
+        } else if (kind == KIND_LATENT) {
+            if (valid && 4 * g < RL) {
+                uint16_t *dst = a.zhl + (size_t)b * 2 * a.L + RL * tt + 4 * g;
+                store_hl4<Coh>(dst, dst + a.L, acc);
+            }
+        } else {
+            f32x4 up;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) up[i] = __shfl_xor(acc[i], 32);
+            if (valid && g < 2) {
+                f32x4 v;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) v[i] = silu_mul(acc[i], up[i]);
+                uint16_t *dst = a.ashhl + (size_t)b * 2 * a.Is + 8 * tt + 4 * g;
+                store_hl4<Coh>(dst, dst + a.Is, v);
+            }
         }
     }
+    __syncthreads();
 }
 
 // ---------------------------------------------------------------------------
 // Expert kernels (2 and 3): shared structure
 // ---------------------------------------------------------------------------
 //
-// A workgroup serves one column unit (one expert, up to 8 of its tokens) and
-// 8 row tiles of that expert, one per wave; each wave runs the whole
-// reduction length K of its tile, so no partial sums cross waves.  K is taken
-// in chunks of S steps (S <= 16, 2048 elements).  Per chunk a wave issues all
-// of its MXFP4 code and scale loads at once (S x 16 B of codes per lane), the
-// workgroup copies the unit's activation rows for the chunk straight from
-// global memory into LDS, and the MFMAs run once everything has landed.  The
-// only round trips a workgroup waits on are its unit record, then one chunk
-// of weights.
+// A unit is one column unit (one expert, up to 8 of its tokens) and 8 row
+// tiles of that expert, one per wave; each wave runs the whole reduction
+// length K of its tile, so no partial sums cross waves.  K is taken in chunks
+// of S steps (S <= 16, 2048 elements).  Per chunk the workgroup copies the
+// unit's activation rows straight from global memory into LDS, every wave
+// issues all of its MXFP4 scale and code loads at once (S x 16 B of codes per
+// lane), and the MFMAs run step by step as the codes land.  The round trips a
+// workgroup waits on are its unit record, the activation copy, then the
+// chunk's weights.
 
 // LDS image of a unit's activation operand for one chunk: row n = 2j + part
 // (pair j's hi or lo values), 16 S chunks of 16 bytes (8 bf16) per row; chunk
@@ -382,9 +352,10 @@ struct Stage {
 // Wave-cooperative copy of rows 0 .. 2 nt - 1 of the operand for K range
 // [k0, k0 + 128 S): source row (j, part) starts at src + row_of(j) * 2 K +
 // part * K + k0 (elements).  Every wave takes every 8th 64-chunk block; each
-// lane moves one 16-byte chunk with a direct global -> LDS load, which lands
-// at the block base + 16 * lane.
-template <int S, typename RowOf>
+// lane moves one 16-byte chunk with a direct global -> LDS load (Coh:
+// coherent, the rows coming from another unit of the same launch), which
+// lands at the block base + 16 * lane.
+template <int S, bool Coh, typename RowOf>
 __device__ __forceinline__ void stage_operand(uint16_t *s_b, const uint16_t *src, int K, int k0,
                                               int nt, RowOf row_of) {
     const int lane = lane_id(), wave = wave_index();
@@ -395,7 +366,7 @@ __device__ __forceinline__ void stage_operand(uint16_t *s_b, const uint16_t *src
         const int q = st ^ (n & 15);
         const int j = n >> 1, part = n & 1;
         const uint16_t *g = src + ((size_t)row_of(j) * 2 + part) * K + k0 + 8 * q;
-        if (c < total) __builtin_amdgcn_global_load_lds(g, s_b + 8 * c0, 16, 0, 0);
+        if (c < total) __builtin_amdgcn_global_load_lds(g, s_b + 8 * c0, 16, 0, cache_aux<Coh>());
     }
 }
 
@@ -492,188 +463,459 @@ __device__ __forceinline__ void mfma_fp4_chunk(const Fp4Chunk<S> &w, const uint1
 }
 
 // ---------------------------------------------------------------------------
-// Kernel 2: expert gate/up (MXFP4) + SwiGLU.
+// Expert units
 // ---------------------------------------------------------------------------
 
-// Tile t of expert e: gate rows 8t .. 8t+7 (MFMA rows 0-7) and up rows
-// I + 8t .. I + 8t + 7 (MFMA rows 8-15), so lanes l and l + 32 hold a gate and
-// its up value.  Output: the activation of each pair as hi/lo bf16 rows.
-template <int S>
-__global__ void __launch_bounds__(kWGThreads) __attribute__((amdgpu_waves_per_eu(4)))
-k_w13(const StepArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t s_b[8 * Stage<S>::kChunks];
+// Reads unit c's record: each lane l < 32 holds word l (its lanes 32..63 a
+// copy); returns the expert, pair count and first pair as scalars.  Coh: the
+// records were written by a unit of the same launch.
+template <bool Coh>
+__device__ __forceinline__ int read_record(const StepArgs &a, int c, int &e, int &nt, int &p0) {
+    const int *p = a.cu_rec + (size_t)c * kRecWords + (lane_id() & 31);
+    int recw;
+    if constexpr (Coh)
+        recw = load_agent(p);
+    else
+        recw = *p;
+    e = (int)readlane((uint32_t)recw, R_EXPERT);
+    nt = (int)readlane((uint32_t)recw, R_COUNT);
+    p0 = (int)readlane((uint32_t)recw, R_PAIR0);
+    return recw;
+}
+
+// Gate/up unit: column unit c, tile group tg.  Tile t of expert e: gate rows
+// 8t .. 8t+7 (MFMA rows 0-7) and up rows I + 8t .. I + 8t + 7 (MFMA rows
+// 8-15), so lanes l and l + 32 hold a gate and its up value.  Output: the
+// activation of each pair as hi/lo bf16 rows.  `reuse`: s_b may still be read
+// by a wave (a barrier comes first).
+template <int S, bool Coh>
+__device__ __forceinline__ void w13_unit(const StepArgs &a, int c, int tg, uint16_t *s_b,
+                                         bool &reuse) {
     const int lane = lane_id(), n = lane & 15, g = lane >> 4, wave = wave_index();
     const int j = n >> 1, part = n & 1;
-    const int NC = min(a.meta[M_N_COLS], a.ncols_cap);  // never beyond the records
     const int OT = a.I >> 3;
-    const int TG = (OT + kWG - 1) / kWG;
     const int nchunk = a.L / (kKStep * S);
     const size_t qrow = a.L / 2, srow = a.L / 32;
-    bool reuse = false;  // s_b holds a previous chunk
-    for (int u = blockIdx.x; u < NC * TG; u += gridDim.x) {
-        const int c = u / TG;
-        const int t = (u % TG) * kWG + wave;
-        const bool active = t < OT;
-        const int recw = a.cu_rec[c * kRecWords + (lane & 31)];
-        const int e = (int)readlane((uint32_t)recw, R_EXPERT);
-        const int nt = (int)readlane((uint32_t)recw, R_COUNT);
-        const int p0 = (int)readlane((uint32_t)recw, R_PAIR0);
-        const int n_eff = j < nt ? n : part;
-        const size_t r = (size_t)e * 2 * a.I + (n < 8 ? 0 : a.I) + 8 * (active ? t : 0) + (n & 7);
-        const uint8_t *qp = a.w13_q + r * qrow + 16 * g;
-        const uint8_t *sp = a.w13_s + r * srow;
-        f32x4 acc = zero4();
-        for (int ch = 0; ch < nchunk; ++ch) {
-            // Every wave loads and multiplies (a wave past the last tile
-            // reads tile 0 again and drops its result), which keeps the
-            // load sequence free of branches: the compiler then waits for
-            // each step's own loads only.  The staging copies go first, so
-            // that the barrier below waits for them alone.
-            if (reuse) __syncthreads();  // every wave is done with s_b
-            reuse = true;
-            Fp4Chunk<S> w;
-            if constexpr (S % 4 != 0) load_fp4_scales<S>(sp + (size_t)ch * S * 4, w);
-            fence_schedule();
-            stage_operand<S>(s_b, a.zhl, a.L, ch * S * kKStep, nt,
-                             [&](int jj) { return __shfl(recw, R_TOKEN + jj); });
-            fence_schedule();
-            if constexpr (S % 4 == 0) load_fp4_scales<S>(sp + (size_t)ch * S * 4, w);
-            load_fp4_codes<S>(qp + (size_t)ch * S * 64, w);
-            fence_schedule();
-            wait_staging<S>();
-            staged_barrier();
-            mfma_fp4_chunk<S>(w, s_b, n_eff, g, acc);
-        }
-        acc = add_pair_column(acc);
-        f32x4 up;
+    const int t = tg * kWG + wave;
+    const bool active = t < OT;
+    int e, nt, p0;
+    const int recw = read_record<Coh>(a, c, e, nt, p0);
+    const int n_eff = j < nt ? n : part;
+    const size_t r = (size_t)e * 2 * a.I + (n < 8 ? 0 : a.I) + 8 * (active ? t : 0) + (n & 7);
+    const uint8_t *qp = a.w13_q + r * qrow + 16 * g;
+    const uint8_t *sp = a.w13_s + r * srow;
+    f32x4 acc = zero4();
+    for (int ch = 0; ch < nchunk; ++ch) {
+        // Every wave loads and multiplies (a wave past the last tile reads
+        // tile 0 again and drops its result), which keeps the load sequence
+        // free of branches: the compiler then waits for each step's own loads
+        // only.  The staging copies go first, so that the barrier below waits
+        // for them alone.
+        if (reuse) __syncthreads();  // every wave is done with s_b
+        reuse = true;
+        Fp4Chunk<S> w;
+        if constexpr (S % 4 != 0) load_fp4_scales<S>(sp + (size_t)ch * S * 4, w);
+        fence_schedule();
+        stage_operand<S, Coh>(s_b, a.zhl, a.L, ch * S * kKStep, nt,
+                         [&](int jj) { return __shfl(recw, R_TOKEN + jj); });
+        fence_schedule();
+        if constexpr (S % 4 == 0) load_fp4_scales<S>(sp + (size_t)ch * S * 4, w);
+        load_fp4_codes<S>(qp + (size_t)ch * S * 64, w);
+        fence_schedule();
+        wait_staging<S>();
+        staged_barrier();
+        mfma_fp4_chunk<S>(w, s_b, n_eff, g, acc);
+    }
+    acc = add_pair_column(acc);
+    f32x4 up;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) up[i] = __shfl_xor(acc[i], 32);
-        if (active && j < nt && part == 0 && g < 2) {
-            f32x4 v;
+    for (int i = 0; i < 4; ++i) up[i] = __shfl_xor(acc[i], 32);
+    if (active && j < nt && part == 0 && g < 2) {
+        f32x4 v;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) v[i] = silu_mul(acc[i], up[i]);
-            uint16_t *dst = a.acthl + (size_t)(p0 + j) * 2 * a.I + 8 * t + 4 * g;
-            store_hl4(dst, dst + a.I, v);
-        }
+        for (int i = 0; i < 4; ++i) v[i] = silu_mul(acc[i], up[i]);
+        uint16_t *dst = a.acthl + (size_t)(p0 + j) * 2 * a.I + 8 * t + 4 * g;
+        store_hl4<Coh>(dst, dst + a.I, v);
     }
 }
 
-// ---------------------------------------------------------------------------
-// Kernel 3: expert down (MXFP4) + weighted combine in latent space.
-// ---------------------------------------------------------------------------
-
-// Tile t of expert e: latent rows 16t .. 16t+15; the routing weight of each
-// pair scales its column before the f32 atomic add into ylat.
-template <int S>
-__global__ void __launch_bounds__(kWGThreads) __attribute__((amdgpu_waves_per_eu(4)))
-k_w2(const StepArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t s_b[8 * Stage<S>::kChunks];
+// Down unit: column unit c, tile group tg.  Tile t of expert e: latent rows
+// 16t .. 16t+15; the routing weight of each pair scales its column before the
+// f32 atomic add into ylat.
+template <int S, bool Coh>
+__device__ __forceinline__ void w2_unit(const StepArgs &a, int c, int tg, uint16_t *s_b,
+                                        bool &reuse) {
     const int lane = lane_id(), n = lane & 15, g = lane >> 4, wave = wave_index();
     const int j = n >> 1, part = n & 1;
-    const int NC = min(a.meta[M_N_COLS], a.ncols_cap);  // never beyond the records
     const int OT = a.L >> 4;
-    const int TG = (OT + kWG - 1) / kWG;
     const int nchunk = a.I / (kKStep * S);
     const size_t qrow = a.I / 2, srow = a.I / 32;
-    bool reuse = false;  // s_b holds a previous chunk
-    for (int u = blockIdx.x; u < NC * TG; u += gridDim.x) {
-        const int c = u / TG;
-        const int t = (u % TG) * kWG + wave;
-        const bool active = t < OT;
-        const int recw = a.cu_rec[c * kRecWords + (lane & 31)];
-        const int e = (int)readlane((uint32_t)recw, R_EXPERT);
-        const int nt = (int)readlane((uint32_t)recw, R_COUNT);
-        const int p0 = (int)readlane((uint32_t)recw, R_PAIR0);
-        const int jc = j < nt ? j : 0;
-        const int tok_j = __shfl(recw, R_TOKEN + jc);
-        const float w_j = __int_as_float(__shfl(recw, R_WEIGHT + jc));
-        const int n_eff = j < nt ? n : part;
-        const size_t r = (size_t)e * a.L + 16 * (active ? t : 0) + n;
-        const uint8_t *qp = a.w2_q + r * qrow + 16 * g;
-        const uint8_t *sp = a.w2_s + r * srow;
-        f32x4 acc = zero4();
-        for (int ch = 0; ch < nchunk; ++ch) {
-            // Every wave loads and multiplies (a wave past the last tile
-            // reads tile 0 again and drops its result), which keeps the
-            // load sequence free of branches: the compiler then waits for
-            // each step's own loads only.  The staging copies go first, so
-            // that the barrier below waits for them alone.
-            if (reuse) __syncthreads();  // every wave is done with s_b
-            reuse = true;
-            Fp4Chunk<S> w;
-            if constexpr (S % 4 != 0) load_fp4_scales<S>(sp + (size_t)ch * S * 4, w);
-            fence_schedule();
-            stage_operand<S>(s_b, a.acthl, a.I, ch * S * kKStep, nt,
-                             [&](int jj) { return p0 + jj; });
-            fence_schedule();
-            if constexpr (S % 4 == 0) load_fp4_scales<S>(sp + (size_t)ch * S * 4, w);
-            load_fp4_codes<S>(qp + (size_t)ch * S * 64, w);
-            fence_schedule();
-            wait_staging<S>();
-            staged_barrier();
-            mfma_fp4_chunk<S>(w, s_b, n_eff, g, acc);
-        }
-        acc = add_pair_column(acc);
-        if (active && j < nt && part == 0) {
-            float *dst = a.ylat + (size_t)tok_j * a.L + 16 * t + 4 * g;
+    const int t = tg * kWG + wave;
+    const bool active = t < OT;
+    int e, nt, p0;
+    const int recw = read_record<Coh>(a, c, e, nt, p0);
+    const int jc = j < nt ? j : 0;
+    const int tok_j = __shfl(recw, R_TOKEN + jc);
+    const float w_j = __int_as_float(__shfl(recw, R_WEIGHT + jc));
+    const int n_eff = j < nt ? n : part;
+    const size_t r = (size_t)e * a.L + 16 * (active ? t : 0) + n;
+    const uint8_t *qp = a.w2_q + r * qrow + 16 * g;
+    const uint8_t *sp = a.w2_s + r * srow;
+    f32x4 acc = zero4();
+    for (int ch = 0; ch < nchunk; ++ch) {
+        // As in w13_unit.
+        if (reuse) __syncthreads();
+        reuse = true;
+        Fp4Chunk<S> w;
+        if constexpr (S % 4 != 0) load_fp4_scales<S>(sp + (size_t)ch * S * 4, w);
+        fence_schedule();
+        stage_operand<S, Coh>(s_b, a.acthl, a.I, ch * S * kKStep, nt,
+                         [&](int jj) { return p0 + jj; });
+        fence_schedule();
+        if constexpr (S % 4 == 0) load_fp4_scales<S>(sp + (size_t)ch * S * 4, w);
+        load_fp4_codes<S>(qp + (size_t)ch * S * 64, w);
+        fence_schedule();
+        wait_staging<S>();
+        staged_barrier();
+        mfma_fp4_chunk<S>(w, s_b, n_eff, g, acc);
+    }
+    acc = add_pair_column(acc);
+    if (active && j < nt && part == 0) {
+        float *dst = a.ylat + (size_t)tok_j * a.L + 16 * t + 4 * g;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) unsafeAtomicAdd(dst + i, w_j * acc[i]);
-        }
+        for (int i = 0; i < 4; ++i) unsafeAtomicAdd(dst + i, w_j * acc[i]);
     }
 }
 
 // ---------------------------------------------------------------------------
-// Kernel 4: latent-up + shared-down, bf16 output.
+// Output unit: one tile of RT = out_rows <= 16 rows (MFMA rows past RT repeat
+// the tile's last row and are dropped) for one column group of 8 tokens.
 // ---------------------------------------------------------------------------
 
-// Output tiles cover RT = out_rows <= 16 rows (MFMA rows past RT repeat the
-// tile's last row and are dropped), chosen so that the tiles split evenly
-// over the compute units.
-__global__ void __launch_bounds__(kWGThreads) __attribute__((amdgpu_waves_per_eu(4)))
-k_out(const StepArgs a) {
-    __shared__ float s_red[kWG * kWave * 4];
-    // The router counter of the dense input kernel is cleared here, where no
-    // wave of the step can touch it any more.
-    if (blockIdx.x == 0 && threadIdx.x == 0) a.gctr[G_ROUTER_DONE] = 0u;
+enum { OUT_BOTH = 0, OUT_SHARED = 1, OUT_LATENT = 2 };
+
+// OUT_BOTH: latent-up and shared-down in one pass, one bf16 rounding (the
+// four-launch step).  OUT_SHARED: shared-down only, f32 sums to ysh.
+// OUT_LATENT: latent-up, plus ysh, one bf16 rounding.  K steps: the wave's
+// slice [kw * spc, (kw + 1) * spc).  Ends with a workgroup barrier.  Coh:
+// ylat and the shared activation come from units of the same launch.
+template <bool Coh>
+__device__ __forceinline__ void out_tile(const StepArgs &a, const Role &ro, int mode, int t,
+                                         bool active, int cg, int spc, float *s_red) {
     const int lane = lane_id(), n = lane & 15, g = lane >> 4;
     const int col = n >> 1, part = n & 1;
-    const Role ro = role_of(a.kw_out);
     const int RT = a.out_rows;
-    const int ncg = (a.B + 7) >> 3;
-    const int n_t = (a.H + RT - 1) / RT;
+    const int b = 8 * cg + col;
+    const bool valid = b < a.B;
+    const int bb = valid ? b : 0;
+    const int h0 = RT * (active ? t : 0);
+    const size_t h = min(h0 + min(n, RT - 1), a.H - 1);
+    TwoSource ts;
+    ts.Aa = a.lat_up + h * a.L + 32 * g;
+    ts.Ab = a.sh_w2 + h * a.Is + 32 * g;
+    ts.Ra = buf_rsrc(a.ylat);
+    ts.Rb = buf_rsrc(a.ashhl);
+    ts.Oa = (uint32_t)(((size_t)bb * a.L + 32 * g) * 4);
+    ts.Ob = (uint32_t)((((size_t)bb * 2 + part) * a.Is + 32 * g) * 2);
+    ts.Ls = mode == OUT_SHARED ? 0 : a.L / kKStep;
+    f32x4 acc = zero4();
+    if (active) dense_chunk_out<Coh>(ts, valid, part, ro.kw * spc, (ro.kw + 1) * spc, acc);
+    const bool leader = reduce_k1(s_red, ro.wave, ro.kw, ro.KW, acc);
+    if (leader && active) {
+        acc = add_pair_column(acc);
+        if (valid && part == 0) {
+            const size_t o = (size_t)b * a.H + h0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 4 * g + i;
+                if (r < RT && h0 + r < a.H) {
+                    if (mode == OUT_SHARED) {
+                        store_agent(a.ysh + o + r, acc[i]);
+                    } else {
+                        const float v = mode == OUT_LATENT ? acc[i] + load_agent(a.ysh + o + r) : acc[i];
+                        a.out[o + r] = (uint16_t)bf16_rne(v);
+                    }
+                }
+            }
+        }
+    }
+    __syncthreads();
+}
+
+// ---------------------------------------------------------------------------
+// Four-launch step
+// ---------------------------------------------------------------------------
+
+// Kernel 0 (f32 router only): logits, scores and keys with plain f32 FMAs;
+// the workgroup whose arrival completes the router routes the step.
+__global__ void __launch_bounds__(kBlock) k_router_f32(const StepArgs a) {
+    __shared__ RouteLds s_route;
+    __shared__ int s_last;
+    const int wave = wave_index();
+    const int lane = lane_id();
+    for (int e = blockIdx.x * kWavesPerBlock + wave; e < a.E; e += gridDim.x * kWavesPerBlock) {
+        const float *row = a.router_w32 + (size_t)e * a.H;
+        for (int b = 0; b < a.B; ++b) {
+            const uint16_t *xb = a.x + (size_t)b * a.H;
+            float acc = 0.f;
+            for (int h = lane; h < a.H; h += kWave) acc = fmaf(row[h], bf16_val(xb[h]), acc);
+            acc = wave_sum(acc);
+            if (lane == 0) {
+                const float s = sigmoidf_(acc);
+                store_agent(a.score + (size_t)b * kMaxExperts + e, s);
+                store_agent(a.key + (size_t)b * kMaxExperts + e, s + (a.bias ? a.bias[e] : 0.f));
+            }
+        }
+    }
+    // One arrival per workgroup, once the stores of all of its waves have
+    // completed.
+    wait_vm_all();
+    __syncthreads();
+    if (wave == 0) {
+        const bool last = wave_publish(&a.gctr[G_ROUTER_DONE]) == (uint32_t)a.router_target - 1u;
+        if (lane == 0) s_last = last;
+    }
+    __syncthreads();
+    if (s_last) route_step(route_args(a), &s_route, kWavesPerBlock);
+}
+
+// Kernel 1: dense-in units over [router | latent | shared] tiles.
+__global__ void __launch_bounds__(kWGThreads) __attribute__((amdgpu_waves_per_eu(4)))
+k_dense_in(const StepArgs a) {
+    __shared__ RouteLds s_route;
+    __shared__ float s_red[kWG * kWave * 4];
+    __shared__ int s_last;
+    const Role ro = role_of(a.kw_in);
+    if (threadIdx.x == 0) s_last = 0;
+    // The latent combine accumulates into ylat with atomics later in the step.
+    for (int i = (blockIdx.x * kWGThreads + threadIdx.x) * 4; i < a.B * a.L;
+         i += gridDim.x * kWGThreads * 4)
+        stf4(a.ylat + i, zero4());
+    const int n_rt = a.n_rtiles, n_lt = a.L / a.latent_rows, n_st = a.Is >> 3;
+    const int n_t = n_rt + n_lt + n_st;
+    const int ncg = (a.B + 15) >> 4;
     const int units = dense_units(n_t, ro.RW, ncg);
     for (int u = blockIdx.x; u < units; u += gridDim.x) {
         int cg, tg;
         dense_unit(u, ncg, cg, tg);
         const int t = tg * ro.RW + ro.rg;
         const bool active = t < n_t;
-        const int b = 8 * cg + col;
-        const bool valid = b < a.B;
-        const int bb = valid ? b : 0;
-        const int h0 = RT * (active ? t : 0);
-        const size_t h = min(h0 + min(n, RT - 1), a.H - 1);
-        TwoSource ts;
-        ts.Aa = a.lat_up + h * a.L + 32 * g;
-        ts.Xa = a.ylat + (size_t)bb * a.L + 32 * g;
-        ts.Ab = a.sh_w2 + h * a.Is + 32 * g;
-        ts.Xb = a.ashhl + ((size_t)bb * 2 + part) * a.Is + 32 * g;
-        ts.Ls = a.L / kKStep;
-        f32x4 acc = zero4();
-        if (active)
-            dense_chunk_out(ts, valid, part, ro.kw * a.spc_out, (ro.kw + 1) * a.spc_out, acc);
-        const bool leader = reduce_k1(s_red, ro.wave, ro.kw, ro.KW, acc);
-        if (leader && active) {
-            acc = add_pair_column(acc);
-            if (valid && part == 0) {
-                uint16_t *dst = a.out + (size_t)b * a.H;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int r = 4 * g + i;
-                    if (r < RT && h0 + r < a.H) dst[h0 + r] = (uint16_t)bf16_rne(acc[i]);
+        const int kind = t < n_rt ? KIND_ROUTER : t < n_rt + n_lt ? KIND_LATENT : KIND_SHARED;
+        const int tl = kind == KIND_ROUTER ? t : kind == KIND_LATENT ? t - n_rt : t - n_rt - n_lt;
+        dense_in_tile<false>(a, ro, kind, tl, active, cg, s_red, &s_last);
+        if (s_last) {  // this workgroup completed the router: route the step
+            route_step(route_args(a), &s_route, kWG);
+            __syncthreads();
+            if (threadIdx.x == 0) s_last = 0;
+        }
+    }
+}
+
+// Kernel 2: gate/up units.
+template <int S>
+__global__ void __launch_bounds__(kWGThreads) __attribute__((amdgpu_waves_per_eu(4)))
+k_w13(const StepArgs a) {
+    __shared__ __attribute__((aligned(16))) uint16_t s_b[8 * Stage<S>::kChunks];
+    const int NC = min(load_agent(a.meta + M_N_COLS), a.ncols_cap);  // never beyond the records
+    const int TG = ((a.I >> 3) + kWG - 1) / kWG;
+    bool reuse = false;
+    for (int u = blockIdx.x; u < NC * TG; u += gridDim.x) w13_unit<S, false>(a, u / TG, u % TG, s_b, reuse);
+}
+
+// Kernel 3: down units.
+template <int S>
+__global__ void __launch_bounds__(kWGThreads) __attribute__((amdgpu_waves_per_eu(4)))
+k_w2(const StepArgs a) {
+    __shared__ __attribute__((aligned(16))) uint16_t s_b[8 * Stage<S>::kChunks];
+    const int NC = min(load_agent(a.meta + M_N_COLS), a.ncols_cap);
+    const int TG = ((a.L >> 4) + kWG - 1) / kWG;
+    bool reuse = false;
+    for (int u = blockIdx.x; u < NC * TG; u += gridDim.x) w2_unit<S, false>(a, u / TG, u % TG, s_b, reuse);
+}
+
+// Kernel 4: output units (latent-up and shared-down in one pass).
+__global__ void __launch_bounds__(kWGThreads) __attribute__((amdgpu_waves_per_eu(4)))
+k_out(const StepArgs a) {
+    __shared__ float s_red[kWG * kWave * 4];
+    // The router counter of the dense input kernel is cleared here, where no
+    // wave of the step can touch it any more.
+    if (blockIdx.x == 0 && threadIdx.x == 0) a.gctr[G_ROUTER_DONE] = 0u;
+    const Role ro = role_of(a.kw_out);
+    const int ncg = (a.B + 7) >> 3;
+    const int n_t = (a.H + a.out_rows - 1) / a.out_rows;
+    const int units = dense_units(n_t, ro.RW, ncg);
+    for (int u = blockIdx.x; u < units; u += gridDim.x) {
+        int cg, tg;
+        dense_unit(u, ncg, cg, tg);
+        const int t = tg * ro.RW + ro.rg;
+        out_tile<false>(a, ro, OUT_BOTH, t, t < n_t, cg, a.spc_out, s_red);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Fused step: one persistent launch
+// ---------------------------------------------------------------------------
+//
+// The units of the step form one list in dependency order:
+//   [router | latent-down | shared gate/up | gate/up | down | shared-down |
+//    latent-up]
+// (ranges a.u_*).  Workgroups take units from an agent-scope counter, so a
+// taken unit always belongs to a running workgroup; a unit waits only for
+// units earlier in the list, hence the step always progresses, whether or not
+// the whole grid is resident.  A
+// unit's outputs are published with agent-scope stores, then one counter
+// increment; a waiting unit polls the counter from one lane (bounded: after
+// kSpinLimit polls it records G_ERROR and goes on instead of hanging).  The
+// last workgroup to leave the queue resets every counter for the next step.
+
+constexpr uint32_t kSpinLimit = 1u << 15;  // ~50 ms of polls: far beyond any legitimate wait
+
+// Counter increment after the whole workgroup's stores have completed.
+__device__ __forceinline__ void wg_publish(uint32_t *ctr, uint32_t v = 1u) {
+    wait_vm_all();
+    __syncthreads();
+    if (threadIdx.x == 0) __hip_atomic_fetch_add(ctr, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Returns once *ctr >= target (the whole workgroup waits at the barrier).
+__device__ __forceinline__ void wg_wait(const StepArgs &a, const uint32_t *ctr, uint32_t target) {
+    if (threadIdx.x == 0) {
+        uint32_t polls = 0;
+        while (load_agent(ctr) < target) {
+            if (++polls >= kSpinLimit) {
+                __hip_atomic_fetch_or(&a.gctr[G_ERROR], 1u, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(32);
+        }
+    }
+    __syncthreads();
+}
+
+// Active column units of the step (known once the routing has published).
+__device__ __forceinline__ int routed_units(const StepArgs &a) {
+    wg_wait(a, &a.gctr[G_ROUTED], 1u);
+    return min(load_agent(a.meta + M_N_COLS), a.ncols_cap);
+}
+
+template <int S13, int S2>
+struct StepLds {
+    static constexpr int kExpert = 8 * Stage<(S13 > S2 ? S13 : S2)>::kChunks * 2;
+    static constexpr int kDense = (int)sizeof(RouteLds) + kWG * kWave * 4 * 4;
+    static constexpr int kBytes = kExpert > kDense ? kExpert : kDense;
+};
+
+template <int S13, int S2>
+__global__ void __launch_bounds__(kWGThreads) __attribute__((amdgpu_waves_per_eu(4)))
+k_step(const StepArgs a) {
+    __shared__ __attribute__((aligned(16))) char s_mem[StepLds<S13, S2>::kBytes];
+    __shared__ int s_last, s_next, s_exit;
+    RouteLds *s_route = (RouteLds *)s_mem;
+    float *s_red = (float *)(s_mem + sizeof(RouteLds));
+    float *s_red_out = (float *)s_mem;
+    uint16_t *s_b = (uint16_t *)s_mem;
+    const Role ro_in = role_of(a.kw_in), ro_sd = role_of(a.kw_sd), ro_lu = role_of(a.kw_lu);
+    const int ncg_in = (a.B + 15) >> 4, ncg_out = (a.B + 7) >> 3;
+    const int n_lt = a.L / a.latent_rows, n_st = a.Is >> 3;
+    const int n_ot = (a.H + a.out_rows - 1) / a.out_rows;
+    if (threadIdx.x == 0) {
+        s_last = 0;
+        s_next = (int)__hip_atomic_fetch_add(&a.gctr[G_WORK], 1u, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    int u = s_next;
+    while (u < a.u_end) {
+        if (u < a.u_sh) {
+            // router or latent-down unit
+            const bool router = u < a.u_lat;
+            const int ui = router ? u : u - a.u_lat;
+            const int cg = ui % ncg_in, t = (ui / ncg_in) * ro_in.RW + ro_in.rg;
+            const int n_kind = router ? a.n_rtiles : n_lt;
+            if (!router) {
+                // This unit's slice of ylat goes to zero before any down unit
+                // can add to it (they wait for every latent unit).
+                const int n4 = a.B * a.L / 4, per = (n4 + a.n_lat_units - 1) / a.n_lat_units;
+                for (int i = ui * per + (int)threadIdx.x; i < min(n4, (ui + 1) * per); i += kWGThreads) {
+                    uint64_t *q = (uint64_t *)(a.ylat + 4 * i);
+                    __hip_atomic_store(q, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    __hip_atomic_store(q + 1, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 }
             }
+            dense_in_tile<true>(a, ro_in, router ? KIND_ROUTER : KIND_LATENT, t, t < n_kind, cg, s_red,
+                          &s_last);
+            if (router) {
+                if (s_last) {  // this workgroup completed the router: route the step
+                    route_step(route_args(a), s_route, kWG);
+                    if (threadIdx.x == 0) s_last = 0;
+                    wg_publish(&a.gctr[G_ROUTED]);
+                }
+            } else {
+                wg_publish(&a.gctr[G_LATENT]);
+            }
+        } else if (u < a.u_13) {
+            // shared gate/up unit
+            const int ui = u - a.u_sh;
+            const int cg = ui % ncg_in, t = (ui / ncg_in) * ro_in.RW + ro_in.rg;
+            dense_in_tile<true>(a, ro_in, KIND_SHARED, t, t < n_st, cg, s_red, &s_last);
+            wg_publish(&a.gctr[G_SHARED]);
+        } else if (u < a.u_2) {
+            // gate/up unit: needs the routing and every z row
+            const int ui = u - a.u_13, c = ui / a.tg13;
+            if (c < routed_units(a)) {
+                wg_wait(a, &a.gctr[G_LATENT], (uint32_t)a.n_lat_units);
+                bool reuse = true;
+                w13_unit<S13, true>(a, c, ui % a.tg13, s_b, reuse);
+                wg_publish(&a.c13[c * kCtrStride]);
+            }
+        } else if (u < a.u_sd) {
+            // down unit: needs its column unit's activations
+            const int ui = u - a.u_2, c = ui / a.tg2;
+            if (c < routed_units(a)) {
+                wg_wait(a, &a.c13[c * kCtrStride], (uint32_t)a.tg13);
+                bool reuse = true;
+                w2_unit<S2, true>(a, c, ui % a.tg2, s_b, reuse);
+                wg_publish(&a.gctr[G_W2]);
+            }
+        } else if (u < a.u_lu) {
+            // shared-down unit: needs every shared activation
+            const int ui = u - a.u_sd;
+            const int cg = ui % ncg_out, t = (ui / ncg_out) * ro_sd.RW + ro_sd.rg;
+            wg_wait(a, &a.gctr[G_SHARED], (uint32_t)a.n_sh_units);
+            out_tile<true>(a, ro_sd, OUT_SHARED, t, t < n_ot, cg, a.spc_sd, s_red_out);
+            wg_publish(&a.gctr[G_SHDOWN]);
+        } else {
+            // latent-up unit: needs the whole latent combine and the
+            // shared-down sums
+            const int ui = u - a.u_lu;
+            const int cg = ui % ncg_out, t = (ui / ncg_out) * ro_lu.RW + ro_lu.rg;
+            const int NC = routed_units(a);
+            wg_wait(a, &a.gctr[G_W2], (uint32_t)(NC * a.tg2));
+            wg_wait(a, &a.gctr[G_SHDOWN], (uint32_t)a.n_sd_units);
+            out_tile<true>(a, ro_lu, OUT_LATENT, t, t < n_ot, cg, a.spc_lu, s_red_out);
         }
+        // The next unit is taken only now: a unit taken while another one
+        // still waits would hold up the units that depend on it.
         __syncthreads();
+        if (threadIdx.x == 0)
+            s_next = (int)__hip_atomic_fetch_add(&a.gctr[G_WORK], 1u, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        u = s_next;
+    }
+    // The last workgroup out of the queue resets the counters: no other
+    // workgroup of this launch touches them any more.
+    if (threadIdx.x == 0)
+        s_exit = __hip_atomic_fetch_add(&a.gctr[G_EXIT], 1u, __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT) == gridDim.x - 1u;
+    __syncthreads();
+    if (s_exit) {
+        for (int i = threadIdx.x; i < G_ERROR; i += kWGThreads)
+            __hip_atomic_store(&a.gctr[i], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int i = threadIdx.x; i < a.ncols_cap; i += kWGThreads)
+            __hip_atomic_store(&a.c13[i * kCtrStride], 0u, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 

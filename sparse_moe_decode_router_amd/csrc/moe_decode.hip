@@ -28,6 +28,8 @@ int cdiv(int a, int b) { return (a + b - 1) / b; }
 struct Split {
     int kw, spc;
 };
+
+typedef void (*StepKernel)(const StepArgs);
 Split choose_split(int nsteps) {
     for (int kw = kWG; kw >= 1; kw /= 2)
         if (nsteps % kw == 0 && nsteps / kw <= kMaxStepsPerChunk) return Split{kw, nsteps / kw};
@@ -60,38 +62,82 @@ long long dense_units_host(int n_t, int RW, int ncg) {
 }
 
 struct Plan {
-    int n_r16, ncg_in, ncg_out, out_rows;
-    Split in, out;
-    int s13, s2;
+    int n_rtiles, ncg_in, ncg_out, out_rows;
+    Split in, out, sd, lu;
+    int s13, s2, tg13, tg2;
     long long units_in, units_out, units_13, units_2;
+    // Fused step: unit ranges (see StepArgs).
+    int u_lat, u_sh, u_13, u_2, u_sd, u_lu, u_end;
+    int router_rows, latent_rows;
 };
 
-Plan make_plan(const moe_decode_config &c, int B, int k) {
+// Rows of the router and latent-down tiles: short in the fused step (the
+// router and z finish early, so the routing and the expert units start
+// sooner), 16 in the four-launch step (fewer units).
+constexpr int kFusedRouterRows = 4, kFusedLatentRows = 8;
+
+Plan make_plan(const moe_decode_config &c, int B, int k, bool fused) {
     Plan p;
-    p.n_r16 = c.router_dtype == MOE_ROUTER_BF16 ? c.n_experts / 16 : 0;
+    p.router_rows = fused ? kFusedRouterRows : 16;
+    p.latent_rows = fused ? kFusedLatentRows : 16;
+    p.n_rtiles = c.router_dtype == MOE_ROUTER_BF16 ? c.n_experts / p.router_rows : 0;
     p.ncg_in = cdiv(B, 16);
     p.ncg_out = cdiv(B, 8);
     p.in = choose_split(c.hidden / kKStep);
     p.out = choose_split((c.latent + c.shared_inter) / kKStep);
     p.s13 = expert_chunk(c.latent / kKStep);
     p.s2 = expert_chunk(c.expert_inter / kKStep);
-    // Dense kernels work on 16-row tiles: router, latent-down, then shared
-    // tiles of 8 gate + 8 up rows.
-    const int n_t_in = p.n_r16 + c.latent / 16 + c.shared_inter / 8;
+    // Dense-in tiles: router, latent-down, then shared tiles of 8 gate + 8 up
+    // rows.
+    const int n_t_in = p.n_rtiles + c.latent / p.latent_rows + c.shared_inter / 8;
     const long long cols = ncols_cap(c.n_experts, B, k);
     p.units_in = dense_units_host(n_t_in, kWG / p.in.kw, p.ncg_in);
     p.out_rows = out_tile_rows(c.hidden);
     p.units_out = dense_units_host(cdiv(c.hidden, p.out_rows), kWG / p.out.kw, p.ncg_out);
     // Expert kernels: 8 row tiles per workgroup (8 gate + 8 up rows, or 16
     // latent rows, per tile).
-    p.units_13 = cols * cdiv(c.expert_inter / 8, kWG);
-    p.units_2 = cols * cdiv(c.latent / 16, kWG);
+    p.tg13 = cdiv(c.expert_inter / 8, kWG);
+    p.tg2 = cdiv(c.latent / 16, kWG);
+    p.units_13 = cols * p.tg13;
+    p.units_2 = cols * p.tg2;
+    // Fused step: the output units split into shared-down (K = Is) and
+    // latent-up (K = L) units; every range holds whole tile groups of one
+    // kind for each column group.
+    p.sd = choose_split(c.shared_inter / kKStep);
+    p.lu = choose_split(c.latent / kKStep);
+    const int rw_in = kWG / std::max(1, p.in.kw);
+    const int n_ot = cdiv(c.hidden, p.out_rows);
+    p.u_lat = cdiv(p.n_rtiles, rw_in) * p.ncg_in;
+    p.u_sh = p.u_lat + cdiv(c.latent / p.latent_rows, rw_in) * p.ncg_in;
+    p.u_13 = p.u_sh + cdiv(c.shared_inter / 8, rw_in) * p.ncg_in;
+    p.u_2 = p.u_13 + (int)p.units_13;
+    p.u_sd = p.u_2 + (int)p.units_2;
+    p.u_lu = p.u_sd + cdiv(n_ot, kWG / std::max(1, p.sd.kw)) * p.ncg_out;
+    p.u_end = p.u_lu + cdiv(n_ot, kWG / std::max(1, p.lu.kw)) * p.ncg_out;
     return p;
 }
 
+// Fused step kernels, one per (gate/up chunk, down chunk) pair of the shapes
+// the library is built for; other shapes run the four-launch step.
+struct FusedEntry {
+    int s13, s2;
+    StepKernel k;
+};
+const FusedEntry kFused[] = {{16, 16, k_step<16, 16>}, {16, 8, k_step<16, 8>},
+                             {16, 4, k_step<16, 4>},   {16, 2, k_step<16, 2>},
+                             {8, 8, k_step<8, 8>},     {4, 3, k_step<4, 3>},
+                             {2, 2, k_step<2, 2>}};
+
+StepKernel fused_kernel(const moe_decode_config &c, const Plan &p) {
+    if (c.router_dtype != MOE_ROUTER_BF16 || p.sd.kw == 0 || p.lu.kw == 0) return nullptr;
+    for (const FusedEntry &f : kFused)
+        if (f.s13 == p.s13 && f.s2 == p.s2) return f.k;
+    return nullptr;
+}
+
 struct Layout {
-    size_t gctr, meta, score, key, idx, wsel, act_expert, act_off, cu_rec, pair_slot,
-        pair_of_slot, zhl, ashhl, acthl, ylat, total;
+    size_t gctr, meta, c13, score, key, idx, wsel, act_expert, act_off, cu_rec, pair_slot,
+        pair_of_slot, zhl, ashhl, acthl, ylat, ysh, total;
     size_t counters_end;  // [0, counters_end) holds every counter: cleared at init
 };
 
@@ -109,6 +155,7 @@ Layout make_layout(const moe_decode_config &c) {
     };
     l.gctr = take(G_COUNT * 4);
     l.meta = take(M_COUNT * 4);
+    l.c13 = take(ncols * kCtrStride * 4);
     l.counters_end = o;
     // Score and key rows are padded to kMaxExperts: the routing reads a whole
     // row with one base address (entries past E are never used).
@@ -125,11 +172,11 @@ Layout make_layout(const moe_decode_config &c) {
     l.ashhl = take(Bm * 2 * Is * 2);
     l.acthl = take(P * 2 * I * 2);
     l.ylat = take(Bm * L * 4);
+    l.ysh = take(Bm * (size_t)c.hidden * 4);
     l.total = o;
     return l;
 }
 
-typedef void (*StepKernel)(const StepArgs);
 #define MOE_SPC_TABLE(K)                                                                      \
     {nullptr, K<1>, K<2>,  K<3>,  K<4>,  K<5>,  K<6>,  K<7>, K<8>,                                \
      K<9>,    K<10>, K<11>, K<12>, K<13>, K<14>, K<15>, K<16>}
@@ -152,6 +199,10 @@ struct moe_decode_ctx {
     moe_decode_dispatch_info last;
     hipEvent_t events[10];  // timing events (caller-owned), n_events = 0: off
     int32_t n_events;
+    int32_t mode;           // MOE_MODE_FUSED or MOE_MODE_FOUR_LAUNCHES
+    int32_t n_cus;          // compute units of the device
+    StepKernel occ_kernel;  // fused kernel whose occupancy is cached
+    int32_t occ_blocks;     // its resident workgroups per compute unit
 };
 
 struct moe_decode_graph {
@@ -209,6 +260,8 @@ StepArgs base_args(const moe_decode_ctx *ctx) {
     a.ashhl = (uint16_t *)(ws + l.ashhl);
     a.acthl = (uint16_t *)(ws + l.acthl);
     a.ylat = (float *)(ws + l.ylat);
+    a.ysh = (float *)(ws + l.ysh);
+    a.c13 = (uint32_t *)(ws + l.c13);
     return a;
 }
 
@@ -297,6 +350,10 @@ moe_status moe_decode_init(const moe_decode_config *cfg, const moe_decode_weight
     ctx->device = dev;
     ctx->last_hip = 0;
     ctx->n_events = 0;
+    ctx->mode = MOE_MODE_FOUR_LAUNCHES;
+    ctx->n_cus = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 1;
+    ctx->occ_kernel = nullptr;
+    ctx->occ_blocks = 1;
     std::memset(&ctx->last, 0, sizeof ctx->last);
 
     // Every counter starts at zero; the step returns them to zero itself.
@@ -323,7 +380,9 @@ moe_status moe_decode_step(moe_decode_ctx *ctx, const uint16_t *x, int32_t batch
         ((uintptr_t)topk_w & 3u))
         return MOE_ERR_INVALID_ARG;
     hipStream_t s = (hipStream_t)stream;
-    const Plan pl = make_plan(c, batch, top_k);
+    Plan pl = make_plan(c, batch, top_k, ctx->mode == MOE_MODE_FUSED);
+    const StepKernel fused = ctx->mode == MOE_MODE_FUSED ? fused_kernel(c, pl) : nullptr;
+    if (!fused) pl = make_plan(c, batch, top_k, false);
     StepArgs a = base_args(ctx);
     a.B = batch;
     a.k = top_k;
@@ -331,14 +390,16 @@ moe_status moe_decode_step(moe_decode_ctx *ctx, const uint16_t *x, int32_t batch
     a.out = out;
     a.user_idx = topk_idx;
     a.user_w = topk_w;
-    a.n_r16 = pl.n_r16;
+    a.n_rtiles = pl.n_rtiles;
     // Arrivals that complete the router: one per router unit of the dense
     // input kernel, or one per workgroup of the f32 router kernel.
-    a.router_target = c.router_dtype == MOE_ROUTER_BF16 ? pl.n_r16 * pl.ncg_in
+    a.router_target = c.router_dtype == MOE_ROUTER_BF16 ? pl.n_rtiles * pl.ncg_in
                                                         : cdiv(c.n_experts, kWavesPerBlock);
     a.kw_in = pl.in.kw;
     a.kw_out = pl.out.kw;
     a.out_rows = pl.out_rows;
+    a.router_rows = pl.router_rows;
+    a.latent_rows = pl.latent_rows;
     a.spc_in = pl.in.spc;
     a.spc_out = pl.out.spc;
     const long long cap = 65528;  // workgroups (a multiple of the XCD count); more units loop
@@ -356,7 +417,40 @@ moe_status moe_decode_step(moe_decode_ctx *ctx, const uint16_t *x, int32_t batch
     d.grid_w2 = grid_for(pl.units_2, cap);
     d.grid_out = grid_for(pl.units_out, cap);
     d.router_f32 = c.router_dtype == MOE_ROUTER_F32;
-    d.n_kernels = 4 + d.router_f32;
+    d.fused = fused != nullptr;
+    d.n_kernels = fused ? 1 : 4 + d.router_f32;
+    d.grid_step = 0;
+    if (fused) {
+        a.u_lat = pl.u_lat;
+        a.u_sh = pl.u_sh;
+        a.u_13 = pl.u_13;
+        a.u_sd = pl.u_sd;
+        a.u_2 = pl.u_2;
+        a.u_lu = pl.u_lu;
+        a.u_end = pl.u_end;
+        a.kw_sd = pl.sd.kw;
+        a.spc_sd = pl.sd.spc;
+        a.kw_lu = pl.lu.kw;
+        a.spc_lu = pl.lu.spc;
+        a.tg13 = pl.tg13;
+        a.tg2 = pl.tg2;
+        a.n_lat_units = pl.u_sh - pl.u_lat;
+        a.n_sh_units = pl.u_13 - pl.u_sh;
+        a.n_sd_units = pl.u_lu - pl.u_sd;
+        // One persistent workgroup per resident slot (the unit queue does
+        // not rely on residency; this only sizes the grid).
+        if (ctx->occ_kernel != fused) {
+            int blocks = 0;
+            if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, fused, kWGThreads, 0) !=
+                    hipSuccess ||
+                blocks < 1)
+                blocks = 1;
+            ctx->occ_kernel = fused;
+            ctx->occ_blocks = blocks;
+        }
+        d.grid_step = (int32_t)std::min<long long>(pl.u_end,
+                                                   (long long)ctx->occ_blocks * ctx->n_cus);
+    }
 
     const bool timed = ctx->n_events == 2 * d.n_kernels;
     int ki = 0;
@@ -368,6 +462,11 @@ moe_status moe_decode_step(moe_decode_ctx *ctx, const uint16_t *x, int32_t batch
             hipLaunchKernelGGL(kernel, dim3(grid), dim3(threads), 0, s, a);
         ++ki;
     };
+    if (fused) {
+        launch(fused, d.grid_step, kWGThreads);
+        const hipError_t e = hipGetLastError();
+        return e == hipSuccess ? MOE_OK : hip_fail(ctx, e);
+    }
     if (d.router_f32) launch(k_router_f32, cdiv(c.n_experts, kWavesPerBlock), kBlock);
     launch(k_dense_in, d.grid_in, kWGThreads);
     launch(kW13[pl.s13], d.grid_w13, kWGThreads);
@@ -455,13 +554,27 @@ moe_status moe_decode_set_timing_events(moe_decode_ctx *ctx, void *const *events
         ctx->n_events = 0;
         return MOE_OK;
     }
-    if (n != want || !events) return MOE_ERR_INVALID_ARG;
+    if ((n != want && n != 2) || !events) return MOE_ERR_INVALID_ARG;
     for (int i = 0; i < n; ++i) {
         if (!events[i]) return MOE_ERR_INVALID_ARG;
         ctx->events[i] = (hipEvent_t)events[i];
     }
     ctx->n_events = n;
     return MOE_OK;
+}
+
+moe_status moe_decode_set_mode(moe_decode_ctx *ctx, int32_t mode) {
+    if (!ctx || (mode != MOE_MODE_FUSED && mode != MOE_MODE_FOUR_LAUNCHES))
+        return MOE_ERR_INVALID_ARG;
+    ctx->mode = mode;
+    return MOE_OK;
+}
+
+moe_status moe_decode_read_flags(moe_decode_ctx *ctx, uint32_t *flags) {
+    if (!ctx || !flags) return MOE_ERR_INVALID_ARG;
+    const hipError_t e = hipMemcpy(flags, ctx->ws + ctx->lay.gctr + 4 * G_ERROR, 4,
+                                   hipMemcpyDeviceToHost);
+    return e == hipSuccess ? MOE_OK : hip_fail(ctx, e);
 }
 
 moe_status moe_decode_debug_export(moe_decode_ctx *ctx, int32_t batch, int32_t top_k,

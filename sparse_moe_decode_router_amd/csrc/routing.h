@@ -246,6 +246,8 @@ __device__ __forceinline__ void topk_token(const RouteArgs &a, int b, RouteLds &
 // routing weight.  A pair's place follows from the token mask of its expert
 // (the token's rank among the expert's tokens), so pairs are placed in
 // parallel; expert offsets come from a two-level scan (lanes, then waves).
+// Everything is written with agent-scope stores: in the fused step the
+// expert units of other workgroups read it within the same launch.
 __device__ __forceinline__ void build_meta(const RouteArgs &a, RouteLds &lds, int nw) {
     const int lane = lane_id(), wave = wave_index();
     const int tid = threadIdx.x, nt = nw * kWave;
@@ -288,13 +290,13 @@ __device__ __forceinline__ void build_meta(const RouteArgs &a, RouteLds &lds, in
         lds.off[e] = pi;
         lds.unit[e] = ci;
         if (!n) continue;
-        a.act_expert[ai] = e;
-        a.act_off[ai] = pi;
+        store_agent(a.act_expert + ai, e);
+        store_agent(a.act_off + ai, pi);
         for (int r = 0; r < n; r += 8, ++ci) {
             int32_t *rec = a.cu_rec + (size_t)ci * kRecWords;
-            rec[R_EXPERT] = e;
-            rec[R_COUNT] = min(8, n - r);
-            rec[R_PAIR0] = pi + r;
+            store_agent(rec + R_EXPERT, e);
+            store_agent(rec + R_COUNT, min(8, n - r));
+            store_agent(rec + R_PAIR0, pi + r);
         }
         ++ai;
         pi += n;
@@ -304,16 +306,16 @@ __device__ __forceinline__ void build_meta(const RouteArgs &a, RouteLds &lds, in
         const int e = lds.idx[p], b = p / k;
         const int r = __popcll(lds.mask[e] & ((1ull << b) - 1ull));
         const int pos = lds.off[e] + r;
-        a.pair_slot[pos] = p;
-        a.pair_of_slot[p] = pos;
+        store_agent(a.pair_slot + pos, p);
+        store_agent(a.pair_of_slot + p, pos);
         int32_t *rec = a.cu_rec + (size_t)(lds.unit[e] + (r >> 3)) * kRecWords;
-        rec[R_TOKEN + (r & 7)] = b;
-        rec[R_WEIGHT + (r & 7)] = __float_as_int(lds.w[p]);
+        store_agent(rec + R_TOKEN + (r & 7), b);
+        store_agent(rec + R_WEIGHT + (r & 7), __float_as_int(lds.w[p]));
     }
     if (tid == 0) {
-        a.meta[M_N_ACTIVE] = D;
-        a.meta[M_N_COLS] = NC;
-        a.act_off[D] = PT;
+        store_agent(a.meta + M_N_ACTIVE, D);
+        store_agent(a.meta + M_N_COLS, NC);
+        store_agent(a.act_off + D, PT);
     }
 }
 

@@ -14,12 +14,21 @@ struct StepArgs {
     int32_t Bm, km;           // capacities (context max_batch / max_top_k)
     // Launch plan: waves of a workgroup that split K in each kernel (the
     // rest of the 8 waves take further row groups).
-    int32_t n_r16;            // 16-row router tiles computed by the dense input kernel
+    int32_t n_rtiles;         // router tiles (router_rows rows each) of the dense-in units
     int32_t router_target;    // arrivals on G_ROUTER_DONE that complete the router
     int32_t kw_in, kw_out;
     int32_t spc_in, spc_out;  // 128-element steps per wave in the dense kernels
     int32_t ncols_cap;        // capacity of the expert column-unit list
     int32_t out_rows;         // rows per output tile (<= 16)
+    // Fused step: unit ranges [0, u_lat) router, [u_lat, u_sh) latent-down,
+    // [u_sh, u_13) shared gate/up, [u_13, u_2) gate/up, [u_2, u_sd) down,
+    // [u_sd, u_lu) shared-down, [u_lu, u_end) latent-up; K splits of the two
+    // output kinds; tile groups per column unit; unit counts waited for.
+    int32_t u_lat, u_sh, u_13, u_2, u_sd, u_lu, u_end;
+    int32_t router_rows, latent_rows;  // valid rows of router / latent-down tiles (<= 16)
+    int32_t kw_sd, spc_sd, kw_lu, spc_lu;
+    int32_t tg13, tg2;
+    int32_t n_lat_units, n_sh_units, n_sd_units;
     // Weights (borrowed).
     const uint16_t *router_w;
     const float *router_w32;
@@ -34,6 +43,7 @@ struct StepArgs {
     float *user_w;
     // Workspace.
     uint32_t *gctr;
+    uint32_t *c13;  // fused step: gate/up units done per column unit [ncols_cap], 256 B apart
     int32_t *meta;
     float *score, *key;
     int32_t *idx;
@@ -43,6 +53,7 @@ struct StepArgs {
     // ashhl [B][2][Is] (row 0: hi = bf16(v), row 1: lo = bf16(v - hi)).
     uint16_t *zhl, *acthl, *ashhl;
     float *ylat;  // f32 latent combine (atomic adds)
+    float *ysh;   // fused step: shared-down sums [B][H] f32
 };
 
 }  // namespace moe

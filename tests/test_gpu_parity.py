@@ -270,8 +270,46 @@ def test_dispatch_follows_the_batch(small_layer, small_ctx):
         x = synth.make_tokens(small_layer.dims, 14, B)
         run(small_ctx, x, 6)
         d = small_ctx.last_dispatch()
-        assert d["batch"] == B and d["col_tiles"] == cg and d["n_kernels"] == 4
-        assert d["grid_in"] >= 1 and d["grid_w13"] >= 1
+        assert d["batch"] == B and d["col_tiles"] == cg
+        assert d["fused"] == 0 and d["n_kernels"] == 4
+        assert d["grid_in"] >= 1 and d["grid_w13"] >= 1 and d["grid_step"] == 0
+    small_ctx.set_mode(binding.MODE_FUSED)
+    try:
+        run(small_ctx, synth.make_tokens(small_layer.dims, 14, 5), 6)
+        d = small_ctx.last_dispatch()
+        assert d["fused"] == 1 and d["n_kernels"] == 1 and d["grid_step"] >= 1
+    finally:
+        small_ctx.set_mode(binding.MODE_FOUR_LAUNCHES)
+
+
+@pytest.mark.parametrize("B", [1, 9, 33, 64])
+def test_four_launch_step_matches_fused(small_layer, B):
+    """The four-launch step and the fused step compute the same values (up to
+    the order of the latent combine's atomic adds); both against the oracle."""
+    k = 6
+    fused = make_ctx(small_layer, 64, 8)
+    fused.set_mode(binding.MODE_FUSED)
+    four = make_ctx(small_layer, 64, 8)
+    x = synth.make_tokens(small_layer.dims, 200 + B, B)
+    a = run(fused, x, k)
+    b = run(four, x, k)
+    assert fused.last_dispatch()["fused"] == 1 and four.last_dispatch()["fused"] == 0
+    assert_same_step(a, b)
+    check_step(small_layer, x, k, *b)
+
+
+def test_fused_step_other_shapes():
+    """Fused kernels of other chunk shapes: K3 latent with a short down row
+    (16, 2) is covered by the TP8 tests; here the (2, 2) shape of a small
+    layer, several steps in a row on one context."""
+    layer = synth.make_layer(small_recipe(k=4), 21)
+    ctx = make_ctx(layer, 16)
+    ctx.set_mode(binding.MODE_FUSED)
+    for B in (1, 7, 16):
+        x = synth.make_tokens(layer.dims, 21 + B, B)
+        out, idx, w = run(ctx, x, 4)
+        assert ctx.last_dispatch()["fused"] == 1
+        check_step(layer, x, 4, out, idx, w)
 
 
 # ---------------------------------------------------------------------------
@@ -320,6 +358,20 @@ def test_k3_layer(k3_layer, k3_dev, bias_kind, B, sample):
     log("  ", r, "distinct experts", len(np.unique(idx)))
 
 
+@pytest.mark.parametrize("bias_kind,B", [("normal", 1), ("zipf", 8), ("normal", 64)])
+def test_k3_fused_step_matches_four_launches(k3_dev, bias_kind, B):
+    """The persistent fused step on the K3 layer (chunk shape 16x16) gives
+    the four-launch step's values."""
+    four, _ = k3_ctx(k3_dev, bias_kind, 64)
+    fused, _ = k3_ctx(k3_dev, bias_kind, 64)
+    fused.set_mode(binding.MODE_FUSED)
+    x = synth.make_tokens(k3_dev.dims, 5, B)
+    a = run(four, x, 16)
+    b = run(fused, x, 16)
+    assert fused.last_dispatch()["fused"] == 1 and four.last_dispatch()["fused"] == 0
+    assert_same_step(a, b)
+
+
 def test_k3_tp8_share_layer():
     layer = synth.make_layer(synth.K3_TP8, synth.TP8_STACK_SEED0)
     ctx = make_ctx(layer, 64, 16)
@@ -331,7 +383,8 @@ def test_k3_tp8_share_layer():
         log("  ", r)
 
 
-def test_c4_eight_layer_graph():
+@pytest.mark.parametrize("mode", ["four_launches", "fused"])
+def test_c4_eight_layer_graph(mode):
     """Eight TP8-share layers (own seeds and inputs) captured in one HIP graph,
     the configuration the stacked benchmark replays: every layer's replayed
     result equals its eager step, and the first and last layers match the
@@ -340,6 +393,8 @@ def test_c4_eight_layer_graph():
     n_layers, B, k = 8, 4, 16
     layers = [synth.make_layer(synth.K3_TP8, synth.TP8_STACK_SEED0 + l) for l in range(n_layers)]
     ctxs = [make_ctx(la, B, k) for la in layers]
+    for c in ctxs:
+        c.set_mode(binding.MODE_FUSED if mode == "fused" else binding.MODE_FOUR_LAUNCHES)
     xs = [synth.make_tokens(la.dims, synth.TP8_STACK_SEED0 + l, B) for l, la in enumerate(layers)]
     xd = [to_dev_tokens(x) for x in xs]
     H = layers[0].dims.hidden
