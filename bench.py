@@ -11,19 +11,20 @@ Prints ONE JSON line:
   value        whole-step algorithmic HBM bytes / time (GB/s)
   ms_per_step  time per layer step (graph replays, K steps between two
                synchronisations); p10/p50/p90 from events between replays
-  roofline     the kernel with the largest time of the four launches, its
-               algorithmic bytes per launch over its average duration (HIP
-               events attached to each kernel's dispatch on eager steps),
-               against 8 TB/s
-  expert_path  k_w13 + k_w2: the routed-expert kernels alone
-  fused        the same inputs run as one persistent launch (opt-in mode)
+  roofline     the kernel with the largest time of the library's default
+               mode, its algorithmic bytes per launch over its average
+               duration (HIP events attached to each kernel's dispatch on
+               eager steps), against 8 TB/s
+  expert_path  k_w13 + k_w2 of the four-launch step: the routed-expert
+               kernels alone
+  modes        the same inputs in every execution mode (four launches, dense-in
+               + one persistent launch, one persistent launch)
   cpu_baseline the binary64 CPU oracle on a bounded sample of the same inputs
   batch_sweep  the same K3 weights at batch 2, 8 (Zipf routing), 64
                (near-uniform routing) and 64 (the batch-1 bias)
 With --workload c4_x8: eight TP8-share layers in one graph, batch 1..64.
 """
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -47,7 +48,19 @@ WORKLOADS = {
 }
 KERNELS_BF16 = ("dense_in", "w13", "w2", "out")
 KERNEL_SYMBOLS = {"dense_in": "k_dense_in", "w13": "k_w13", "w2": "k_w2", "out": "k_out",
-                  "router_f32": "k_router_f32", "step": "k_step"}
+                  "router_f32": "k_router_f32", "step": "k_step", "tail": "k_tail"}
+
+
+def modes():
+    """Execution modes of the library by name."""
+    from sparse_moe_decode_router_amd import binding
+    return {"four_launches": binding.MODE_FOUR_LAUNCHES,
+            "two_launches": binding.MODE_TWO_LAUNCHES, "fused": binding.MODE_FUSED}
+
+
+def default_mode():
+    from sparse_moe_decode_router_amd import binding
+    return {v: n for n, v in modes().items()}[binding.DEFAULT_MODE]
 
 
 def log(*a):
@@ -76,16 +89,6 @@ def kernel_bytes(d, B, k, D):
     return b
 
 
-def source_digest():
-    h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "sparse_moe_decode_router_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode())
-            h.update(f.read())
-    return h.hexdigest()[:16]
-
-
 def load_traffic(kernel, workload):
     """HBM bytes per launch measured with rocprofv3 counters for this kernel
     source, from profiles/traffic.json; None when absent or stale."""
@@ -94,6 +97,7 @@ def load_traffic(kernel, workload):
         return None
     with open(path) as f:
         t = json.load(f)
+    from sparse_moe_decode_router_amd.build import source_digest
     e = t.get(workload, {}).get(kernel)
     if not e or e.get("source_digest") != source_digest():
         return None
@@ -150,9 +154,15 @@ def measure(dev, d, B, k, xs, steps, warmup, mode):
         Ds.append(int(np.unique(idx.cpu().numpy()).size))
     disp = ctx.last_dispatch()
     fused = bool(disp["fused"])
-    if fused:
+    if disp["fused"] == 1:
         names = ("step",)
         kb = [{"step": sum(kernel_bytes(d, B, k, D).values())} for D in Ds]
+    elif disp["fused"] == 2:
+        names = ("dense_in", "tail")
+        kb = []
+        for D in Ds:
+            b = kernel_bytes(d, B, k, D)
+            kb.append({"dense_in": b["dense_in"], "tail": b["w13"] + b["w2"] + b["out"]})
     else:
         names = (("router_f32",) if d.router_f32 else ()) + KERNELS_BF16
         kb = [kernel_bytes(d, B, k, D) for D in Ds]
@@ -251,16 +261,16 @@ def measure(dev, d, B, k, xs, steps, warmup, mode):
     }
 
 
-def summary(name, B, m, mf):
-    """Four-launch figures of one configuration, with the persistent fused
-    step's time beside them."""
+def summary(name, B, m, alt):
+    """Figures of one configuration in the default mode, with every mode's
+    time per step beside them."""
     return {"workload": name, "batch": B, "us_per_step": round(m["ms"] * 1e3, 2),
             "us_p10": round(m["us_p10"], 2), "us_p50": round(m["us_p50"], 2),
             "us_p90": round(m["us_p90"], 2), "tokens_per_s": round(B / (m["ms"] * 1e-3), 1),
             "gbs": round(m["value"], 1), "pct_hbm_peak": round(100 * m["value"] / HBM_PEAK_GBS, 2),
             "distinct_experts_mean": round(sum(m["Ds"]) / len(m["Ds"]), 1),
-            "expert_path": m["expert_path"],
-            "fused_us_per_step": round(mf["ms"] * 1e3, 2)}
+            "expert_path": alt["four_launches"]["expert_path"],
+            "us_per_step_by_mode": {n: round(x["ms"] * 1e3, 2) for n, x in alt.items()}}
 
 
 # Batch sweep on the K3 layer's weights (the bias alone changes): name ->
@@ -315,19 +325,21 @@ def run_c4(args):
         step_bytes = [sum(sum(kernel_bytes(d, B, k, D).values()) for D in ds) for ds in Ds]
         ms = replay_ms(graphs, R)
         mean_bytes = sum(step_bytes[i % R] for i in range(args.steps)) / args.steps
-        for g in graphs:
-            g.close()
-        for c in ctxs:
-            c.set_mode(binding.MODE_FUSED)
-        graphs = [binding.Graph(ctxs, xd[r], B, k, outs, idxs, wts) for r in range(R)]
-        msf = replay_ms(graphs, R)
-        assert all(c.read_flags() == 0 for c in ctxs), "a bounded wait of the fused step ran out"
+        by_mode = {}
+        for name, mode in modes().items():
+            for g in graphs:
+                g.close()
+            for c in ctxs:
+                c.set_mode(mode)
+            graphs = [binding.Graph(ctxs, xd[r], B, k, outs, idxs, wts) for r in range(R)]
+            by_mode[name] = round(replay_ms(graphs, R) * 1e3 / n_layers, 2)
+        assert all(c.read_flags() == 0 for c in ctxs), "a bounded wait of a persistent step ran out"
         results.append({"batch": B, "us_per_8_layers": round(ms * 1e3, 2),
                         "us_per_layer": round(ms * 1e3 / n_layers, 2),
                         "tokens_per_s": round(B / (ms * 1e-3), 1),
                         "gbs": round(mean_bytes / (ms * 1e-3) / 1e9, 1),
                         "distinct_experts_mean": round(float(np.mean(Ds)), 1),
-                        "fused_us_per_layer": round(msf * 1e3 / n_layers, 2)})
+                        "us_per_layer_by_mode": by_mode})
         log(f"[bench] C4 B={B}: {results[-1]}")
         for g in graphs:
             g.close()
@@ -387,26 +399,28 @@ def main():
     dev = binding.DeviceLayer(layer)
     xs = [synth.make_tokens(d, seed, B, draw=r) for r in range(args.rotate)]
     log(f"[bench] timing {args.workload}: {args.steps} steps")
-    m = measure(dev, d, B, k, xs, args.steps, args.warmup, binding.MODE_FOUR_LAUNCHES)
+    alt = {}
+    for name, mode in modes().items():
+        log(f"[bench] mode {name}")
+        alt[name] = measure(dev, d, B, k, xs, args.steps, args.warmup, mode)
+    m = alt[default_mode()]
     log(f"[bench] distinct experts per input {m['Ds']}; dispatch {m['dispatch']}")
-    log("[bench] the same inputs as one persistent launch")
-    mf = measure(dev, d, B, k, xs, args.steps, args.warmup, binding.MODE_FUSED)
     per_kernel = m["per_kernel"]
     dom = max(m["names"], key=lambda n: per_kernel[n]["us"])
     pk = per_kernel[dom]
 
     sweep = None
     if not args.no_sweep and recipe_name == "k3" and B == 1:
-        sweep = [summary(args.workload, B, m, mf)]
+        sweep = [summary(args.workload, B, m, alt)]
         for name, bias_recipe, Bs in SWEEP:
             bias = synth.make_bias(synth.RECIPES[bias_recipe], 0)
             xs_s = [synth.make_tokens(d, 0, Bs, draw=r) for r in range(args.rotate)]
             n_s = max(50, args.steps // 2)
             log(f"[bench] sweep {name}")
             dvb = dev.with_bias(bias)
-            ms_ = measure(dvb, d, Bs, k, xs_s, n_s, args.warmup, binding.MODE_FOUR_LAUNCHES)
-            msf = measure(dvb, d, Bs, k, xs_s, n_s, args.warmup, binding.MODE_FUSED)
-            sweep.append(summary(name, Bs, ms_, msf))
+            alt_s = {n: measure(dvb, d, Bs, k, xs_s, n_s, args.warmup, mode)
+                     for n, mode in modes().items()}
+            sweep.append(summary(name, Bs, alt_s[default_mode()], alt_s))
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -430,11 +444,12 @@ def main():
         "tokens_per_s": round(B / (ms * 1e-3), 1),
         "pct_hbm_peak": round(100 * m["value"] / HBM_PEAK_GBS, 2),
         "distinct_experts": m["Ds"],
-        "expert_path": m["expert_path"],
+        "mode": default_mode(),
+        "expert_path": alt["four_launches"]["expert_path"],
         "kernels": per_kernel,
         "ms_per_step_eager": round(m["ms_eager"], 5),
-        "fused": {"us_per_step": round(mf["ms"] * 1e3, 2),
-                  "gbs": round(mf["value"], 1), "kernels": mf["per_kernel"]},
+        "modes": {n: {"us_per_step": round(x["ms"] * 1e3, 2), "gbs": round(x["value"], 1),
+                      "kernels": x["per_kernel"]} for n, x in alt.items()},
         "roofline": {"bound": "hbm", "kernel": pk["symbol"], "achieved": pk["gbs"],
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": pk["frac"],
                      "traffic": load_traffic(pk["symbol"], args.workload)},

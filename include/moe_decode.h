@@ -172,27 +172,30 @@ typedef struct {
     int32_t split_in;      /* waves of a workgroup splitting K: router / latent-down / shared gate-up */
     int32_t split_out;     /* ... latent-up + shared-down */
     int32_t split_w13;     /* ... expert gate/up */
-    int32_t split_w2;      /* ... expert down */
+    int32_t split_w2;      /* ... expert down (waves per tile) */
     int32_t grid_in, grid_w13, grid_w2, grid_out; /* workgroups launched */
     int32_t router_f32;    /* 1 when the f32 router kernel ran */
     int32_t n_kernels;     /* kernels launched by the step */
-    int32_t fused;         /* 1 when the step ran as the one persistent kernel */
-    int32_t grid_step;     /* its workgroups (0 for the four-launch step) */
+    int32_t fused;         /* 1: one persistent launch; 2: dense-in + persistent launch;
+                              0: four launches */
+    int32_t grid_step;     /* workgroups of the persistent launch (0 for four launches) */
 } moe_decode_dispatch_info;
 moe_status moe_decode_last_dispatch(const moe_decode_ctx *ctx, moe_decode_dispatch_info *info);
 
 /* Execution mode of a context's later steps.
  *   MOE_MODE_FOUR_LAUNCHES (the default): dense-in, expert gate/up, expert
  *     down, output;
- *   MOE_MODE_FUSED: one persistent launch whose workgroups take
- *     the step's units (router, latent, shared and expert tiles) from a queue
- *     in dependency order and wait on completion counters instead of kernel
- *     boundaries, the single-launch design of [P-NV] "一个工程师、1.2万行代码、
- *     AI辅助开发"; shapes without a built fused kernel (the f32 router, other
- *     expert chunk shapes) run the four launches.
- * Both compute the same values.  Returns MOE_ERR_INVALID_ARG for another
- * mode.  Host-only. */
-enum { MOE_MODE_FUSED = 0, MOE_MODE_FOUR_LAUNCHES = 1 };
+ *   MOE_MODE_TWO_LAUNCHES: the dense-in launch, then one persistent launch
+ *     whose workgroups take the expert gate/up, shared-down, expert down and
+ *     latent-up units from a queue in dependency order and wait on completion
+ *     counters instead of kernel boundaries;
+ *   MOE_MODE_FUSED: the whole step as one persistent launch of that kind
+ *     (router, latent and shared units too), the single-launch design of
+ *     [P-NV] "一个工程师、1.2万行代码、AI辅助开发".
+ * Shapes without a built persistent kernel (the f32 router, other expert
+ * chunk shapes) run the four launches.  All modes compute the same values.
+ * Returns MOE_ERR_INVALID_ARG for another mode.  Host-only. */
+enum { MOE_MODE_FUSED = 0, MOE_MODE_FOUR_LAUNCHES = 1, MOE_MODE_TWO_LAUNCHES = 2 };
 moe_status moe_decode_set_mode(moe_decode_ctx *ctx, int32_t mode);
 
 /* Reads the context's sticky fault flags into *flags (synchronous copy from
@@ -207,8 +210,9 @@ moe_status moe_decode_read_flags(moe_decode_ctx *ctx, uint32_t *flags);
  * attached to its dispatch (hipExtLaunchKernel), so that their elapsed time is
  * the kernel's own execution time, as a kernel trace reports it.  n = 0
  * (events may be NULL) switches timing off.  Returns MOE_ERR_INVALID_ARG when
- * n fits neither the four-launch step (8, or 10 with the f32 router) nor the
- * fused step (2); a step whose kernel count differs from n is not timed. */
+ * n fits none of the step's forms (8, or 10 with the f32 router, for four
+ * launches; 4 for two launches; 2 for one); a step whose kernel count differs
+ * from n is not timed. */
 moe_status moe_decode_set_timing_events(moe_decode_ctx *ctx, void *const *events, int32_t n);
 
 /* Copies the intermediates of the last step out of the workspace as f32

@@ -45,7 +45,8 @@ class Debug(ctypes.Structure):
                 ("score", "key", "z", "act", "ylat", "ash", "n_active")]
 
 
-MODE_FUSED, MODE_FOUR_LAUNCHES = 0, 1
+MODE_FUSED, MODE_FOUR_LAUNCHES, MODE_TWO_LAUNCHES = 0, 1, 2
+DEFAULT_MODE = MODE_FOUR_LAUNCHES  # what moe_decode_init selects
 
 EXPORTED = ("moe_decode_validate_config", "moe_decode_workspace_size", "moe_decode_init",
             "moe_decode_step", "moe_decode_destroy", "moe_decode_status_string",

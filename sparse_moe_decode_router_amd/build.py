@@ -4,6 +4,7 @@ One translation unit (``csrc/moe_decode.hip``) holds the kernels and the C ABI
 declared in ``include/moe_decode.h``.  Packed-f32 instruction selection is
 switched off for the device code.
 """
+import hashlib
 import os
 import subprocess
 import sys
@@ -31,6 +32,18 @@ def build(verbose: bool = False, extra=()) -> str:
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIB)
     return LIB
+
+
+def source_digest() -> str:
+    """Digest of the device sources: ties a stored hardware-counter reading
+    to the kernels it was taken on."""
+    h = hashlib.sha256()
+    csrc = os.path.join(HERE, "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 if __name__ == "__main__":

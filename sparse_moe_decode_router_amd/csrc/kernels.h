@@ -30,15 +30,18 @@
 // split while it is loaded); hi and lo occupy two adjacent columns of
 // the same MFMA (8 tokens per column group) and the two column sums are added
 // afterwards, which keeps f32-grade precision at one MFMA per K slice.  Data
-// one unit hands to another (scores, keys, z, a, ash, the shared-down sums,
-// the expert records) is written with agent-scope stores and read with
-// coherent (sc1) loads, so that it is visible across XCDs without cache
-// maintenance.
+// one unit hands to another within one launch (scores, keys; in the
+// persistent kernels also z, a, ash, the shared-down sums and the expert
+// records) is written with agent-scope stores and read with coherent (sc1)
+// loads, so that it is visible across XCDs without cache maintenance; data
+// crossing a kernel boundary uses plain accesses.
 //
-// K layout within one 128-element step: lane group g = lane/16 owns the 32
-// consecutive elements [32g, 32g+32) of the step, one MX block for MXFP4 rows
-// (16 code bytes, one scale byte), and feeds them to four MFMAs of 8 elements
-// each; the activation operand is read with the same layout, so the
+// K layout within one 128-element step.  MXFP4 rows: lane group g = lane/16
+// owns the 32 consecutive elements [32g, 32g+32) of the step, one MX block
+// (16 code bytes, one scale byte), and feeds them to four MFMAs of 8
+// elements each.  bf16 rows: MFMA j takes elements [32j + 8g, 32j + 8g + 8)
+// from lane group g, so each load instruction reads 64 contiguous bytes of a
+// row.  The activation operand is read with the layout of its weights, so the
 // permutation of K cancels in the dot product.
 #pragma once
 
@@ -64,7 +67,7 @@ __device__ __forceinline__ void load_cols_bf16(const uint16_t *X, bool valid, in
     const uint16_t *p = X + (size_t)s * kKStep;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        const u32x4 v = ld16(p + 8 * j);
+        const u32x4 v = ld16(p + 32 * j);
         rb[j] = valid ? v : (u32x4){0u, 0u, 0u, 0u};
     }
 }
@@ -79,7 +82,7 @@ __device__ __forceinline__ uint32_t pack_part(float a, float b, int part) {
 
 // Column operands an earlier unit wrote, read through a buffer resource
 // (Coh: coherent loads, the writer being a unit of the same launch): `off` is
-// the byte offset of the lane's row plus its 32-element slot.  bf16 rows (hi
+// the byte offset of the lane's row plus its first element 8g.  bf16 rows (hi
 // or lo) as they are; f32 values split into the lane's half.
 template <bool Coh>
 __device__ __forceinline__ void buf_cols_bf16(rsrc_t r, uint32_t off, bool valid, int s,
@@ -87,7 +90,7 @@ __device__ __forceinline__ void buf_cols_bf16(rsrc_t r, uint32_t off, bool valid
     const uint32_t o = off + (uint32_t)s * kKStep * 2;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        const u32x4 v = buf_ld16<Coh>(r, o + 16 * j);
+        const u32x4 v = buf_ld16<Coh>(r, o + 64 * j);
         rb[j] = valid ? v : (u32x4){0u, 0u, 0u, 0u};
     }
 }
@@ -98,7 +101,7 @@ __device__ __forceinline__ void buf_cols_f32(rsrc_t r, uint32_t off, bool valid,
     const uint32_t o = off + (uint32_t)s * kKStep * 4;
     f32x4 v[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = __builtin_bit_cast(f32x4, buf_ld16<Coh>(r, o + 16 * j));
+    for (int j = 0; j < 8; ++j) v[j] = __builtin_bit_cast(f32x4, buf_ld16<Coh>(r, o + 128 * (j >> 1) + 16 * (j & 1)));
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const f32x4 a = v[2 * j], b = v[2 * j + 1];
@@ -118,12 +121,12 @@ __device__ __forceinline__ void buf_cols_f32(rsrc_t r, uint32_t off, bool valid,
 // step and serialises several memory round trips per step.
 __device__ __forceinline__ void fence_schedule() { __builtin_amdgcn_sched_barrier(0); }
 
-// One 16-row bf16 tile: lane (r = l%16, g = l/16) loads row r's 64 bytes at
-// elements [32g, 32g+32) of step s.
+// One 16-row bf16 tile: lane (r = l%16, g = l/16) loads row r's elements
+// [32j + 8g, 32j + 8g + 8) of step s for MFMA j (A points at element 8g).
 __device__ __forceinline__ void load_tile_bf16(const uint16_t *A, int s, u32x4 (&ra)[4]) {
     const uint16_t *p = A + (size_t)s * kKStep;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) ra[j] = ld_weight16(p + 8 * j);
+    for (int j = 0; j < 4; ++j) ra[j] = ld_weight16(p + 32 * j);
 }
 
 __device__ __forceinline__ void mfma_tile(const u32x4 (&ra)[4], const u32x4 (&rb)[4], f32x4 &acc) {
@@ -160,10 +163,10 @@ __device__ __forceinline__ void dense_chunk_x(const uint16_t *A, const uint16_t 
 // hi/lo while loading), the rest against sh_w2 and the shared activation
 // (hi/lo bf16 rows).
 struct TwoSource {
-    const uint16_t *Aa;  // lane's lat_up row + its 32-element slot
-    const uint16_t *Ab;  // lane's sh_w2 row + slot
+    const uint16_t *Aa;  // lane's lat_up row + its first element 8g
+    const uint16_t *Ab;  // lane's sh_w2 row + 8g
     rsrc_t Ra, Rb;       // ylat, ashhl
-    uint32_t Oa, Ob;     // byte offsets of the lane's column row + slot
+    uint32_t Oa, Ob;     // byte offsets of the lane's column row + 8g
     int Ls;              // steps against the first source
 };
 
@@ -284,9 +287,9 @@ __device__ __forceinline__ void dense_in_tile(const StepArgs &a, const Role &ro,
         A = a.sh_w13 + (size_t)((n < 8 ? 0 : a.Is) + 8 * tt + (n & 7)) * a.H;
     const int b = 16 * cg + n;
     const bool valid = b < a.B;
-    const uint16_t *X = a.x + (size_t)(valid ? b : 0) * a.H + 32 * g;
+    const uint16_t *X = a.x + (size_t)(valid ? b : 0) * a.H + 8 * g;
     f32x4 acc = zero4();
-    if (active) dense_chunk_x(A + 32 * g, X, valid, ro.kw * a.spc_in, (ro.kw + 1) * a.spc_in, acc);
+    if (active) dense_chunk_x(A + 8 * g, X, valid, ro.kw * a.spc_in, (ro.kw + 1) * a.spc_in, acc);
     const bool leader = reduce_k1(s_red, ro.wave, ro.kw, ro.KW, acc);
     if (leader && active) {
         if (kind == KIND_ROUTER) {
@@ -442,19 +445,21 @@ __device__ __forceinline__ void staged_barrier() {
 
 // The MFMAs of one chunk; the activation operand of step s + 1 is read from
 // LDS while step s multiplies.  The compiler waits for each step's weight
-// registers just before their first use.
-template <int S>
+// registers just before their first use.  The wave's S steps are steps
+// s_off .. s_off + S - 1 of the staged operand (SS steps per row).
+template <int S, int SS = S>
 __device__ __forceinline__ void mfma_fp4_chunk(const Fp4Chunk<S> &w, const uint16_t *s_b,
-                                               int n_eff, int g, f32x4 &acc) {
+                                               int n_eff, int g, int s_off, f32x4 &acc) {
     const int sh = 8 * g;
     bf16x8 b[2][4];
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) b[0][jj] = stage_read<S>(s_b, n_eff, g, 0, jj);
+    for (int jj = 0; jj < 4; ++jj) b[0][jj] = stage_read<SS>(s_b, n_eff, g, s_off, jj);
 #pragma unroll
     for (int s = 0; s < S; ++s) {
         if (s + 1 < S) {
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) b[(s + 1) & 1][jj] = stage_read<S>(s_b, n_eff, g, s + 1, jj);
+            for (int jj = 0; jj < 4; ++jj)
+                b[(s + 1) & 1][jj] = stage_read<SS>(s_b, n_eff, g, s_off + s + 1, jj);
         }
         const float f = e8m0_scale((w.scale[s] >> sh) & 0xFFu);
 #pragma unroll
@@ -467,8 +472,8 @@ __device__ __forceinline__ void mfma_fp4_chunk(const Fp4Chunk<S> &w, const uint1
 // ---------------------------------------------------------------------------
 
 // Reads unit c's record: each lane l < 32 holds word l (its lanes 32..63 a
-// copy); returns the expert, pair count and first pair as scalars.  Coh: the
-// records were written by a unit of the same launch.
+// copy); returns the expert, pair count and first pair as scalars.  Coh: with
+// an agent-scope load (records written by a unit of the same launch).
 template <bool Coh>
 __device__ __forceinline__ int read_record(const StepArgs &a, int c, int &e, int &nt, int &p0) {
     const int *p = a.cu_rec + (size_t)c * kRecWords + (lane_id() & 31);
@@ -487,8 +492,10 @@ __device__ __forceinline__ int read_record(const StepArgs &a, int c, int &e, int
 // 8t .. 8t+7 (MFMA rows 0-7) and up rows I + 8t .. I + 8t + 7 (MFMA rows
 // 8-15), so lanes l and l + 32 hold a gate and its up value.  Output: the
 // activation of each pair as hi/lo bf16 rows.  `reuse`: s_b may still be read
-// by a wave (a barrier comes first).
-template <int S, bool Coh>
+// by a wave (a barrier comes first).  CohIn: the record and z rows come from
+// units of the same launch; CohOut: the activation rows go to units of the
+// same launch (agent-scope stores).
+template <int S, bool CohIn, bool CohOut>
 __device__ __forceinline__ void w13_unit(const StepArgs &a, int c, int tg, uint16_t *s_b,
                                          bool &reuse) {
     const int lane = lane_id(), n = lane & 15, g = lane >> 4, wave = wave_index();
@@ -499,7 +506,7 @@ __device__ __forceinline__ void w13_unit(const StepArgs &a, int c, int tg, uint1
     const int t = tg * kWG + wave;
     const bool active = t < OT;
     int e, nt, p0;
-    const int recw = read_record<Coh>(a, c, e, nt, p0);
+    const int recw = read_record<CohIn>(a, c, e, nt, p0);
     const int n_eff = j < nt ? n : part;
     const size_t r = (size_t)e * 2 * a.I + (n < 8 ? 0 : a.I) + 8 * (active ? t : 0) + (n & 7);
     const uint8_t *qp = a.w13_q + r * qrow + 16 * g;
@@ -516,7 +523,7 @@ __device__ __forceinline__ void w13_unit(const StepArgs &a, int c, int tg, uint1
         Fp4Chunk<S> w;
         if constexpr (S % 4 != 0) load_fp4_scales<S>(sp + (size_t)ch * S * 4, w);
         fence_schedule();
-        stage_operand<S, Coh>(s_b, a.zhl, a.L, ch * S * kKStep, nt,
+        stage_operand<S, CohIn>(s_b, a.zhl, a.L, ch * S * kKStep, nt,
                          [&](int jj) { return __shfl(recw, R_TOKEN + jj); });
         fence_schedule();
         if constexpr (S % 4 == 0) load_fp4_scales<S>(sp + (size_t)ch * S * 4, w);
@@ -524,7 +531,7 @@ __device__ __forceinline__ void w13_unit(const StepArgs &a, int c, int tg, uint1
         fence_schedule();
         wait_staging<S>();
         staged_barrier();
-        mfma_fp4_chunk<S>(w, s_b, n_eff, g, acc);
+        mfma_fp4_chunk<S>(w, s_b, n_eff, g, 0, acc);
     }
     acc = add_pair_column(acc);
     f32x4 up;
@@ -535,22 +542,26 @@ __device__ __forceinline__ void w13_unit(const StepArgs &a, int c, int tg, uint1
 #pragma unroll
         for (int i = 0; i < 4; ++i) v[i] = silu_mul(acc[i], up[i]);
         uint16_t *dst = a.acthl + (size_t)(p0 + j) * 2 * a.I + 8 * t + 4 * g;
-        store_hl4<Coh>(dst, dst + a.I, v);
+        store_hl4<CohOut>(dst, dst + a.I, v);
     }
 }
 
 // Down unit: column unit c, tile group tg.  Tile t of expert e: latent rows
 // 16t .. 16t+15; the routing weight of each pair scales its column before the
-// f32 atomic add into ylat.
-template <int S, bool Coh>
+// f32 atomic add into ylat.  Coh: the record and activation rows come from
+// units of the same launch.  KS: waves per tile (8 / KS tiles per unit), each
+// taking S / KS steps of every chunk and adding its own partial sums.
+template <int S, bool Coh, int KS = 1>
 __device__ __forceinline__ void w2_unit(const StepArgs &a, int c, int tg, uint16_t *s_b,
                                         bool &reuse) {
+    static_assert(S % KS == 0, "steps per wave");
+    constexpr int SW = S / KS;
     const int lane = lane_id(), n = lane & 15, g = lane >> 4, wave = wave_index();
     const int j = n >> 1, part = n & 1;
     const int OT = a.L >> 4;
     const int nchunk = a.I / (kKStep * S);
     const size_t qrow = a.I / 2, srow = a.I / 32;
-    const int t = tg * kWG + wave;
+    const int t = tg * (kWG / KS) + wave / KS, kh = wave % KS;
     const bool active = t < OT;
     int e, nt, p0;
     const int recw = read_record<Coh>(a, c, e, nt, p0);
@@ -566,18 +577,19 @@ __device__ __forceinline__ void w2_unit(const StepArgs &a, int c, int tg, uint16
         // As in w13_unit.
         if (reuse) __syncthreads();
         reuse = true;
-        Fp4Chunk<S> w;
-        if constexpr (S % 4 != 0) load_fp4_scales<S>(sp + (size_t)ch * S * 4, w);
+        Fp4Chunk<SW> w;
+        const size_t s0 = (size_t)ch * S + kh * SW;  // the wave's first step
+        if constexpr (SW % 4 != 0) load_fp4_scales<SW>(sp + s0 * 4, w);
         fence_schedule();
         stage_operand<S, Coh>(s_b, a.acthl, a.I, ch * S * kKStep, nt,
                          [&](int jj) { return p0 + jj; });
         fence_schedule();
-        if constexpr (S % 4 == 0) load_fp4_scales<S>(sp + (size_t)ch * S * 4, w);
-        load_fp4_codes<S>(qp + (size_t)ch * S * 64, w);
+        if constexpr (SW % 4 == 0) load_fp4_scales<SW>(sp + s0 * 4, w);
+        load_fp4_codes<SW>(qp + s0 * 64, w);
         fence_schedule();
-        wait_staging<S>();
+        wait_staging<SW>();
         staged_barrier();
-        mfma_fp4_chunk<S>(w, s_b, n_eff, g, acc);
+        mfma_fp4_chunk<SW, S>(w, s_b, n_eff, g, kh * SW, acc);
     }
     acc = add_pair_column(acc);
     if (active && j < nt && part == 0) {
@@ -611,12 +623,12 @@ __device__ __forceinline__ void out_tile(const StepArgs &a, const Role &ro, int 
     const int h0 = RT * (active ? t : 0);
     const size_t h = min(h0 + min(n, RT - 1), a.H - 1);
     TwoSource ts;
-    ts.Aa = a.lat_up + h * a.L + 32 * g;
-    ts.Ab = a.sh_w2 + h * a.Is + 32 * g;
+    ts.Aa = a.lat_up + h * a.L + 8 * g;
+    ts.Ab = a.sh_w2 + h * a.Is + 8 * g;
     ts.Ra = buf_rsrc(a.ylat);
     ts.Rb = buf_rsrc(a.ashhl);
-    ts.Oa = (uint32_t)(((size_t)bb * a.L + 32 * g) * 4);
-    ts.Ob = (uint32_t)((((size_t)bb * 2 + part) * a.Is + 32 * g) * 2);
+    ts.Oa = (uint32_t)(((size_t)bb * a.L + 8 * g) * 4);
+    ts.Ob = (uint32_t)((((size_t)bb * 2 + part) * a.Is + 8 * g) * 2);
     ts.Ls = mode == OUT_SHARED ? 0 : a.L / kKStep;
     f32x4 acc = zero4();
     if (active) dense_chunk_out<Coh>(ts, valid, part, ro.kw * spc, (ro.kw + 1) * spc, acc);
@@ -719,18 +731,19 @@ k_w13(const StepArgs a) {
     const int NC = min(load_agent(a.meta + M_N_COLS), a.ncols_cap);  // never beyond the records
     const int TG = ((a.I >> 3) + kWG - 1) / kWG;
     bool reuse = false;
-    for (int u = blockIdx.x; u < NC * TG; u += gridDim.x) w13_unit<S, false>(a, u / TG, u % TG, s_b, reuse);
+    for (int u = blockIdx.x; u < NC * TG; u += gridDim.x) w13_unit<S, false, false>(a, u / TG, u % TG, s_b, reuse);
 }
 
-// Kernel 3: down units.
-template <int S>
+// Kernel 3: down units (KS waves per tile).
+template <int S, int KS>
 __global__ void __launch_bounds__(kWGThreads) __attribute__((amdgpu_waves_per_eu(4)))
 k_w2(const StepArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t s_b[8 * Stage<S>::kChunks];
     const int NC = min(load_agent(a.meta + M_N_COLS), a.ncols_cap);
-    const int TG = ((a.L >> 4) + kWG - 1) / kWG;
+    const int TG = ((a.L >> 4) + kWG / KS - 1) / (kWG / KS);
     bool reuse = false;
-    for (int u = blockIdx.x; u < NC * TG; u += gridDim.x) w2_unit<S, false>(a, u / TG, u % TG, s_b, reuse);
+    for (int u = blockIdx.x; u < NC * TG; u += gridDim.x)
+        w2_unit<S, false, KS>(a, u / TG, u % TG, s_b, reuse);
 }
 
 // Kernel 4: output units (latent-up and shared-down in one pass).
@@ -866,7 +879,7 @@ k_step(const StepArgs a) {
             if (c < routed_units(a)) {
                 wg_wait(a, &a.gctr[G_LATENT], (uint32_t)a.n_lat_units);
                 bool reuse = true;
-                w13_unit<S13, true>(a, c, ui % a.tg13, s_b, reuse);
+                w13_unit<S13, true, true>(a, c, ui % a.tg13, s_b, reuse);
                 wg_publish(&a.c13[c * kCtrStride]);
             }
         } else if (u < a.u_sd) {
@@ -914,6 +927,98 @@ k_step(const StepArgs a) {
         for (int i = threadIdx.x; i < G_ERROR; i += kWGThreads)
             __hip_atomic_store(&a.gctr[i], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         for (int i = threadIdx.x; i < a.ncols_cap; i += kWGThreads)
+            __hip_atomic_store(&a.c13[i * kCtrStride], 0u, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Two-launch step: the dense-in kernel (router, routing, latent-down, shared
+// gate/up), then one persistent launch for the rest
+// ---------------------------------------------------------------------------
+//
+// The second launch runs the units
+//   [gate/up (NC x tg13) | shared-down, first part | down (NC x tg2) |
+//    shared-down, rest | latent-up]
+// from one queue in this order, NC being the routing's active column units.
+// The shared-down units depend on nothing in this launch: placed between the
+// dependent phases, they keep the compute units streaming weights while the
+// down units wait for their column's gate/up units and the latent-up units
+// for the whole latent combine.  The same progress argument as the fused
+// step holds (a unit waits only for units earlier in the queue).
+
+template <int S13, int S2>
+struct TailLds {
+    static constexpr int kExpert = 8 * Stage<(S13 > S2 ? S13 : S2)>::kChunks * 2;
+    static constexpr int kOut = kWG * kWave * 4 * 4;
+    static constexpr int kBytes = kExpert > kOut ? kExpert : kOut;
+};
+
+template <int S13, int S2>
+__global__ void __launch_bounds__(kWGThreads) __attribute__((amdgpu_waves_per_eu(4)))
+k_tail(const StepArgs a) {
+    __shared__ __attribute__((aligned(16))) char s_mem[TailLds<S13, S2>::kBytes];
+    __shared__ int s_next, s_exit;
+    uint16_t *s_b = (uint16_t *)s_mem;
+    float *s_red = (float *)s_mem;
+    const Role ro_sd = role_of(a.kw_sd), ro_lu = role_of(a.kw_lu);
+    const int ncg_out = (a.B + 7) >> 3;
+    const int n_ot = (a.H + a.out_rows - 1) / a.out_rows;
+    // Written by the dense-in launch; never beyond the records.
+    const int NC = min(a.meta[M_N_COLS], a.ncols_cap);
+    const int r13 = NC * a.tg13, rsa = r13 + a.n_sd_first, r2 = rsa + NC * a.tg2;
+    const int rsb = r2 + (a.n_sd_units - a.n_sd_first), rend = rsb + a.n_lu_units;
+    if (threadIdx.x == 0)
+        s_next = (int)__hip_atomic_fetch_add(&a.gctr[G_WORK], 1u, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    int u = s_next;
+    while (u < rend) {
+        if (u < r13) {
+            // gate/up unit: z and the records come from the dense-in launch
+            const int c = u / a.tg13;
+            bool reuse = true;
+            w13_unit<S13, false, true>(a, c, u % a.tg13, s_b, reuse);
+            wg_publish(&a.c13[c * kCtrStride]);
+        } else if (u < rsa || (u >= r2 && u < rsb)) {
+            // shared-down unit: the shared activation comes from the dense-in
+            // launch
+            const int ui = u < rsa ? u - r13 : a.n_sd_first + (u - r2);
+            const int cg = ui % ncg_out, t = (ui / ncg_out) * ro_sd.RW + ro_sd.rg;
+            out_tile<false>(a, ro_sd, OUT_SHARED, t, t < n_ot, cg, a.spc_sd, s_red);
+            wg_publish(&a.gctr[G_SHDOWN]);
+        } else if (u < r2) {
+            // down unit: needs its column unit's activations
+            const int ui = u - rsa, c = ui / a.tg2;
+            wg_wait(a, &a.c13[c * kCtrStride], (uint32_t)a.tg13);
+            bool reuse = true;
+            w2_unit<S2, true>(a, c, ui % a.tg2, s_b, reuse);
+            wg_publish(&a.gctr[G_W2]);
+        } else {
+            // latent-up unit: needs the whole latent combine and the
+            // shared-down sums
+            const int ui = u - rsb;
+            const int cg = ui % ncg_out, t = (ui / ncg_out) * ro_lu.RW + ro_lu.rg;
+            wg_wait(a, &a.gctr[G_W2], (uint32_t)(NC * a.tg2));
+            wg_wait(a, &a.gctr[G_SHDOWN], (uint32_t)a.n_sd_units);
+            out_tile<true>(a, ro_lu, OUT_LATENT, t, t < n_ot, cg, a.spc_lu, s_red);
+        }
+        __syncthreads();
+        if (threadIdx.x == 0)
+            s_next = (int)__hip_atomic_fetch_add(&a.gctr[G_WORK], 1u, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        u = s_next;
+    }
+    // The last workgroup out resets the counters of both launches.
+    if (threadIdx.x == 0)
+        s_exit = __hip_atomic_fetch_add(&a.gctr[G_EXIT], 1u, __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT) == gridDim.x - 1u;
+    __syncthreads();
+    if (s_exit) {
+        for (int i = threadIdx.x; i < G_ERROR; i += kWGThreads)
+            __hip_atomic_store(&a.gctr[i], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int i = threadIdx.x; i < NC; i += kWGThreads)
             __hip_atomic_store(&a.c13[i * kCtrStride], 0u, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
     }

@@ -128,6 +128,19 @@ const FusedEntry kFused[] = {{16, 16, k_step<16, 16>}, {16, 8, k_step<16, 8>},
                              {8, 8, k_step<8, 8>},     {4, 3, k_step<4, 3>},
                              {2, 2, k_step<2, 2>}};
 
+// Second launch of the two-launch step, for the same chunk shapes.
+const FusedEntry kTail[] = {{16, 16, k_tail<16, 16>}, {16, 8, k_tail<16, 8>},
+                            {16, 4, k_tail<16, 4>},   {16, 2, k_tail<16, 2>},
+                            {8, 8, k_tail<8, 8>},     {4, 3, k_tail<4, 3>},
+                            {2, 2, k_tail<2, 2>}};
+
+StepKernel tail_kernel(const moe_decode_config &c, const Plan &p) {
+    if (c.router_dtype != MOE_ROUTER_BF16 || p.sd.kw == 0 || p.lu.kw == 0) return nullptr;
+    for (const FusedEntry &f : kTail)
+        if (f.s13 == p.s13 && f.s2 == p.s2) return f.k;
+    return nullptr;
+}
+
 StepKernel fused_kernel(const moe_decode_config &c, const Plan &p) {
     if (c.router_dtype != MOE_ROUTER_BF16 || p.sd.kw == 0 || p.lu.kw == 0) return nullptr;
     for (const FusedEntry &f : kFused)
@@ -181,8 +194,19 @@ Layout make_layout(const moe_decode_config &c) {
     {nullptr, K<1>, K<2>,  K<3>,  K<4>,  K<5>,  K<6>,  K<7>, K<8>,                                \
      K<9>,    K<10>, K<11>, K<12>, K<13>, K<14>, K<15>, K<16>}
 const StepKernel kW13[] = MOE_SPC_TABLE(k_w13);
-const StepKernel kW2[] = MOE_SPC_TABLE(k_w2);
 #undef MOE_SPC_TABLE
+#define MOE_W2_TABLE(KS)                                                                       \
+    {nullptr,        k_w2<1, KS>,  k_w2<2, KS>,  k_w2<3, KS>,  k_w2<4, KS>,  k_w2<5, KS>,        \
+     k_w2<6, KS>,    k_w2<7, KS>,  k_w2<8, KS>,  k_w2<9, KS>,  k_w2<10, KS>, k_w2<11, KS>,       \
+     k_w2<12, KS>,   k_w2<13, KS>, k_w2<14, KS>, k_w2<15, KS>, k_w2<16, KS>}
+const StepKernel kW2[] = MOE_W2_TABLE(1);
+#undef MOE_W2_TABLE
+// Down kernels with two waves per tile (even chunk shapes only).
+const StepKernel kW2Split[] = {nullptr,        nullptr,       k_w2<2, 2>,  nullptr,
+                               k_w2<4, 2>,     nullptr,       k_w2<6, 2>,  nullptr,
+                               k_w2<8, 2>,     nullptr,       k_w2<10, 2>, nullptr,
+                               k_w2<12, 2>,    nullptr,       k_w2<14, 2>, nullptr,
+                               k_w2<16, 2>};
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -383,6 +407,7 @@ moe_status moe_decode_step(moe_decode_ctx *ctx, const uint16_t *x, int32_t batch
     Plan pl = make_plan(c, batch, top_k, ctx->mode == MOE_MODE_FUSED);
     const StepKernel fused = ctx->mode == MOE_MODE_FUSED ? fused_kernel(c, pl) : nullptr;
     if (!fused) pl = make_plan(c, batch, top_k, false);
+    const StepKernel tail = ctx->mode == MOE_MODE_TWO_LAUNCHES ? tail_kernel(c, pl) : nullptr;
     StepArgs a = base_args(ctx);
     a.B = batch;
     a.k = top_k;
@@ -411,15 +436,50 @@ moe_status moe_decode_step(moe_decode_ctx *ctx, const uint16_t *x, int32_t batch
     d.split_in = pl.in.kw;
     d.split_out = pl.out.kw;
     d.split_w13 = 1;
-    d.split_w2 = 1;
+    // Four-launch down kernel: when its units would fill less than the two
+    // resident workgroups per compute unit, two waves share each tile (twice
+    // the units, half the steps per wave).
+    const bool split2 = !fused && !tail && pl.s2 % 2 == 0 && pl.units_2 < 2LL * ctx->n_cus;
+    if (split2) pl.units_2 = (long long)ncols_cap(c.n_experts, batch, top_k) *
+                             cdiv(c.latent / 16, kWG / 2);
+    d.split_w2 = split2 ? 2 : 1;
     d.grid_in = grid_for(pl.units_in, cap);
     d.grid_w13 = grid_for(pl.units_13, cap);
     d.grid_w2 = grid_for(pl.units_2, cap);
     d.grid_out = grid_for(pl.units_out, cap);
     d.router_f32 = c.router_dtype == MOE_ROUTER_F32;
-    d.fused = fused != nullptr;
-    d.n_kernels = fused ? 1 : 4 + d.router_f32;
+    d.fused = fused ? 1 : tail ? 2 : 0;
+    d.n_kernels = fused ? 1 : tail ? 2 : 4 + d.router_f32;
     d.grid_step = 0;
+    // One persistent workgroup per resident slot of `kernel` (the unit
+    // queues do not rely on residency; this only sizes the grid).
+    auto persistent_grid = [&](StepKernel kernel, long long units) {
+        if (ctx->occ_kernel != kernel) {
+            int blocks = 0;
+            if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, kernel, kWGThreads, 0) !=
+                    hipSuccess ||
+                blocks < 1)
+                blocks = 1;
+            ctx->occ_kernel = kernel;
+            ctx->occ_blocks = blocks;
+        }
+        return (int32_t)std::max(1LL, std::min<long long>(units, (long long)ctx->occ_blocks *
+                                                                     ctx->n_cus));
+    };
+    if (tail) {
+        a.kw_sd = pl.sd.kw;
+        a.spc_sd = pl.sd.spc;
+        a.kw_lu = pl.lu.kw;
+        a.spc_lu = pl.lu.spc;
+        a.tg13 = pl.tg13;
+        a.tg2 = pl.tg2;
+        const int n_ot = cdiv(c.hidden, pl.out_rows);
+        a.n_sd_units = cdiv(n_ot, kWG / pl.sd.kw) * pl.ncg_out;
+        a.n_lu_units = cdiv(n_ot, kWG / pl.lu.kw) * pl.ncg_out;
+        a.n_sd_first = a.n_sd_units / 2;
+        d.grid_step = persistent_grid(tail, pl.units_13 + pl.units_2 + a.n_sd_units +
+                                                a.n_lu_units);
+    }
     if (fused) {
         a.u_lat = pl.u_lat;
         a.u_sh = pl.u_sh;
@@ -437,19 +497,7 @@ moe_status moe_decode_step(moe_decode_ctx *ctx, const uint16_t *x, int32_t batch
         a.n_lat_units = pl.u_sh - pl.u_lat;
         a.n_sh_units = pl.u_13 - pl.u_sh;
         a.n_sd_units = pl.u_lu - pl.u_sd;
-        // One persistent workgroup per resident slot (the unit queue does
-        // not rely on residency; this only sizes the grid).
-        if (ctx->occ_kernel != fused) {
-            int blocks = 0;
-            if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, fused, kWGThreads, 0) !=
-                    hipSuccess ||
-                blocks < 1)
-                blocks = 1;
-            ctx->occ_kernel = fused;
-            ctx->occ_blocks = blocks;
-        }
-        d.grid_step = (int32_t)std::min<long long>(pl.u_end,
-                                                   (long long)ctx->occ_blocks * ctx->n_cus);
+        d.grid_step = persistent_grid(fused, pl.u_end);
     }
 
     const bool timed = ctx->n_events == 2 * d.n_kernels;
@@ -469,8 +517,13 @@ moe_status moe_decode_step(moe_decode_ctx *ctx, const uint16_t *x, int32_t batch
     }
     if (d.router_f32) launch(k_router_f32, cdiv(c.n_experts, kWavesPerBlock), kBlock);
     launch(k_dense_in, d.grid_in, kWGThreads);
+    if (tail) {
+        launch(tail, d.grid_step, kWGThreads);
+        const hipError_t e = hipGetLastError();
+        return e == hipSuccess ? MOE_OK : hip_fail(ctx, e);
+    }
     launch(kW13[pl.s13], d.grid_w13, kWGThreads);
-    launch(kW2[pl.s2], d.grid_w2, kWGThreads);
+    launch(split2 ? kW2Split[pl.s2] : kW2[pl.s2], d.grid_w2, kWGThreads);
     launch(k_out, d.grid_out, kWGThreads);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(ctx, e);
@@ -554,7 +607,7 @@ moe_status moe_decode_set_timing_events(moe_decode_ctx *ctx, void *const *events
         ctx->n_events = 0;
         return MOE_OK;
     }
-    if ((n != want && n != 2) || !events) return MOE_ERR_INVALID_ARG;
+    if ((n != want && n != 2 && n != 4) || !events) return MOE_ERR_INVALID_ARG;
     for (int i = 0; i < n; ++i) {
         if (!events[i]) return MOE_ERR_INVALID_ARG;
         ctx->events[i] = (hipEvent_t)events[i];
@@ -564,7 +617,8 @@ moe_status moe_decode_set_timing_events(moe_decode_ctx *ctx, void *const *events
 }
 
 moe_status moe_decode_set_mode(moe_decode_ctx *ctx, int32_t mode) {
-    if (!ctx || (mode != MOE_MODE_FUSED && mode != MOE_MODE_FOUR_LAUNCHES))
+    if (!ctx || (mode != MOE_MODE_FUSED && mode != MOE_MODE_FOUR_LAUNCHES &&
+                 mode != MOE_MODE_TWO_LAUNCHES))
         return MOE_ERR_INVALID_ARG;
     ctx->mode = mode;
     return MOE_OK;

@@ -29,6 +29,9 @@ struct StepArgs {
     int32_t kw_sd, spc_sd, kw_lu, spc_lu;
     int32_t tg13, tg2;
     int32_t n_lat_units, n_sh_units, n_sd_units;
+    // Two-launch step (dense-in, then one persistent launch): shared-down
+    // units placed before the down units, latent-up units.
+    int32_t n_sd_first, n_lu_units;
     // Weights (borrowed).
     const uint16_t *router_w;
     const float *router_w32;

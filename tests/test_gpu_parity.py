@@ -273,42 +273,54 @@ def test_dispatch_follows_the_batch(small_layer, small_ctx):
         assert d["batch"] == B and d["col_tiles"] == cg
         assert d["fused"] == 0 and d["n_kernels"] == 4
         assert d["grid_in"] >= 1 and d["grid_w13"] >= 1 and d["grid_step"] == 0
-    small_ctx.set_mode(binding.MODE_FUSED)
     try:
-        run(small_ctx, synth.make_tokens(small_layer.dims, 14, 5), 6)
-        d = small_ctx.last_dispatch()
-        assert d["fused"] == 1 and d["n_kernels"] == 1 and d["grid_step"] >= 1
+        for mode, fused, n in ((binding.MODE_FUSED, 1, 1), (binding.MODE_TWO_LAUNCHES, 2, 2)):
+            small_ctx.set_mode(mode)
+            run(small_ctx, synth.make_tokens(small_layer.dims, 14, 5), 6)
+            d = small_ctx.last_dispatch()
+            assert d["fused"] == fused and d["n_kernels"] == n and d["grid_step"] >= 1
     finally:
         small_ctx.set_mode(binding.MODE_FOUR_LAUNCHES)
 
 
+PERSISTENT_MODES = [("fused", 1), ("two_launches", 2)]
+
+
+def mode_const(name):
+    return {"fused": binding.MODE_FUSED, "two_launches": binding.MODE_TWO_LAUNCHES,
+            "four_launches": binding.MODE_FOUR_LAUNCHES}[name]
+
+
+@pytest.mark.parametrize("mode,kind", PERSISTENT_MODES)
 @pytest.mark.parametrize("B", [1, 9, 33, 64])
-def test_four_launch_step_matches_fused(small_layer, B):
-    """The four-launch step and the fused step compute the same values (up to
-    the order of the latent combine's atomic adds); both against the oracle."""
+def test_four_launch_step_matches_persistent(small_layer, B, mode, kind):
+    """The four-launch step and the persistent-kernel steps compute the same
+    values (up to the order of the latent combine's atomic adds); both against
+    the oracle."""
     k = 6
     fused = make_ctx(small_layer, 64, 8)
-    fused.set_mode(binding.MODE_FUSED)
+    fused.set_mode(mode_const(mode))
     four = make_ctx(small_layer, 64, 8)
     x = synth.make_tokens(small_layer.dims, 200 + B, B)
     a = run(fused, x, k)
     b = run(four, x, k)
-    assert fused.last_dispatch()["fused"] == 1 and four.last_dispatch()["fused"] == 0
+    assert fused.last_dispatch()["fused"] == kind and four.last_dispatch()["fused"] == 0
     assert_same_step(a, b)
-    check_step(small_layer, x, k, *b)
+    check_step(small_layer, x, k, *a)
 
 
-def test_fused_step_other_shapes():
-    """Fused kernels of other chunk shapes: K3 latent with a short down row
-    (16, 2) is covered by the TP8 tests; here the (2, 2) shape of a small
+@pytest.mark.parametrize("mode,kind", PERSISTENT_MODES)
+def test_persistent_step_other_shapes(mode, kind):
+    """Persistent kernels of other chunk shapes: K3 latent with a short down
+    row (16, 2) is covered by the TP8 tests; here the (2, 2) shape of a small
     layer, several steps in a row on one context."""
     layer = synth.make_layer(small_recipe(k=4), 21)
     ctx = make_ctx(layer, 16)
-    ctx.set_mode(binding.MODE_FUSED)
+    ctx.set_mode(mode_const(mode))
     for B in (1, 7, 16):
         x = synth.make_tokens(layer.dims, 21 + B, B)
         out, idx, w = run(ctx, x, 4)
-        assert ctx.last_dispatch()["fused"] == 1
+        assert ctx.last_dispatch()["fused"] == kind
         check_step(layer, x, 4, out, idx, w)
 
 
@@ -354,21 +366,24 @@ def test_k3_layer(k3_layer, k3_dev, bias_kind, B, sample):
     layer = layer_with_bias(k3_layer, bias_kind)
     x = synth.make_tokens(layer.dims, 0, B)
     out, idx, w = run(ctx, x, 16)
+    # Batch 1 leaves the down kernel short of units: two waves per tile.
+    assert ctx.last_dispatch()["split_w2"] == (2 if B == 1 else 1)
     r = check_step(layer, x, 16, out, idx, w, sample=sample)
     log("  ", r, "distinct experts", len(np.unique(idx)))
 
 
+@pytest.mark.parametrize("mode,kind", PERSISTENT_MODES)
 @pytest.mark.parametrize("bias_kind,B", [("normal", 1), ("zipf", 8), ("normal", 64)])
-def test_k3_fused_step_matches_four_launches(k3_dev, bias_kind, B):
-    """The persistent fused step on the K3 layer (chunk shape 16x16) gives
+def test_k3_persistent_step_matches_four_launches(k3_dev, bias_kind, B, mode, kind):
+    """The persistent-kernel steps on the K3 layer (chunk shape 16x16) give
     the four-launch step's values."""
     four, _ = k3_ctx(k3_dev, bias_kind, 64)
     fused, _ = k3_ctx(k3_dev, bias_kind, 64)
-    fused.set_mode(binding.MODE_FUSED)
+    fused.set_mode(mode_const(mode))
     x = synth.make_tokens(k3_dev.dims, 5, B)
     a = run(four, x, 16)
     b = run(fused, x, 16)
-    assert fused.last_dispatch()["fused"] == 1 and four.last_dispatch()["fused"] == 0
+    assert fused.last_dispatch()["fused"] == kind and four.last_dispatch()["fused"] == 0
     assert_same_step(a, b)
 
 
@@ -383,7 +398,7 @@ def test_k3_tp8_share_layer():
         log("  ", r)
 
 
-@pytest.mark.parametrize("mode", ["four_launches", "fused"])
+@pytest.mark.parametrize("mode", ["four_launches", "two_launches", "fused"])
 def test_c4_eight_layer_graph(mode):
     """Eight TP8-share layers (own seeds and inputs) captured in one HIP graph,
     the configuration the stacked benchmark replays: every layer's replayed
@@ -394,7 +409,7 @@ def test_c4_eight_layer_graph(mode):
     layers = [synth.make_layer(synth.K3_TP8, synth.TP8_STACK_SEED0 + l) for l in range(n_layers)]
     ctxs = [make_ctx(la, B, k) for la in layers]
     for c in ctxs:
-        c.set_mode(binding.MODE_FUSED if mode == "fused" else binding.MODE_FOUR_LAUNCHES)
+        c.set_mode(mode_const(mode))
     xs = [synth.make_tokens(la.dims, synth.TP8_STACK_SEED0 + l, B) for l, la in enumerate(layers)]
     xd = [to_dev_tokens(x) for x in xs]
     H = layers[0].dims.hidden
