@@ -159,6 +159,29 @@ __device__ __forceinline__ void dense_chunk_x(const uint16_t *A, const uint16_t 
     }
 }
 
+// acc[c] += bf16 tile A . columns X[c] for NCG column groups over steps
+// [s0, s1): each weight step is loaded once and multiplied against every
+// group's columns (one step in flight; NCG = 1 is dense_chunk_x).
+template <int NCG>
+__device__ __forceinline__ void dense_chunk_xn(const uint16_t *A, const uint16_t *const (&X)[NCG],
+                                               const bool (&valid)[NCG], int s0, int s1,
+                                               f32x4 (&acc)[NCG]) {
+    if constexpr (NCG == 1) {
+        dense_chunk_x(A, X[0], valid[0], s0, s1, acc[0]);
+    } else {
+#pragma unroll 1
+        for (int s = s0; s < s1; ++s) {
+            u32x4 ra[4], rb[NCG][4];
+            load_tile_bf16(A, s, ra);
+#pragma unroll
+            for (int c = 0; c < NCG; ++c) load_cols_bf16(X[c], valid[c], s, rb[c]);
+            fence_schedule();
+#pragma unroll
+            for (int c = 0; c < NCG; ++c) mfma_tile(ra, rb[c], acc[c]);
+        }
+    }
+}
+
 // Output units: K steps s < Ls run against lat_up and ylat (f32, split into
 // hi/lo while loading), the rest against sh_w2 and the shared activation
 // (hi/lo bf16 rows).
@@ -203,6 +226,46 @@ __device__ __forceinline__ void dense_chunk_out(const TwoSource &t, bool valid, 
     }
 }
 
+// dense_chunk_out for NCG column groups (per-group byte offsets Oa[c],
+// Ob[c]): each weight step is loaded once.  Steps against the f32 source take
+// the groups two at a time (their raw loads need twice the registers), the
+// bf16 steps all groups at once.
+template <bool Coh, int NCG>
+__device__ __forceinline__ void dense_chunk_out_n(const TwoSource &t, const uint32_t (&Oa)[NCG],
+                                                  const uint32_t (&Ob)[NCG],
+                                                  const bool (&valid)[NCG], int part, int s0,
+                                                  int s1, f32x4 (&acc)[NCG]) {
+#pragma unroll 1
+    for (int s = s0; s < s1; ++s) {
+        u32x4 ra[4];
+        if (s < t.Ls) {
+            load_tile_bf16(t.Aa, s, ra);
+#pragma unroll
+            for (int c0 = 0; c0 < NCG; c0 += 2) {
+                constexpr int kPair = NCG > 1 ? 2 : 1;
+                u32x4 rb[kPair][4];
+#pragma unroll
+                for (int q = 0; q < kPair; ++q)
+                    if (c0 + q < NCG)
+                        buf_cols_f32<Coh>(t.Ra, Oa[c0 + q], valid[c0 + q], part, s, rb[q]);
+                fence_schedule();
+#pragma unroll
+                for (int q = 0; q < kPair; ++q)
+                    if (c0 + q < NCG) mfma_tile(ra, rb[q], acc[c0 + q]);
+            }
+        } else {
+            load_tile_bf16(t.Ab, s - t.Ls, ra);
+            u32x4 rb[NCG][4];
+#pragma unroll
+            for (int c = 0; c < NCG; ++c)
+                buf_cols_bf16<Coh>(t.Rb, Ob[c], valid[c], s - t.Ls, rb[c]);
+            fence_schedule();
+#pragma unroll
+            for (int c = 0; c < NCG; ++c) mfma_tile(ra, rb[c], acc[c]);
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Workgroup split-K reduction
 // ---------------------------------------------------------------------------
@@ -221,6 +284,31 @@ __device__ __forceinline__ bool reduce_k1(float *s_red, int wave, int kw, int KW
         for (int j = 0; j < KW; ++j) acc += ldf4(s_red + ((wave + j) * kWave + lane) * 4);
     }
     return true;
+}
+
+// reduce_k1 for NCG accumulators at once (s_red holds NCG slices).
+template <int NCG>
+__device__ __forceinline__ bool reduce_kn(float *s_red, int wave, int kw, int KW,
+                                          f32x4 (&acc)[NCG]) {
+    if constexpr (NCG == 1) {
+        return reduce_k1(s_red, wave, kw, KW, acc[0]);
+    } else {
+        const int lane = lane_id();
+        constexpr int kSlice = kWG * kWave * 4;
+#pragma unroll
+        for (int c = 0; c < NCG; ++c) stf4(s_red + c * kSlice + (wave * kWave + lane) * 4, acc[c]);
+        __syncthreads();
+        if (kw != 0) return false;
+        if (KW > 1) {
+#pragma unroll
+            for (int c = 0; c < NCG; ++c) {
+                acc[c] = zero4();
+                for (int j = 0; j < KW; ++j)
+                    acc[c] += ldf4(s_red + c * kSlice + ((wave + j) * kWave + lane) * 4);
+            }
+        }
+        return true;
+    }
 }
 
 struct Role {
@@ -321,6 +409,83 @@ __device__ __forceinline__ void dense_in_tile(const StepArgs &a, const Role &ro,
                 for (int i = 0; i < 4; ++i) v[i] = silu_mul(acc[i], up[i]);
                 uint16_t *dst = a.ashhl + (size_t)b * 2 * a.Is + 8 * tt + 4 * g;
                 store_hl4<Coh>(dst, dst + a.Is, v);
+            }
+        }
+    }
+    __syncthreads();
+}
+
+// dense_in_tile for the NCG >= 2 column groups cg0 .. cg0 + NCG - 1 (s_red:
+// NCG reduction slices): every weight step is loaded once for all of them.
+template <bool Coh, int NCG>
+__device__ __forceinline__ void dense_in_tile_n(const StepArgs &a, const Role &ro, int kind, int t,
+                                              bool active, int cg0, float *s_red, int *s_last) {
+    const int lane = lane_id(), n = lane & 15, g = lane >> 4;
+    const int tt = active ? t : 0;
+    const uint16_t *A;
+    const int RR = a.router_rows, RL = a.latent_rows;
+    if (kind == KIND_ROUTER)
+        A = a.router_w + (size_t)(RR * tt + min(n, RR - 1)) * a.H;
+    else if (kind == KIND_LATENT)
+        A = a.lat_down + (size_t)(RL * tt + min(n, RL - 1)) * a.H;
+    else
+        A = a.sh_w13 + (size_t)((n < 8 ? 0 : a.Is) + 8 * tt + (n & 7)) * a.H;
+    const uint16_t *X[NCG];
+    bool valid[NCG];
+    f32x4 acc[NCG];
+#pragma unroll
+    for (int c = 0; c < NCG; ++c) {
+        const int b = 16 * (cg0 + c) + n;
+        valid[c] = b < a.B;
+        X[c] = a.x + (size_t)(valid[c] ? b : 0) * a.H + 8 * g;
+        acc[c] = zero4();
+    }
+    if (active)
+        dense_chunk_xn<NCG>(A + 8 * g, X, valid, ro.kw * a.spc_in, (ro.kw + 1) * a.spc_in, acc);
+    const bool leader = reduce_kn<NCG>(s_red, ro.wave, ro.kw, ro.KW, acc);
+    if (leader && active) {
+        if (kind == KIND_ROUTER) {
+            const int e = RR * tt + 4 * g;
+            // Rows past RR (short router tiles) have no bias entry.
+            const f32x4 bv = a.bias && 4 * g < RR ? ldf4(a.bias + e) : zero4();
+#pragma unroll
+            for (int c = 0; c < NCG; ++c) {
+                const int b = 16 * (cg0 + c) + n;
+                if (valid[c] && 4 * g < RR) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float sv = sigmoidf_(acc[c][i]);
+                        store_agent(a.score + (size_t)b * kMaxExperts + e + i, sv);
+                        store_agent(a.key + (size_t)b * kMaxExperts + e + i, sv + bv[i]);
+                    }
+                }
+            }
+            if (wave_publish(&a.gctr[G_ROUTER_DONE]) == (uint32_t)a.router_target - 1u &&
+                lane == 0)
+                *s_last = 1;
+        } else if (kind == KIND_LATENT) {
+#pragma unroll
+            for (int c = 0; c < NCG; ++c) {
+                const int b = 16 * (cg0 + c) + n;
+                if (valid[c] && 4 * g < RL) {
+                    uint16_t *dst = a.zhl + (size_t)b * 2 * a.L + RL * tt + 4 * g;
+                    store_hl4<Coh>(dst, dst + a.L, acc[c]);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int c = 0; c < NCG; ++c) {
+                const int b = 16 * (cg0 + c) + n;
+                f32x4 up;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) up[i] = __shfl_xor(acc[c][i], 32);
+                if (valid[c] && g < 2) {
+                    f32x4 v;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) v[i] = silu_mul(acc[c][i], up[i]);
+                    uint16_t *dst = a.ashhl + (size_t)b * 2 * a.Is + 8 * tt + 4 * g;
+                    store_hl4<Coh>(dst, dst + a.Is, v);
+                }
             }
         }
     }
@@ -613,6 +778,68 @@ enum { OUT_BOTH = 0, OUT_SHARED = 1, OUT_LATENT = 2 };
 // ylat and the shared activation come from units of the same launch.
 template <bool Coh>
 __device__ __forceinline__ void out_tile(const StepArgs &a, const Role &ro, int mode, int t,
+                                         bool active, int cg, int spc, float *s_red);
+
+// OUT_BOTH for the NCG column groups cg0 .. cg0 + NCG - 1 (s_red: NCG
+// reduction slices); every weight step is loaded once for all of them.
+template <int NCG>
+__device__ __forceinline__ void out_tile_n(const StepArgs &a, const Role &ro, int t, bool active,
+                                           int cg0, float *s_red) {
+    const int lane = lane_id(), n = lane & 15, g = lane >> 4;
+    const int col = n >> 1, part = n & 1;
+    const int RT = a.out_rows;
+    const int h0 = RT * (active ? t : 0);
+    const size_t h = min(h0 + min(n, RT - 1), a.H - 1);
+    TwoSource ts;
+    ts.Aa = a.lat_up + h * a.L + 8 * g;
+    ts.Ab = a.sh_w2 + h * a.Is + 8 * g;
+    ts.Ra = buf_rsrc(a.ylat);
+    ts.Rb = buf_rsrc(a.ashhl);
+    ts.Ls = a.L / kKStep;
+    uint32_t Oa[NCG], Ob[NCG];
+    bool valid[NCG];
+    f32x4 acc[NCG];
+#pragma unroll
+    for (int c = 0; c < NCG; ++c) {
+        const int b = 8 * (cg0 + c) + col;
+        valid[c] = b < a.B;
+        const int bb = valid[c] ? b : 0;
+        Oa[c] = (uint32_t)(((size_t)bb * a.L + 8 * g) * 4);
+        Ob[c] = (uint32_t)((((size_t)bb * 2 + part) * a.Is + 8 * g) * 2);
+        acc[c] = zero4();
+    }
+    if (active) {
+        if constexpr (NCG == 1) {  // one group: two steps in flight
+            ts.Oa = Oa[0];
+            ts.Ob = Ob[0];
+            dense_chunk_out<false>(ts, valid[0], part, ro.kw * a.spc_out, (ro.kw + 1) * a.spc_out,
+                                   acc[0]);
+        } else {
+            dense_chunk_out_n<false, NCG>(ts, Oa, Ob, valid, part, ro.kw * a.spc_out,
+                                          (ro.kw + 1) * a.spc_out, acc);
+        }
+    }
+    const bool leader = reduce_kn<NCG>(s_red, ro.wave, ro.kw, ro.KW, acc);
+    if (leader && active) {
+#pragma unroll
+        for (int c = 0; c < NCG; ++c) {
+            const f32x4 v = add_pair_column(acc[c]);
+            const int b = 8 * (cg0 + c) + col;
+            if (valid[c] && part == 0) {
+                const size_t o = (size_t)b * a.H + h0;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = 4 * g + i;
+                    if (r < RT && h0 + r < a.H) a.out[o + r] = (uint16_t)bf16_rne(v[i]);
+                }
+            }
+        }
+    }
+    __syncthreads();
+}
+
+template <bool Coh>
+__device__ __forceinline__ void out_tile(const StepArgs &a, const Role &ro, int mode, int t,
                                          bool active, int cg, int spc, float *s_red) {
     const int lane = lane_id(), n = lane & 15, g = lane >> 4;
     const int col = n >> 1, part = n & 1;
@@ -691,11 +918,14 @@ __global__ void __launch_bounds__(kBlock) k_router_f32(const StepArgs a) {
     if (s_last) route_step(route_args(a), &s_route, kWavesPerBlock);
 }
 
-// Kernel 1: dense-in units over [router | latent | shared] tiles.
+// Kernel 1: dense-in units over [router | latent | shared] tiles; each unit
+// covers all NCG = ceil(B / 16) column groups, so every weight tile is read
+// once per step.
+template <int NCG>
 __global__ void __launch_bounds__(kWGThreads) __attribute__((amdgpu_waves_per_eu(4)))
 k_dense_in(const StepArgs a) {
     __shared__ RouteLds s_route;
-    __shared__ float s_red[kWG * kWave * 4];
+    __shared__ float s_red[NCG * kWG * kWave * 4];
     __shared__ int s_last;
     const Role ro = role_of(a.kw_in);
     if (threadIdx.x == 0) s_last = 0;
@@ -705,7 +935,7 @@ k_dense_in(const StepArgs a) {
         stf4(a.ylat + i, zero4());
     const int n_rt = a.n_rtiles, n_lt = a.L / a.latent_rows, n_st = a.Is >> 3;
     const int n_t = n_rt + n_lt + n_st;
-    const int ncg = (a.B + 15) >> 4;
+    const int ncg = NCG == 1 ? (a.B + 15) >> 4 : 1;  // 1 whenever B <= 16
     const int units = dense_units(n_t, ro.RW, ncg);
     for (int u = blockIdx.x; u < units; u += gridDim.x) {
         int cg, tg;
@@ -714,7 +944,10 @@ k_dense_in(const StepArgs a) {
         const bool active = t < n_t;
         const int kind = t < n_rt ? KIND_ROUTER : t < n_rt + n_lt ? KIND_LATENT : KIND_SHARED;
         const int tl = kind == KIND_ROUTER ? t : kind == KIND_LATENT ? t - n_rt : t - n_rt - n_lt;
-        dense_in_tile<false>(a, ro, kind, tl, active, cg, s_red, &s_last);
+        if constexpr (NCG == 1)
+            dense_in_tile<false>(a, ro, kind, tl, active, cg, s_red, &s_last);
+        else
+            dense_in_tile_n<false, NCG>(a, ro, kind, tl, active, 0, s_red, &s_last);
         if (s_last) {  // this workgroup completed the router: route the step
             route_step(route_args(a), &s_route, kWG);
             __syncthreads();
@@ -746,22 +979,24 @@ k_w2(const StepArgs a) {
         w2_unit<S, false, KS>(a, u / TG, u % TG, s_b, reuse);
 }
 
-// Kernel 4: output units (latent-up and shared-down in one pass).
+// Kernel 4: output units (latent-up and shared-down in one pass), each over
+// NCG column groups of 8 tokens: ceil(ceil(B / 8) / NCG) units per tile.
+template <int NCG>
 __global__ void __launch_bounds__(kWGThreads) __attribute__((amdgpu_waves_per_eu(4)))
 k_out(const StepArgs a) {
-    __shared__ float s_red[kWG * kWave * 4];
+    __shared__ float s_red[NCG * kWG * kWave * 4];
     // The router counter of the dense input kernel is cleared here, where no
     // wave of the step can touch it any more.
     if (blockIdx.x == 0 && threadIdx.x == 0) a.gctr[G_ROUTER_DONE] = 0u;
     const Role ro = role_of(a.kw_out);
-    const int ncg = (a.B + 7) >> 3;
+    const int nblk = (((a.B + 7) >> 3) + NCG - 1) / NCG;
     const int n_t = (a.H + a.out_rows - 1) / a.out_rows;
-    const int units = dense_units(n_t, ro.RW, ncg);
+    const int units = dense_units(n_t, ro.RW, nblk);
     for (int u = blockIdx.x; u < units; u += gridDim.x) {
-        int cg, tg;
-        dense_unit(u, ncg, cg, tg);
+        int cb, tg;
+        dense_unit(u, nblk, cb, tg);
         const int t = tg * ro.RW + ro.rg;
-        out_tile<false>(a, ro, OUT_BOTH, t, t < n_t, cg, a.spc_out, s_red);
+        out_tile_n<NCG>(a, ro, t, t < n_t, cb * NCG, s_red);
     }
 }
 

@@ -62,7 +62,7 @@ long long dense_units_host(int n_t, int RW, int ncg) {
 }
 
 struct Plan {
-    int n_rtiles, ncg_in, ncg_out, out_rows;
+    int n_rtiles, ncg_in, ncg_out, ncg_unit_out, out_rows;
     Split in, out, sd, lu;
     int s13, s2, tg13, tg2;
     long long units_in, units_out, units_13, units_2;
@@ -91,9 +91,15 @@ Plan make_plan(const moe_decode_config &c, int B, int k, bool fused) {
     // rows.
     const int n_t_in = p.n_rtiles + c.latent / p.latent_rows + c.shared_inter / 8;
     const long long cols = ncols_cap(c.n_experts, B, k);
-    p.units_in = dense_units_host(n_t_in, kWG / p.in.kw, p.ncg_in);
+    // Four-launch dense-in units cover every column group; the fused step's
+    // take one group each.
+    p.units_in = dense_units_host(n_t_in, kWG / p.in.kw, fused ? p.ncg_in : 1);
     p.out_rows = out_tile_rows(c.hidden);
-    p.units_out = dense_units_host(cdiv(c.hidden, p.out_rows), kWG / p.out.kw, p.ncg_out);
+    // Output units: NCG column groups of 8 tokens each (at most 4, whose f32
+    // operand loads still fit the registers), every tile once per block.
+    p.ncg_unit_out = p.ncg_out <= 4 ? p.ncg_out : cdiv(p.ncg_out, 2);
+    p.units_out = dense_units_host(cdiv(c.hidden, p.out_rows), kWG / p.out.kw,
+                                   cdiv(p.ncg_out, p.ncg_unit_out));
     // Expert kernels: 8 row tiles per workgroup (8 gate + 8 up rows, or 16
     // latent rows, per tile).
     p.tg13 = cdiv(c.expert_inter / 8, kWG);
@@ -418,7 +424,7 @@ moe_status moe_decode_step(moe_decode_ctx *ctx, const uint16_t *x, int32_t batch
     a.n_rtiles = pl.n_rtiles;
     // Arrivals that complete the router: one per router unit of the dense
     // input kernel, or one per workgroup of the f32 router kernel.
-    a.router_target = c.router_dtype == MOE_ROUTER_BF16 ? pl.n_rtiles * pl.ncg_in
+    a.router_target = c.router_dtype == MOE_ROUTER_BF16 ? pl.n_rtiles * (fused ? pl.ncg_in : 1)
                                                         : cdiv(c.n_experts, kWavesPerBlock);
     a.kw_in = pl.in.kw;
     a.kw_out = pl.out.kw;
@@ -516,7 +522,8 @@ moe_status moe_decode_step(moe_decode_ctx *ctx, const uint16_t *x, int32_t batch
         return e == hipSuccess ? MOE_OK : hip_fail(ctx, e);
     }
     if (d.router_f32) launch(k_router_f32, cdiv(c.n_experts, kWavesPerBlock), kBlock);
-    launch(k_dense_in, d.grid_in, kWGThreads);
+    const StepKernel dense_in[] = {k_dense_in<1>, k_dense_in<2>, k_dense_in<3>, k_dense_in<4>};
+    launch(dense_in[pl.ncg_in - 1], d.grid_in, kWGThreads);
     if (tail) {
         launch(tail, d.grid_step, kWGThreads);
         const hipError_t e = hipGetLastError();
@@ -524,7 +531,8 @@ moe_status moe_decode_step(moe_decode_ctx *ctx, const uint16_t *x, int32_t batch
     }
     launch(kW13[pl.s13], d.grid_w13, kWGThreads);
     launch(split2 ? kW2Split[pl.s2] : kW2[pl.s2], d.grid_w2, kWGThreads);
-    launch(k_out, d.grid_out, kWGThreads);
+    const StepKernel out_k[] = {k_out<1>, k_out<2>, k_out<3>, k_out<4>};
+    launch(out_k[pl.ncg_unit_out - 1], d.grid_out, kWGThreads);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(ctx, e);
     return MOE_OK;
