@@ -48,13 +48,15 @@ WORKLOADS = {
 }
 KERNELS_BF16 = ("dense_in", "w13", "w2", "out")
 KERNEL_SYMBOLS = {"dense_in": "k_dense_in", "w13": "k_w13", "w2": "k_w2", "out": "k_out",
-                  "router_f32": "k_router_f32", "step": "k_step", "tail": "k_tail"}
+                  "router_f32": "k_router_f32", "step": "k_step", "tail": "k_tail",
+                  "shared_gu": "k_dense_in", "shared_down": "k_out_part", "lat_up": "k_out_part"}
 
 
 def modes():
     """Execution modes of the library by name."""
     from sparse_moe_decode_router_amd import binding
     return {"four_launches": binding.MODE_FOUR_LAUNCHES,
+            "side_stream": binding.MODE_SIDE_STREAM,
             "two_launches": binding.MODE_TWO_LAUNCHES, "fused": binding.MODE_FUSED}
 
 
@@ -87,6 +89,19 @@ def kernel_bytes(d, B, k, D):
     if d.router_f32:
         b["router_f32"] = router + B * H * 2 + B * E * 8 + P * 8
     return b
+
+
+def kernel_bytes_side(d, B, k, D):
+    """kernel_bytes split the way the side-stream step launches: dense-in
+    (router + latent-down + routing), shared gate/up, gate/up, down,
+    shared-down, latent-up."""
+    H, L, E, Is = d.hidden, d.latent, d.n_experts, d.shared_inter
+    b = kernel_bytes(d, B, k, D)
+    shared_gu = 2 * Is * H * 2 + B * H * 2 + B * Is * 4
+    shared_down = H * Is * 2 + B * Is * 4 + B * H * 4
+    return {"dense_in": b["dense_in"] - shared_gu + B * H * 2, "shared_gu": shared_gu,
+            "w13": b["w13"], "w2": b["w2"], "shared_down": shared_down,
+            "lat_up": H * L * 2 + B * L * 4 + B * H * 4 + B * H * 2}
 
 
 def load_traffic(kernel, workload):
@@ -157,6 +172,13 @@ def measure(dev, d, B, k, xs, steps, warmup, mode):
     if disp["fused"] == 1:
         names = ("step",)
         kb = [{"step": sum(kernel_bytes(d, B, k, D).values())} for D in Ds]
+    elif disp["fused"] == 3:
+        names = (("router_f32",) if d.router_f32 else ()) + (
+            "dense_in", "shared_gu", "w13", "w2", "shared_down", "lat_up")
+        kb = [kernel_bytes_side(d, B, k, D) for D in Ds]
+        if d.router_f32:
+            for D, x in zip(Ds, kb):
+                x["router_f32"] = kernel_bytes(d, B, k, D)["router_f32"]
     elif disp["fused"] == 2:
         names = ("dense_in", "tail")
         kb = []

@@ -177,7 +177,7 @@ typedef struct {
     int32_t router_f32;    /* 1 when the f32 router kernel ran */
     int32_t n_kernels;     /* kernels launched by the step */
     int32_t fused;         /* 1: one persistent launch; 2: dense-in + persistent launch;
-                              0: four launches */
+                              3: side stream; 0: four launches */
     int32_t grid_step;     /* workgroups of the persistent launch (0 for four launches) */
 } moe_decode_dispatch_info;
 moe_status moe_decode_last_dispatch(const moe_decode_ctx *ctx, moe_decode_dispatch_info *info);
@@ -189,13 +189,25 @@ moe_status moe_decode_last_dispatch(const moe_decode_ctx *ctx, moe_decode_dispat
  *     whose workgroups take the expert gate/up, shared-down, expert down and
  *     latent-up units from a queue in dependency order and wait on completion
  *     counters instead of kernel boundaries;
+ *   MOE_MODE_SIDE_STREAM: the shared expert on a second stream of the
+ *     context, as [P-vLLM] "他们换掉了什么" places it: on the caller's stream
+ *     dense-in for the router and latent-down rows (and the routing), expert
+ *     gate/up, expert down; on the side stream the shared gate/up and
+ *     shared-down launches, which depend on x alone; then, on the caller's
+ *     stream after an event join, latent-up plus the shared sums.  The
+ *     step stays capturable (fork and join are event record/wait pairs);
  *   MOE_MODE_FUSED: the whole step as one persistent launch of that kind
  *     (router, latent and shared units too), the single-launch design of
  *     [P-NV] "一个工程师、1.2万行代码、AI辅助开发".
  * Shapes without a built persistent kernel (the f32 router, other expert
  * chunk shapes) run the four launches.  All modes compute the same values.
  * Returns MOE_ERR_INVALID_ARG for another mode.  Host-only. */
-enum { MOE_MODE_FUSED = 0, MOE_MODE_FOUR_LAUNCHES = 1, MOE_MODE_TWO_LAUNCHES = 2 };
+enum {
+    MOE_MODE_FUSED = 0,
+    MOE_MODE_FOUR_LAUNCHES = 1,
+    MOE_MODE_TWO_LAUNCHES = 2,
+    MOE_MODE_SIDE_STREAM = 3
+};
 moe_status moe_decode_set_mode(moe_decode_ctx *ctx, int32_t mode);
 
 /* Reads the context's sticky fault flags into *flags (synchronous copy from
@@ -211,8 +223,9 @@ moe_status moe_decode_read_flags(moe_decode_ctx *ctx, uint32_t *flags);
  * the kernel's own execution time, as a kernel trace reports it.  n = 0
  * (events may be NULL) switches timing off.  Returns MOE_ERR_INVALID_ARG when
  * n fits none of the step's forms (8, or 10 with the f32 router, for four
- * launches; 4 for two launches; 2 for one); a step whose kernel count differs
- * from n is not timed. */
+ * launches; 12 or 14 with the side stream, in launch order: dense-in main,
+ * shared gate/up, gate/up, down, shared-down, latent-up; 4 for two launches;
+ * 2 for one); a step whose kernel count differs from n is not timed. */
 moe_status moe_decode_set_timing_events(moe_decode_ctx *ctx, void *const *events, int32_t n);
 
 /* Copies the intermediates of the last step out of the workspace as f32

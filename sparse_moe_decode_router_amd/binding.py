@@ -45,7 +45,7 @@ class Debug(ctypes.Structure):
                 ("score", "key", "z", "act", "ylat", "ash", "n_active")]
 
 
-MODE_FUSED, MODE_FOUR_LAUNCHES, MODE_TWO_LAUNCHES = 0, 1, 2
+MODE_FUSED, MODE_FOUR_LAUNCHES, MODE_TWO_LAUNCHES, MODE_SIDE_STREAM = 0, 1, 2, 3
 DEFAULT_MODE = MODE_FOUR_LAUNCHES  # what moe_decode_init selects
 
 EXPORTED = ("moe_decode_validate_config", "moe_decode_workspace_size", "moe_decode_init",
@@ -240,8 +240,9 @@ class MoEDecode:
         _check(lib().moe_decode_set_timing_events(self.handle, arr, len(events)), "timing events")
 
     def set_mode(self, mode: int) -> None:
-        """MODE_FUSED (one persistent launch where the shape has one) or
-        MODE_FOUR_LAUNCHES."""
+        """MODE_FOUR_LAUNCHES (default), MODE_SIDE_STREAM (shared expert on
+        the context's second stream), MODE_TWO_LAUNCHES or MODE_FUSED (one
+        persistent launch where the shape has one)."""
         _check(lib().moe_decode_set_mode(self.handle, mode), "set_mode")
 
     def read_flags(self) -> int:

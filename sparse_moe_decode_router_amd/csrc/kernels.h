@@ -918,9 +918,9 @@ __global__ void __launch_bounds__(kBlock) k_router_f32(const StepArgs a) {
     if (s_last) route_step(route_args(a), &s_route, kWavesPerBlock);
 }
 
-// Kernel 1: dense-in units over [router | latent | shared] tiles; each unit
-// covers all NCG = ceil(B / 16) column groups, so every weight tile is read
-// once per step.
+// Kernel 1: dense-in units over tiles [dense_lo, dense_hi) of the list
+// [router | latent | shared]; each unit covers all NCG = ceil(B / 16) column
+// groups, so every weight tile is read once per step.
 template <int NCG>
 __global__ void __launch_bounds__(kWGThreads) __attribute__((amdgpu_waves_per_eu(4)))
 k_dense_in(const StepArgs a) {
@@ -930,18 +930,18 @@ k_dense_in(const StepArgs a) {
     const Role ro = role_of(a.kw_in);
     if (threadIdx.x == 0) s_last = 0;
     // The latent combine accumulates into ylat with atomics later in the step.
-    for (int i = (blockIdx.x * kWGThreads + threadIdx.x) * 4; i < a.B * a.L;
-         i += gridDim.x * kWGThreads * 4)
-        stf4(a.ylat + i, zero4());
-    const int n_rt = a.n_rtiles, n_lt = a.L / a.latent_rows, n_st = a.Is >> 3;
-    const int n_t = n_rt + n_lt + n_st;
+    if (a.zero_ylat)
+        for (int i = (blockIdx.x * kWGThreads + threadIdx.x) * 4; i < a.B * a.L;
+             i += gridDim.x * kWGThreads * 4)
+            stf4(a.ylat + i, zero4());
+    const int n_rt = a.n_rtiles, n_lt = a.L / a.latent_rows;
     const int ncg = NCG == 1 ? (a.B + 15) >> 4 : 1;  // 1 whenever B <= 16
-    const int units = dense_units(n_t, ro.RW, ncg);
+    const int units = dense_units(a.dense_hi - a.dense_lo, ro.RW, ncg);
     for (int u = blockIdx.x; u < units; u += gridDim.x) {
         int cg, tg;
         dense_unit(u, ncg, cg, tg);
-        const int t = tg * ro.RW + ro.rg;
-        const bool active = t < n_t;
+        const int t = a.dense_lo + tg * ro.RW + ro.rg;
+        const bool active = t < a.dense_hi;
         const int kind = t < n_rt ? KIND_ROUTER : t < n_rt + n_lt ? KIND_LATENT : KIND_SHARED;
         const int tl = kind == KIND_ROUTER ? t : kind == KIND_LATENT ? t - n_rt : t - n_rt - n_lt;
         if constexpr (NCG == 1)
@@ -997,6 +997,30 @@ k_out(const StepArgs a) {
         dense_unit(u, nblk, cb, tg);
         const int t = tg * ro.RW + ro.rg;
         out_tile_n<NCG>(a, ro, t, t < n_t, cb * NCG, s_red);
+    }
+}
+
+// Output kernels of the side-stream step: shared-down (MODE = OUT_SHARED,
+// f32 sums to ysh, on the side stream) and latent-up (MODE = OUT_LATENT,
+// adds ysh, one bf16 rounding, on the caller's stream after the join); one
+// column group of 8 tokens per unit.
+template <int MODE>
+__global__ void __launch_bounds__(kWGThreads) __attribute__((amdgpu_waves_per_eu(4)))
+k_out_part(const StepArgs a) {
+    __shared__ float s_red[kWG * kWave * 4];
+    // The latent-up launch ends the step: it clears the router counter of the
+    // dense input kernel, as k_out does.
+    if (MODE == OUT_LATENT && blockIdx.x == 0 && threadIdx.x == 0) a.gctr[G_ROUTER_DONE] = 0u;
+    const Role ro = role_of(MODE == OUT_SHARED ? a.kw_sd : a.kw_lu);
+    const int spc = MODE == OUT_SHARED ? a.spc_sd : a.spc_lu;
+    const int ncg = (a.B + 7) >> 3;
+    const int n_t = (a.H + a.out_rows - 1) / a.out_rows;
+    const int units = dense_units(n_t, ro.RW, ncg);
+    for (int u = blockIdx.x; u < units; u += gridDim.x) {
+        int cg, tg;
+        dense_unit(u, ncg, cg, tg);
+        const int t = tg * ro.RW + ro.rg;
+        out_tile<false>(a, ro, MODE, t, t < n_t, cg, spc, s_red);
     }
 }
 

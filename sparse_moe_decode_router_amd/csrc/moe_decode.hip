@@ -227,9 +227,13 @@ struct moe_decode_ctx {
     int device;
     int32_t last_hip;
     moe_decode_dispatch_info last;
-    hipEvent_t events[10];  // timing events (caller-owned), n_events = 0: off
+    hipEvent_t events[14];  // timing events (caller-owned), n_events = 0: off
     int32_t n_events;
-    int32_t mode;           // MOE_MODE_FUSED or MOE_MODE_FOUR_LAUNCHES
+    int32_t mode;           // MOE_MODE_*
+    // Side-stream step: the library's second stream (default priority) and
+    // the fork / join events between it and the caller's stream.
+    hipStream_t side;
+    hipEvent_t fork_ev, join_ev;
     int32_t n_cus;          // compute units of the device
     StepKernel occ_kernel;  // fused kernel whose occupancy is cached
     int32_t occ_blocks;     // its resident workgroups per compute unit
@@ -384,7 +388,16 @@ moe_status moe_decode_init(const moe_decode_config *cfg, const moe_decode_weight
     ctx->n_cus = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 1;
     ctx->occ_kernel = nullptr;
     ctx->occ_blocks = 1;
+    ctx->side = nullptr;
+    ctx->fork_ev = ctx->join_ev = nullptr;
     std::memset(&ctx->last, 0, sizeof ctx->last);
+    e = hipStreamCreateWithFlags(&ctx->side, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&ctx->fork_ev, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&ctx->join_ev, hipEventDisableTiming);
+    if (e != hipSuccess) {
+        moe_decode_destroy(ctx);
+        return MOE_ERR_HIP;
+    }
 
     // Every counter starts at zero; the step returns them to zero itself.
     const size_t nwords = lay.counters_end / 4;
@@ -393,7 +406,7 @@ moe_status moe_decode_init(const moe_decode_config *cfg, const moe_decode_weight
     e = hipGetLastError();
     if (e == hipSuccess) e = hipStreamSynchronize(nullptr);
     if (e != hipSuccess) {
-        delete ctx;
+        moe_decode_destroy(ctx);
         return MOE_ERR_HIP;
     }
     *out = ctx;
@@ -414,6 +427,7 @@ moe_status moe_decode_step(moe_decode_ctx *ctx, const uint16_t *x, int32_t batch
     const StepKernel fused = ctx->mode == MOE_MODE_FUSED ? fused_kernel(c, pl) : nullptr;
     if (!fused) pl = make_plan(c, batch, top_k, false);
     const StepKernel tail = ctx->mode == MOE_MODE_TWO_LAUNCHES ? tail_kernel(c, pl) : nullptr;
+    const bool side = ctx->mode == MOE_MODE_SIDE_STREAM && pl.sd.kw > 0 && pl.lu.kw > 0;
     StepArgs a = base_args(ctx);
     a.B = batch;
     a.k = top_k;
@@ -433,6 +447,10 @@ moe_status moe_decode_step(moe_decode_ctx *ctx, const uint16_t *x, int32_t batch
     a.latent_rows = pl.latent_rows;
     a.spc_in = pl.in.spc;
     a.spc_out = pl.out.spc;
+    const int n_main = pl.n_rtiles + c.latent / pl.latent_rows;  // router + latent-down tiles
+    a.dense_lo = 0;
+    a.dense_hi = n_main + c.shared_inter / 8;
+    a.zero_ylat = 1;
     const long long cap = 65528;  // workgroups (a multiple of the XCD count); more units loop
 
     moe_decode_dispatch_info &d = ctx->last;
@@ -454,8 +472,8 @@ moe_status moe_decode_step(moe_decode_ctx *ctx, const uint16_t *x, int32_t batch
     d.grid_w2 = grid_for(pl.units_2, cap);
     d.grid_out = grid_for(pl.units_out, cap);
     d.router_f32 = c.router_dtype == MOE_ROUTER_F32;
-    d.fused = fused ? 1 : tail ? 2 : 0;
-    d.n_kernels = fused ? 1 : tail ? 2 : 4 + d.router_f32;
+    d.fused = fused ? 1 : tail ? 2 : side ? 3 : 0;
+    d.n_kernels = fused ? 1 : tail ? 2 : side ? 6 + d.router_f32 : 4 + d.router_f32;
     d.grid_step = 0;
     // One persistent workgroup per resident slot of `kernel` (the unit
     // queues do not rely on residency; this only sizes the grid).
@@ -508,21 +526,59 @@ moe_status moe_decode_step(moe_decode_ctx *ctx, const uint16_t *x, int32_t batch
 
     const bool timed = ctx->n_events == 2 * d.n_kernels;
     int ki = 0;
-    auto launch = [&](StepKernel kernel, unsigned grid, unsigned threads) {
+    auto launch_on = [&](hipStream_t st, StepKernel kernel, unsigned grid, unsigned threads,
+                         const StepArgs &args) {
         if (timed)
-            hipExtLaunchKernelGGL(kernel, dim3(grid), dim3(threads), 0, s, ctx->events[2 * ki],
-                                  ctx->events[2 * ki + 1], 0, a);
+            hipExtLaunchKernelGGL(kernel, dim3(grid), dim3(threads), 0, st, ctx->events[2 * ki],
+                                  ctx->events[2 * ki + 1], 0, args);
         else
-            hipLaunchKernelGGL(kernel, dim3(grid), dim3(threads), 0, s, a);
+            hipLaunchKernelGGL(kernel, dim3(grid), dim3(threads), 0, st, args);
         ++ki;
+    };
+    auto launch = [&](StepKernel kernel, unsigned grid, unsigned threads) {
+        launch_on(s, kernel, grid, threads, a);
     };
     if (fused) {
         launch(fused, d.grid_step, kWGThreads);
         const hipError_t e = hipGetLastError();
         return e == hipSuccess ? MOE_OK : hip_fail(ctx, e);
     }
-    if (d.router_f32) launch(k_router_f32, cdiv(c.n_experts, kWavesPerBlock), kBlock);
     const StepKernel dense_in[] = {k_dense_in<1>, k_dense_in<2>, k_dense_in<3>, k_dense_in<4>};
+    if (side) {
+        // The shared expert depends on x alone: its gate/up and down launches
+        // run on the side stream while the routed path runs on the caller's;
+        // the latent-up launch joins them.
+        a.kw_sd = pl.sd.kw;
+        a.spc_sd = pl.sd.spc;
+        a.kw_lu = pl.lu.kw;
+        a.spc_lu = pl.lu.spc;
+        const int rw_in = kWG / pl.in.kw, n_ot = cdiv(c.hidden, pl.out_rows);
+        StepArgs sa = a;
+        a.dense_hi = n_main;
+        sa.dense_lo = n_main;
+        sa.zero_ylat = 0;
+        hipError_t e = hipEventRecord(ctx->fork_ev, s);
+        if (e == hipSuccess) e = hipStreamWaitEvent(ctx->side, ctx->fork_ev, 0);
+        if (e != hipSuccess) return hip_fail(ctx, e);
+        if (d.router_f32) launch(k_router_f32, cdiv(c.n_experts, kWavesPerBlock), kBlock);
+        launch(dense_in[pl.ncg_in - 1], grid_for(dense_units_host(n_main, rw_in, 1), cap),
+               kWGThreads);
+        launch_on(ctx->side, dense_in[pl.ncg_in - 1],
+                  grid_for(dense_units_host(c.shared_inter / 8, rw_in, 1), cap), kWGThreads, sa);
+        launch(kW13[pl.s13], d.grid_w13, kWGThreads);
+        launch(split2 ? kW2Split[pl.s2] : kW2[pl.s2], d.grid_w2, kWGThreads);
+        launch_on(ctx->side, k_out_part<OUT_SHARED>,
+                  grid_for(dense_units_host(n_ot, kWG / pl.sd.kw, pl.ncg_out), cap), kWGThreads,
+                  sa);
+        e = hipEventRecord(ctx->join_ev, ctx->side);
+        if (e == hipSuccess) e = hipStreamWaitEvent(s, ctx->join_ev, 0);
+        if (e != hipSuccess) return hip_fail(ctx, e);
+        launch(k_out_part<OUT_LATENT>,
+               grid_for(dense_units_host(n_ot, kWG / pl.lu.kw, pl.ncg_out), cap), kWGThreads);
+        e = hipGetLastError();
+        return e == hipSuccess ? MOE_OK : hip_fail(ctx, e);
+    }
+    if (d.router_f32) launch(k_router_f32, cdiv(c.n_experts, kWavesPerBlock), kBlock);
     launch(dense_in[pl.ncg_in - 1], d.grid_in, kWGThreads);
     if (tail) {
         launch(tail, d.grid_step, kWGThreads);
@@ -540,6 +596,9 @@ moe_status moe_decode_step(moe_decode_ctx *ctx, const uint16_t *x, int32_t batch
 
 moe_status moe_decode_destroy(moe_decode_ctx *ctx) {
     if (!ctx) return MOE_ERR_INVALID_ARG;
+    if (ctx->side) (void)hipStreamDestroy(ctx->side);
+    if (ctx->fork_ev) (void)hipEventDestroy(ctx->fork_ev);
+    if (ctx->join_ev) (void)hipEventDestroy(ctx->join_ev);
     delete ctx;
     return MOE_OK;
 }
@@ -615,7 +674,8 @@ moe_status moe_decode_set_timing_events(moe_decode_ctx *ctx, void *const *events
         ctx->n_events = 0;
         return MOE_OK;
     }
-    if ((n != want && n != 2 && n != 4) || !events) return MOE_ERR_INVALID_ARG;
+    const int32_t want_side = want + 4;  // six (seven with the f32 router) launches
+    if ((n != want && n != want_side && n != 2 && n != 4) || !events) return MOE_ERR_INVALID_ARG;
     for (int i = 0; i < n; ++i) {
         if (!events[i]) return MOE_ERR_INVALID_ARG;
         ctx->events[i] = (hipEvent_t)events[i];
@@ -626,7 +686,7 @@ moe_status moe_decode_set_timing_events(moe_decode_ctx *ctx, void *const *events
 
 moe_status moe_decode_set_mode(moe_decode_ctx *ctx, int32_t mode) {
     if (!ctx || (mode != MOE_MODE_FUSED && mode != MOE_MODE_FOUR_LAUNCHES &&
-                 mode != MOE_MODE_TWO_LAUNCHES))
+                 mode != MOE_MODE_TWO_LAUNCHES && mode != MOE_MODE_SIDE_STREAM))
         return MOE_ERR_INVALID_ARG;
     ctx->mode = mode;
     return MOE_OK;

@@ -120,23 +120,26 @@ struct RouteLds {
     int wsum[kMaxRouteWaves][4];
 };
 
-// Best remaining experts of one lane, best first: orderable keys (0: none)
-// and slots (expert = lane + 64 * slot).
+// Best remaining experts of one lane, best first: orderable keys (0: none),
+// slots (expert = lane + 64 * slot) and scores.
 constexpr int kList = 4;
 struct LaneList {
     uint32_t k[kList];
     int i[kList];
+    float s[kList];
 };
 
 // The lane's kList best experts among those that come after (after_k,
 // after_i) in selection order: larger key first, equal keys by lower slot
 // (= lower expert id).  Branch-free insertion over the lane's slots.
 __device__ __forceinline__ void fill_list(LaneList &L, const uint32_t (&ok)[kKeysPerLane],
-                                          uint32_t after_k, int after_i) {
+                                          const float (&sc)[kKeysPerLane], uint32_t after_k,
+                                          int after_i) {
 #pragma unroll
     for (int j = 0; j < kList; ++j) {
         L.k[j] = 0u;
         L.i[j] = 0;
+        L.s[j] = 0.f;
     }
 #pragma unroll
     for (int i = 0; i < kKeysPerLane; ++i) {
@@ -150,22 +153,24 @@ __device__ __forceinline__ void fill_list(LaneList &L, const uint32_t (&ok)[kKey
         for (int j = kList - 1; j >= 1; --j) {
             L.k[j] = gt[j - 1] ? L.k[j - 1] : (gt[j] ? w : L.k[j]);
             L.i[j] = gt[j - 1] ? L.i[j - 1] : (gt[j] ? i : L.i[j]);
+            L.s[j] = gt[j - 1] ? L.s[j - 1] : (gt[j] ? sc[i] : L.s[j]);
         }
         L.k[0] = gt[0] ? w : L.k[0];
         L.i[0] = gt[0] ? i : L.i[0];
+        L.s[0] = gt[0] ? sc[i] : L.s[0];
     }
 }
 
 // Top-k of one token, by one wave.  Lane l owns experts l, l+64, ... and
-// keeps their keys in registers and a short list of its best remaining ones.
-// Each round takes the wave-wide largest list head (equal keys: the lowest
-// expert id), the winning lane pops its head (and refills its list after
-// kList pops), and the selection is recorded in lane r (round r) together
-// with its rank among the selected ids.  Then lane r fetches the score of
-// its selection; the sum of the selected scores is taken in selection order
-// and the ids are written in ascending order with weights s_e / sum(s).
-// Scores and keys are read with agent-scope loads: they were published by
-// other workgroups.
+// keeps their keys and scores in registers and a short list of its best
+// remaining ones.  Each round takes the wave-wide largest list head (equal
+// keys: the lowest expert id); lane r keeps the id and score of round r's
+// winner, and the winning lane drops its head (and rebuilds its list after
+// kList drops).  The round does nothing else: ranks among the selected ids
+// and the sum of the selected scores (in selection order) follow the last
+// round, and the ids are written in ascending order with weights
+// s_e / sum(s).  Scores and keys are read with agent-scope loads, all in one
+// batch: they were published by other workgroups.
 __device__ __forceinline__ void topk_token(const RouteArgs &a, int b, RouteLds &lds) {
     const int lane = lane_id();
     const int E = a.E, k = a.k;
@@ -176,17 +181,21 @@ __device__ __forceinline__ void topk_token(const RouteArgs &a, int b, RouteLds &
     // program order, so a use between two of them would serialise the round
     // trips.
     uint32_t ok[kKeysPerLane];
+    float sc[kKeysPerLane];
 #pragma unroll
     for (int i = 0; i < kKeysPerLane; ++i) ok[i] = __float_as_uint(load_agent(keyrow + lane + kWave * i));
+#pragma unroll
+    for (int i = 0; i < kKeysPerLane; ++i) sc[i] = load_agent(srow + lane + kWave * i);
 #pragma unroll
     for (int i = 0; i < kKeysPerLane; ++i) {
         const bool in = i < nk && lane + kWave * i < E;
         ok[i] = in ? orderable(__uint_as_float(ok[i])) : 0u;
     }
     LaneList L;
-    fill_list(L, ok, 0xFFFFFFFFu, -1);
+    fill_list(L, ok, sc, 0xFFFFFFFFu, -1);
     int npop = 0;
-    int mine = 0, rank = 0;
+    int mine = 0;
+    float s_mine = 0.f;
     for (int r = 0; r < k; ++r) {
         const uint32_t ck = L.k[0];
         const int cid = lane + kWave * L.i[0];
@@ -198,33 +207,38 @@ __device__ __forceinline__ void topk_token(const RouteArgs &a, int b, RouteLds &
             wl = (int)(wave_min_u32(id) & (kWave - 1));
         }
         const int e = (int)readlane((uint32_t)cid, wl);
-        // Ranks: earlier selections above e move up; the new one counts the
-        // earlier selections below it.
-        const bool earlier = lane < r;
-        rank += (earlier && mine > e) ? 1 : 0;
-        const unsigned long long below = __ballot(earlier && mine < e);
-        if (lane == r) {
-            mine = e;
-            rank = __popcll(below);
-        }
-        if (lane == wl) {
-            const uint32_t pk = L.k[0];
-            const int pi = L.i[0];
+        const float se = __uint_as_float(readlane(__float_as_uint(L.s[0]), wl));
+        mine = lane == r ? e : mine;
+        s_mine = lane == r ? se : s_mine;
+        // The winning lane drops its head; every lane runs the same
+        // selects, so the round has no branch.
+        const bool pop = lane == wl;
+        const uint32_t pk = L.k[0];
+        const int pi = L.i[0];
 #pragma unroll
-            for (int j = 0; j + 1 < kList; ++j) {
-                L.k[j] = L.k[j + 1];
-                L.i[j] = L.i[j + 1];
-            }
-            L.k[kList - 1] = 0u;
-            if (++npop == kList) {
-                fill_list(L, ok, pk, pi);
+        for (int j = 0; j + 1 < kList; ++j) {
+            L.k[j] = pop ? L.k[j + 1] : L.k[j];
+            L.i[j] = pop ? L.i[j + 1] : L.i[j];
+            L.s[j] = pop ? L.s[j + 1] : L.s[j];
+        }
+        L.k[kList - 1] = pop ? 0u : L.k[kList - 1];
+        npop += pop ? 1 : 0;
+        if (__ballot(npop == kList)) {  // rare: some lane used its whole list
+            if (npop == kList) {
+                fill_list(L, ok, sc, pk, pi);
                 npop = 0;
             }
         }
     }
-    const float s_mine = lane < k ? load_agent(srow + mine) : 0.f;
+    // Rank of each selection among the selected ids; sum of the selected
+    // scores in selection order.
+    int rank = 0;
     float total = 0.f;
-    for (int r = 0; r < k; ++r) total += __uint_as_float(readlane(__float_as_uint(s_mine), r));
+    for (int r = 0; r < k; ++r) {
+        const int other = (int)readlane((uint32_t)mine, r);
+        rank += other < mine ? 1 : 0;
+        total += __uint_as_float(readlane(__float_as_uint(s_mine), r));
+    }
     if (lane < k) {
         const float w = s_mine / total;
         const int o = b * k + rank;

@@ -32,6 +32,9 @@ struct StepArgs {
     // Two-launch step (dense-in, then one persistent launch): shared-down
     // units placed before the down units, latent-up units.
     int32_t n_sd_first, n_lu_units;
+    // Dense-in launch: tiles [dense_lo, dense_hi) of the list [router |
+    // latent-down | shared gate/up]; zero_ylat: this launch clears ylat.
+    int32_t dense_lo, dense_hi, zero_ylat;
     // Weights (borrowed).
     const uint16_t *router_w;
     const float *router_w32;

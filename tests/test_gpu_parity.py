@@ -274,21 +274,24 @@ def test_dispatch_follows_the_batch(small_layer, small_ctx):
         assert d["fused"] == 0 and d["n_kernels"] == 4
         assert d["grid_in"] >= 1 and d["grid_w13"] >= 1 and d["grid_step"] == 0
     try:
-        for mode, fused, n in ((binding.MODE_FUSED, 1, 1), (binding.MODE_TWO_LAUNCHES, 2, 2)):
+        for mode, fused, n in ((binding.MODE_FUSED, 1, 1), (binding.MODE_TWO_LAUNCHES, 2, 2),
+                               (binding.MODE_SIDE_STREAM, 3, 6)):
             small_ctx.set_mode(mode)
             run(small_ctx, synth.make_tokens(small_layer.dims, 14, 5), 6)
             d = small_ctx.last_dispatch()
-            assert d["fused"] == fused and d["n_kernels"] == n and d["grid_step"] >= 1
+            assert d["fused"] == fused and d["n_kernels"] == n
+            assert (d["grid_step"] >= 1) == (fused in (1, 2))  # persistent launches only
     finally:
         small_ctx.set_mode(binding.MODE_FOUR_LAUNCHES)
 
 
-PERSISTENT_MODES = [("fused", 1), ("two_launches", 2)]
+PERSISTENT_MODES = [("fused", 1), ("two_launches", 2), ("side_stream", 3)]
 
 
 def mode_const(name):
     return {"fused": binding.MODE_FUSED, "two_launches": binding.MODE_TWO_LAUNCHES,
-            "four_launches": binding.MODE_FOUR_LAUNCHES}[name]
+            "four_launches": binding.MODE_FOUR_LAUNCHES,
+            "side_stream": binding.MODE_SIDE_STREAM}[name]
 
 
 @pytest.mark.parametrize("mode,kind", PERSISTENT_MODES)
@@ -398,7 +401,7 @@ def test_k3_tp8_share_layer():
         log("  ", r)
 
 
-@pytest.mark.parametrize("mode", ["four_launches", "two_launches", "fused"])
+@pytest.mark.parametrize("mode", ["four_launches", "side_stream", "two_launches", "fused"])
 def test_c4_eight_layer_graph(mode):
     """Eight TP8-share layers (own seeds and inputs) captured in one HIP graph,
     the configuration the stacked benchmark replays: every layer's replayed
