@@ -882,6 +882,35 @@ __device__ __forceinline__ void out_tile(const StepArgs &a, const Role &ro, int 
 }
 
 // ---------------------------------------------------------------------------
+// Completion counters shared by workgroups of one launch
+// ---------------------------------------------------------------------------
+
+constexpr uint32_t kSpinLimit = 1u << 15;  // ~50 ms of polls: far beyond any legitimate wait
+
+// Counter increment after the whole workgroup's stores have completed.
+__device__ __forceinline__ void wg_publish(uint32_t *ctr, uint32_t v = 1u) {
+    wait_vm_all();
+    __syncthreads();
+    if (threadIdx.x == 0) __hip_atomic_fetch_add(ctr, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Returns once *ctr >= target (the whole workgroup waits at the barrier).
+__device__ __forceinline__ void wg_wait(const StepArgs &a, const uint32_t *ctr, uint32_t target) {
+    if (threadIdx.x == 0) {
+        uint32_t polls = 0;
+        while (load_agent(ctr) < target) {
+            if (++polls >= kSpinLimit) {
+                __hip_atomic_fetch_or(&a.gctr[G_ERROR], 1u, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(32);
+        }
+    }
+    __syncthreads();
+}
+
+// ---------------------------------------------------------------------------
 // Four-launch step
 // ---------------------------------------------------------------------------
 
@@ -948,10 +977,37 @@ k_dense_in(const StepArgs a) {
             dense_in_tile<false>(a, ro, kind, tl, active, cg, s_red, &s_last);
         else
             dense_in_tile_n<false, NCG>(a, ro, kind, tl, active, 0, s_red, &s_last);
-        if (s_last) {  // this workgroup completed the router: route the step
+        if (s_last && !a.route_units) {  // this workgroup completed the router: route the step
             route_step(route_args(a), &s_route, kWG);
             __syncthreads();
             if (threadIdx.x == 0) s_last = 0;
+        }
+    }
+    // Routing units (large batches): after the dense units, unit r routes
+    // tokens 8r .. 8r + 7 (a wave each) once the router is complete, and the
+    // last routing unit to finish builds the metadata from every unit's
+    // selections.  A routing unit waits only for router units, which come
+    // first in the grid.
+    for (int r = (int)blockIdx.x - units; r >= 0 && r < a.route_units; r += gridDim.x) {
+        wg_wait(a, &a.gctr[G_ROUTER_DONE], (uint32_t)a.router_target);
+        const RouteArgs ra = route_args(a);
+        const int b = kWG * r + wave_index();
+        if (b < a.B) topk_token(ra, b, s_route);
+        wait_vm_all();
+        __syncthreads();
+        if (threadIdx.x == 0)
+            s_last = __hip_atomic_fetch_add(&a.gctr[G_ROUTED], 1u, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT) ==
+                     (uint32_t)a.route_units - 1u;
+        __syncthreads();
+        if (s_last) {
+            for (int p = threadIdx.x; p < a.B * a.k; p += kWGThreads) {
+                s_route.idx[p] = (int16_t)load_agent(a.idx + p);
+                s_route.w[p] = load_agent(a.wsel + p);
+            }
+            __syncthreads();
+            build_meta(ra, s_route, kWG);
+            if (threadIdx.x == 0) store_agent(&a.gctr[G_ROUTED], 0u);  // ready for the next step
         }
     }
 }
@@ -1039,31 +1095,6 @@ k_out_part(const StepArgs a) {
 // increment; a waiting unit polls the counter from one lane (bounded: after
 // kSpinLimit polls it records G_ERROR and goes on instead of hanging).  The
 // last workgroup to leave the queue resets every counter for the next step.
-
-constexpr uint32_t kSpinLimit = 1u << 15;  // ~50 ms of polls: far beyond any legitimate wait
-
-// Counter increment after the whole workgroup's stores have completed.
-__device__ __forceinline__ void wg_publish(uint32_t *ctr, uint32_t v = 1u) {
-    wait_vm_all();
-    __syncthreads();
-    if (threadIdx.x == 0) __hip_atomic_fetch_add(ctr, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Returns once *ctr >= target (the whole workgroup waits at the barrier).
-__device__ __forceinline__ void wg_wait(const StepArgs &a, const uint32_t *ctr, uint32_t target) {
-    if (threadIdx.x == 0) {
-        uint32_t polls = 0;
-        while (load_agent(ctr) < target) {
-            if (++polls >= kSpinLimit) {
-                __hip_atomic_fetch_or(&a.gctr[G_ERROR], 1u, __ATOMIC_RELAXED,
-                                      __HIP_MEMORY_SCOPE_AGENT);
-                break;
-            }
-            __builtin_amdgcn_s_sleep(32);
-        }
-    }
-    __syncthreads();
-}
 
 // Active column units of the step (known once the routing has published).
 __device__ __forceinline__ int routed_units(const StepArgs &a) {

@@ -451,6 +451,9 @@ moe_status moe_decode_step(moe_decode_ctx *ctx, const uint16_t *x, int32_t batch
     a.dense_lo = 0;
     a.dense_hi = n_main + c.shared_inter / 8;
     a.zero_ylat = 1;
+    // Above 8 tokens the routing is spread over routing units (8 tokens
+    // each) appended to the dense-in launch.
+    a.route_units = c.router_dtype == MOE_ROUTER_BF16 && batch > 8 ? cdiv(batch, kWG) : 0;
     const long long cap = 65528;  // workgroups (a multiple of the XCD count); more units loop
 
     moe_decode_dispatch_info &d = ctx->last;
@@ -467,7 +470,7 @@ moe_status moe_decode_step(moe_decode_ctx *ctx, const uint16_t *x, int32_t batch
     if (split2) pl.units_2 = (long long)ncols_cap(c.n_experts, batch, top_k) *
                              cdiv(c.latent / 16, kWG / 2);
     d.split_w2 = split2 ? 2 : 1;
-    d.grid_in = grid_for(pl.units_in, cap);
+    d.grid_in = (int32_t)(pl.units_in + a.route_units);  // every unit its own workgroup
     d.grid_w13 = grid_for(pl.units_13, cap);
     d.grid_w2 = grid_for(pl.units_2, cap);
     d.grid_out = grid_for(pl.units_out, cap);
@@ -557,11 +560,12 @@ moe_status moe_decode_step(moe_decode_ctx *ctx, const uint16_t *x, int32_t batch
         a.dense_hi = n_main;
         sa.dense_lo = n_main;
         sa.zero_ylat = 0;
+        sa.route_units = 0;
         hipError_t e = hipEventRecord(ctx->fork_ev, s);
         if (e == hipSuccess) e = hipStreamWaitEvent(ctx->side, ctx->fork_ev, 0);
         if (e != hipSuccess) return hip_fail(ctx, e);
         if (d.router_f32) launch(k_router_f32, cdiv(c.n_experts, kWavesPerBlock), kBlock);
-        launch(dense_in[pl.ncg_in - 1], grid_for(dense_units_host(n_main, rw_in, 1), cap),
+        launch(dense_in[pl.ncg_in - 1], (unsigned)(dense_units_host(n_main, rw_in, 1) + a.route_units),
                kWGThreads);
         launch_on(ctx->side, dense_in[pl.ncg_in - 1],
                   grid_for(dense_units_host(c.shared_inter / 8, rw_in, 1), cap), kWGThreads, sa);

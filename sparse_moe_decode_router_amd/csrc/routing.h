@@ -244,8 +244,10 @@ __device__ __forceinline__ void topk_token(const RouteArgs &a, int b, RouteLds &
         const int o = b * k + rank;
         lds.idx[o] = (int16_t)mine;
         lds.w[o] = w;
-        a.idx[o] = mine;
-        a.wsel[o] = w;
+        // Agent-scope: with routing units, another workgroup of the launch
+        // builds the metadata from these.
+        store_agent(a.idx + o, mine);
+        store_agent(a.wsel + o, w);
         if (a.user_idx) a.user_idx[o] = mine;
         if (a.user_w) a.user_w[o] = w;
     }

@@ -35,6 +35,9 @@ struct StepArgs {
     // Dense-in launch: tiles [dense_lo, dense_hi) of the list [router |
     // latent-down | shared gate/up]; zero_ylat: this launch clears ylat.
     int32_t dense_lo, dense_hi, zero_ylat;
+    // Routing units appended to the dense-in launch (0: the workgroup that
+    // completes the router routes the whole step).
+    int32_t route_units;
     // Weights (borrowed).
     const uint16_t *router_w;
     const float *router_w32;
