@@ -415,21 +415,78 @@ __device__ __forceinline__ void dense_in_tile(const StepArgs &a, const Role &ro,
     __syncthreads();
 }
 
+// Row pointer of lane (row n = lane % 16) in dense-in tile t of `kind`.
+__device__ __forceinline__ const uint16_t *dense_in_row(const StepArgs &a, int kind, int tt) {
+    const int n = lane_id() & 15;
+    const int RR = a.router_rows, RL = a.latent_rows;
+    if (kind == KIND_ROUTER) return a.router_w + (size_t)(RR * tt + min(n, RR - 1)) * a.H;
+    if (kind == KIND_LATENT) return a.lat_down + (size_t)(RL * tt + min(n, RL - 1)) * a.H;
+    return a.sh_w13 + (size_t)((n < 8 ? 0 : a.Is) + 8 * tt + (n & 7)) * a.H;
+}
+
+// Epilogue of dense-in tile tt of `kind` for the NCG column groups cg0 ..
+// cg0 + NCG - 1 (acc: the tile's full sums, MFMA layout), run by the one
+// wave that holds them: router scores and keys (then an arrival on the router
+// counter, *s_last set by the arrival that completes it), z or the shared
+// activation as hi/lo rows.
+template <bool Coh, int NCG>
+__device__ __forceinline__ void dense_in_epilogue(const StepArgs &a, int kind, int tt, int cg0,
+                                                  const f32x4 (&acc)[NCG], int *s_last) {
+    const int lane = lane_id(), n = lane & 15, g = lane >> 4;
+    const int RR = a.router_rows, RL = a.latent_rows;
+    if (kind == KIND_ROUTER) {
+        const int e = RR * tt + 4 * g;
+        // Rows past RR (short router tiles) have no bias entry.
+        const f32x4 bv = a.bias && 4 * g < RR ? ldf4(a.bias + e) : zero4();
+#pragma unroll
+        for (int c = 0; c < NCG; ++c) {
+            const int b = 16 * (cg0 + c) + n;
+            if (b < a.B && 4 * g < RR) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float sv = sigmoidf_(acc[c][i]);
+                    store_agent(a.score + (size_t)b * kMaxExperts + e + i, sv);
+                    store_agent(a.key + (size_t)b * kMaxExperts + e + i, sv + bv[i]);
+                }
+            }
+        }
+        if (wave_publish(&a.gctr[G_ROUTER_DONE]) == (uint32_t)a.router_target - 1u && lane == 0)
+            *s_last = 1;
+    } else if (kind == KIND_LATENT) {
+#pragma unroll
+        for (int c = 0; c < NCG; ++c) {
+            const int b = 16 * (cg0 + c) + n;
+            if (b < a.B && 4 * g < RL) {
+                uint16_t *dst = a.zhl + (size_t)b * 2 * a.L + RL * tt + 4 * g;
+                store_hl4<Coh>(dst, dst + a.L, acc[c]);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int c = 0; c < NCG; ++c) {
+            const int b = 16 * (cg0 + c) + n;
+            f32x4 up;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) up[i] = __shfl_xor(acc[c][i], 32);
+            if (b < a.B && g < 2) {
+                f32x4 v;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) v[i] = silu_mul(acc[c][i], up[i]);
+                uint16_t *dst = a.ashhl + (size_t)b * 2 * a.Is + 8 * tt + 4 * g;
+                store_hl4<Coh>(dst, dst + a.Is, v);
+            }
+        }
+    }
+}
+
 // dense_in_tile for the NCG >= 2 column groups cg0 .. cg0 + NCG - 1 (s_red:
 // NCG reduction slices): every weight step is loaded once for all of them.
 template <bool Coh, int NCG>
 __device__ __forceinline__ void dense_in_tile_n(const StepArgs &a, const Role &ro, int kind, int t,
-                                              bool active, int cg0, float *s_red, int *s_last) {
-    const int lane = lane_id(), n = lane & 15, g = lane >> 4;
+                                                bool active, int cg0, float *s_red, int *s_last) {
+    const int n = lane_id() & 15, g = lane_id() >> 4;
     const int tt = active ? t : 0;
-    const uint16_t *A;
-    const int RR = a.router_rows, RL = a.latent_rows;
-    if (kind == KIND_ROUTER)
-        A = a.router_w + (size_t)(RR * tt + min(n, RR - 1)) * a.H;
-    else if (kind == KIND_LATENT)
-        A = a.lat_down + (size_t)(RL * tt + min(n, RL - 1)) * a.H;
-    else
-        A = a.sh_w13 + (size_t)((n < 8 ? 0 : a.Is) + 8 * tt + (n & 7)) * a.H;
+    const uint16_t *A = dense_in_row(a, kind, tt);
     const uint16_t *X[NCG];
     bool valid[NCG];
     f32x4 acc[NCG];
@@ -443,52 +500,7 @@ __device__ __forceinline__ void dense_in_tile_n(const StepArgs &a, const Role &r
     if (active)
         dense_chunk_xn<NCG>(A + 8 * g, X, valid, ro.kw * a.spc_in, (ro.kw + 1) * a.spc_in, acc);
     const bool leader = reduce_kn<NCG>(s_red, ro.wave, ro.kw, ro.KW, acc);
-    if (leader && active) {
-        if (kind == KIND_ROUTER) {
-            const int e = RR * tt + 4 * g;
-            // Rows past RR (short router tiles) have no bias entry.
-            const f32x4 bv = a.bias && 4 * g < RR ? ldf4(a.bias + e) : zero4();
-#pragma unroll
-            for (int c = 0; c < NCG; ++c) {
-                const int b = 16 * (cg0 + c) + n;
-                if (valid[c] && 4 * g < RR) {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const float sv = sigmoidf_(acc[c][i]);
-                        store_agent(a.score + (size_t)b * kMaxExperts + e + i, sv);
-                        store_agent(a.key + (size_t)b * kMaxExperts + e + i, sv + bv[i]);
-                    }
-                }
-            }
-            if (wave_publish(&a.gctr[G_ROUTER_DONE]) == (uint32_t)a.router_target - 1u &&
-                lane == 0)
-                *s_last = 1;
-        } else if (kind == KIND_LATENT) {
-#pragma unroll
-            for (int c = 0; c < NCG; ++c) {
-                const int b = 16 * (cg0 + c) + n;
-                if (valid[c] && 4 * g < RL) {
-                    uint16_t *dst = a.zhl + (size_t)b * 2 * a.L + RL * tt + 4 * g;
-                    store_hl4<Coh>(dst, dst + a.L, acc[c]);
-                }
-            }
-        } else {
-#pragma unroll
-            for (int c = 0; c < NCG; ++c) {
-                const int b = 16 * (cg0 + c) + n;
-                f32x4 up;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) up[i] = __shfl_xor(acc[c][i], 32);
-                if (valid[c] && g < 2) {
-                    f32x4 v;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) v[i] = silu_mul(acc[c][i], up[i]);
-                    uint16_t *dst = a.ashhl + (size_t)b * 2 * a.Is + 8 * tt + 4 * g;
-                    store_hl4<Coh>(dst, dst + a.Is, v);
-                }
-            }
-        }
-    }
+    if (leader && active) dense_in_epilogue<Coh, NCG>(a, kind, tt, cg0, acc, s_last);
     __syncthreads();
 }
 
@@ -947,6 +959,37 @@ __global__ void __launch_bounds__(kBlock) k_router_f32(const StepArgs a) {
     if (s_last) route_step(route_args(a), &s_route, kWavesPerBlock);
 }
 
+// Routing units (large batches), after the `units` dense units of the
+// launch: unit r routes tokens 8r .. 8r + 7 (a wave each) once the router is
+// complete, and the last routing unit to finish builds the metadata from
+// every unit's selections.  A routing unit waits only for router units,
+// which come first in the grid.
+__device__ __forceinline__ void routing_units(const StepArgs &a, int units, RouteLds &s_route,
+                                              int *s_flag) {
+    for (int r = (int)blockIdx.x - units; r >= 0 && r < a.route_units; r += gridDim.x) {
+        wg_wait(a, &a.gctr[G_ROUTER_DONE], (uint32_t)a.router_target);
+        const RouteArgs ra = route_args(a);
+        const int b = kWG * r + wave_index();
+        if (b < a.B) topk_token(ra, b, s_route);
+        wait_vm_all();
+        __syncthreads();
+        if (threadIdx.x == 0)
+            *s_flag = __hip_atomic_fetch_add(&a.gctr[G_ROUTED], 1u, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT) ==
+                      (uint32_t)a.route_units - 1u;
+        __syncthreads();
+        if (*s_flag) {
+            for (int p = threadIdx.x; p < a.B * a.k; p += kWGThreads) {
+                s_route.idx[p] = (int16_t)load_agent(a.idx + p);
+                s_route.w[p] = load_agent(a.wsel + p);
+            }
+            __syncthreads();
+            build_meta(ra, s_route, kWG);
+            if (threadIdx.x == 0) store_agent(&a.gctr[G_ROUTED], 0u);  // ready for the next step
+        }
+    }
+}
+
 // Kernel 1: dense-in units over tiles [dense_lo, dense_hi) of the list
 // [router | latent | shared]; each unit covers all NCG = ceil(B / 16) column
 // groups, so every weight tile is read once per step.
@@ -983,33 +1026,132 @@ k_dense_in(const StepArgs a) {
             if (threadIdx.x == 0) s_last = 0;
         }
     }
-    // Routing units (large batches): after the dense units, unit r routes
-    // tokens 8r .. 8r + 7 (a wave each) once the router is complete, and the
-    // last routing unit to finish builds the metadata from every unit's
-    // selections.  A routing unit waits only for router units, which come
-    // first in the grid.
-    for (int r = (int)blockIdx.x - units; r >= 0 && r < a.route_units; r += gridDim.x) {
-        wg_wait(a, &a.gctr[G_ROUTER_DONE], (uint32_t)a.router_target);
-        const RouteArgs ra = route_args(a);
-        const int b = kWG * r + wave_index();
-        if (b < a.B) topk_token(ra, b, s_route);
+    routing_units(a, units, s_route, &s_last);
+}
+
+// Kernel 1 for more than 16 tokens (NCG = ceil(B / 16) >= 2 column groups).
+// A unit is a row group (8 tiles, one per wave) times a K slice of a.kx_sps
+// steps.  Per pair of steps the workgroup copies the x columns of every
+// token (64 rows x 128 bf16 per step) straight into LDS once, and all 8 waves
+// multiply their own weight rows against that copy: x is read once per row
+// group and step instead of once per tile and step.  A slice's partial sums
+// go to a.part; the last slice of a row group to arrive sums them in slice
+// order and runs the tile epilogues, so the results do not depend on the
+// order of arrival.
+constexpr int kXRows = 64;  // token rows of one staged step
+
+// Copies the x columns of step s into buf: row b (token b; rows past B copy
+// token 0 and are never used) at b * 128 elements, its 16-byte chunk q at
+// position q ^ (b & 15), so that the 16 rows of one MFMA operand read sit on
+// distinct banks.  Two 16-byte copies per thread, landing at their wave's
+// block base + 16 * lane.
+__device__ __forceinline__ void stage_x_step(uint16_t *buf, const StepArgs &a, int s) {
+    const int lane = lane_id(), wave = wave_index();
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int c0 = 64 * (wave + kWG * h), c = c0 + lane;
+        const int b = c >> 4, q = (c & 15) ^ (b & 15);
+        const uint16_t *gp = a.x + (size_t)(b < a.B ? b : 0) * a.H + (size_t)s * kKStep + 8 * q;
+        __builtin_amdgcn_global_load_lds(gp, buf + 8 * c0, 16, 0, 0);
+    }
+}
+
+// MFMA j's x operand of column group c from a staged step: token 16c + n,
+// elements [32j + 8g, 32j + 8g + 8).
+__device__ __forceinline__ bf16x8 x_operand(const uint16_t *buf, int c, int j) {
+    const int lane = lane_id(), n = lane & 15, g = lane >> 4;
+    return as_bf16x8(*(const u32x4 *)(buf + (16 * c + n) * kKStep + 8 * ((4 * j + g) ^ n)));
+}
+
+template <int NCG>
+__global__ void __launch_bounds__(kWGThreads) __attribute__((amdgpu_waves_per_eu(4)))
+k_dense_in_kx(const StepArgs a) {
+    __shared__ __attribute__((aligned(16))) uint16_t s_x[2][kXRows * kKStep];
+    __shared__ RouteLds s_route;
+    __shared__ int s_last, s_arrive;
+    const int lane = lane_id(), wave = wave_index(), g = lane >> 4;
+    if (threadIdx.x == 0) s_last = 0;
+    if (a.zero_ylat)
+        for (int i = (blockIdx.x * kWGThreads + threadIdx.x) * 4; i < a.B * a.L;
+             i += gridDim.x * kWGThreads * 4)
+            stf4(a.ylat + i, zero4());
+    const int n_rt = a.n_rtiles, n_lt = a.L / a.latent_rows;
+    const int nsteps = a.H / kKStep, sps = a.kx_sps, nsl = (nsteps + sps - 1) / sps;
+    const int nrg = (a.dense_hi - a.dense_lo + kWG - 1) / kWG;
+    const int units = nrg * nsl;
+    const rsrc_t rpart = buf_rsrc(a.part);
+    for (int u = blockIdx.x; u < units; u += gridDim.x) {
+        const int rg = u / nsl, ks = u % nsl;
+        const int t = a.dense_lo + rg * kWG + wave;
+        const bool active = t < a.dense_hi;
+        const int kind = t < n_rt ? KIND_ROUTER : t < n_rt + n_lt ? KIND_LATENT : KIND_SHARED;
+        const int tl = kind == KIND_ROUTER ? t : kind == KIND_LATENT ? t - n_rt : t - n_rt - n_lt;
+        const int tt = active ? tl : 0;
+        const uint16_t *A = dense_in_row(a, kind, tt) + 8 * g;
+        const int s0 = ks * sps, s1 = min(nsteps, s0 + sps);
+        f32x4 acc[NCG];
+#pragma unroll
+        for (int c = 0; c < NCG; ++c) acc[c] = zero4();
+        for (int s = s0; s < s1; s += 2) {
+            const bool two = s + 1 < s1;
+            __syncthreads();  // every wave is done with the staged copies
+            u32x4 ra0[4], ra1[4];
+            stage_x_step(s_x[0], a, s);
+            stage_x_step(s_x[1], a, two ? s + 1 : s);
+            load_tile_bf16(A, s, ra0);
+            load_tile_bf16(A, two ? s + 1 : s, ra1);
+            fence_schedule();
+            wait_vm_all();  // this thread's copies and weights have landed
+            staged_barrier();
+#pragma unroll
+            for (int c = 0; c < NCG; ++c)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[c] = mfma(as_bf16x8(ra0[j]), x_operand(s_x[0], c, j), acc[c]);
+            if (two) {
+#pragma unroll
+                for (int c = 0; c < NCG; ++c)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        acc[c] = mfma(as_bf16x8(ra1[j]), x_operand(s_x[1], c, j), acc[c]);
+            }
+        }
+        // Partial sums of the slice, in MFMA layout: part[ks][t][c][lane].
+        if (active) {
+#pragma unroll
+            for (int c = 0; c < NCG; ++c) {
+                uint64_t *dst = (uint64_t *)(a.part + ((((size_t)ks * a.kx_tiles + t) * NCG + c) * kWave + lane) * 4);
+                const uint64_t lo = (uint64_t)__float_as_uint(acc[c][0]) | ((uint64_t)__float_as_uint(acc[c][1]) << 32);
+                const uint64_t hi = (uint64_t)__float_as_uint(acc[c][2]) | ((uint64_t)__float_as_uint(acc[c][3]) << 32);
+                __hip_atomic_store(dst, lo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(dst + 1, hi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
         wait_vm_all();
         __syncthreads();
+        uint32_t *rgc = a.rgc + (size_t)(a.dense_lo ? a.kx_groups : 0) * kCtrStride + (size_t)rg * kCtrStride;
         if (threadIdx.x == 0)
-            s_last = __hip_atomic_fetch_add(&a.gctr[G_ROUTED], 1u, __ATOMIC_RELAXED,
-                                            __HIP_MEMORY_SCOPE_AGENT) ==
-                     (uint32_t)a.route_units - 1u;
+            s_arrive = __hip_atomic_fetch_add(rgc, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                       (uint32_t)nsl - 1u;
         __syncthreads();
-        if (s_last) {
-            for (int p = threadIdx.x; p < a.B * a.k; p += kWGThreads) {
-                s_route.idx[p] = (int16_t)load_agent(a.idx + p);
-                s_route.w[p] = load_agent(a.wsel + p);
+        if (s_arrive) {  // the row group's last slice: sum the slices in order
+            if (active) {
+                f32x4 sum[NCG];
+#pragma unroll
+                for (int c = 0; c < NCG; ++c) sum[c] = zero4();
+                for (int k2 = 0; k2 < nsl; ++k2) {
+#pragma unroll
+                    for (int c = 0; c < NCG; ++c) {
+                        const uint32_t off = (uint32_t)(((((size_t)k2 * a.kx_tiles + t) * NCG + c) * kWave + lane) * 16);
+                        sum[c] += __builtin_bit_cast(f32x4, buf_ld16<true>(rpart, off));
+                    }
+                }
+                dense_in_epilogue<false, NCG>(a, kind, tt, 0, sum, &s_last);
             }
-            __syncthreads();
-            build_meta(ra, s_route, kWG);
-            if (threadIdx.x == 0) store_agent(&a.gctr[G_ROUTED], 0u);  // ready for the next step
+            if (threadIdx.x == 0) store_agent(rgc, 0u);  // ready for the next step
         }
+        __syncthreads();
     }
+    routing_units(a, units, s_route, &s_last);
 }
 
 // Kernel 2: gate/up units.

@@ -154,9 +154,17 @@ StepKernel fused_kernel(const moe_decode_config &c, const Plan &p) {
     return nullptr;
 }
 
+// Dense-in tiles of the four-launch plan (16-row router and latent tiles,
+// shared tiles of 8 gate + 8 up rows) and their row groups of 8.
+int dense_tiles(const moe_decode_config &c) {
+    return (c.router_dtype == MOE_ROUTER_BF16 ? c.n_experts / 16 : 0) + c.latent / 16 +
+           c.shared_inter / 8;
+}
+constexpr int kMaxSlices = 16;  // K slices of the large-batch dense-in kernel
+
 struct Layout {
-    size_t gctr, meta, c13, score, key, idx, wsel, act_expert, act_off, cu_rec, pair_slot,
-        pair_of_slot, zhl, ashhl, acthl, ylat, ysh, total;
+    size_t gctr, meta, c13, rgc, score, key, idx, wsel, act_expert, act_off, cu_rec, pair_slot,
+        pair_of_slot, zhl, ashhl, acthl, ylat, ysh, part, total;
     size_t counters_end;  // [0, counters_end) holds every counter: cleared at init
 };
 
@@ -175,6 +183,8 @@ Layout make_layout(const moe_decode_config &c) {
     l.gctr = take(G_COUNT * 4);
     l.meta = take(M_COUNT * 4);
     l.c13 = take(ncols * kCtrStride * 4);
+    const size_t groups = (size_t)cdiv(dense_tiles(c), kWG);
+    l.rgc = take(2 * groups * kCtrStride * 4);  // caller's and side stream's launches
     l.counters_end = o;
     // Score and key rows are padded to kMaxExperts: the routing reads a whole
     // row with one base address (entries past E are never used).
@@ -192,6 +202,9 @@ Layout make_layout(const moe_decode_config &c) {
     l.acthl = take(P * 2 * I * 2);
     l.ylat = take(Bm * L * 4);
     l.ysh = take(Bm * (size_t)c.hidden * 4);
+    // Slice partials of the large-batch dense-in kernel (batches above 16).
+    const size_t ncg = (size_t)cdiv(c.max_batch, 16);
+    l.part = take(ncg >= 2 ? (size_t)kMaxSlices * dense_tiles(c) * ncg * kWave * 16 : 0);
     l.total = o;
     return l;
 }
@@ -296,6 +309,10 @@ StepArgs base_args(const moe_decode_ctx *ctx) {
     a.ylat = (float *)(ws + l.ylat);
     a.ysh = (float *)(ws + l.ysh);
     a.c13 = (uint32_t *)(ws + l.c13);
+    a.part = (float *)(ws + l.part);
+    a.rgc = (uint32_t *)(ws + l.rgc);
+    a.kx_tiles = dense_tiles(ctx->cfg);
+    a.kx_groups = cdiv(a.kx_tiles, kWG);
     return a;
 }
 
@@ -547,6 +564,28 @@ moe_status moe_decode_step(moe_decode_ctx *ctx, const uint16_t *x, int32_t batch
         return e == hipSuccess ? MOE_OK : hip_fail(ctx, e);
     }
     const StepKernel dense_in[] = {k_dense_in<1>, k_dense_in<2>, k_dense_in<3>, k_dense_in<4>};
+    const StepKernel dense_in_kx[] = {nullptr, k_dense_in_kx<2>, k_dense_in_kx<3>,
+                                      k_dense_in_kx<4>};
+    // Above 16 tokens the dense-in launch stages x in LDS per row group of 8
+    // tiles and splits K into slices, about two units per compute unit.
+    const bool kx = pl.ncg_in >= 2 && pl.latent_rows == 16 && pl.router_rows == 16;
+    auto dense_launch = [&](hipStream_t st, StepArgs &args) {
+        if (!kx) {
+            const int rw_in = kWG / pl.in.kw;
+            launch_on(st, dense_in[pl.ncg_in - 1],
+                      (unsigned)(dense_units_host(args.dense_hi - args.dense_lo, rw_in, 1) +
+                                 args.route_units),
+                      kWGThreads, args);
+            return;
+        }
+        const int nsteps = c.hidden / kKStep;
+        const int nrg = cdiv(args.dense_hi - args.dense_lo, kWG);
+        int nsl = std::max(1, std::min({kMaxSlices, nsteps, (2 * ctx->n_cus + nrg / 2) / nrg}));
+        args.kx_sps = cdiv(nsteps, nsl);
+        nsl = cdiv(nsteps, args.kx_sps);
+        launch_on(st, dense_in_kx[pl.ncg_in - 1], (unsigned)(nrg * nsl + args.route_units),
+                  kWGThreads, args);
+    };
     if (side) {
         // The shared expert depends on x alone: its gate/up and down launches
         // run on the side stream while the routed path runs on the caller's;
@@ -555,7 +594,7 @@ moe_status moe_decode_step(moe_decode_ctx *ctx, const uint16_t *x, int32_t batch
         a.spc_sd = pl.sd.spc;
         a.kw_lu = pl.lu.kw;
         a.spc_lu = pl.lu.spc;
-        const int rw_in = kWG / pl.in.kw, n_ot = cdiv(c.hidden, pl.out_rows);
+        const int n_ot = cdiv(c.hidden, pl.out_rows);
         StepArgs sa = a;
         a.dense_hi = n_main;
         sa.dense_lo = n_main;
@@ -565,10 +604,8 @@ moe_status moe_decode_step(moe_decode_ctx *ctx, const uint16_t *x, int32_t batch
         if (e == hipSuccess) e = hipStreamWaitEvent(ctx->side, ctx->fork_ev, 0);
         if (e != hipSuccess) return hip_fail(ctx, e);
         if (d.router_f32) launch(k_router_f32, cdiv(c.n_experts, kWavesPerBlock), kBlock);
-        launch(dense_in[pl.ncg_in - 1], (unsigned)(dense_units_host(n_main, rw_in, 1) + a.route_units),
-               kWGThreads);
-        launch_on(ctx->side, dense_in[pl.ncg_in - 1],
-                  grid_for(dense_units_host(c.shared_inter / 8, rw_in, 1), cap), kWGThreads, sa);
+        dense_launch(s, a);
+        dense_launch(ctx->side, sa);
         launch(kW13[pl.s13], d.grid_w13, kWGThreads);
         launch(split2 ? kW2Split[pl.s2] : kW2[pl.s2], d.grid_w2, kWGThreads);
         launch_on(ctx->side, k_out_part<OUT_SHARED>,
@@ -583,7 +620,7 @@ moe_status moe_decode_step(moe_decode_ctx *ctx, const uint16_t *x, int32_t batch
         return e == hipSuccess ? MOE_OK : hip_fail(ctx, e);
     }
     if (d.router_f32) launch(k_router_f32, cdiv(c.n_experts, kWavesPerBlock), kBlock);
-    launch(dense_in[pl.ncg_in - 1], d.grid_in, kWGThreads);
+    dense_launch(s, a);
     if (tail) {
         launch(tail, d.grid_step, kWGThreads);
         const hipError_t e = hipGetLastError();

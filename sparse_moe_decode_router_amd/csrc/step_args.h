@@ -38,6 +38,9 @@ struct StepArgs {
     // Routing units appended to the dense-in launch (0: the workgroup that
     // completes the router routes the whole step).
     int32_t route_units;
+    // Dense-in above 16 tokens: steps per K slice, tiles and row groups of
+    // the whole tile list (partial-buffer stride and counter offset).
+    int32_t kx_sps, kx_tiles, kx_groups;
     // Weights (borrowed).
     const uint16_t *router_w;
     const float *router_w32;
@@ -63,6 +66,8 @@ struct StepArgs {
     uint16_t *zhl, *acthl, *ashhl;
     float *ylat;  // f32 latent combine (atomic adds)
     float *ysh;   // fused step: shared-down sums [B][H] f32
+    float *part;    // dense-in above 16 tokens: slice partials [slice][tile][group][lane][4]
+    uint32_t *rgc;  // ... arrivals per row group, 256 B apart (two sets: caller / side stream)
 };
 
 }  // namespace moe

@@ -197,6 +197,22 @@ def assert_same_step(a, b):
     assert np.mean(a[0] != b[0]) < 1e-2
 
 
+def assert_modes_agree(a, b):
+    """Two execution modes of one step.  Above 16 tokens the four-launch
+    dense-in kernel sums the router's K slices in another order than the
+    single-launch step, so scores can differ in their last f32 bits: a near
+    tie may then select another expert.  Tokens with the same experts must
+    have weights within 2e-6 and outputs within the bound of assert_same_step;
+    at most 5 % of the tokens may differ in their experts."""
+    same = np.all(a[1] == b[1], axis=1)
+    assert np.mean(same) >= 0.95
+    np.testing.assert_allclose(a[2][same], b[2][same], rtol=0, atol=2e-6)
+    fa, fb = bf16_f64(a[0][same]), bf16_f64(b[0][same])
+    rms = np.sqrt(np.mean(fa * fa, axis=1, keepdims=True))
+    ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(fa), np.abs(fb)) + 1e-300)) - 7)
+    assert np.all(np.abs(fa - fb) <= np.maximum(ulp, rms * 2.0 ** -16))
+
+
 def test_repeated_steps_agree(small_layer, small_ctx):
     x = synth.make_tokens(small_layer.dims, 11, 24)
     a = run(small_ctx, x, 6)
@@ -308,7 +324,7 @@ def test_four_launch_step_matches_persistent(small_layer, B, mode, kind):
     a = run(fused, x, k)
     b = run(four, x, k)
     assert fused.last_dispatch()["fused"] == kind and four.last_dispatch()["fused"] == 0
-    assert_same_step(a, b)
+    assert_modes_agree(a, b)
     check_step(small_layer, x, k, *a)
 
 
@@ -387,7 +403,7 @@ def test_k3_persistent_step_matches_four_launches(k3_dev, bias_kind, B, mode, ki
     a = run(four, x, 16)
     b = run(fused, x, 16)
     assert fused.last_dispatch()["fused"] == kind and four.last_dispatch()["fused"] == 0
-    assert_same_step(a, b)
+    assert_modes_agree(a, b)
 
 
 def test_k3_tp8_share_layer():
