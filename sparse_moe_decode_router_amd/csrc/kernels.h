@@ -1198,6 +1198,175 @@ k_out(const StepArgs a) {
     }
 }
 
+// Kernel 4 for more than 8 tokens (NCG in {2, 4, 8} column groups of 8
+// tokens), built like k_dense_in_kx: a unit is 8 output tiles (one per wave)
+// times a K slice of a.kx_sps_out steps.  Per pair of steps the workgroup
+// copies every token's column operand into LDS once: ylat as f32 at
+// latent-up steps (64 rows of 128 values; each lane splits its values into
+// the hi or lo half when it reads them) and the hi/lo rows of the shared
+// activation at shared-down steps (128 rows of 128 bf16).  The tile's last
+// slice adds the partial sums in slice order, then each token's hi and lo
+// columns, and rounds to bf16 once.
+constexpr int kOutStage = 32768;  // bytes of one staged step (both kinds)
+
+__device__ __forceinline__ void stage_out_step(char *buf, const StepArgs &a, int s, int Ls) {
+    const int lane = lane_id(), wave = wave_index();
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+        const int c0 = 64 * (wave + kWG * h), c = c0 + lane;  // 16-byte chunk 0 .. 2047
+        const void *gp;
+        if (s < Ls) {
+            // ylat row b (32 chunks of 4 f32), chunk q at position q ^ 2(b & 7)
+            const int b = c >> 5, q = (c & 31) ^ (2 * (b & 7));
+            gp = a.ylat + (size_t)(b < a.B ? b : 0) * a.L + (size_t)s * kKStep + 4 * q;
+        } else {
+            // ash row r = 2b + part (16 chunks of 8 bf16), chunk q at q ^ (r & 15)
+            const int r = c >> 4, b = r >> 1, q = (c & 15) ^ (r & 15);
+            gp = a.ashhl + ((size_t)(b < a.B ? b : 0) * 2 + (r & 1)) * a.Is +
+                 (size_t)(s - Ls) * kKStep + 8 * q;
+        }
+        __builtin_amdgcn_global_load_lds(gp, buf + 16 * c0, 16, 0, 0);
+    }
+}
+
+// Turns a staged ylat step (f32 rows) in place into the layout of a staged
+// shared-activation step: row 2b + part holds token b's hi (part 0) or lo
+// (part 1) bf16 halves, chunk q at position q ^ (row & 15).  Thread i takes
+// token i / 8 and its 16 values [16 (i % 8), + 16): all read, then all
+// write.  Starts and ends with a workgroup barrier.
+__device__ __forceinline__ void ylat_to_hl(char *buf) {
+    const int i = threadIdx.x, b = i >> 3, e0 = 16 * (i & 7), sw = 2 * (b & 7);
+    const float *row = (const float *)(buf + b * (kKStep * 4));
+    f32x4 v[4];
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < 4; ++m) v[m] = *(const f32x4 *)(row + 4 * (((e0 >> 2) + m) ^ sw));
+    uint32_t hi[8], lo[8];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        split_hl2(v[m][0], v[m][1], hi[2 * m], lo[2 * m]);
+        split_hl2(v[m][2], v[m][3], hi[2 * m + 1], lo[2 * m + 1]);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int part = 0; part < 2; ++part) {
+        const int r = 2 * b + part;
+        const uint32_t *w = part ? lo : hi;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int q = (e0 >> 3) + h;  // 8 bf16 per chunk
+            *(u32x4 *)(buf + r * (kKStep * 2) + 16 * (q ^ (r & 15))) =
+                (u32x4){w[4 * h], w[4 * h + 1], w[4 * h + 2], w[4 * h + 3]};
+        }
+    }
+    __syncthreads();
+}
+
+// MFMA j's column operand of group c from a staged step in the hi/lo row
+// layout: lane (n, g) takes row 16c + n (token 8c + n/2, hi for n even, lo
+// for n odd), elements [32j + 8g, 32j + 8g + 8).
+__device__ __forceinline__ bf16x8 out_operand(const char *buf, int c, int j) {
+    const int lane = lane_id(), n = lane & 15, g = lane >> 4;
+    const int r = 16 * c + n;
+    return as_bf16x8(*(const u32x4 *)(buf + r * (kKStep * 2) + 16 * ((4 * j + g) ^ n)));
+}
+
+template <int NCG>
+__global__ void __launch_bounds__(kWGThreads) __attribute__((amdgpu_waves_per_eu(4)))
+k_out_kx(const StepArgs a) {
+    __shared__ __attribute__((aligned(16))) char s_o[2][kOutStage];
+    __shared__ int s_arrive;
+    // The router counter of the dense input kernel is cleared here, as in k_out.
+    if (blockIdx.x == 0 && threadIdx.x == 0) a.gctr[G_ROUTER_DONE] = 0u;
+    const int lane = lane_id(), wave = wave_index(), n = lane & 15, g = lane >> 4;
+    const int RT = a.out_rows, n_ot = (a.H + RT - 1) / RT;
+    const int Ls = a.L / kKStep, nsteps = Ls + a.Is / kKStep;
+    const int sps = a.kx_sps_out, nsl = (nsteps + sps - 1) / sps;
+    const int units = ((n_ot + kWG - 1) / kWG) * nsl;
+    const rsrc_t rpart = buf_rsrc(a.part);
+    for (int u = blockIdx.x; u < units; u += gridDim.x) {
+        const int rg = u / nsl, ks = u % nsl;
+        const int t = rg * kWG + wave;
+        const bool active = t < n_ot;
+        const int h0 = RT * (active ? t : 0);
+        const size_t h = min(h0 + min(n, RT - 1), a.H - 1);
+        const uint16_t *Aa = a.lat_up + h * a.L + 8 * g, *Ab = a.sh_w2 + h * a.Is + 8 * g;
+        const int s0 = ks * sps, s1 = min(nsteps, s0 + sps);
+        f32x4 acc[NCG];
+#pragma unroll
+        for (int c = 0; c < NCG; ++c) acc[c] = zero4();
+        for (int s = s0; s < s1; s += 2) {
+            const int s2 = s + 1 < s1 ? s + 1 : s;
+            __syncthreads();  // every wave is done with the staged copies
+            u32x4 ra0[4], ra1[4];
+            stage_out_step(s_o[0], a, s, Ls);
+            stage_out_step(s_o[1], a, s2, Ls);
+            if (s < Ls) load_tile_bf16(Aa, s, ra0); else load_tile_bf16(Ab, s - Ls, ra0);
+            if (s2 < Ls) load_tile_bf16(Aa, s2, ra1); else load_tile_bf16(Ab, s2 - Ls, ra1);
+            fence_schedule();
+            wait_vm_all();  // this thread's copies and weights have landed
+            staged_barrier();
+            if (s < Ls) ylat_to_hl(s_o[0]);
+            if (s2 != s && s2 < Ls) ylat_to_hl(s_o[1]);
+#pragma unroll
+            for (int c = 0; c < NCG; ++c)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[c] = mfma(as_bf16x8(ra0[j]), out_operand(s_o[0], c, j), acc[c]);
+            if (s2 != s) {
+#pragma unroll
+                for (int c = 0; c < NCG; ++c)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        acc[c] = mfma(as_bf16x8(ra1[j]), out_operand(s_o[1], c, j), acc[c]);
+            }
+        }
+        // Partial sums of the slice, in MFMA layout: part[ks][t][c][lane].
+        if (active) {
+#pragma unroll
+            for (int c = 0; c < NCG; ++c) {
+                uint64_t *dst = (uint64_t *)(a.part + ((((size_t)ks * n_ot + t) * NCG + c) * kWave + lane) * 4);
+                const uint64_t lo = (uint64_t)__float_as_uint(acc[c][0]) | ((uint64_t)__float_as_uint(acc[c][1]) << 32);
+                const uint64_t hi = (uint64_t)__float_as_uint(acc[c][2]) | ((uint64_t)__float_as_uint(acc[c][3]) << 32);
+                __hip_atomic_store(dst, lo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(dst + 1, hi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+        wait_vm_all();
+        __syncthreads();
+        uint32_t *rgc = a.rgc + (size_t)rg * kCtrStride;
+        if (threadIdx.x == 0)
+            s_arrive = __hip_atomic_fetch_add(rgc, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                       (uint32_t)nsl - 1u;
+        __syncthreads();
+        if (s_arrive) {  // the tiles' last slice: sum the slices in order, round once
+            if (active) {
+                const int col = n >> 1, part = n & 1;
+#pragma unroll
+                for (int c = 0; c < NCG; ++c) {
+                    f32x4 sum = zero4();
+                    for (int k2 = 0; k2 < nsl; ++k2) {
+                        const uint32_t off = (uint32_t)(((((size_t)k2 * n_ot + t) * NCG + c) * kWave + lane) * 16);
+                        sum += __builtin_bit_cast(f32x4, buf_ld16<true>(rpart, off));
+                    }
+                    const f32x4 v = add_pair_column(sum);
+                    const int b = 8 * c + col;
+                    if (b < a.B && part == 0) {
+                        const size_t o = (size_t)b * a.H + h0;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int r = 4 * g + i;
+                            if (r < RT && h0 + r < a.H) a.out[o + r] = (uint16_t)bf16_rne(v[i]);
+                        }
+                    }
+                }
+            }
+            if (threadIdx.x == 0) store_agent(rgc, 0u);  // ready for the next step
+        }
+        __syncthreads();
+    }
+}
+
 // Output kernels of the side-stream step: shared-down (MODE = OUT_SHARED,
 // f32 sums to ysh, on the side stream) and latent-up (MODE = OUT_LATENT,
 // adds ysh, one bf16 rounding, on the caller's stream after the join); one

@@ -160,7 +160,9 @@ int dense_tiles(const moe_decode_config &c) {
     return (c.router_dtype == MOE_ROUTER_BF16 ? c.n_experts / 16 : 0) + c.latent / 16 +
            c.shared_inter / 8;
 }
-constexpr int kMaxSlices = 16;  // K slices of the large-batch dense-in kernel
+constexpr int kMaxSlices = 16;     // K slices of the large-batch dense-in kernel
+constexpr int kMaxSlicesOut = 8;   // ... and of the large-batch output kernel
+constexpr int kMaxGroupsOut = 8;   // column groups of 8 tokens per output unit
 
 struct Layout {
     size_t gctr, meta, c13, rgc, score, key, idx, wsel, act_expert, act_off, cu_rec, pair_slot,
@@ -183,7 +185,8 @@ Layout make_layout(const moe_decode_config &c) {
     l.gctr = take(G_COUNT * 4);
     l.meta = take(M_COUNT * 4);
     l.c13 = take(ncols * kCtrStride * 4);
-    const size_t groups = (size_t)cdiv(dense_tiles(c), kWG);
+    const size_t n_ot = (size_t)cdiv(c.hidden, out_tile_rows(c.hidden));
+    const size_t groups = std::max<size_t>(cdiv(dense_tiles(c), kWG), (n_ot + kWG - 1) / kWG);
     l.rgc = take(2 * groups * kCtrStride * 4);  // caller's and side stream's launches
     l.counters_end = o;
     // Score and key rows are padded to kMaxExperts: the routing reads a whole
@@ -202,9 +205,12 @@ Layout make_layout(const moe_decode_config &c) {
     l.acthl = take(P * 2 * I * 2);
     l.ylat = take(Bm * L * 4);
     l.ysh = take(Bm * (size_t)c.hidden * 4);
-    // Slice partials of the large-batch dense-in kernel (batches above 16).
+    // Slice partials of the large-batch dense-in (above 16 tokens) and output
+    // (above 8 tokens) kernels; the two never run at the same time.
     const size_t ncg = (size_t)cdiv(c.max_batch, 16);
-    l.part = take(ncg >= 2 ? (size_t)kMaxSlices * dense_tiles(c) * ncg * kWave * 16 : 0);
+    const size_t part_in = ncg >= 2 ? (size_t)kMaxSlices * dense_tiles(c) * ncg * kWave * 16 : 0;
+    const size_t part_out = c.max_batch > 8 ? kMaxSlicesOut * n_ot * kMaxGroupsOut * kWave * 16 : 0;
+    l.part = take(std::max(part_in, part_out));
     l.total = o;
     return l;
 }
@@ -628,8 +634,21 @@ moe_status moe_decode_step(moe_decode_ctx *ctx, const uint16_t *x, int32_t batch
     }
     launch(kW13[pl.s13], d.grid_w13, kWGThreads);
     launch(split2 ? kW2Split[pl.s2] : kW2[pl.s2], d.grid_w2, kWGThreads);
-    const StepKernel out_k[] = {k_out<1>, k_out<2>, k_out<3>, k_out<4>};
-    launch(out_k[pl.ncg_unit_out - 1], d.grid_out, kWGThreads);
+    if (pl.ncg_out >= 2) {
+        // Above 8 tokens: the column operands staged in LDS per group of 8
+        // output tiles, K in slices (about two units per compute unit).
+        const int n_ot = cdiv(c.hidden, pl.out_rows), nrg = cdiv(n_ot, kWG);
+        const int nsteps = (c.latent + c.shared_inter) / kKStep;
+        int nsl = std::max(1, std::min({kMaxSlicesOut, nsteps, (2 * ctx->n_cus + nrg / 2) / nrg}));
+        a.kx_sps_out = cdiv(nsteps, nsl);
+        nsl = cdiv(nsteps, a.kx_sps_out);
+        const StepKernel out_kx = pl.ncg_out <= 2 ? k_out_kx<2> : pl.ncg_out <= 4 ? k_out_kx<4>
+                                                                                    : k_out_kx<8>;
+        launch(out_kx, (unsigned)(nrg * nsl), kWGThreads);
+    } else {
+        const StepKernel out_k[] = {k_out<1>, k_out<2>, k_out<3>, k_out<4>};
+        launch(out_k[pl.ncg_unit_out - 1], d.grid_out, kWGThreads);
+    }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(ctx, e);
     return MOE_OK;

@@ -41,6 +41,7 @@ struct StepArgs {
     // Dense-in above 16 tokens: steps per K slice, tiles and row groups of
     // the whole tile list (partial-buffer stride and counter offset).
     int32_t kx_sps, kx_tiles, kx_groups;
+    int32_t kx_sps_out;  // output kernel above 8 tokens: steps per K slice
     // Weights (borrowed).
     const uint16_t *router_w;
     const float *router_w32;
