@@ -1029,6 +1029,35 @@ k_dense_in(const StepArgs a) {
     routing_units(a, units, s_route, &s_last);
 }
 
+// Sum over the nsl slices of tile t's partials part[k][t][c][lane] (T tiles
+// per slice), in slice order.  The loads of a batch of slices are all issued
+// before their sums (indices clamped to the last slice, the extra values
+// dropped), so a batch costs one round trip.
+template <int NCG>
+__device__ __forceinline__ void sum_slices(rsrc_t rpart, int nsl, int T, int t, f32x4 (&sum)[NCG]) {
+    constexpr int SB = NCG <= 4 ? 16 / NCG : 2;  // slices per batch: 16 loads
+    const int lane = lane_id();
+#pragma unroll
+    for (int c = 0; c < NCG; ++c) sum[c] = zero4();
+    for (int k0 = 0; k0 < nsl; k0 += SB) {
+        f32x4 v[SB][NCG];
+#pragma unroll
+        for (int q = 0; q < SB; ++q) {
+            const int k = min(k0 + q, nsl - 1);
+#pragma unroll
+            for (int c = 0; c < NCG; ++c)
+                v[q][c] = __builtin_bit_cast(
+                    f32x4, buf_ld16<true>(rpart, (uint32_t)(((((size_t)k * T + t) * NCG + c) * kWave + lane) * 16)));
+        }
+#pragma unroll
+        for (int q = 0; q < SB; ++q)
+            if (k0 + q < nsl) {
+#pragma unroll
+                for (int c = 0; c < NCG; ++c) sum[c] += v[q][c];
+            }
+    }
+}
+
 // Kernel 1 for more than 16 tokens (NCG = ceil(B / 16) >= 2 column groups).
 // A unit is a row group (8 tiles, one per wave) times a K slice of a.kx_sps
 // steps.  Per pair of steps the workgroup copies the x columns of every
@@ -1136,15 +1165,7 @@ k_dense_in_kx(const StepArgs a) {
         if (s_arrive) {  // the row group's last slice: sum the slices in order
             if (active) {
                 f32x4 sum[NCG];
-#pragma unroll
-                for (int c = 0; c < NCG; ++c) sum[c] = zero4();
-                for (int k2 = 0; k2 < nsl; ++k2) {
-#pragma unroll
-                    for (int c = 0; c < NCG; ++c) {
-                        const uint32_t off = (uint32_t)(((((size_t)k2 * a.kx_tiles + t) * NCG + c) * kWave + lane) * 16);
-                        sum[c] += __builtin_bit_cast(f32x4, buf_ld16<true>(rpart, off));
-                    }
-                }
+                sum_slices<NCG>(rpart, nsl, a.kx_tiles, t, sum);
                 dense_in_epilogue<false, NCG>(a, kind, tt, 0, sum, &s_last);
             }
             if (threadIdx.x == 0) store_agent(rgc, 0u);  // ready for the next step
@@ -1342,14 +1363,11 @@ k_out_kx(const StepArgs a) {
         if (s_arrive) {  // the tiles' last slice: sum the slices in order, round once
             if (active) {
                 const int col = n >> 1, part = n & 1;
+                f32x4 sums[NCG];
+                sum_slices<NCG>(rpart, nsl, n_ot, t, sums);
 #pragma unroll
                 for (int c = 0; c < NCG; ++c) {
-                    f32x4 sum = zero4();
-                    for (int k2 = 0; k2 < nsl; ++k2) {
-                        const uint32_t off = (uint32_t)(((((size_t)k2 * n_ot + t) * NCG + c) * kWave + lane) * 16);
-                        sum += __builtin_bit_cast(f32x4, buf_ld16<true>(rpart, off));
-                    }
-                    const f32x4 v = add_pair_column(sum);
+                    const f32x4 v = add_pair_column(sums[c]);
                     const int b = 8 * c + col;
                     if (b < a.B && part == 0) {
                         const size_t o = (size_t)b * a.H + h0;
