@@ -52,12 +52,20 @@ KERNEL_SYMBOLS = {"dense_in": "k_dense_in", "w13": "k_w13", "w2": "k_w2", "out":
                   "shared_gu": "k_dense_in", "shared_down": "k_out_part", "lat_up": "k_out_part"}
 
 
+MODE_FILTER = None  # names selected with --modes (None: all)
+
+
 def modes():
-    """Execution modes of the library by name."""
+    """Execution modes of the library by name (those selected with --modes,
+    and the default one)."""
     from sparse_moe_decode_router_amd import binding
-    return {"four_launches": binding.MODE_FOUR_LAUNCHES,
+    allm = {"four_launches": binding.MODE_FOUR_LAUNCHES,
             "side_stream": binding.MODE_SIDE_STREAM,
             "two_launches": binding.MODE_TWO_LAUNCHES, "fused": binding.MODE_FUSED}
+    if MODE_FILTER is None:
+        return allm
+    dflt = {v: n for n, v in allm.items()}[binding.DEFAULT_MODE]
+    return {n: v for n, v in allm.items() if n in MODE_FILTER or n == dflt}
 
 
 def default_mode():
@@ -291,7 +299,7 @@ def summary(name, B, m, alt):
             "us_p90": round(m["us_p90"], 2), "tokens_per_s": round(B / (m["ms"] * 1e-3), 1),
             "gbs": round(m["value"], 1), "pct_hbm_peak": round(100 * m["value"] / HBM_PEAK_GBS, 2),
             "distinct_experts_mean": round(sum(m["Ds"]) / len(m["Ds"]), 1),
-            "expert_path": alt["four_launches"]["expert_path"],
+            "expert_path": alt.get("four_launches", m)["expert_path"],
             "us_per_step_by_mode": {n: round(x["ms"] * 1e3, 2) for n, x in alt.items()}}
 
 
@@ -391,7 +399,13 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true", help="skip the batch sweep of the K3 layer")
+    ap.add_argument("--modes", default=None,
+                    help="comma-separated execution modes to run (default: all; the "
+                         "library's default mode is always run)")
     args = ap.parse_args()
+    global MODE_FILTER
+    if args.modes:
+        MODE_FILTER = set(args.modes.split(","))
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -467,7 +481,7 @@ def main():
         "pct_hbm_peak": round(100 * m["value"] / HBM_PEAK_GBS, 2),
         "distinct_experts": m["Ds"],
         "mode": default_mode(),
-        "expert_path": alt["four_launches"]["expert_path"],
+        "expert_path": alt.get("four_launches", m)["expert_path"],
         "kernels": per_kernel,
         "ms_per_step_eager": round(m["ms_eager"], 5),
         "modes": {n: {"us_per_step": round(x["ms"] * 1e3, 2), "gbs": round(x["value"], 1),

@@ -209,7 +209,9 @@ Layout make_layout(const moe_decode_config &c) {
     // (above 8 tokens) kernels; the two never run at the same time.
     const size_t ncg = (size_t)cdiv(c.max_batch, 16);
     const size_t part_in = ncg >= 2 ? (size_t)kMaxSlices * dense_tiles(c) * ncg * kWave * 16 : 0;
-    const size_t part_out = c.max_batch > 8 ? kMaxSlicesOut * n_ot * kMaxGroupsOut * kWave * 16 : 0;
+    // The output kernel's column groups per unit: 2, 4 or 8 (ceil(B / 8) rounded up).
+    const size_t gout = c.max_batch <= 16 ? 2 : c.max_batch <= 32 ? 4 : kMaxGroupsOut;
+    const size_t part_out = c.max_batch > 8 ? kMaxSlicesOut * n_ot * gout * kWave * 16 : 0;
     l.part = take(std::max(part_in, part_out));
     l.total = o;
     return l;
