@@ -3,14 +3,18 @@
 
 One step = one pass of the whole layer (router + top-k, latent-down, MXFP4
 experts, combine, shared expert, latent-up) over one batch of synthetic
-tokens, replayed from a HIP graph.  Inputs rotate through R pre-generated
+tokens.  Steps are replayed from HIP graphs of 8 consecutive steps (8
+different inputs), as a decode engine captures many layers per graph, so a
+graph launch is paid once per 8 steps.  Inputs rotate through R pre-generated
 batches (different routing each step) that are resident in HBM before the
 timed region starts.
 
 Prints ONE JSON line:
   value        whole-step algorithmic HBM bytes / time (GB/s)
   ms_per_step  time per layer step (graph replays, K steps between two
-               synchronisations); p10/p50/p90 from events between replays
+               synchronisations); p10/p50/p90 from events between replays;
+               ms_per_step_one_step_graphs (a graph launch per step) and
+               ms_per_step_eager (no graph) for comparison
   roofline     the kernel with the largest time of the library's default
                mode, its algorithmic bytes per launch over its average
                duration (HIP events attached to each kernel's dispatch on
@@ -53,6 +57,7 @@ KERNEL_SYMBOLS = {"dense_in": "k_dense_in", "w13": "k_w13", "w2": "k_w2", "out":
 
 
 MODE_FILTER = None  # names selected with --modes (None: all)
+GRAPH_STEPS = 8     # consecutive steps (different inputs) per replayed graph
 
 
 def modes():
@@ -200,8 +205,36 @@ def measure(dev, d, B, k, xs, steps, warmup, mode):
     assert ctx.read_flags() == 0
 
     stream = torch.cuda.Stream()
-    graphs = [binding.Graph([ctx], [xd[r]], B, k, [out], [idx], [wts]) for r in range(R)]
+    # Graphs of G consecutive steps (G different inputs), as a decode engine
+    # captures many layers per graph: one graph launch per G steps.
+    G = GRAPH_STEPS if R % GRAPH_STEPS == 0 else 1
+    NG = R // G
+    graphs = [binding.Graph([ctx] * G, xd[G * q:G * q + G], B, k, [out] * G, [idx] * G,
+                            [wts] * G) for q in range(NG)]
+    reps = max(1, steps // G)
     # Timed region: back-to-back replays between two synchronisations.
+    for i in range(max(1, warmup // G)):
+        graphs[i % NG].launch(stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(reps):
+        graphs[i % NG].launch(stream)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / (reps * G)
+    mean_bytes = sum(step_bytes[(G * (i % NG) + j) % R] for i in range(reps)
+                     for j in range(G)) / (reps * G)
+    # Per-replay spread (per step): an event between consecutive replays.
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    evs[0].record(stream)
+    for i in range(reps):
+        graphs[i % NG].launch(stream)
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per = [evs[i].elapsed_time(evs[i + 1]) * 1e3 / G for i in range(reps)]
+    for g in graphs:
+        g.close()
+    # One step per graph, for comparison (a graph launch per step).
+    graphs = [binding.Graph([ctx], [xd[r]], B, k, [out], [idx], [wts]) for r in range(R)]
     for i in range(warmup):
         graphs[i % R].launch(stream)
     torch.cuda.synchronize()
@@ -209,16 +242,7 @@ def measure(dev, d, B, k, xs, steps, warmup, mode):
     for i in range(steps):
         graphs[i % R].launch(stream)
     torch.cuda.synchronize()
-    ms = (time.perf_counter() - t0) * 1e3 / steps
-    mean_bytes = sum(step_bytes[i % R] for i in range(steps)) / steps
-    # Per-replay spread: an event between consecutive replays.
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
-    evs[0].record(stream)
-    for i in range(steps):
-        graphs[i % R].launch(stream)
-        evs[i + 1].record(stream)
-    torch.cuda.synchronize()
-    per = [evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(steps)]
+    ms_graph1 = (time.perf_counter() - t0) * 1e3 / steps
 
     # Eager steps (launches without a graph), for comparison.
     for i in range(warmup):
@@ -285,6 +309,7 @@ def measure(dev, d, B, k, xs, steps, warmup, mode):
     ctx.close()
     return {
         "ms": ms, "value": mean_bytes / (ms * 1e-3) / 1e9, "ms_eager": ms_eager,
+        "ms_graph1": ms_graph1,
         "us_p10": pct(per, 10), "us_p50": pct(per, 50), "us_p90": pct(per, 90),
         "Ds": Ds, "step_bytes": step_bytes, "per_kernel": per_kernel, "dispatch": disp,
         "names": names, "expert_path": expert,
@@ -484,6 +509,8 @@ def main():
         "expert_path": alt.get("four_launches", m)["expert_path"],
         "kernels": per_kernel,
         "ms_per_step_eager": round(m["ms_eager"], 5),
+        "ms_per_step_one_step_graphs": round(m["ms_graph1"], 5),
+        "graph_steps": GRAPH_STEPS,
         "modes": {n: {"us_per_step": round(x["ms"] * 1e3, 2), "gbs": round(x["value"], 1),
                       "kernels": x["per_kernel"]} for n, x in alt.items()},
         "roofline": {"bound": "hbm", "kernel": pk["symbol"], "achieved": pk["gbs"],
