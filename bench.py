@@ -25,7 +25,9 @@ Prints ONE JSON line:
                + one persistent launch, one persistent launch)
   cpu_baseline the binary64 CPU oracle on a bounded sample of the same inputs
   batch_sweep  the same K3 weights at batch 2, 8 (Zipf routing), 64
-               (near-uniform routing) and 64 (the batch-1 bias)
+               (near-uniform routing), 64 (the batch-1 bias) and two
+               speculative-decoding verify batches (1 user x 8 tokens, 8
+               users x 4 tokens; tokens of a user correlated, rho 0.8)
 With --workload c4_x8: eight TP8-share layers in one graph, batch 1..64.
 """
 import argparse
@@ -330,8 +332,10 @@ def summary(name, B, m, alt):
 
 # Batch sweep on the K3 layer's weights (the bias alone changes): name ->
 # (bias recipe, batch).
-SWEEP = (("k3_b2", "k3", 2), ("k3_zipf_b8", "k3_zipf", 8), ("k3_flat_b64", "k3_flat", 64),
-         ("k3_b64", "k3", 64))
+SWEEP = (("k3_b2", "k3", 2, None), ("k3_zipf_b8", "k3_zipf", 8, None),
+         ("k3_flat_b64", "k3_flat", 64, None), ("k3_b64", "k3", 64, None),
+         # speculative-decoding verify batches: users x (drafts + 1) correlated tokens
+         ("k3_spec_u1_d7", "k3", 8, (1, 7)), ("k3_spec_u8_d3", "k3", 32, (8, 3)))
 
 
 def run_c4(args):
@@ -388,6 +392,15 @@ def run_c4(args):
                 c.set_mode(mode)
             graphs = [binding.Graph(ctxs, xd[r], B, k, outs, idxs, wts) for r in range(R)]
             by_mode[name] = round(replay_ms(graphs, R) * 1e3 / n_layers, 2)
+        # The default form with each layer prefetching the next one's router
+        # and latent-down rows while it routes.
+        for g in graphs:
+            g.close()
+        for c in ctxs:
+            c.set_mode(binding.DEFAULT_MODE)
+        graphs = [binding.Graph(ctxs, xd[r], B, k, outs, idxs, wts, prefetch_next=True)
+                  for r in range(R)]
+        by_mode["four_launches_prefetch"] = round(replay_ms(graphs, R) * 1e3 / n_layers, 2)
         assert all(c.read_flags() == 0 for c in ctxs), "a bounded wait of a persistent step ran out"
         results.append({"batch": B, "us_per_8_layers": round(ms * 1e3, 2),
                         "us_per_layer": round(ms * 1e3 / n_layers, 2),
@@ -473,9 +486,13 @@ def main():
     sweep = None
     if not args.no_sweep and recipe_name == "k3" and B == 1:
         sweep = [summary(args.workload, B, m, alt)]
-        for name, bias_recipe, Bs in SWEEP:
+        for name, bias_recipe, Bs, spec in SWEEP:
             bias = synth.make_bias(synth.RECIPES[bias_recipe], 0)
-            xs_s = [synth.make_tokens(d, 0, Bs, draw=r) for r in range(args.rotate)]
+            if spec:
+                xs_s = [synth.make_spec_tokens(d, 0, spec[0], spec[1], draw=r)
+                        for r in range(args.rotate)]
+            else:
+                xs_s = [synth.make_tokens(d, 0, Bs, draw=r) for r in range(args.rotate)]
             n_s = max(50, args.steps // 2)
             log(f"[bench] sweep {name}")
             dvb = dev.with_bias(bias)

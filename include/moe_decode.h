@@ -210,6 +210,17 @@ enum {
 };
 moe_status moe_decode_set_mode(moe_decode_ctx *ctx, int32_t mode);
 
+/* Next-layer prefetch, the one-GPU analogue of the side-stream weight
+ * prefetch of [P-vLLM] "他们换掉了什么": while a step of ctx routes (the
+ * memory then streams little), its dense-in launch reads next's router and
+ * latent-down rows, so that they sit in the last-level cache when next's step
+ * streams them.  The values are dropped; nothing is written.  next must stay
+ * alive while ctx uses it (next = NULL switches the prefetch off; next ==
+ * ctx is refused with MOE_ERR_INVALID_ARG).  Applies to the dense-in launch
+ * of the four-launch and two-launch forms and to the routed side of the
+ * side-stream form.  Host-only. */
+moe_status moe_decode_set_next_layer(moe_decode_ctx *ctx, const moe_decode_ctx *next);
+
 /* Reads the context's sticky fault flags into *flags (synchronous copy from
  * the workspace; call after the steps completed): bit 0 set when a fused
  * step's bounded wait on a completion counter ran out (the step then

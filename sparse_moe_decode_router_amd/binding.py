@@ -53,7 +53,7 @@ EXPORTED = ("moe_decode_validate_config", "moe_decode_workspace_size", "moe_deco
             "moe_decode_last_hip_error", "moe_decode_graph_create", "moe_decode_graph_launch",
             "moe_decode_graph_destroy", "moe_decode_last_dispatch", "moe_decode_debug_export",
             "moe_decode_debug_dequant", "moe_decode_set_timing_events", "moe_decode_set_mode",
-            "moe_decode_read_flags")
+            "moe_decode_read_flags", "moe_decode_set_next_layer")
 
 
 class MoEError(RuntimeError):
@@ -105,6 +105,8 @@ def lib() -> ctypes.CDLL:
     L.moe_decode_set_mode.restype = i32
     L.moe_decode_read_flags.argtypes = [vp, ctypes.POINTER(ctypes.c_uint32)]
     L.moe_decode_read_flags.restype = i32
+    L.moe_decode_set_next_layer.argtypes = [vp, vp]
+    L.moe_decode_set_next_layer.restype = i32
     _lib = L
     return L
 
@@ -245,6 +247,13 @@ class MoEDecode:
         persistent launch where the shape has one)."""
         _check(lib().moe_decode_set_mode(self.handle, mode), "set_mode")
 
+    def set_next_layer(self, nxt: Optional["MoEDecode"]) -> None:
+        """Prefetch nxt's router and latent-down rows while this context's
+        steps route (None: off); nxt must outlive this setting."""
+        self._next = nxt
+        _check(lib().moe_decode_set_next_layer(self.handle, nxt.handle if nxt else None),
+               "set_next_layer")
+
     def read_flags(self) -> int:
         """Sticky fault flags of the context's fused steps (0: none)."""
         v = ctypes.c_uint32(0)
@@ -290,8 +299,15 @@ class Graph:
     """Several layers' steps captured into one HIP graph."""
 
     def __init__(self, ctxs: Sequence[MoEDecode], xs, batch: int, top_k: int, outs, idxs=None,
-                 ws=None):
+                 ws=None, prefetch_next: bool = False):
+        """prefetch_next: each layer's step prefetches the next layer's
+        router and latent-down rows while it routes (captured that way; the
+        contexts' own setting is restored afterwards)."""
         n = len(ctxs)
+        if prefetch_next:
+            for i in range(n - 1):
+                if ctxs[i + 1] is not ctxs[i]:
+                    lib().moe_decode_set_next_layer(ctxs[i].handle, ctxs[i + 1].handle)
         VP = ctypes.c_void_p
         arr = lambda vals: (VP * n)(*vals)  # noqa: E731
         self._keep = (ctxs, xs, outs, idxs, ws)
@@ -301,6 +317,10 @@ class Graph:
             arr([o.data_ptr() for o in outs]),
             arr([i.data_ptr() for i in idxs]) if idxs is not None else None,
             arr([w.data_ptr() for w in ws]) if ws is not None else None, ctypes.byref(g))
+        if prefetch_next:
+            for c in ctxs:
+                nxt = getattr(c, "_next", None)
+                lib().moe_decode_set_next_layer(c.handle, nxt.handle if nxt else None)
         _check(rc, "moe_decode_graph_create", ctxs[0].handle)
         self.handle = g
 

@@ -990,6 +990,35 @@ __device__ __forceinline__ void routing_units(const StepArgs &a, int units, Rout
     }
 }
 
+// Prefetch units, after the routing units: unit r reads bytes [r U, r U + U)
+// (U = kPfUnit) of a following layer's router and latent-down rows with
+// plain loads, once the router is complete, so that those rows sit in the
+// last-level cache when that layer's step streams them; the values are
+// dropped.  They run while the routing leaves the memory idle.
+constexpr int kPfUnit = 256 * 1024;
+__device__ __forceinline__ void prefetch_units(const StepArgs &a, int first) {
+    const int r = (int)blockIdx.x - first;
+    if (r < 0 || r >= a.pf_units) return;
+    wg_wait(a, &a.gctr[G_ROUTER_DONE], (uint32_t)a.router_target);
+    constexpr int kPer = kPfUnit / (kWGThreads * 16);  // 16-byte loads per thread
+    constexpr int kBatch = 8;
+    const uint64_t total = a.pf_bytes0 + a.pf_bytes1;
+    uint32_t acc = 0;
+    for (int i0 = 0; i0 < kPer; i0 += kBatch) {
+        u32x4 v[kBatch];
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+            uint64_t off = (uint64_t)r * kPfUnit + ((uint64_t)(i0 + j) * kWGThreads + threadIdx.x) * 16;
+            off = off < total ? off : 0;  // past the end: re-read the first chunk
+            const uint8_t *p = off < a.pf_bytes0 ? a.pf0 + off : a.pf1 + (off - a.pf_bytes0);
+            v[j] = ld16(p);
+        }
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) acc ^= v[j][0] ^ v[j][1] ^ v[j][2] ^ v[j][3];
+    }
+    if (a.pf_units < 0) a.out[acc & 1] = 0;  // never taken (pf_units > 0 here): keeps the loads
+}
+
 // Kernel 1: dense-in units over tiles [dense_lo, dense_hi) of the list
 // [router | latent | shared]; each unit covers all NCG = ceil(B / 16) column
 // groups, so every weight tile is read once per step.
@@ -1027,6 +1056,7 @@ k_dense_in(const StepArgs a) {
         }
     }
     routing_units(a, units, s_route, &s_last);
+    prefetch_units(a, units + a.route_units);
 }
 
 // Sum over the nsl slices of tile t's partials part[k][t][c][lane] (T tiles
@@ -1173,6 +1203,7 @@ k_dense_in_kx(const StepArgs a) {
         __syncthreads();
     }
     routing_units(a, units, s_route, &s_last);
+    prefetch_units(a, units + a.route_units);
 }
 
 // Kernel 2: gate/up units.

@@ -255,6 +255,9 @@ struct moe_decode_ctx {
     // the fork / join events between it and the caller's stream.
     hipStream_t side;
     hipEvent_t fork_ev, join_ev;
+    // Layer whose router and latent-down rows the dense-in launch prefetches
+    // (moe_decode_set_next_layer; NULL: none).
+    const moe_decode_ctx *next;
     int32_t n_cus;          // compute units of the device
     StepKernel occ_kernel;  // fused kernel whose occupancy is cached
     int32_t occ_blocks;     // its resident workgroups per compute unit
@@ -415,6 +418,7 @@ moe_status moe_decode_init(const moe_decode_config *cfg, const moe_decode_weight
     ctx->occ_blocks = 1;
     ctx->side = nullptr;
     ctx->fork_ev = ctx->join_ev = nullptr;
+    ctx->next = nullptr;
     std::memset(&ctx->last, 0, sizeof ctx->last);
     e = hipStreamCreateWithFlags(&ctx->side, hipStreamNonBlocking);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&ctx->fork_ev, hipEventDisableTiming);
@@ -479,6 +483,16 @@ moe_status moe_decode_step(moe_decode_ctx *ctx, const uint16_t *x, int32_t batch
     // Above 8 tokens the routing is spread over routing units (8 tokens
     // each) appended to the dense-in launch.
     a.route_units = c.router_dtype == MOE_ROUTER_BF16 && batch > 8 ? cdiv(batch, kWG) : 0;
+    a.pf_units = 0;
+    if (ctx->next) {
+        const moe_decode_config &nc = ctx->next->cfg;
+        a.pf0 = (const uint8_t *)ctx->next->w.router_w;
+        a.pf_bytes0 = (uint64_t)nc.n_experts * nc.hidden *
+                      (nc.router_dtype == MOE_ROUTER_F32 ? 4 : 2);
+        a.pf1 = (const uint8_t *)ctx->next->w.lat_down;
+        a.pf_bytes1 = (uint64_t)nc.latent * nc.hidden * 2;
+        a.pf_units = (int32_t)((a.pf_bytes0 + a.pf_bytes1 + kPfUnit - 1) / kPfUnit);
+    }
     const long long cap = 65528;  // workgroups (a multiple of the XCD count); more units loop
 
     moe_decode_dispatch_info &d = ctx->last;
@@ -582,7 +596,7 @@ moe_status moe_decode_step(moe_decode_ctx *ctx, const uint16_t *x, int32_t batch
             const int rw_in = kWG / pl.in.kw;
             launch_on(st, dense_in[pl.ncg_in - 1],
                       (unsigned)(dense_units_host(args.dense_hi - args.dense_lo, rw_in, 1) +
-                                 args.route_units),
+                                 args.route_units + args.pf_units),
                       kWGThreads, args);
             return;
         }
@@ -591,8 +605,8 @@ moe_status moe_decode_step(moe_decode_ctx *ctx, const uint16_t *x, int32_t batch
         int nsl = std::max(1, std::min({kMaxSlices, nsteps, (2 * ctx->n_cus + nrg / 2) / nrg}));
         args.kx_sps = cdiv(nsteps, nsl);
         nsl = cdiv(nsteps, args.kx_sps);
-        launch_on(st, dense_in_kx[pl.ncg_in - 1], (unsigned)(nrg * nsl + args.route_units),
-                  kWGThreads, args);
+        launch_on(st, dense_in_kx[pl.ncg_in - 1],
+                  (unsigned)(nrg * nsl + args.route_units + args.pf_units), kWGThreads, args);
     };
     if (side) {
         // The shared expert depends on x alone: its gate/up and down launches
@@ -608,6 +622,7 @@ moe_status moe_decode_step(moe_decode_ctx *ctx, const uint16_t *x, int32_t batch
         sa.dense_lo = n_main;
         sa.zero_ylat = 0;
         sa.route_units = 0;
+        sa.pf_units = 0;
         hipError_t e = hipEventRecord(ctx->fork_ev, s);
         if (e == hipSuccess) e = hipStreamWaitEvent(ctx->side, ctx->fork_ev, 0);
         if (e != hipSuccess) return hip_fail(ctx, e);
@@ -743,6 +758,12 @@ moe_status moe_decode_set_timing_events(moe_decode_ctx *ctx, void *const *events
         ctx->events[i] = (hipEvent_t)events[i];
     }
     ctx->n_events = n;
+    return MOE_OK;
+}
+
+moe_status moe_decode_set_next_layer(moe_decode_ctx *ctx, const moe_decode_ctx *next) {
+    if (!ctx || next == ctx) return MOE_ERR_INVALID_ARG;
+    ctx->next = next;
     return MOE_OK;
 }
 

@@ -42,6 +42,11 @@ struct StepArgs {
     // the whole tile list (partial-buffer stride and counter offset).
     int32_t kx_sps, kx_tiles, kx_groups;
     int32_t kx_sps_out;  // output kernel above 8 tokens: steps per K slice
+    // Prefetch units of the dense-in launch (0: none): a following layer's
+    // rows [pf0, pf0 + pf_bytes0) and [pf1, pf1 + pf_bytes1).
+    int32_t pf_units;
+    const uint8_t *pf0, *pf1;
+    uint64_t pf_bytes0, pf_bytes1;
     // Weights (borrowed).
     const uint16_t *router_w;
     const float *router_w32;

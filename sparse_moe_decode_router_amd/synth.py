@@ -39,7 +39,7 @@ import numpy as np
 # on its own.
 _T_X, _T_ROUTER, _T_BIAS, _T_LDOWN, _T_LUP = 1, 2, 3, 4, 5
 _T_W13Q, _T_W13S, _T_W2Q, _T_W2S, _T_SH13, _T_SH2 = 6, 7, 8, 9, 10, 11
-_T_CALIB, _T_ZIPF_RANK, _T_FLAT_BIAS = 12, 13, 14
+_T_CALIB, _T_ZIPF_RANK, _T_FLAT_BIAS, _T_SPEC = 12, 13, 14, 15
 
 REPO_ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 ZIPF_BIAS_FILE = os.path.join(REPO_ROOT, "tests", "golden", "k3_zipf_bias.txt")
@@ -220,6 +220,26 @@ def make_tokens(dims: LayerDims, seed: int, batch: int, draw: int = 0) -> np.nda
     independent batch (benchmarks rotate through several)."""
     g = _rng(seed, _T_X, draw)
     return to_bf16_bits(g.standard_normal((batch, dims.hidden), dtype=np.float32))
+
+
+# Correlation of the hidden states of one sequence's verify window (the
+# accepted token and its drafts); the pages give none, 0.8 is a reading.
+SPEC_RHO = 0.8
+
+
+def make_spec_tokens(dims: LayerDims, seed: int, users: int, drafts: int, draw: int = 0,
+                     rho: float = SPEC_RHO) -> np.ndarray:
+    """A speculative-decoding verify batch: `users` sequences, each with its
+    last accepted token and `drafts` draft tokens, in bf16, shape
+    [users * (drafts + 1)][H], rows of one user adjacent.  Within a user the
+    rows share a base: x = sqrt(rho) base_u + sqrt(1 - rho) noise, so each
+    row is N(0, 1) and two rows of one user correlate with coefficient rho
+    (their routing overlaps); users are independent."""
+    g = _rng(seed, _T_SPEC, draw)
+    base = g.standard_normal((users, 1, dims.hidden), dtype=np.float32)
+    noise = g.standard_normal((users, drafts + 1, dims.hidden), dtype=np.float32)
+    x = np.float32(np.sqrt(rho)) * base + np.float32(np.sqrt(1.0 - rho)) * noise
+    return to_bf16_bits(x.reshape(users * (drafts + 1), dims.hidden))
 
 
 def make_calibration_tokens(dims: LayerDims, seed: int, count: int) -> np.ndarray:

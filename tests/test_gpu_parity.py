@@ -406,6 +406,19 @@ def test_k3_persistent_step_matches_four_launches(k3_dev, bias_kind, B, mode, ki
     assert_modes_agree(a, b)
 
 
+@pytest.mark.parametrize("users,drafts,sample", [(1, 7, None), (8, 3, [0, 5, 31])])
+def test_k3_spec_verify_batch(k3_layer, k3_dev, users, drafts, sample):
+    """Speculative-decoding verify batches (tokens of one user correlated):
+    parity with the oracle, and the correlation shows as shared experts."""
+    ctx, _ = k3_ctx(k3_dev, "normal", 64)
+    x = synth.make_spec_tokens(k3_layer.dims, 3, users, drafts)
+    out, idx, w = run(ctx, x, 16)
+    r = check_step(k3_layer, x, 16, out, idx, w, sample=sample)
+    B = users * (drafts + 1)
+    log(f"  spec u{users} d{drafts}:", r, "distinct experts", len(np.unique(idx)), "of", B * 16)
+    assert len(np.unique(idx)) < 0.75 * min(B * 16, 896)
+
+
 def test_k3_tp8_share_layer():
     layer = synth.make_layer(synth.K3_TP8, synth.TP8_STACK_SEED0)
     ctx = make_ctx(layer, 64, 16)
@@ -417,7 +430,8 @@ def test_k3_tp8_share_layer():
         log("  ", r)
 
 
-@pytest.mark.parametrize("mode", ["four_launches", "side_stream", "two_launches", "fused"])
+@pytest.mark.parametrize("mode", ["four_launches", "prefetch", "side_stream", "two_launches",
+                                  "fused"])
 def test_c4_eight_layer_graph(mode):
     """Eight TP8-share layers (own seeds and inputs) captured in one HIP graph,
     the configuration the stacked benchmark replays: every layer's replayed
@@ -428,14 +442,16 @@ def test_c4_eight_layer_graph(mode):
     layers = [synth.make_layer(synth.K3_TP8, synth.TP8_STACK_SEED0 + l) for l in range(n_layers)]
     ctxs = [make_ctx(la, B, k) for la in layers]
     for c in ctxs:
-        c.set_mode(mode_const(mode))
+        c.set_mode(mode_const("four_launches" if mode == "prefetch" else mode))
     xs = [synth.make_tokens(la.dims, synth.TP8_STACK_SEED0 + l, B) for l, la in enumerate(layers)]
     xd = [to_dev_tokens(x) for x in xs]
     H = layers[0].dims.hidden
     outs = [torch.empty((B, H), dtype=torch.int16, device="cuda") for _ in range(n_layers)]
     idxs = [torch.empty((B, k), dtype=torch.int32, device="cuda") for _ in range(n_layers)]
     ws = [torch.empty((B, k), dtype=torch.float32, device="cuda") for _ in range(n_layers)]
-    g = binding.Graph(ctxs, xd, B, k, outs, idxs, ws)
+    # "prefetch": each layer prefetches the next layer's router and
+    # latent-down rows while it routes; results are unchanged.
+    g = binding.Graph(ctxs, xd, B, k, outs, idxs, ws, prefetch_next=mode == "prefetch")
     stream = torch.cuda.Stream()
     for rep in range(2):
         g.launch(stream)
