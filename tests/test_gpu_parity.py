@@ -198,19 +198,22 @@ def assert_same_step(a, b):
 
 
 def assert_modes_agree(a, b):
-    """Two execution modes of one step.  Above 16 tokens the four-launch
-    dense-in kernel sums the router's K slices in another order than the
-    single-launch step, so scores can differ in their last f32 bits: a near
-    tie may then select another expert.  Tokens with the same experts must
-    have weights within 2e-6 and outputs within the bound of assert_same_step;
-    at most 5 % of the tokens may differ in their experts."""
+    """Two execution modes of one step.  The modes reduce in different
+    orders: above 16 tokens the router's K slices (so scores can differ in
+    their last f32 bits and a near tie may select another expert), and the
+    output either as one sum over latent-up and shared-down or as two.  Two
+    f32 reduction trees over K = 6144 terms of size up to the row's rms differ
+    by far less than K 2^-24 rms (typically sqrt(K) 2^-24 rms); the bound is
+    one bf16 step of the value or 2^-12 rms.  Tokens with the same experts
+    must have weights within 2e-6 and outputs within that bound; at most 5 %
+    of the tokens may differ in their experts."""
     same = np.all(a[1] == b[1], axis=1)
     assert np.mean(same) >= 0.95
     np.testing.assert_allclose(a[2][same], b[2][same], rtol=0, atol=2e-6)
     fa, fb = bf16_f64(a[0][same]), bf16_f64(b[0][same])
     rms = np.sqrt(np.mean(fa * fa, axis=1, keepdims=True))
     ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(fa), np.abs(fb)) + 1e-300)) - 7)
-    assert np.all(np.abs(fa - fb) <= np.maximum(ulp, rms * 2.0 ** -16))
+    assert np.all(np.abs(fa - fb) <= np.maximum(ulp, rms * 2.0 ** -12))
 
 
 def test_repeated_steps_agree(small_layer, small_ctx):
@@ -393,7 +396,7 @@ def test_k3_layer(k3_layer, k3_dev, bias_kind, B, sample):
 
 @pytest.mark.parametrize("mode,kind", PERSISTENT_MODES)
 @pytest.mark.parametrize("bias_kind,B", [("normal", 1), ("zipf", 8), ("normal", 64)])
-def test_k3_persistent_step_matches_four_launches(k3_dev, bias_kind, B, mode, kind):
+def test_k3_persistent_step_matches_four_launches(k3_layer, k3_dev, bias_kind, B, mode, kind):
     """The persistent-kernel steps on the K3 layer (chunk shape 16x16) give
     the four-launch step's values."""
     four, _ = k3_ctx(k3_dev, bias_kind, 64)
@@ -404,6 +407,7 @@ def test_k3_persistent_step_matches_four_launches(k3_dev, bias_kind, B, mode, ki
     b = run(fused, x, 16)
     assert fused.last_dispatch()["fused"] == kind and four.last_dispatch()["fused"] == 0
     assert_modes_agree(a, b)
+    check_step(layer_with_bias(k3_layer, bias_kind), x, 16, *b, sample=[0, B - 1])
 
 
 @pytest.mark.parametrize("users,drafts,sample", [(1, 7, None), (8, 3, [0, 5, 31])])
