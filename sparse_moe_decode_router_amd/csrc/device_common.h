@@ -209,6 +209,15 @@ __device__ __forceinline__ u32x4 buf_ld16(rsrc_t r, uint32_t byte_off) {
                               __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, cache_aux<Coh>()));
 }
 
+// 16-byte store through a buffer resource.  Coh: with the sc1 cache policy
+// that agent-scope atomic stores use, for values another workgroup of the
+// same launch reads (one 16-byte store per lane instead of two 8-byte atomic
+// stores, so a wave writes whole 1 KiB blocks).
+template <bool Coh>
+__device__ __forceinline__ void buf_st16(rsrc_t r, uint32_t byte_off, u32x4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, byte_off, 0, cache_aux<Coh>());
+}
+
 // Waits for every vector memory access of the wave (stores included).
 __device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 

@@ -1177,13 +1177,9 @@ k_dense_in_kx(const StepArgs a) {
         // Partial sums of the slice, in MFMA layout: part[ks][t][c][lane].
         if (active) {
 #pragma unroll
-            for (int c = 0; c < NCG; ++c) {
-                uint64_t *dst = (uint64_t *)(a.part + ((((size_t)ks * a.kx_tiles + t) * NCG + c) * kWave + lane) * 4);
-                const uint64_t lo = (uint64_t)__float_as_uint(acc[c][0]) | ((uint64_t)__float_as_uint(acc[c][1]) << 32);
-                const uint64_t hi = (uint64_t)__float_as_uint(acc[c][2]) | ((uint64_t)__float_as_uint(acc[c][3]) << 32);
-                __hip_atomic_store(dst, lo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                __hip_atomic_store(dst + 1, hi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
+            for (int c = 0; c < NCG; ++c)
+                buf_st16<true>(rpart, (uint32_t)(((((size_t)ks * a.kx_tiles + t) * NCG + c) * kWave + lane) * 16),
+                               __builtin_bit_cast(u32x4, acc[c]));
         }
         wait_vm_all();
         __syncthreads();
@@ -1376,13 +1372,9 @@ k_out_kx(const StepArgs a) {
         // Partial sums of the slice, in MFMA layout: part[ks][t][c][lane].
         if (active) {
 #pragma unroll
-            for (int c = 0; c < NCG; ++c) {
-                uint64_t *dst = (uint64_t *)(a.part + ((((size_t)ks * n_ot + t) * NCG + c) * kWave + lane) * 4);
-                const uint64_t lo = (uint64_t)__float_as_uint(acc[c][0]) | ((uint64_t)__float_as_uint(acc[c][1]) << 32);
-                const uint64_t hi = (uint64_t)__float_as_uint(acc[c][2]) | ((uint64_t)__float_as_uint(acc[c][3]) << 32);
-                __hip_atomic_store(dst, lo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                __hip_atomic_store(dst + 1, hi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
+            for (int c = 0; c < NCG; ++c)
+                buf_st16<true>(rpart, (uint32_t)(((((size_t)ks * n_ot + t) * NCG + c) * kWave + lane) * 16),
+                               __builtin_bit_cast(u32x4, acc[c]));
         }
         wait_vm_all();
         __syncthreads();

@@ -708,15 +708,15 @@ moe_status moe_decode_graph_create(moe_decode_ctx *const *ctxs, int32_t n_layers
     }
     hipGraphExec_t ex = nullptr;
     if (e == hipSuccess && st == MOE_OK) e = hipGraphInstantiate(&ex, g, nullptr, nullptr, 0);
-    hipStreamDestroy(cs);
+    (void)hipStreamDestroy(cs);
     if (st != MOE_OK || e != hipSuccess) {
-        if (g) hipGraphDestroy(g);
+        if (g) (void)hipGraphDestroy(g);
         return st != MOE_OK ? st : hip_fail(ctxs[0], e);
     }
     moe_decode_graph *gr = new (std::nothrow) moe_decode_graph();
     if (!gr) {
-        hipGraphExecDestroy(ex);
-        hipGraphDestroy(g);
+        (void)hipGraphExecDestroy(ex);
+        (void)hipGraphDestroy(g);
         return MOE_ERR_HIP;
     }
     gr->graph = g;
@@ -732,8 +732,8 @@ moe_status moe_decode_graph_launch(moe_decode_graph *graph, moe_stream_t stream)
 
 moe_status moe_decode_graph_destroy(moe_decode_graph *graph) {
     if (!graph) return MOE_ERR_INVALID_ARG;
-    hipGraphExecDestroy(graph->exec);
-    hipGraphDestroy(graph->graph);
+    (void)hipGraphExecDestroy(graph->exec);
+    (void)hipGraphDestroy(graph->graph);
     delete graph;
     return MOE_OK;
 }

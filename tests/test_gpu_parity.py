@@ -158,6 +158,29 @@ def test_zero_router_picks_lowest_ids_with_equal_weights():
     check_step(layer, x, 5, out, idx, w)
 
 
+@pytest.mark.parametrize("B", [4, 12])
+@pytest.mark.parametrize("k,want", [(5, [3, 7, 69, 130, 200]),
+                                    (8, [3, 7, 69, 130, 131, 192, 200, 250])])
+def test_ties_at_the_threshold_go_to_the_lowest_ids(B, k, want):
+    """Keys equal at the k-th largest value, spread over several lane slots
+    (expert e sits in slot e // 64): the selection takes the lowest ids among
+    them, also when the cut falls between two ids of one slot (130 taken,
+    131 not).  Zero router: every score is 0.5, so the keys are exactly
+    1.5, 0.75 or 0.5 and the weights 1/k.  B = 12 routes through the routing
+    units."""
+    layer = synth.make_layer(small_recipe(E=256, bias="none", k=k), 11)
+    layer.router_w[:] = 0
+    layer.bias = np.zeros(256, np.float32)
+    layer.bias[[200, 3]] = 1.0
+    layer.bias[[250, 7, 69, 130, 131, 192]] = 0.25
+    ctx = make_ctx(layer, B, 8)
+    x = synth.make_tokens(layer.dims, 11, B)
+    out, idx, w = run(ctx, x, k)
+    np.testing.assert_array_equal(idx, np.tile(np.array(want), (B, 1)))
+    assert np.all(w == np.float32(1.0 / k))
+    check_step(layer, x, k, out, idx, w)
+
+
 def test_hot_experts_serve_every_token():
     """A bias that sends all 64 tokens to the same experts: more than 8
     tokens per expert, several column units per expert."""
