@@ -154,6 +154,16 @@ def cpu_baseline(layer, xs, k, bytes_per_step, seconds):
                       f"(batch {xs[0].shape[0]}), {per_step:.3f} s per step single-threaded"}
 
 
+def device_info():
+    """The GPU the figures come from, and the peak they are priced against."""
+    import torch
+    p = torch.cuda.get_device_properties(0)
+    return {"name": torch.cuda.get_device_name(0), "arch": getattr(p, "gcnArchName", None),
+            "compute_units": p.multi_processor_count,
+            "memory_gib": round(p.total_memory / 2**30, 1),
+            "hbm_peak_assumed_gbs": HBM_PEAK_GBS}
+
+
 def pct(v, q):
     import numpy as np
     return float(np.percentile(np.asarray(v), q))
@@ -245,6 +255,29 @@ def measure(dev, d, B, k, xs, steps, warmup, mode):
         graphs[i % R].launch(stream)
     torch.cuda.synchronize()
     ms_graph1 = (time.perf_counter() - t0) * 1e3 / steps
+    # Cold against warm: events around single one-step replays, each cold one
+    # after a 1 GiB read on the same stream, which evicts the last-level cache
+    # (256 MB on MI355X), so that no weight row comes from an earlier step;
+    # the warm ones run the same way without the read.  (A scrub by writing
+    # leaves up to the whole cache dirty, and the replay then pays for its
+    # write-back: about 50 us at batch 1.)
+    scrub = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    sink = torch.zeros(1, dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    n_cold = min(steps, 32)
+    cw = {}
+    for kind in ("warm", "cold"):
+        ce = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n_cold)]
+        for i in range(n_cold):
+            if kind == "cold":
+                with torch.cuda.stream(stream):
+                    sink.add_(scrub.sum())
+            ce[2 * i].record(stream)
+            graphs[i % R].launch(stream)
+            ce[2 * i + 1].record(stream)
+        torch.cuda.synchronize()
+        cw[kind] = pct([ce[2 * i].elapsed_time(ce[2 * i + 1]) * 1e3 for i in range(n_cold)], 50)
+    del scrub, sink
 
     # Eager steps (launches without a graph), for comparison.
     for i in range(warmup):
@@ -313,6 +346,10 @@ def measure(dev, d, B, k, xs, steps, warmup, mode):
         "ms": ms, "value": mean_bytes / (ms * 1e-3) / 1e9, "ms_eager": ms_eager,
         "ms_graph1": ms_graph1,
         "us_p10": pct(per, 10), "us_p50": pct(per, 50), "us_p90": pct(per, 90),
+        "cold": {"us_warm": round(cw["warm"], 2), "us_cold": round(cw["cold"], 2),
+                 "ratio": round(cw["cold"] / cw["warm"], 3),
+                 "method": "median of one-step graph replays timed by events; cold ones "
+                           "each after a 1 GiB read that evicts the last-level cache"},
         "Ds": Ds, "step_bytes": step_bytes, "per_kernel": per_kernel, "dispatch": disp,
         "names": names, "expert_path": expert,
     }
@@ -327,6 +364,7 @@ def summary(name, B, m, alt):
             "gbs": round(m["value"], 1), "pct_hbm_peak": round(100 * m["value"] / HBM_PEAK_GBS, 2),
             "distinct_experts_mean": round(sum(m["Ds"]) / len(m["Ds"]), 1),
             "expert_path": alt.get("four_launches", m)["expert_path"],
+            "cold": m["cold"],
             "us_per_step_by_mode": {n: round(x["ms"] * 1e3, 2) for n, x in alt.items()}}
 
 
@@ -423,6 +461,7 @@ def run_c4(args):
                    "MXFP4 experts of inter 256, top-16, shared 512) in one HIP graph, batch 1",
                    "batch": 1, "layers": n_layers, "parallelism": "1 GPU"},
         "batch_sweep": results, "roofline": None, "cpu_baseline": None,
+        "device": device_info(),
     }
     print(json.dumps(line), flush=True)
 
@@ -524,6 +563,8 @@ def main():
         "distinct_experts": m["Ds"],
         "mode": default_mode(),
         "expert_path": alt.get("four_launches", m)["expert_path"],
+        "cold": m["cold"],
+        "device": device_info(),
         "kernels": per_kernel,
         "ms_per_step_eager": round(m["ms_eager"], 5),
         "ms_per_step_one_step_graphs": round(m["ms_graph1"], 5),
