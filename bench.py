@@ -154,6 +154,32 @@ def cpu_baseline(layer, xs, k, bytes_per_step, seconds):
                       f"(batch {xs[0].shape[0]}), {per_step:.3f} s per step single-threaded"}
 
 
+def cpu_baseline_all_cores(layer, xs, k, bytes_per_step, seconds):
+    """The same oracle on several host cores at once: one whole step per
+    thread (the C oracle is reentrant and ctypes releases the interpreter
+    lock during the call), rounds of as many steps as threads until about
+    `seconds` have passed.  At most 16 threads, the host share of one GPU."""
+    import os
+    from concurrent.futures import ThreadPoolExecutor
+
+    import oracle
+    oracle.lib()
+    n = max(1, min(16, os.cpu_count() or 1))
+    done, i = 0, 0
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(max_workers=n) as pool:
+        while time.perf_counter() - t0 < seconds:
+            batch = [xs[(i + j) % len(xs)] for j in range(n)]
+            i += n
+            list(pool.map(lambda x: oracle.moe_step(layer, x, rounding="output"), batch))
+            done += n
+    elapsed = time.perf_counter() - t0
+    return {"value": bytes_per_step * done / elapsed / 1e9, "unit": "GB/s", "cores": n,
+            "kind": "oracle",
+            "sample": f"{done} whole steps (batch {xs[0].shape[0]}) of the rotating inputs, "
+                      f"{n} at a time on {n} threads, {elapsed:.1f} s"}
+
+
 def device_info():
     """The GPU the figures come from, and the peak they are priced against."""
     import torch
@@ -539,10 +565,13 @@ def main():
                      for n, mode in modes().items()}
             sweep.append(summary(name, Bs, alt_s[default_mode()], alt_s))
 
-    cpu = None
+    cpu = cpu_all = None
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
         cpu = cpu_baseline(layer, xs, k, float(np.mean(m["step_bytes"])), args.cpu_seconds)
+        log("[bench] timing the CPU oracle on all host cores")
+        cpu_all = cpu_baseline_all_cores(layer, xs, k, float(np.mean(m["step_bytes"])),
+                                         args.cpu_seconds)
 
     ms = m["ms"]
     line = {
@@ -575,6 +604,7 @@ def main():
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": pk["frac"],
                      "traffic": load_traffic(pk["symbol"], args.workload)},
         "cpu_baseline": cpu,
+        "cpu_baseline_all_cores": cpu_all,
         "batch_sweep": sweep,
         "dispatch": m["dispatch"],
     }
