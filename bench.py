@@ -31,6 +31,7 @@ Prints ONE JSON line:
 With --workload c4_x8: eight TP8-share layers in one graph, batch 1..64.
 """
 import argparse
+import dataclasses
 import json
 import os
 import sys
@@ -178,6 +179,35 @@ def cpu_baseline_all_cores(layer, xs, k, bytes_per_step, seconds):
             "kind": "oracle",
             "sample": f"{done} whole steps (batch {xs[0].shape[0]}) of the rotating inputs, "
                       f"{n} at a time on {n} threads, {elapsed:.1f} s"}
+
+
+def cpu_oracle_sampled(layer, xs, bytes_per_step, seconds):
+    """The oracle on all host cores (up to 16 threads) for a batch too large to
+    time whole: single tokens of the rotating inputs, one per thread call,
+    for about `seconds`.  Tokens are independent in the oracle, so a step of
+    B tokens costs B token times; the figure is the step's bytes over that."""
+    import os
+    from concurrent.futures import ThreadPoolExecutor
+
+    import oracle
+    oracle.lib()
+    B = xs[0].shape[0]
+    toks = [x[b:b + 1] for x in xs for b in range(B)]
+    n = max(1, min(16, os.cpu_count() or 1))
+    done, i = 0, 0
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(max_workers=n) as pool:
+        while time.perf_counter() - t0 < seconds:
+            batch = [toks[(i + j) % len(toks)] for j in range(n)]
+            i += n
+            list(pool.map(lambda x: oracle.moe_step(layer, x, rounding="output"), batch))
+            done += n
+    elapsed = time.perf_counter() - t0
+    s_step = B * elapsed / done
+    return {"value": bytes_per_step / s_step / 1e9, "unit": "GB/s", "cores": n,
+            "kind": "oracle", "us_per_step": round(s_step * 1e6, 1),
+            "sample": f"{done} single tokens of the rotating batches on {n} threads in "
+                      f"{elapsed:.1f} s, times {B} tokens per step"}
 
 
 def device_info():
@@ -500,6 +530,8 @@ def main():
     ap.add_argument("--workload", default="k3_b1", choices=sorted(WORKLOADS) + ["c4_x8"])
     ap.add_argument("--rotate", type=int, default=32, help="distinct input batches cycled")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--sweep-cpu-seconds", type=float, default=4.0,
+                    help="oracle time per batch-sweep configuration (all host cores)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true", help="skip the batch sweep of the K3 layer")
     ap.add_argument("--modes", default=None,
@@ -564,6 +596,11 @@ def main():
             alt_s = {n: measure(dvb, d, Bs, k, xs_s, n_s, args.warmup, mode)
                      for n, mode in modes().items()}
             sweep.append(summary(name, Bs, alt_s[default_mode()], alt_s))
+            if not args.no_cpu_baseline:
+                log(f"[bench] timing the CPU oracle on {name}")
+                sweep[-1]["cpu_oracle"] = cpu_oracle_sampled(
+                    dataclasses.replace(layer, bias=bias), xs_s,
+                    float(np.mean(alt_s[default_mode()]["step_bytes"])), args.sweep_cpu_seconds)
 
     cpu = cpu_all = None
     if not args.no_cpu_baseline:
