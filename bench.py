@@ -545,7 +545,8 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures the decode step on one GPU only; multi-GPU runs "
-              f"(--gpus {args.gpus}, WORLD_SIZE {world}) are not part of this build.",
+              f"(--gpus {args.gpus}, WORLD_SIZE {world}) are not supported: the library has no "
+              "multi-GPU path.",
               file=sys.stderr)
         sys.exit(2)
 
