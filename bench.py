@@ -383,7 +383,8 @@ def measure(dev, d, B, k, xs, steps, warmup, mode):
         avg_ms = sums[n] / steps
         avg_bytes = kbytes[n] / steps
         gbs = avg_bytes / (avg_ms * 1e-3) / 1e9
-        per_kernel[n] = {"symbol": KERNEL_SYMBOLS[n], "us": round(avg_ms * 1e3, 2),
+        sym = "k_out_st" if n == "out" and disp.get("out_staged") else KERNEL_SYMBOLS[n]
+        per_kernel[n] = {"symbol": sym, "us": round(avg_ms * 1e3, 2),
                          "bytes": int(avg_bytes), "gbs": round(gbs, 1),
                          "frac": round(gbs / HBM_PEAK_GBS, 4)}
     expert = None

@@ -611,6 +611,17 @@ __device__ __forceinline__ void wait_staging() {
     __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | 0x0F70);
 }
 
+// Workgroup barrier after LDS writes that does not wait for global loads in
+// flight, as __syncthreads would: each wave's LDS accesses have completed
+// (lgkmcnt(0)) when it arrives.
+__device__ __forceinline__ void lds_reuse_barrier() {
+    fence_schedule();
+    // s_waitcnt lgkmcnt(0), with vmcnt and expcnt at their maxima (no wait).
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_s_barrier();
+    fence_schedule();
+}
+
 // Workgroup barrier after wait_staging: LDS holds every wave's copy once all
 // waves pass it.  A plain barrier, without the memory fence of
 // __syncthreads, which would also wait for the weight loads still in flight.
@@ -1223,6 +1234,131 @@ k_w2(const StepArgs a) {
     bool reuse = false;
     for (int u = blockIdx.x; u < NC * TG; u += gridDim.x)
         w2_unit<S, false, KS>(a, u / TG, u % TG, s_b, reuse);
+}
+
+// Kernel 4 up to kOutStTokens tokens: the column operands of the whole
+// reduction (ylat split into hi/lo bf16, then the shared activation's hi/lo
+// rows; row 2b + part, L + Is elements each) are staged in LDS once per
+// workgroup, and every MFMA operand is read from there instead of loaded and
+// split by every wave at every step.  The staging loads are issued before
+// the wave's first weight loads and waited for alone (vector loads complete
+// in issue order), so their round trip overlaps the weight stream's.  A
+// workgroup runs one output unit (the grid has one per unit); lanes without
+// a token read the last staged row and their columns are dropped.
+constexpr int kOutStTokens = 2;
+constexpr int kOutStBytes = 2 * kOutStTokens * 6144 * 2;  // LDS limit of the staged operand
+
+// Weights of output step s: latent-up rows below Ls, shared-down rows above.
+__device__ __forceinline__ void load_out_w(const TwoSource &t, int s, u32x4 (&ra)[4]) {
+    if (s < t.Ls)
+        load_tile_bf16(t.Aa, s, ra);
+    else
+        load_tile_bf16(t.Ab, s - t.Ls, ra);
+}
+
+__device__ __forceinline__ void mfma_tile_lds(const u32x4 (&ra)[4], const uint16_t *op, int s,
+                                              f32x4 &acc) {
+    const uint16_t *p = op + (size_t)s * kKStep;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc = mfma(as_bf16x8(ra[j]), as_bf16x8(*(const u32x4 *)(p + 32 * j)), acc);
+}
+
+__global__ void __launch_bounds__(kWGThreads) __attribute__((amdgpu_waves_per_eu(4)))
+k_out_st(const StepArgs a) {
+    extern __shared__ __attribute__((aligned(16))) uint16_t s_op[];  // [2B][L + Is]
+    __shared__ float s_red[kWG * kWave * 4];
+    if (blockIdx.x == 0 && threadIdx.x == 0) a.gctr[G_ROUTER_DONE] = 0u;
+    const Role ro = role_of(a.kw_out);
+    const int lane = lane_id(), n = lane & 15, g = lane >> 4;
+    const int col = n >> 1, part = n & 1;
+    const int K = a.L + a.Is, RT = a.out_rows;
+    const int n_t = (a.H + RT - 1) / RT;
+    const int units = dense_units(n_t, ro.RW, 1);
+    const int u = blockIdx.x;
+    if (u >= units) return;
+    int cb, tg;
+    dense_unit(u, 1, cb, tg);
+    const int t = tg * ro.RW + ro.rg;
+    const bool active = t < n_t;
+    // Staging loads: chunk q = 8 elements e .. e + 7 of token b (q < B K / 8),
+    // two 16-byte loads each (f32 ylat values, or the hi and the lo row of
+    // the shared activation), at most three chunks per thread.
+    const int nq = a.B * K / 8;
+    constexpr int kQ = (kOutStTokens * 6144 / 8 + kWGThreads - 1) / kWGThreads;
+    u32x4 st0[kQ], st1[kQ];
+#pragma unroll
+    for (int i = 0; i < kQ; ++i) {
+        const int q = min((int)threadIdx.x + kWGThreads * i, nq - 1);
+        const int b = q / (K / 8), e = 8 * (q % (K / 8));
+        const bool lat = e < a.L;
+        const uint8_t *p0 = lat ? (const uint8_t *)(a.ylat + (size_t)b * a.L + e)
+                                : (const uint8_t *)(a.ashhl + (size_t)b * 2 * a.Is + (e - a.L));
+        const uint8_t *p1 = lat ? p0 + 16 : p0 + (size_t)a.Is * 2;
+        st0[i] = ld16(p0);
+        st1[i] = ld16(p1);
+    }
+    fence_schedule();
+    // The wave's first two weight steps, issued behind the staging loads.
+    const int h0 = RT * (active ? t : 0);
+    const size_t h = min(h0 + min(n, RT - 1), a.H - 1);
+    TwoSource ts;
+    ts.Aa = a.lat_up + h * a.L + 8 * g;
+    ts.Ab = a.sh_w2 + h * a.Is + 8 * g;
+    ts.Ls = a.L / kKStep;
+    const int s0 = ro.kw * a.spc_out, s1 = s0 + a.spc_out;
+    u32x4 ra0[4], ra1[4];
+    load_out_w(ts, s0, ra0);
+    load_out_w(ts, s0 + 1 < s1 ? s0 + 1 : s0, ra1);
+    fence_schedule();
+    __builtin_amdgcn_s_waitcnt(8 | 0x0F70);  // vmcnt(8): the staging loads have landed
+#pragma unroll
+    for (int i = 0; i < kQ; ++i) {
+        const int q = (int)threadIdx.x + kWGThreads * i;
+        if (q < nq) {
+            const int b = q / (K / 8), e = 8 * (q % (K / 8));
+            u32x4 hi = st0[i], lo = st1[i];
+            if (e < a.L) {  // f32 values: split into hi and lo bf16
+                const f32x4 v0 = __builtin_bit_cast(f32x4, st0[i]), v1 = __builtin_bit_cast(f32x4, st1[i]);
+                uint32_t h[4], l[4];
+                split_hl2(v0[0], v0[1], h[0], l[0]);
+                split_hl2(v0[2], v0[3], h[1], l[1]);
+                split_hl2(v1[0], v1[1], h[2], l[2]);
+                split_hl2(v1[2], v1[3], h[3], l[3]);
+                hi = (u32x4){h[0], h[1], h[2], h[3]};
+                lo = (u32x4){l[0], l[1], l[2], l[3]};
+            }
+            *(u32x4 *)(s_op + (size_t)(2 * b) * K + e) = hi;
+            *(u32x4 *)(s_op + (size_t)(2 * b + 1) * K + e) = lo;
+        }
+    }
+    lds_reuse_barrier();  // the staged operand is complete (weight loads still in flight)
+    const uint16_t *op = s_op + (size_t)min(n, 2 * a.B - 1) * K + 8 * g;
+    f32x4 acc = zero4();
+    if (active) {
+        mfma_tile_lds(ra0, op, s0, acc);
+        if (s0 + 1 < s1) mfma_tile_lds(ra1, op, s0 + 1, acc);
+#pragma unroll 1
+        for (int s = s0 + 2; s < s1; s += 2) {
+            const bool two = s + 1 < s1;
+            load_out_w(ts, s, ra0);
+            load_out_w(ts, two ? s + 1 : s, ra1);
+            fence_schedule();
+            mfma_tile_lds(ra0, op, s, acc);
+            if (two) mfma_tile_lds(ra1, op, s + 1, acc);
+        }
+    }
+    const bool leader = reduce_k1(s_red, ro.wave, ro.kw, ro.KW, acc);
+    if (leader && active) {
+        const f32x4 v = add_pair_column(acc);
+        if (col < a.B && part == 0) {
+            const size_t o = (size_t)col * a.H + h0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 4 * g + i;
+                if (r < RT && h0 + r < a.H) a.out[o + r] = (uint16_t)bf16_rne(v[i]);
+            }
+        }
+    }
 }
 
 // Kernel 4: output units (latent-up and shared-down in one pass), each over

@@ -517,6 +517,7 @@ moe_status moe_decode_step(moe_decode_ctx *ctx, const uint16_t *x, int32_t batch
     d.fused = fused ? 1 : tail ? 2 : side ? 3 : 0;
     d.n_kernels = fused ? 1 : tail ? 2 : side ? 6 + d.router_f32 : 4 + d.router_f32;
     d.grid_step = 0;
+    d.out_staged = 0;
     // One persistent workgroup per resident slot of `kernel` (the unit
     // queues do not rely on residency; this only sizes the grid).
     auto persistent_grid = [&](StepKernel kernel, long long units) {
@@ -569,12 +570,12 @@ moe_status moe_decode_step(moe_decode_ctx *ctx, const uint16_t *x, int32_t batch
     const bool timed = ctx->n_events == 2 * d.n_kernels;
     int ki = 0;
     auto launch_on = [&](hipStream_t st, StepKernel kernel, unsigned grid, unsigned threads,
-                         const StepArgs &args) {
+                         const StepArgs &args, size_t lds = 0) {
         if (timed)
-            hipExtLaunchKernelGGL(kernel, dim3(grid), dim3(threads), 0, st, ctx->events[2 * ki],
+            hipExtLaunchKernelGGL(kernel, dim3(grid), dim3(threads), lds, st, ctx->events[2 * ki],
                                   ctx->events[2 * ki + 1], 0, args);
         else
-            hipLaunchKernelGGL(kernel, dim3(grid), dim3(threads), 0, st, args);
+            hipLaunchKernelGGL(kernel, dim3(grid), dim3(threads), lds, st, args);
         ++ki;
     };
     auto launch = [&](StepKernel kernel, unsigned grid, unsigned threads) {
@@ -663,8 +664,17 @@ moe_status moe_decode_step(moe_decode_ctx *ctx, const uint16_t *x, int32_t batch
                                                                                     : k_out_kx<8>;
         launch(out_kx, (unsigned)(nrg * nsl), kWGThreads);
     } else {
-        const StepKernel out_k[] = {k_out<1>, k_out<2>, k_out<3>, k_out<4>};
-        launch(out_k[pl.ncg_unit_out - 1], d.grid_out, kWGThreads);
+        // Up to two tokens the column operands of the whole reduction fit in
+        // LDS: staged once per workgroup.
+        const size_t st_lds = (size_t)4 * batch * (c.latent + c.shared_inter);
+        if (batch <= kOutStTokens && st_lds <= (size_t)kOutStBytes && pl.out.kw > 0 &&
+            d.grid_out == (int32_t)pl.units_out) {
+            launch_on(s, k_out_st, d.grid_out, kWGThreads, a, st_lds);
+            d.out_staged = 1;
+        } else {
+            const StepKernel out_k[] = {k_out<1>, k_out<2>, k_out<3>, k_out<4>};
+            launch(out_k[pl.ncg_unit_out - 1], d.grid_out, kWGThreads);
+        }
     }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(ctx, e);
