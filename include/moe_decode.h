@@ -179,8 +179,9 @@ typedef struct {
     int32_t fused;         /* 1: one persistent launch; 2: dense-in + persistent launch;
                               3: side stream; 0: four launches */
     int32_t grid_step;     /* workgroups of the persistent launch (0 for four launches) */
-    int32_t out_staged;    /* 1 when the output launch staged its column operands in LDS
-                              (four launches, at most two tokens) */
+    int32_t out_staged;    /* four launches: 1 when the output launch staged its whole
+                              column operand in LDS (at most two tokens), 2 when it
+                              staged the latent part (at most eight tokens), else 0 */
 } moe_decode_dispatch_info;
 moe_status moe_decode_last_dispatch(const moe_decode_ctx *ctx, moe_decode_dispatch_info *info);
 

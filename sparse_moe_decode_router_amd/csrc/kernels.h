@@ -1236,17 +1236,22 @@ k_w2(const StepArgs a) {
         w2_unit<S, false, KS>(a, u / TG, u % TG, s_b, reuse);
 }
 
-// Kernel 4 up to kOutStTokens tokens: the column operands of the whole
-// reduction (ylat split into hi/lo bf16, then the shared activation's hi/lo
-// rows; row 2b + part, L + Is elements each) are staged in LDS once per
-// workgroup, and every MFMA operand is read from there instead of loaded and
-// split by every wave at every step.  The staging loads are issued before
-// the wave's first weight loads and waited for alone (vector loads complete
-// in issue order), so their round trip overlaps the weight stream's.  A
-// workgroup runs one output unit (the grid has one per unit); lanes without
-// a token read the last staged row and their columns are dropped.
+// Kernel 4 up to 8 tokens with column operands staged in LDS once per
+// workgroup, instead of loaded (and, for ylat, split into hi/lo) by every wave
+// at every step.  Full (up to kOutStTokens tokens): the whole reduction's
+// operand, ylat split into hi/lo bf16 and then the shared activation's hi/lo
+// rows (row 2b + part, L + Is elements).  Otherwise (up to 8 tokens): the
+// ylat part only (L elements a row); the shared-down steps load their bf16
+// operand from global memory with the weights, as k_out does.  The staging
+// loads are issued before the wave's first two weight steps and waited for
+// alone (vector loads complete in issue order), so their round trip overlaps
+// the weight stream's.  A workgroup runs one output unit (the grid has one per
+// unit); lanes without a token read the last staged row and their columns are
+// dropped.
 constexpr int kOutStTokens = 2;
-constexpr int kOutStBytes = 2 * kOutStTokens * 6144 * 2;  // LDS limit of the staged operand
+constexpr int kOutStBytes = 2 * kOutStTokens * 6144 * 2;  // LDS limit of the full operand
+constexpr int kOutStLatTokens = 8;
+constexpr int kOutStLatBytes = 65536;                     // LDS limit of the ylat operand
 
 // Weights of output step s: latent-up rows below Ls, shared-down rows above.
 __device__ __forceinline__ void load_out_w(const TwoSource &t, int s, u32x4 (&ra)[4]) {
@@ -1263,15 +1268,17 @@ __device__ __forceinline__ void mfma_tile_lds(const u32x4 (&ra)[4], const uint16
     for (int j = 0; j < 4; ++j) acc = mfma(as_bf16x8(ra[j]), as_bf16x8(*(const u32x4 *)(p + 32 * j)), acc);
 }
 
+template <bool Full>
 __global__ void __launch_bounds__(kWGThreads) __attribute__((amdgpu_waves_per_eu(4)))
 k_out_st(const StepArgs a) {
-    extern __shared__ __attribute__((aligned(16))) uint16_t s_op[];  // [2B][L + Is]
+    extern __shared__ __attribute__((aligned(16))) uint16_t s_op[];  // [2B][KS]
     __shared__ float s_red[kWG * kWave * 4];
     if (blockIdx.x == 0 && threadIdx.x == 0) a.gctr[G_ROUTER_DONE] = 0u;
     const Role ro = role_of(a.kw_out);
     const int lane = lane_id(), n = lane & 15, g = lane >> 4;
     const int col = n >> 1, part = n & 1;
-    const int K = a.L + a.Is, RT = a.out_rows;
+    const int KS = Full ? a.L + a.Is : a.L;  // staged elements per row
+    const int RT = a.out_rows;
     const int n_t = (a.H + RT - 1) / RT;
     const int units = dense_units(n_t, ro.RW, 1);
     const int u = blockIdx.x;
@@ -1280,17 +1287,17 @@ k_out_st(const StepArgs a) {
     dense_unit(u, 1, cb, tg);
     const int t = tg * ro.RW + ro.rg;
     const bool active = t < n_t;
-    // Staging loads: chunk q = 8 elements e .. e + 7 of token b (q < B K / 8),
+    // Staging loads: chunk q = 8 elements e .. e + 7 of token b (q < B KS / 8),
     // two 16-byte loads each (f32 ylat values, or the hi and the lo row of
-    // the shared activation), at most three chunks per thread.
-    const int nq = a.B * K / 8;
-    constexpr int kQ = (kOutStTokens * 6144 / 8 + kWGThreads - 1) / kWGThreads;
+    // the shared activation).
+    const int nq = a.B * KS / 8;
+    constexpr int kQ = ((Full ? kOutStBytes : kOutStLatBytes) / 32 + kWGThreads - 1) / kWGThreads;
     u32x4 st0[kQ], st1[kQ];
 #pragma unroll
     for (int i = 0; i < kQ; ++i) {
         const int q = min((int)threadIdx.x + kWGThreads * i, nq - 1);
-        const int b = q / (K / 8), e = 8 * (q % (K / 8));
-        const bool lat = e < a.L;
+        const int b = q / (KS / 8), e = 8 * (q % (KS / 8));
+        const bool lat = !Full || e < a.L;
         const uint8_t *p0 = lat ? (const uint8_t *)(a.ylat + (size_t)b * a.L + e)
                                 : (const uint8_t *)(a.ashhl + (size_t)b * 2 * a.Is + (e - a.L));
         const uint8_t *p1 = lat ? p0 + 16 : p0 + (size_t)a.Is * 2;
@@ -1315,36 +1322,52 @@ k_out_st(const StepArgs a) {
     for (int i = 0; i < kQ; ++i) {
         const int q = (int)threadIdx.x + kWGThreads * i;
         if (q < nq) {
-            const int b = q / (K / 8), e = 8 * (q % (K / 8));
+            const int b = q / (KS / 8), e = 8 * (q % (KS / 8));
             u32x4 hi = st0[i], lo = st1[i];
-            if (e < a.L) {  // f32 values: split into hi and lo bf16
+            if (!Full || e < a.L) {  // f32 values: split into hi and lo bf16
                 const f32x4 v0 = __builtin_bit_cast(f32x4, st0[i]), v1 = __builtin_bit_cast(f32x4, st1[i]);
-                uint32_t h[4], l[4];
-                split_hl2(v0[0], v0[1], h[0], l[0]);
-                split_hl2(v0[2], v0[3], h[1], l[1]);
-                split_hl2(v1[0], v1[1], h[2], l[2]);
-                split_hl2(v1[2], v1[3], h[3], l[3]);
-                hi = (u32x4){h[0], h[1], h[2], h[3]};
-                lo = (u32x4){l[0], l[1], l[2], l[3]};
+                uint32_t hh[4], ll[4];
+                split_hl2(v0[0], v0[1], hh[0], ll[0]);
+                split_hl2(v0[2], v0[3], hh[1], ll[1]);
+                split_hl2(v1[0], v1[1], hh[2], ll[2]);
+                split_hl2(v1[2], v1[3], hh[3], ll[3]);
+                hi = (u32x4){hh[0], hh[1], hh[2], hh[3]};
+                lo = (u32x4){ll[0], ll[1], ll[2], ll[3]};
             }
-            *(u32x4 *)(s_op + (size_t)(2 * b) * K + e) = hi;
-            *(u32x4 *)(s_op + (size_t)(2 * b + 1) * K + e) = lo;
+            *(u32x4 *)(s_op + (size_t)(2 * b) * KS + e) = hi;
+            *(u32x4 *)(s_op + (size_t)(2 * b + 1) * KS + e) = lo;
         }
     }
     lds_reuse_barrier();  // the staged operand is complete (weight loads still in flight)
-    const uint16_t *op = s_op + (size_t)min(n, 2 * a.B - 1) * K + 8 * g;
+    const uint16_t *op = s_op + (size_t)min(n, 2 * a.B - 1) * KS + 8 * g;
+    // Shared-down operand from global memory (the ylat-only form).
+    const bool valid = col < a.B;
+    const rsrc_t rb_ash = buf_rsrc(a.ashhl);
+    const uint32_t ob = (uint32_t)((((size_t)(valid ? col : 0) * 2 + part) * a.Is + 8 * g) * 2);
     f32x4 acc = zero4();
     if (active) {
-        mfma_tile_lds(ra0, op, s0, acc);
-        if (s0 + 1 < s1) mfma_tile_lds(ra1, op, s0 + 1, acc);
 #pragma unroll 1
-        for (int s = s0 + 2; s < s1; s += 2) {
+        for (int s = s0; s < s1; s += 2) {
             const bool two = s + 1 < s1;
-            load_out_w(ts, s, ra0);
-            load_out_w(ts, two ? s + 1 : s, ra1);
+            const int s2 = two ? s + 1 : s;
+            if (s > s0) {
+                load_out_w(ts, s, ra0);
+                load_out_w(ts, s2, ra1);
+            }
+            u32x4 rb0[4], rb1[4];
+            if (!Full && s >= ts.Ls) buf_cols_bf16<false>(rb_ash, ob, valid, s - ts.Ls, rb0);
+            if (!Full && s2 >= ts.Ls) buf_cols_bf16<false>(rb_ash, ob, valid, s2 - ts.Ls, rb1);
             fence_schedule();
-            mfma_tile_lds(ra0, op, s, acc);
-            if (two) mfma_tile_lds(ra1, op, s + 1, acc);
+            if (Full || s < ts.Ls)
+                mfma_tile_lds(ra0, op, s, acc);
+            else
+                mfma_tile(ra0, rb0, acc);
+            if (two) {
+                if (Full || s2 < ts.Ls)
+                    mfma_tile_lds(ra1, op, s2, acc);
+                else
+                    mfma_tile(ra1, rb1, acc);
+            }
         }
     }
     const bool leader = reduce_k1(s_red, ro.wave, ro.kw, ro.KW, acc);

@@ -665,12 +665,16 @@ moe_status moe_decode_step(moe_decode_ctx *ctx, const uint16_t *x, int32_t batch
         launch(out_kx, (unsigned)(nrg * nsl), kWGThreads);
     } else {
         // Up to two tokens the column operands of the whole reduction fit in
-        // LDS: staged once per workgroup.
-        const size_t st_lds = (size_t)4 * batch * (c.latent + c.shared_inter);
-        if (batch <= kOutStTokens && st_lds <= (size_t)kOutStBytes && pl.out.kw > 0 &&
-            d.grid_out == (int32_t)pl.units_out) {
-            launch_on(s, k_out_st, d.grid_out, kWGThreads, a, st_lds);
+        // LDS, up to eight their ylat part: staged once per workgroup.
+        const size_t st_full = (size_t)4 * batch * (c.latent + c.shared_inter);
+        const size_t st_lat = (size_t)4 * batch * c.latent;
+        const bool one_unit = pl.out.kw > 0 && d.grid_out == (int32_t)pl.units_out;
+        if (one_unit && batch <= kOutStTokens && st_full <= (size_t)kOutStBytes) {
+            launch_on(s, k_out_st<true>, d.grid_out, kWGThreads, a, st_full);
             d.out_staged = 1;
+        } else if (one_unit && batch <= kOutStLatTokens && st_lat <= (size_t)kOutStLatBytes) {
+            launch_on(s, k_out_st<false>, d.grid_out, kWGThreads, a, st_lat);
+            d.out_staged = 2;
         } else {
             const StepKernel out_k[] = {k_out<1>, k_out<2>, k_out<3>, k_out<4>};
             launch(out_k[pl.ncg_unit_out - 1], d.grid_out, kWGThreads);
