@@ -109,7 +109,9 @@ def mxfp4_element(q_row: np.ndarray, s_row: np.ndarray, j: int) -> float:
 # ---- routing ----
 
 def topk(key: np.ndarray, k: int) -> np.ndarray:
-    key = _c(key, np.float32)
+    """The k largest of binary64 keys (full sort, equal keys to the lower
+    index), in ascending index."""
+    key = _c(key, np.float64)
     out = np.empty(k, np.int32)
     if lib().oracle_topk(_p(key), key.size, k, _p(out)) != 0:
         raise ValueError("oracle_topk: bad arguments")
@@ -130,10 +132,11 @@ def router_scores(dims, x: np.ndarray, router_w: np.ndarray):
 
 
 def select(dims, score: np.ndarray, bias: Optional[np.ndarray], forced_idx=None):
-    """(key f32 [B][E], idx [B][k], weight [B][k]) from scores."""
+    """(key [B][E], idx [B][k], weight [B][k]) from scores, all binary64
+    except idx."""
     score = _c(score, np.float64)
     B = score.shape[0]
-    key = np.empty((B, dims.n_experts), np.float32)
+    key = np.empty((B, dims.n_experts), np.float64)
     idx = np.empty((B, dims.top_k), np.int32)
     w = np.empty((B, dims.top_k))
     ds = dims_struct(dims)
@@ -167,7 +170,7 @@ def moe_step(layer, x: np.ndarray, rounding: str = "output", forced_idx=None,
     B = x.shape[0]
     H, L, E, I, Is, k = d.hidden, d.latent, d.n_experts, d.expert_inter, d.shared_inter, d.top_k
     shapes = {"logit": ((B, E), np.float64), "score": ((B, E), np.float64),
-              "key": ((B, E), np.float32), "idx": ((B, k), np.int32),
+              "key": ((B, E), np.float64), "idx": ((B, k), np.int32),
               "weight": ((B, k), np.float64), "z": ((B, L), np.float64),
               "act": ((B, k, I), np.float64), "ylat": ((B, L), np.float64),
               "ash": ((B, Is), np.float64), "sh": ((B, H), np.float64),
@@ -191,24 +194,50 @@ def moe_step(layer, x: np.ndarray, rounding: str = "output", forced_idx=None,
     return res
 
 
-def near_tie_alternatives(key64_row: np.ndarray, k: int, tau: float):
-    """Valid selections for one token whose k-th/(k+1)-th keys lie within tau.
+def _is_valid_selection(key64_row: np.ndarray, sel, tau: float) -> bool:
+    """min over the selection >= max over the rest - tau."""
+    mask = np.zeros(key64_row.size, bool)
+    mask[list(sel)] = True
+    if mask.all():
+        return True
+    return bool(key64_row[mask].min() >= key64_row[~mask].max() - tau)
 
-    Experts whose binary64 key is within tau of the boundary key may trade
-    places; every selection of k experts that keeps all experts clearly above
-    the boundary and fills the rest from the near-boundary set is valid.
-    Returns (is_near_tie, list of sorted index arrays).
+
+def near_tie_alternatives(key64_row: np.ndarray, k: int, tau: float, limit: int = 200000):
+    """Every selection of k experts that a decision on keys within tau / 2 of
+    the binary64 keys can produce, for one token.
+
+    A set S is the top-k of some key vector that differs from key64_row by at
+    most tau / 2 per element exactly when min_{e in S} key_e >= max_{e not in
+    S} key_e - tau (raise S by tau / 2, lower the rest by tau / 2).  Every such
+    S contains each expert whose key exceeds the (k+1)-th largest key by more
+    than tau, and lies within the experts whose key is at least the k-th
+    largest key minus tau; the sets in between are enumerated and filtered by
+    the condition.  More than one set qualifies exactly when the k-th and
+    (k+1)-th largest keys lie within tau of each other.
+
+    Returns (is_near_tie, list of sorted int32 index arrays).  Raises
+    ValueError when more than `limit` sets would be listed.
     """
     import itertools
-    order = np.lexsort((np.arange(key64_row.size), -key64_row))
-    kth = key64_row[order[k - 1]]
-    near = [int(e) for e in np.nonzero(np.abs(key64_row - kth) <= tau)[0]]
-    sure = [int(e) for e in order[:k] if key64_row[e] - kth > tau]
-    free = k - len(sure)
-    gap = key64_row[order[k - 1]] - key64_row[order[k]] if k < key64_row.size else np.inf
-    if gap > tau:
-        return False, [np.sort(order[:k]).astype(np.int32)]
+    from math import comb
+    key64_row = np.asarray(key64_row, np.float64)
+    E = key64_row.size
+    order = np.lexsort((np.arange(E), -key64_row))
+    top = np.sort(order[:k]).astype(np.int32)
+    if k >= E:
+        return False, [top]
+    v_k, v_k1 = key64_row[order[k - 1]], key64_row[order[k]]
+    if v_k - v_k1 > tau:
+        return False, [top]
+    must = [int(e) for e in np.nonzero(key64_row > v_k1 + tau)[0]]
+    cand = [int(e) for e in np.nonzero((key64_row >= v_k - tau) & (key64_row <= v_k1 + tau))[0]]
+    free = k - len(must)
+    if comb(len(cand), free) > limit:
+        raise ValueError(f"{comb(len(cand), free)} candidate selections")
     alts = []
-    for combo in itertools.combinations(sorted(near), free):
-        alts.append(np.sort(np.array(sure + list(combo), np.int32)))
-    return True, alts
+    for combo in itertools.combinations(cand, free):
+        sel = must + list(combo)
+        if _is_valid_selection(key64_row, sel, tau):
+            alts.append(np.sort(np.array(sel, np.int32)))
+    return len(alts) > 1, alts

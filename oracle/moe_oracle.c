@@ -46,7 +46,7 @@ typedef struct {
 typedef struct {           /* every pointer optional (NULL = not wanted)   */
     double  *logit;        /* [B][E]       router logits                    */
     double  *score;        /* [B][E]       sigmoid scores                   */
-    float   *key;          /* [B][E]       selection keys, binary32         */
+    double  *key;          /* [B][E]       selection keys s + bias          */
     int32_t *idx;          /* [B][k]       chosen experts, ascending id     */
     double  *weight;       /* [B][k]       renormalised weights             */
     double  *z;            /* [B][L]       latent input of the experts      */
@@ -177,7 +177,7 @@ int32_t oracle_router_scores(const oracle_dims *d, int32_t B, const uint16_t *x,
 }
 
 typedef struct {
-    float key;
+    double key;
     int32_t id;
 } keyed_expert;
 
@@ -198,7 +198,7 @@ static int by_id(const void *pa, const void *pb)
 
 /* Top-k of E keys: sort all E experts by (key descending, id ascending), keep
  * the first k, return them in ascending id. */
-int32_t oracle_topk(const float *key, int32_t E, int32_t k, int32_t *idx_out)
+int32_t oracle_topk(const double *key, int32_t E, int32_t k, int32_t *idx_out)
 {
     if (k < 1 || k > E) return -1;
     keyed_expert *order = malloc(sizeof(keyed_expert) * (size_t)E);
@@ -215,25 +215,24 @@ int32_t oracle_topk(const float *key, int32_t E, int32_t k, int32_t *idx_out)
 }
 
 /* Selection and weights for B tokens from their scores.
- *   key_e = binary32(score_e + bias_e)   (READING: the bias moves only the
- *                                         selection key; the decision is
- *                                         taken in binary32, the precision
- *                                         the kernel decides in)
- *   S     = top-k by key (ties -> lower id), or forced_idx when given
+ *   key_e = score_e + bias_e   in binary64 (READING: the bias moves only the
+ *                              selection key)
+ *   S     = top-k by key (full sort; ties -> lower id), or forced_idx when
+ *           given
  *   w_e   = score_e / sum_{j in S} score_j  (READING: unbiased scores,
  *                                            renormalised, no extra factor)
  * bias may be NULL (zero).  key / weight may be NULL. */
 int32_t oracle_select(const oracle_dims *d, int32_t B, const double *score, const float *bias,
-                      const int32_t *forced_idx, float *key, int32_t *idx, double *weight)
+                      const int32_t *forced_idx, double *key, int32_t *idx, double *weight)
 {
     const int32_t E = d->n_experts, k = d->top_k;
-    float *kb = malloc(sizeof(float) * (size_t)E);
+    double *kb = malloc(sizeof(double) * (size_t)E);
     if (!kb) return -1;
     for (int32_t b = 0; b < B; ++b) {
         const double *s = score + (int64_t)b * E;
         for (int32_t e = 0; e < E; ++e)
-            kb[e] = (float)(s[e] + (bias ? (double)bias[e] : 0.0));
-        if (key) memcpy(key + (int64_t)b * E, kb, sizeof(float) * (size_t)E);
+            kb[e] = s[e] + (bias ? (double)bias[e] : 0.0);
+        if (key) memcpy(key + (int64_t)b * E, kb, sizeof(double) * (size_t)E);
         int32_t *sel = idx + (int64_t)b * k;
         if (forced_idx) {
             memcpy(sel, forced_idx + (int64_t)b * k, sizeof(int32_t) * (size_t)k);

@@ -85,14 +85,14 @@ def dense_reference(layer, x, rounding="output", forced_idx=None):
     logit = xv @ rw.T
     score = 1.0 / (1.0 + np.exp(-logit))
     bias = np.zeros(E) if layer.bias is None else layer.bias.astype(np.float64)
-    key = (score + bias).astype(np.float32)
+    key = score + bias
     B = xv.shape[0]
     idx = np.empty((B, k), np.int64)
     for b in range(B):
         if forced_idx is not None:
             idx[b] = np.sort(forced_idx[b])
         else:
-            order = np.lexsort((np.arange(E), -key[b].astype(np.float64)))
+            order = np.lexsort((np.arange(E), -key[b]))
             idx[b] = np.sort(order[:k])
     sel = np.take_along_axis(score, idx, axis=1)
     w = sel / sel.sum(axis=1, keepdims=True)
@@ -237,7 +237,11 @@ def test_topk_tiny_layer_all_635376_subsets():
     _, score = oracle.router_scores(d, x, layer.router_w)
     key, idx, _ = oracle.select(d, score, layer.bias)
     combos = np.array(list(itertools.combinations(range(d.n_experts), d.top_k)))
-    sums = key[0].astype(np.float64)[combos].sum(axis=1)   # exact: 4 binary32 terms
+    # Sums of 4 binary64 keys in [1/8, 2) need at most 53 + 4 + 2 significant
+    # bits: exact in the 64-bit significand of the x87 extended format.
+    assert np.finfo(np.longdouble).nmant >= 63
+    assert key.min() >= 0.125 and key.max() < 2.0
+    sums = key[0].astype(np.longdouble)[combos].sum(axis=1)
     best = combos[np.flatnonzero(sums == sums.max())[0]]    # first = lexicographically least
     np.testing.assert_array_equal(idx[0], best)
 
@@ -245,7 +249,7 @@ def test_topk_tiny_layer_all_635376_subsets():
 def test_topk_threshold_invariant_large():
     rng = np.random.default_rng(3)
     for _ in range(20):
-        key = rng.standard_normal(896).astype(np.float32)
+        key = rng.standard_normal(896)
         key[rng.integers(0, 896, 50)] = key[0]                 # plant ties
         sel = oracle.topk(key, 16)
         assert np.all(np.diff(sel) > 0)
@@ -254,6 +258,105 @@ def test_topk_threshold_invariant_large():
         # ties at the boundary resolved toward lower ids
         t = key[sel].min()
         assert not np.any((key[rest] == t) & (rest < sel[key[sel] == t].max()))
+
+
+def test_select_decides_on_binary64_keys():
+    """The top-k is taken on the binary64 keys s + bias: two experts whose keys
+    differ by 2^-40 (below binary32 resolution at 0.5) are ordered by that
+    difference, not by the id tie-break that binary32 keys would force."""
+    dims = small_recipe(E=8, k=1).dims
+    score = np.full((1, 8), 0.25)
+    score[0, 3] = 0.5
+    score[0, 5] = 0.5 + 2.0 ** -40
+    assert np.float32(score[0, 3]) == np.float32(score[0, 5])
+    key, idx, w = oracle.select(dims, score, None)
+    assert idx.tolist() == [[5]] and w.tolist() == [[1.0]]
+    assert key[0, 5] - key[0, 3] == 2.0 ** -40
+    # the same through a bias: equal scores, biases apart by 2^-30 in binary32
+    bias = np.zeros(8, np.float32)
+    bias[2] = np.float32(2.0 ** -30)
+    _, idx2, _ = oracle.select(dims, np.full((1, 8), 0.75), bias)
+    assert idx2.tolist() == [[2]]
+
+
+# ---------------------------------------------------------------------------
+# Near ties: the selections the parity tests accept from the GPU
+# ---------------------------------------------------------------------------
+
+def explainable_bruteforce(key: np.ndarray, k: int, tau: float):
+    """Every k-subset S for which some key vector within tau / 2 of `key`, per
+    element, has S among its top-k sets: raise S by tau / 2, lower the rest by
+    tau / 2 and ask whether S's smallest key is still at least the largest
+    other key (equal keys may then be ordered either way)."""
+    E = key.size
+    res = []
+    for combo in itertools.combinations(range(E), k):
+        up = np.array([key[e] + tau / 2 if e in combo else key[e] - tau / 2 for e in range(E)])
+        rest = [e for e in range(E) if e not in combo]
+        if not rest or min(up[list(combo)]) >= max(up[rest]):
+            res.append(combo)
+    return res
+
+
+def planted_keys(rng, E, k, tau, case):
+    """Keys with a planted configuration at the k-th / (k+1)-th boundary (no
+    two keys exactly tau apart, where rounding would decide the comparison)."""
+    key = 0.5 + rng.permutation(E).astype(np.float64) * 4 * tau   # distinct, 4 tau apart
+    order = np.argsort(-key, kind="stable")
+    if k >= E:                                  # no boundary: every expert is chosen
+        return key
+    kth, k1 = order[k - 1], order[k]
+    if case == "exact tie":
+        key[k1] = key[kth]
+    elif case == "gap just below tau":
+        key[k1] = key[kth] - 0.999 * tau
+    elif case == "gap just above tau":
+        key[k1] = key[kth] - 1.001 * tau
+    elif case == "key within tau above the k-th":
+        if k >= 2:
+            key[order[k - 2]] = key[kth] + 0.4 * tau
+        key[k1] = key[kth] - 0.45 * tau
+    elif case == "many within tau":
+        band = order[max(0, k - 3):k + 3]
+        key[band] = key[kth] + rng.uniform(-tau / 2, tau / 2, band.size)
+    elif case == "all equal":
+        key[:] = 0.5
+    return key
+
+
+@pytest.mark.parametrize("case", ["exact tie", "gap just below tau", "gap just above tau",
+                                  "key within tau above the k-th", "many within tau",
+                                  "all equal", "random"])
+@pytest.mark.parametrize("E,k", [(6, 1), (8, 3), (10, 4), (12, 2), (9, 9)])
+def test_near_tie_alternatives_match_bruteforce(case, E, k):
+    tau = 1e-5
+    rng = np.random.default_rng(E * 100 + k * 7 + len(case))
+    for trial in range(6):
+        key = planted_keys(rng, E, k, tau, case) if case != "random" else \
+            0.5 + rng.uniform(-3 * tau, 3 * tau, E)
+        want = explainable_bruteforce(key, k, tau)
+        is_near, alts = oracle.near_tie_alternatives(key, k, tau)
+        got = sorted(tuple(int(e) for e in a) for a in alts)
+        assert got == sorted(want), (case, key)
+        assert is_near == (len(want) > 1)
+        # the oracle's own selection is always among them
+        assert tuple(oracle.topk(key, k).tolist()) in got
+        if k < E:
+            srt = np.sort(key)[::-1]
+            assert is_near == (srt[k - 1] - srt[k] <= tau)
+            # an expert more than tau above the (k+1)-th key is in every set
+            for e in np.nonzero(key > srt[k] + tau)[0]:
+                assert all(e in a for a in got)
+
+
+def test_near_tie_gap_above_tau_accepts_only_the_oracle_selection():
+    rng = np.random.default_rng(11)
+    key = rng.uniform(0, 1, 896)
+    srt = np.sort(key)[::-1]
+    key[key == srt[16]] = srt[15] - 1.5e-5
+    is_near, alts = oracle.near_tie_alternatives(key, 16, 1e-5)
+    assert not is_near and len(alts) == 1
+    np.testing.assert_array_equal(alts[0], oracle.topk(key, 16))
 
 
 def test_weights_invariants():
