@@ -7,8 +7,11 @@ Acceptance (per token):
     may pick any equally valid set; the GPU's selection is then the one the
     oracle is re-run with;
   * weights: |w_gpu - w_oracle| <= 1e-5;
-  * output: relative L2 error over the batch <= 2e-3 against the oracle with
-    intermediates in binary64 and the output rounded to bf16 once.
+  * output: relative L2 error <= 2e-3 against the oracle with intermediates in
+    binary64 and the output rounded to bf16 once, over the batch and for every
+    token on its own; and element by element within one bf16 step of the
+    value or 2^-12 of the token's rms (element_bound);
+  * near ties: at most near_tie_max(B) tokens of a batch.
 """
 from __future__ import annotations
 
@@ -20,6 +23,15 @@ from sparse_moe_decode_router_amd import binding, synth
 TAU = 1e-5            # near-tie width on binary64 keys
 REL_L2_GATE = 2e-3    # output tolerance of the layer definition
 W_TOL = 1e-5
+ORACLE_THREADS = 16   # host threads of the oracle (the host share of one GPU)
+
+
+def near_tie_max(B: int) -> int:
+    """Near-tie tokens a batch may hold.  With the K3 router the gap between
+    the 16th and 17th key is below 1e-5 for about 0.4 % of tokens; the bound
+    leaves room for small layers with denser keys while still failing when
+    the GPU's selections stop matching the oracle's."""
+    return max(1, -(-B // 16))
 
 
 def bf16_f64(bits) -> np.ndarray:
@@ -75,16 +87,50 @@ def with_k(layer, k):
     return dataclasses.replace(layer, dims=dataclasses.replace(layer.dims, top_k=k))
 
 
+def oracle_step(layer, x, forced_idx=None, want=("idx", "weight", "out"), threads=None):
+    """oracle.moe_step over the tokens of x, spread over host threads (tokens
+    are independent; the C oracle is reentrant and releases the interpreter
+    lock).  Results are concatenated in token order."""
+    from concurrent.futures import ThreadPoolExecutor
+    B = x.shape[0]
+    n = max(1, min(threads or ORACLE_THREADS, B))
+    if n == 1:
+        return oracle.moe_step(layer, x, rounding="output", forced_idx=forced_idx, want=want)
+    parts = np.array_split(np.arange(B), n)
+
+    def one(p):
+        return oracle.moe_step(layer, x[p], rounding="output",
+                               forced_idx=None if forced_idx is None else forced_idx[p],
+                               want=want)
+    with ThreadPoolExecutor(max_workers=n) as pool:
+        res = list(pool.map(one, parts))
+    return {k: np.concatenate([r[k] for r in res]) for k in res[0]}
+
+
+def element_bound(got: np.ndarray, ref: np.ndarray) -> np.ndarray:
+    """Per-element bound between a bf16 output and the oracle's (both as
+    float64 [T][H]): one bf16 step of the larger value (the GPU rounds its f32
+    sum, the oracle its binary64 one; a value near a rounding boundary may go
+    either way), or 2^-12 of the token's rms, which bounds the difference of
+    two f32 / binary64 reduction trees over K <= 8192 terms of size up to the
+    rms (K 2^-24 <= 2^-11; typically sqrt(K) 2^-24) and is the slack for
+    values that cancel to almost zero."""
+    rms = np.sqrt(np.mean(ref * ref, axis=1, keepdims=True))
+    ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(got), np.abs(ref)) + 1e-300)) - 7)
+    return np.maximum(ulp, rms * 2.0 ** -12)
+
+
 def check_step(layer, x, top_k, out, idx, w, sample=None, gate=REL_L2_GATE):
     """Full parity check of one GPU step (numpy arrays from the device).
-    `sample`: token indices the oracle evaluates end to end (None = all);
-    selection is checked for every token.  Returns a dict of measured errors."""
+    `sample`: token indices the oracle evaluates end to end (None = every
+    token); selection is checked for every token.  Returns a dict of measured
+    errors."""
     B = x.shape[0]
     near = check_selection(layer, x, idx, top_k)
+    assert near <= near_tie_max(B), f"{near} near-tie tokens in a batch of {B}"
     toks = np.arange(B) if sample is None else np.asarray(sample)
     lk = with_k(layer, top_k)
-    ref = oracle.moe_step(lk, x[toks], rounding="output", forced_idx=idx[toks],
-                          want=("idx", "weight", "out"))
+    ref = oracle_step(lk, x[toks], forced_idx=idx[toks])
     np.testing.assert_array_equal(ref["idx"], idx[toks])
     werr = float(np.max(np.abs(ref["weight"] - w[toks].astype(np.float64))))
     assert werr <= W_TOL, f"weights differ by {werr}"
@@ -92,7 +138,16 @@ def check_step(layer, x, top_k, out, idx, w, sample=None, gate=REL_L2_GATE):
     err = rel_l2(got, ref["out"])
     per_tok = [rel_l2(got[i], ref["out"][i]) for i in range(len(toks))]
     assert err <= gate, f"relative L2 error {err} > {gate} (per token max {max(per_tok)})"
-    return {"rel_l2": err, "max_token_rel_l2": max(per_tok), "w_err": werr, "near_ties": near}
+    worst = int(np.argmax(per_tok))
+    assert per_tok[worst] <= gate, f"token {toks[worst]}: relative L2 error {per_tok[worst]}"
+    bound = element_bound(got, ref["out"])
+    excess = np.abs(got - ref["out"]) / bound
+    if np.any(excess > 1):
+        t, h = np.unravel_index(int(np.argmax(excess)), excess.shape)
+        raise AssertionError(f"token {toks[t]} element {h}: GPU {got[t, h]} oracle "
+                             f"{ref['out'][t, h]} beyond the bound {bound[t, h]}")
+    return {"tokens": len(toks), "rel_l2": err, "max_token_rel_l2": max(per_tok),
+            "max_elem_over_bound": float(excess.max()), "w_err": werr, "near_ties": near}
 
 
 def run(ctx: binding.MoEDecode, x: np.ndarray, top_k: int):
