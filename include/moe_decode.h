@@ -53,8 +53,13 @@
  * Ownership.  Every pointer is borrowed.  Weights must stay alive and unchanged
  * until moe_decode_destroy.  The workspace (device memory of at least
  * moe_decode_workspace_size bytes, 256-byte aligned) belongs to the context
- * until destroy; several contexts may share one workspace when their steps
- * are ordered on one stream.  The library never allocates device memory.
+ * until destroy.  Several contexts, of the same or of different
+ * configurations, may share one workspace (at least the largest of their
+ * sizes) when their steps are ordered on one stream: the counters every step
+ * returns to zero sit at the same offsets for every configuration, and the
+ * rest of the workspace only carries values within one step.  Contexts that
+ * share a workspace also share its fault flag (moe_decode_read_flags).  The
+ * library never allocates device memory.
  *
  * Errors.  Every call returns a moe_status; nothing is thrown, printed or
  * aborted.  After MOE_ERR_HIP the HIP error code is kept in the context
@@ -129,7 +134,8 @@ size_t moe_decode_workspace_size(const moe_decode_config *cfg);
 /* Creates a context on the current HIP device.  Checks the configuration, the
  * weight pointers and the device (must be gfx950), carves the workspace and
  * clears its counters (one small kernel on the default stream, then waits for
- * it).  On success *out receives the context. */
+ * it; so no step of another context may be in flight on a shared workspace).
+ * On success *out receives the context. */
 moe_status moe_decode_init(const moe_decode_config *cfg, const moe_decode_weights *weights,
                            void *workspace, size_t workspace_bytes, moe_decode_ctx **out);
 
@@ -225,9 +231,14 @@ moe_status moe_decode_set_mode(moe_decode_ctx *ctx, int32_t mode);
 moe_status moe_decode_set_next_layer(moe_decode_ctx *ctx, const moe_decode_ctx *next);
 
 /* Reads the context's sticky fault flags into *flags (synchronous copy from
- * the workspace; call after the steps completed): bit 0 set when a fused
- * step's bounded wait on a completion counter ran out (the step then
- * finished with wrong values instead of hanging).  0 means no fault. */
+ * the workspace; call after the steps completed).  Bit 0 is set when a bounded
+ * wait of any step on this workspace ran out: a persistent step's wait on a
+ * completion counter, or, in the multi-launch forms, the wait of a routing
+ * unit (batches above 8) or a prefetch unit for the router to complete.  The
+ * step then finished instead of hanging, and its outputs are invalid.  The
+ * flag stays set for the life of the workspace.  A wait runs out
+ * only when the GPU does not run the step's workgroups concurrently (e.g.
+ * preemption), after about 50 ms.  0 means no fault. */
 moe_status moe_decode_read_flags(moe_decode_ctx *ctx, uint32_t *flags);
 
 /* Per-kernel timing.  With events set (n = 2 x the step's kernel count, see

@@ -7,6 +7,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "moe_limits.h"
+
 namespace moe {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -14,41 +16,6 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-constexpr int kWave = 64;
-constexpr int kWavesPerBlock = 4;
-constexpr int kBlock = kWave * kWavesPerBlock;
-constexpr int kKStep = 128;      // K elements one lane group covers per step (4 x 32)
-constexpr int kMaxExperts = 1024;
-constexpr int kMaxBatch = 64;
-constexpr int kMaxTopK = 64;
-constexpr int kMaxStepsPerChunk = 8;
-
-// Global counter slots (u32) at the head of the workspace.
-// Counter slots (u32 word indices into the counter area).  G_ROUTER_DONE:
-// router arrivals.  The fused step also uses: the unit queue (G_WORK),
-// workgroups that left it (G_EXIT), the routing published (G_ROUTED),
-// latent-down / shared gate/up / shared-down / down units done, and a sticky
-// error flag (a bounded wait ran out).  Counters sit 256 bytes apart: atomics
-// and polls on one line from many workgroups serialise at the memory side.
-constexpr int kCtrStride = 64;
-enum {
-    G_ROUTER_DONE = 0,
-    G_WORK = 1 * kCtrStride,
-    G_EXIT = 2 * kCtrStride,
-    G_ROUTED = 3 * kCtrStride,
-    G_LATENT = 4 * kCtrStride,
-    G_SHARED = 5 * kCtrStride,
-    G_SHDOWN = 6 * kCtrStride,
-    G_W2 = 7 * kCtrStride,
-    G_ERROR = 8 * kCtrStride,
-    G_COUNT = 9 * kCtrStride
-};
-// Routing metadata header (i32).
-enum { M_N_ACTIVE = 0, M_N_COLS = 1, M_COUNT = 16 };
-// Column-unit record (i32 words): expert, pair count (<= 8), first pair index,
-// then the token and the routing weight (f32 bits) of each pair.
-enum { R_EXPERT = 0, R_COUNT = 1, R_PAIR0 = 2, R_TOKEN = 8, R_WEIGHT = 16, kRecWords = 32 };
 
 __device__ __forceinline__ int lane_id() {
     return (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));

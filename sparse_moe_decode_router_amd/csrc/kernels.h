@@ -51,10 +51,6 @@
 
 namespace moe {
 
-constexpr int kWG = 8;              // waves per workgroup of the step kernels
-constexpr int kWGThreads = kWG * kWave;
-constexpr int kXcds = 8;            // XCDs of MI355X; workgroup i runs on XCD i % 8
-
 // ---------------------------------------------------------------------------
 // Operand loads
 // ---------------------------------------------------------------------------

@@ -374,6 +374,32 @@ def test_persistent_step_other_shapes(mode, kind):
         check_step(layer, x, 4, out, idx, w)
 
 
+def test_contexts_of_different_shapes_share_a_workspace(small_layer):
+    """Two contexts of different configurations (experts, top-k, maximum
+    batch) on one workspace, stepped alternately in the four-launch, two-launch
+    and one-launch forms: every step matches the oracle.  The counters that a
+    step returns to zero sit at the same offsets for both configurations."""
+    import torch
+    other = synth.make_layer(small_recipe(H=512, L=256, E=64, I=256, Is=256, k=4), 17)
+    da, db = binding.DeviceLayer(small_layer), binding.DeviceLayer(other)
+    size = max(binding.workspace_size(small_layer.dims, 64, 8),
+               binding.workspace_size(other.dims, 8, 4))
+    ws = torch.empty(size, dtype=torch.uint8, device="cuda")
+    a = binding.MoEDecode(da, 64, 8, workspace=ws)
+    b = binding.MoEDecode(db, 8, 4, workspace=ws)
+    steps = [(a, small_layer, 33, 8, "fused"), (b, other, 8, 4, "four_launches"),
+             (a, small_layer, 64, 6, "two_launches"), (b, other, 3, 4, "fused"),
+             (a, small_layer, 9, 8, "four_launches"), (b, other, 1, 2, "two_launches"),
+             (a, small_layer, 17, 6, "fused"), (b, other, 8, 4, "fused"),
+             (a, small_layer, 64, 8, "four_launches")]
+    for i, (ctx, layer, B, k, mode) in enumerate(steps):
+        log(f"  shared workspace step {i}: B={B} k={k} {mode}")
+        ctx.set_mode(mode_const(mode))
+        x = synth.make_tokens(layer.dims, 300 + i, B)
+        out, idx, w = run(ctx, x, k)
+        check_step(layer, x, k, out, idx, w)
+
+
 # ---------------------------------------------------------------------------
 # K3-scale layer (configuration of the benchmark)
 # ---------------------------------------------------------------------------
