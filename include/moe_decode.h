@@ -168,6 +168,30 @@ moe_status moe_decode_graph_create(moe_decode_ctx *const *ctxs, int32_t n_layers
 moe_status moe_decode_graph_launch(moe_decode_graph *graph, moe_stream_t stream);
 moe_status moe_decode_graph_destroy(moe_decode_graph *graph);
 
+/* ---- A step that allocates nothing ------------------------------------ */
+
+/* For callers that cannot allocate device memory: code under HIP graph
+ * capture, serving loops and harnesses that forbid allocation.  The
+ * four-launch step of moe_decode_step (same arguments, same results) for the
+ * configuration *cfg and the weights *w, without a context and without a
+ * caller workspace: the workspace is a static device array of
+ * MOE_DECODE_STATIC_WORKSPACE_BYTES that the library holds on each device it
+ * runs on until the process ends.  The call clears the array's counters with
+ * a small kernel on `stream`, then enqueues the step there; it calls no
+ * allocation routine and performs no host synchronisation (the first call on
+ * a device also reads the device's properties and the array's address).
+ * Returns MOE_ERR_WORKSPACE when the configuration needs a larger workspace
+ * than the array (moe_decode_workspace_size: the K3-scale layer fits at
+ * max_batch up to 64), and otherwise the errors of moe_decode_init and
+ * moe_decode_step.  Every call on one device uses the same array, which keeps
+ * the last call's contents: calls whose work may overlap on one device (other
+ * streams, other threads) race and give wrong results; order them on one
+ * stream. */
+#define MOE_DECODE_STATIC_WORKSPACE_BYTES ((size_t)64 << 20)
+moe_status moe_decode_step_static(const moe_decode_config *cfg, const moe_decode_weights *weights,
+                                  const uint16_t *x, int32_t batch, int32_t top_k, uint16_t *out,
+                                  int32_t *topk_idx, float *topk_w, moe_stream_t stream);
+
 /* ---- Introspection (tests and profiling) ------------------------------- */
 
 /* Which kernel shapes the last step of a context used (the batch-dependent

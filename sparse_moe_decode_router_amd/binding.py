@@ -53,7 +53,9 @@ EXPORTED = ("moe_decode_validate_config", "moe_decode_workspace_size", "moe_deco
             "moe_decode_last_hip_error", "moe_decode_graph_create", "moe_decode_graph_launch",
             "moe_decode_graph_destroy", "moe_decode_last_dispatch", "moe_decode_debug_export",
             "moe_decode_debug_dequant", "moe_decode_set_timing_events", "moe_decode_set_mode",
-            "moe_decode_read_flags", "moe_decode_set_next_layer")
+            "moe_decode_read_flags", "moe_decode_set_next_layer", "moe_decode_step_static")
+
+STATIC_WORKSPACE_BYTES = 64 << 20  # MOE_DECODE_STATIC_WORKSPACE_BYTES
 
 
 class MoEError(RuntimeError):
@@ -107,6 +109,9 @@ def lib() -> ctypes.CDLL:
     L.moe_decode_read_flags.restype = i32
     L.moe_decode_set_next_layer.argtypes = [vp, vp]
     L.moe_decode_set_next_layer.restype = i32
+    L.moe_decode_step_static.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(Weights), vp,
+                                         i32, i32, vp, vp, vp, vp]
+    L.moe_decode_step_static.restype = i32
     _lib = L
     return L
 
@@ -337,6 +342,27 @@ class Graph:
             self.close()
         except Exception:
             pass
+
+
+def step_static(dev_layer: DeviceLayer, max_batch: int, max_top_k: int, x, top_k: int,
+                out=None, idx=None, w=None, stream=None):
+    """moe_decode_step_static: one step of the layer with the library's static
+    workspace (no context, no allocation by the library).  x: int16 [B][H]
+    device tensor.  Returns (out, idx, w)."""
+    import torch
+    cfg = make_config(dev_layer.dims, max_batch, max_top_k)
+    weights = dev_layer.weights_struct()
+    B = x.shape[0]
+    if out is None:
+        out = torch.empty((B, dev_layer.dims.hidden), dtype=torch.int16, device=x.device)
+    if idx is None:
+        idx = torch.empty((B, top_k), dtype=torch.int32, device=x.device)
+    if w is None:
+        w = torch.empty((B, top_k), dtype=torch.float32, device=x.device)
+    _check(lib().moe_decode_step_static(ctypes.byref(cfg), ctypes.byref(weights), x.data_ptr(),
+                                        B, top_k, out.data_ptr(), idx.data_ptr(), w.data_ptr(),
+                                        _stream_ptr(stream)), "moe_decode_step_static")
+    return out, idx, w
 
 
 def dequant(q, s, stream=None):

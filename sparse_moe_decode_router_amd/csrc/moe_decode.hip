@@ -7,6 +7,7 @@
 #include <algorithm>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -634,3 +635,78 @@ moe_status moe_decode_debug_dequant(const uint8_t *q, const uint8_t *s, int64_t 
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// The step without a caller workspace
+// ---------------------------------------------------------------------------
+
+namespace {
+
+// The workspace of moe_decode_step_static: one static array per device, held
+// by the loaded code object until the process ends.  In host code `scratch`
+// names a host-side stand-in, not device memory: its device address is taken
+// once per device with hipGetSymbolAddress and used from then on.
+static __device__ __align__(256) unsigned char scratch[MOE_DECODE_STATIC_WORKSPACE_BYTES];
+
+constexpr int kMaxDevices = 64;
+
+struct StaticDevice {
+    std::once_flag once;
+    hipError_t err = hipSuccess;
+    bool gfx950 = false;
+    int n_cus = 1;
+    char *ptr = nullptr;  // device address of `scratch` on this device
+};
+StaticDevice g_static[kMaxDevices];
+
+}  // namespace
+
+extern "C" moe_status moe_decode_step_static(const moe_decode_config *cfg,
+                                             const moe_decode_weights *w, const uint16_t *x,
+                                             int32_t batch, int32_t top_k, uint16_t *out,
+                                             int32_t *topk_idx, float *topk_w,
+                                             moe_stream_t stream) {
+    moe_status st = plan::validate_config(cfg);
+    if (st != MOE_OK) return st;
+    if (!w) return MOE_ERR_INVALID_ARG;
+    const void *req[] = {w->router_w, w->lat_down, w->lat_up, w->w13_q, w->w13_s,
+                         w->w2_q,     w->w2_s,     w->sh_w13, w->sh_w2};
+    for (const void *p : req)
+        if (!p || !aligned16(p)) return MOE_ERR_INVALID_ARG;
+    if (w->router_bias && !aligned16(w->router_bias)) return MOE_ERR_INVALID_ARG;
+    const Layout lay = make_layout(*cfg);
+    if (lay.total > (size_t)MOE_DECODE_STATIC_WORKSPACE_BYTES) return MOE_ERR_WORKSPACE;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+    StaticDevice &sd = g_static[dev];
+    std::call_once(sd.once, [&sd, dev]() {
+        hipDeviceProp_t prop;
+        sd.err = hipGetDeviceProperties(&prop, dev);
+        if (sd.err != hipSuccess) return;
+        sd.gfx950 = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+        sd.n_cus = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 1;
+        if (sd.gfx950) sd.err = hipGetSymbolAddress((void **)&sd.ptr, HIP_SYMBOL(scratch));
+    });
+    if (sd.err != hipSuccess) return MOE_ERR_HIP;
+    if (!sd.gfx950) return MOE_ERR_UNSUPPORTED;
+    if (!sd.ptr) return MOE_ERR_HIP;
+    // A context on the stack over the static array, in the four-launch form.
+    moe_decode_ctx ctx{};
+    ctx.cfg = *cfg;
+    ctx.w = *w;
+    ctx.ws = sd.ptr;
+    ctx.ws_bytes = MOE_DECODE_STATIC_WORKSPACE_BYTES;
+    ctx.lay = lay;
+    ctx.device = dev;
+    ctx.mode = MOE_MODE_FOUR_LAUNCHES;
+    ctx.n_cus = sd.n_cus;
+    ctx.occ_blocks = 1;
+    // The array keeps what the last call left: the counters start at zero
+    // (a fill kernel, not a memset, so that the call stays capturable).
+    const size_t nwords = lay.counters_end / 4;
+    hipLaunchKernelGGL(k_fill_u32, dim3((unsigned)std::min<size_t>(1024, (nwords + 255) / 256)),
+                       dim3(256), 0, (hipStream_t)stream, (uint32_t *)sd.ptr, nwords, 0u);
+    if (hipGetLastError() != hipSuccess) return MOE_ERR_HIP;
+    return moe_decode_step(&ctx, x, batch, top_k, out, topk_idx, topk_w, stream);
+}
