@@ -3,32 +3,33 @@
 
 One step = one pass of the whole layer (router + top-k, latent-down, MXFP4
 experts, combine, shared expert, latent-up) over one batch of synthetic
-tokens.  Steps are replayed from HIP graphs of 8 consecutive steps (8
-different inputs), as a decode engine captures many layers per graph, so a
-graph launch is paid once per 8 steps.  Inputs rotate through R pre-generated
-batches (different routing each step) that are resident in HBM before the
-timed region starts.
+tokens.  The timed region is K launches of one-step HIP graphs (one graph per
+input; the per-layer graph of a decode engine), back to back between two
+synchronisations.  Inputs rotate through R pre-generated batches (different
+routing each step) that are resident in HBM before the timed region starts.
 
 Prints ONE JSON line:
   value        whole-step algorithmic HBM bytes / time (GB/s)
-  ms_per_step  time per layer step (graph replays, K steps between two
-               synchronisations); p10/p50/p90 from events between replays;
-               ms_per_step_one_step_graphs (a graph launch per step) and
-               ms_per_step_eager (no graph) for comparison
+  ms_per_step  time per layer step over the K timed launches; p10/p50/p90
+               from events between further launches; the same steps from
+               graphs of 8 consecutive steps and as eager launches beside
   roofline     the kernel with the largest time of the library's default
                mode, its algorithmic bytes per launch over its average
                duration (HIP events attached to each kernel's dispatch on
                eager steps), against 8 TB/s
   expert_path  k_w13 + k_w2 of the four-launch step: the routed-expert
-               kernels alone
-  modes        the same inputs in every execution mode (four launches, dense-in
-               + one persistent launch, one persistent launch)
+               kernels alone, bytes of the distinct experts the GPU selected
+  modes        the same inputs in every execution mode
   cpu_baseline the binary64 CPU oracle on a bounded sample of the same inputs
   batch_sweep  the same K3 weights at batch 2, 8 (Zipf routing), 64
                (near-uniform routing), 64 (the batch-1 bias) and two
-               speculative-decoding verify batches (1 user x 8 tokens, 8
-               users x 4 tokens; tokens of a user correlated, rho 0.8)
-With --workload c4_x8: eight TP8-share layers in one graph, batch 1..64.
+               speculative-decoding verify batches, each with the oracle on
+               all host cores beside it
+  c0_tiny_b1   the 64-expert layer at batch 1 (cache-resident: latency only)
+  c4_x8        eight TP8-share layers in one graph at batch 1, 8 and 64: time
+               per launch and per layer, one layer's kernels, expert path and
+               roofline, the oracle on one layer at batch 1 and 64
+With --workload c4_x8: the eight-layer graph at batch 1..64 in every mode.
 """
 import argparse
 import dataclasses
@@ -68,6 +69,8 @@ def modes():
     and the default one)."""
     from sparse_moe_decode_router_amd import binding
     allm = {"four_launches": binding.MODE_FOUR_LAUNCHES,
+            "late_routing": binding.MODE_LATE_ROUTING,
+            "dense_routing": binding.MODE_DENSE_ROUTING,
             "side_stream": binding.MODE_SIDE_STREAM,
             "two_launches": binding.MODE_TWO_LAUNCHES, "fused": binding.MODE_FUSED}
     if MODE_FILTER is None:
@@ -225,6 +228,66 @@ def pct(v, q):
     return float(np.percentile(np.asarray(v), q))
 
 
+def kernel_durations(ctx, names, kb, xd, k, out, idx, wts, steps, stream, out_staged):
+    """Per-kernel durations: HIP events attached to each kernel's dispatch
+    (start and stop of the kernel itself) on `steps` eager steps on `stream`,
+    one event set per rotating input, read back before it is reused; each
+    kernel's algorithmic bytes (kb[r][name]) over its average duration."""
+    import torch
+    R = len(xd)
+    kev = []
+    for r in range(R):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2 * len(names))]
+        for x in e:
+            x.record(stream)
+        kev.append(e)
+    torch.cuda.synchronize()
+    sums = {n: 0.0 for n in names}
+    kbytes = {n: 0.0 for n in names}
+    pending = [False] * R
+
+    def collect(r):
+        e = kev[r]
+        e[-1].synchronize()
+        for j, n in enumerate(names):
+            sums[n] += e[2 * j].elapsed_time(e[2 * j + 1])
+            kbytes[n] += kb[r][n]
+
+    for i in range(steps):
+        r = i % R
+        if pending[r]:
+            collect(r)
+        ctx.set_timing_events(kev[r])
+        ctx.step(xd[r], k, out, idx, wts, stream=stream)
+        pending[r] = True
+    ctx.set_timing_events(None)
+    torch.cuda.synchronize()
+    for r in range(R):
+        if pending[r]:
+            collect(r)
+    per_kernel = {}
+    for n in names:
+        avg_ms = sums[n] / steps
+        avg_bytes = kbytes[n] / steps
+        gbs = avg_bytes / (avg_ms * 1e-3) / 1e9
+        sym = "k_out_st" if n == "out" and out_staged else KERNEL_SYMBOLS[n]
+        per_kernel[n] = {"symbol": sym, "us": round(avg_ms * 1e3, 2),
+                         "bytes": int(avg_bytes), "gbs": round(gbs, 1),
+                         "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    return per_kernel
+
+
+def expert_path(per_kernel):
+    """k_w13 + k_w2 of the four-launch step: bytes of the distinct active
+    experts (and their activations) over the two kernels' durations."""
+    ex_us = per_kernel["w13"]["us"] + per_kernel["w2"]["us"]
+    ex_bytes = per_kernel["w13"]["bytes"] + per_kernel["w2"]["bytes"]
+    ex_gbs = ex_bytes / (ex_us * 1e-6) / 1e9
+    return {"us": round(ex_us, 2), "gbs": round(ex_gbs, 1),
+            "pct_hbm_peak": round(100 * ex_gbs / HBM_PEAK_GBS, 2),
+            "from": "k_w13 + k_w2 of the four-launch step"}
+
+
 def measure(dev, d, B, k, xs, steps, warmup, mode):
     """One configuration in one execution mode: graph replays (wall clock over
     `steps` replays, then per-replay events for percentiles) and eager steps
@@ -273,35 +336,9 @@ def measure(dev, d, B, k, xs, steps, warmup, mode):
     assert ctx.read_flags() == 0
 
     stream = torch.cuda.Stream()
-    # Graphs of G consecutive steps (G different inputs), as a decode engine
-    # captures many layers per graph: one graph launch per G steps.
-    G = GRAPH_STEPS if R % GRAPH_STEPS == 0 else 1
-    NG = R // G
-    graphs = [binding.Graph([ctx] * G, xd[G * q:G * q + G], B, k, [out] * G, [idx] * G,
-                            [wts] * G) for q in range(NG)]
-    reps = max(1, steps // G)
-    # Timed region: back-to-back replays between two synchronisations.
-    for i in range(max(1, warmup // G)):
-        graphs[i % NG].launch(stream)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(reps):
-        graphs[i % NG].launch(stream)
-    torch.cuda.synchronize()
-    ms = (time.perf_counter() - t0) * 1e3 / (reps * G)
-    mean_bytes = sum(step_bytes[(G * (i % NG) + j) % R] for i in range(reps)
-                     for j in range(G)) / (reps * G)
-    # Per-replay spread (per step): an event between consecutive replays.
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
-    evs[0].record(stream)
-    for i in range(reps):
-        graphs[i % NG].launch(stream)
-        evs[i + 1].record(stream)
-    torch.cuda.synchronize()
-    per = [evs[i].elapsed_time(evs[i + 1]) * 1e3 / G for i in range(reps)]
-    for g in graphs:
-        g.close()
-    # One step per graph, for comparison (a graph launch per step).
+    # The timed region: one graph per input, a graph launch per step (the
+    # per-layer graph of a decode engine); `steps` launches back to back
+    # between two synchronisations.
     graphs = [binding.Graph([ctx], [xd[r]], B, k, [out], [idx], [wts]) for r in range(R)]
     for i in range(warmup):
         graphs[i % R].launch(stream)
@@ -310,7 +347,35 @@ def measure(dev, d, B, k, xs, steps, warmup, mode):
     for i in range(steps):
         graphs[i % R].launch(stream)
     torch.cuda.synchronize()
-    ms_graph1 = (time.perf_counter() - t0) * 1e3 / steps
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    mean_bytes = sum(step_bytes[i % R] for i in range(steps)) / steps
+    # Per-launch spread, outside the timed region: an event between
+    # consecutive launches, over at least 64 launches.
+    n_ev = max(steps, 64)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev + 1)]
+    evs[0].record(stream)
+    for i in range(n_ev):
+        graphs[i % R].launch(stream)
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per = [evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(n_ev)]
+    # Graphs of G consecutive steps (G different inputs) for comparison: a
+    # graph launch per G steps, as when many layers share one graph.
+    G = GRAPH_STEPS if R % GRAPH_STEPS == 0 else 1
+    NG = R // G
+    graphs_g = [binding.Graph([ctx] * G, xd[G * q:G * q + G], B, k, [out] * G, [idx] * G,
+                              [wts] * G) for q in range(NG)]
+    reps = max(1, steps // G)
+    for i in range(max(1, warmup // G)):
+        graphs_g[i % NG].launch(stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(reps):
+        graphs_g[i % NG].launch(stream)
+    torch.cuda.synchronize()
+    ms_graph_g = (time.perf_counter() - t0) * 1e3 / (reps * G)
+    for g in graphs_g:
+        g.close()
     # Cold against warm: events around single one-step replays, each cold one
     # after a 1 GiB read on the same stream, which evicts the last-level cache
     # (256 MB on MI355X), so that no weight row comes from an earlier step;
@@ -345,63 +410,16 @@ def measure(dev, d, B, k, xs, steps, warmup, mode):
     torch.cuda.synchronize()
     ms_eager = (time.perf_counter() - t0) * 1e3 / steps
 
-    # Per-kernel durations: events attached to each kernel's dispatch (start
-    # and stop of the kernel itself) on eager steps; one event set per
-    # rotating input, read back before it is reused.
-    kev = []
-    for r in range(R):
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(2 * len(names))]
-        for x in e:
-            x.record(stream)
-        kev.append(e)
-    torch.cuda.synchronize()
-    sums = {n: 0.0 for n in names}
-    kbytes = {n: 0.0 for n in names}
-    pending = [False] * R
-
-    def collect(r):
-        e = kev[r]
-        e[-1].synchronize()
-        for j, n in enumerate(names):
-            sums[n] += e[2 * j].elapsed_time(e[2 * j + 1])
-            kbytes[n] += kb[r][n]
-
-    for i in range(steps):
-        r = i % R
-        if pending[r]:
-            collect(r)
-        ctx.set_timing_events(kev[r])
-        ctx.step(xd[r], k, out, idx, wts, stream=stream)
-        pending[r] = True
-    ctx.set_timing_events(None)
-    torch.cuda.synchronize()
-    for r in range(R):
-        if pending[r]:
-            collect(r)
-    per_kernel = {}
-    for n in names:
-        avg_ms = sums[n] / steps
-        avg_bytes = kbytes[n] / steps
-        gbs = avg_bytes / (avg_ms * 1e-3) / 1e9
-        sym = "k_out_st" if n == "out" and disp.get("out_staged") else KERNEL_SYMBOLS[n]
-        per_kernel[n] = {"symbol": sym, "us": round(avg_ms * 1e3, 2),
-                         "bytes": int(avg_bytes), "gbs": round(gbs, 1),
-                         "frac": round(gbs / HBM_PEAK_GBS, 4)}
-    expert = None
-    if not fused:
-        ex_us = per_kernel["w13"]["us"] + per_kernel["w2"]["us"]
-        ex_bytes = per_kernel["w13"]["bytes"] + per_kernel["w2"]["bytes"]
-        ex_gbs = ex_bytes / (ex_us * 1e-6) / 1e9
-        expert = {"us": round(ex_us, 2), "gbs": round(ex_gbs, 1),
-                  "pct_hbm_peak": round(100 * ex_gbs / HBM_PEAK_GBS, 2),
-                  "from": "k_w13 + k_w2 of the four-launch step"}
+    per_kernel = kernel_durations(ctx, names, kb, xd, k, out, idx, wts, steps, stream,
+                                  disp.get("out_staged"))
+    expert = None if fused else expert_path(per_kernel)
     assert ctx.read_flags() == 0, "a bounded wait of the fused step ran out"
     for g in graphs:
         g.close()
     ctx.close()
     return {
         "ms": ms, "value": mean_bytes / (ms * 1e-3) / 1e9, "ms_eager": ms_eager,
-        "ms_graph1": ms_graph1,
+        "ms_graph_g": ms_graph_g, "n_launches_timed": steps, "n_launches_percentiles": n_ev,
         "us_p10": pct(per, 10), "us_p50": pct(per, 50), "us_p90": pct(per, 90),
         "cold": {"us_warm": round(cw["warm"], 2), "us_cold": round(cw["cold"], 2),
                  "ratio": round(cw["cold"] / cw["warm"], 3),
@@ -523,6 +541,143 @@ def run_c4(args):
     print(json.dumps(line), flush=True)
 
 
+def c4_summary(args, batches=(1, 8, 64), oracle_batches=(1, 64)):
+    """Eight TP8-share layers (own seeds and inputs) captured in one HIP graph,
+    at each batch of `batches`: the time per graph launch (all eight layers,
+    `args.steps` launches between two synchronisations), per layer, tokens/s
+    and GB/s; the per-kernel durations of one layer's eager steps (events
+    attached to each dispatch), its expert path and its kernel with the largest
+    time against 8 TB/s; the oracle on one layer at `oracle_batches`."""
+    import numpy as np
+    import torch
+
+    from sparse_moe_decode_router_amd import binding, synth
+
+    recipe = synth.K3_TP8
+    d = recipe.dims
+    n_layers, k, R = 8, 16, 4
+    t0 = time.time()
+    layers = [synth.make_layer(recipe, synth.TP8_STACK_SEED0 + l) for l in range(n_layers)]
+    devs = [binding.DeviceLayer(la) for la in layers]
+    log(f"[bench] C4 layers generated and copied in {time.time() - t0:.1f} s")
+    stream = torch.cuda.Stream()
+    res = []
+    for B in batches:
+        ctxs = [binding.MoEDecode(dv, B, k) for dv in devs]
+        xs = [[synth.make_tokens(d, synth.TP8_STACK_SEED0 + l, B, draw=r)
+               for l in range(n_layers)] for r in range(R)]
+        xd = [[torch.from_numpy(x.view(np.int16)).cuda() for x in row] for row in xs]
+        outs = [torch.empty((B, d.hidden), dtype=torch.int16, device="cuda")
+                for _ in range(n_layers)]
+        idxs = [torch.empty((B, k), dtype=torch.int32, device="cuda") for _ in range(n_layers)]
+        wts = [torch.empty((B, k), dtype=torch.float32, device="cuda") for _ in range(n_layers)]
+        graphs = [binding.Graph(ctxs, xd[r], B, k, outs, idxs, wts) for r in range(R)]
+        Ds = []
+        for r in range(R):
+            graphs[r].launch(stream)
+            torch.cuda.synchronize()
+            Ds.append([int(np.unique(i.cpu().numpy()).size) for i in idxs])
+        step_bytes = [sum(sum(kernel_bytes(d, B, k, D).values()) for D in ds) for ds in Ds]
+        for i in range(args.warmup):
+            graphs[i % R].launch(stream)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for i in range(args.steps):
+            graphs[i % R].launch(stream)
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t1) * 1e3 / args.steps
+        mean_bytes = sum(step_bytes[i % R] for i in range(args.steps)) / args.steps
+        assert all(c.read_flags() == 0 for c in ctxs)
+        for g in graphs:
+            g.close()
+        # The same graphs in the other multi-launch forms, for comparison.
+        by_mode = {default_mode(): round(ms * 1e3 / n_layers, 2)}
+        for name in ("four_launches", "late_routing", "dense_routing"):
+            if name == default_mode() or name not in modes():
+                continue
+            for c in ctxs:
+                c.set_mode(modes()[name])
+            gm = [binding.Graph(ctxs, xd[r], B, k, outs, idxs, wts) for r in range(R)]
+            for i in range(args.warmup):
+                gm[i % R].launch(stream)
+            torch.cuda.synchronize()
+            t1 = time.perf_counter()
+            for i in range(args.steps):
+                gm[i % R].launch(stream)
+            torch.cuda.synchronize()
+            by_mode[name] = round((time.perf_counter() - t1) * 1e6 / args.steps / n_layers, 2)
+            for g in gm:
+                g.close()
+            for c in ctxs:
+                c.set_mode(binding.DEFAULT_MODE)
+        # One layer's kernels, eager, events on each dispatch.
+        kb = [kernel_bytes(d, B, k, Ds[r][0]) for r in range(R)]
+        per_kernel = kernel_durations(ctxs[0], KERNELS_BF16, kb, [xd[r][0] for r in range(R)],
+                                      k, outs[0], idxs[0], wts[0], max(args.steps, 20), stream,
+                                      ctxs[0].last_dispatch().get("out_staged"))
+        dom = max(KERNELS_BF16, key=lambda n: per_kernel[n]["us"])
+        pk = per_kernel[dom]
+        entry = {"batch": B, "us_per_8_layers": round(ms * 1e3, 2),
+                 "us_per_layer": round(ms * 1e3 / n_layers, 2),
+                 "tokens_per_s": round(B / (ms * 1e-3), 1),
+                 "gbs": round(mean_bytes / (ms * 1e-3) / 1e9, 1),
+                 "pct_hbm_peak": round(100 * mean_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+                 "distinct_experts_mean": round(float(np.mean(Ds)), 1),
+                 "us_per_layer_by_mode": by_mode,
+                 "layer_kernels": per_kernel, "expert_path": expert_path(per_kernel),
+                 "roofline": {"bound": "hbm", "kernel": pk["symbol"], "achieved": pk["gbs"],
+                              "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": pk["frac"],
+                              "traffic": load_traffic(pk["symbol"], f"c4_b{B}")},
+                 "timed": f"{args.steps} launches of the eight-layer graph"}
+        if B in oracle_batches and not args.no_cpu_baseline:
+            log(f"[bench] timing the CPU oracle on one C4 layer at batch {B}")
+            entry["cpu_oracle_one_layer"] = cpu_oracle_sampled(
+                layers[0], [xs[r][0] for r in range(R)], float(np.mean([b["dense_in"] + b["w13"]
+                                                                        + b["w2"] + b["out"]
+                                                                        for b in kb])),
+                args.sweep_cpu_seconds)
+        log(f"[bench] C4 B={B}: {entry['us_per_layer']} us per layer, "
+            f"{entry['pct_hbm_peak']} % of peak")
+        res.append(entry)
+        for c in ctxs:
+            c.close()
+        del xd, outs, idxs, wts
+    del devs
+    torch.cuda.empty_cache()
+    return {"workload": "eight TP8-share layers (hidden 7168, latent 2048, 896 MXFP4 experts of "
+                        "inter 256, top-16, shared 512) in one HIP graph",
+            "batches": res}
+
+
+def c0_summary(args):
+    """The 64-expert layer at batch 1 (its weights fit the last-level cache):
+    time per step of one-step graph launches, and the oracle's."""
+    import numpy as np
+
+    from sparse_moe_decode_router_amd import binding, synth
+
+    layer = synth.make_layer(synth.TINY, 0)
+    d = layer.dims
+    dev = binding.DeviceLayer(layer)
+    xs = [synth.make_tokens(d, 0, 1, draw=r) for r in range(8)]
+    m = measure(dev, d, 1, d.top_k, xs, max(args.steps, 20), args.warmup, binding.DEFAULT_MODE)
+    res = {"workload": "64-expert layer, batch 1 (hidden 512, latent 256, top-4, f32 router)",
+           "us_per_step": round(m["ms"] * 1e3, 2), "us_p50": round(m["us_p50"], 2),
+           "us_p10": round(m["us_p10"], 2), "us_p90": round(m["us_p90"], 2),
+           "kernels": {n: v["us"] for n, v in m["per_kernel"].items()},
+           "note": "working set cache-resident: latency only, no % of HBM peak"}
+    if not args.no_cpu_baseline:
+        import oracle
+        oracle.lib()
+        t0, n = time.perf_counter(), 0
+        while time.perf_counter() - t0 < 2.0:
+            oracle.moe_step(layer, xs[n % len(xs)], rounding="output")
+            n += 1
+        res["cpu_oracle_us_per_step"] = round((time.perf_counter() - t0) / n * 1e6, 1)
+        res["cpu_oracle_cores"] = 1
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -535,6 +690,9 @@ def main():
                     help="oracle time per batch-sweep configuration (all host cores)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true", help="skip the batch sweep of the K3 layer")
+    ap.add_argument("--no-c0", action="store_true", help="skip the 64-expert layer's latency")
+    ap.add_argument("--no-c4", action="store_true",
+                    help="skip the eight-layer TP8-share graph at batch 1, 8 and 64")
     ap.add_argument("--modes", default=None,
                     help="comma-separated execution modes to run (default: all; the "
                          "library's default mode is always run)")
@@ -604,6 +762,15 @@ def main():
                     dataclasses.replace(layer, bias=bias), xs_s,
                     float(np.mean(alt_s[default_mode()]["step_bytes"])), args.sweep_cpu_seconds)
 
+    c0 = c4 = None
+    if not args.no_c0:
+        log("[bench] 64-expert layer at batch 1")
+        c0 = c0_summary(args)
+    if not args.no_c4 and recipe_name == "k3" and B == 1:
+        del dev
+        log("[bench] eight TP8-share layers in one graph")
+        c4 = c4_summary(args)
+
     cpu = cpu_all = None
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
@@ -634,9 +801,11 @@ def main():
         "cold": m["cold"],
         "device": device_info(),
         "kernels": per_kernel,
+        "timed": f"{m['n_launches_timed']} launches of one-step graphs (a graph per input, "
+                 f"{args.rotate} inputs rotating) between two synchronisations; percentiles "
+                 f"from events between {m['n_launches_percentiles']} further launches",
         "ms_per_step_eager": round(m["ms_eager"], 5),
-        "ms_per_step_one_step_graphs": round(m["ms_graph1"], 5),
-        "graph_steps": GRAPH_STEPS,
+        f"ms_per_step_{GRAPH_STEPS}_step_graphs": round(m["ms_graph_g"], 5),
         "modes": {n: {"us_per_step": round(x["ms"] * 1e3, 2), "gbs": round(x["value"], 1),
                       "kernels": x["per_kernel"]} for n, x in alt.items()},
         "roofline": {"bound": "hbm", "kernel": pk["symbol"], "achieved": pk["gbs"],
@@ -645,6 +814,8 @@ def main():
         "cpu_baseline": cpu,
         "cpu_baseline_all_cores": cpu_all,
         "batch_sweep": sweep,
+        "c0_tiny_b1": c0,
+        "c4_x8": c4,
         "dispatch": m["dispatch"],
     }
     print(json.dumps(line), flush=True)

@@ -212,12 +212,20 @@ typedef struct {
     int32_t out_staged;    /* four launches: 1 when the output launch staged its whole
                               column operand in LDS (at most two tokens), 2 when it
                               staged the latent part (at most eight tokens), else 0 */
+    int32_t routing;       /* where the routing ran: 0 in the dense-in launch (the
+                              workgroup that completed the router), 1 in routing units
+                              of the dense-in launch (above 8 tokens), 2 at the start
+                              of the gate/up launch, 3 in the f32 router kernel */
 } moe_decode_dispatch_info;
 moe_status moe_decode_last_dispatch(const moe_decode_ctx *ctx, moe_decode_dispatch_info *info);
 
 /* Execution mode of a context's later steps.
  *   MOE_MODE_FOUR_LAUNCHES (the default): dense-in, expert gate/up, expert
- *     down, output;
+ *     down, output.  The routing (top-k and unit records) runs at the end of
+ *     the dense-in launch, or, for up to 8 tokens and 128 token-expert pairs
+ *     when the dense-in launch fits in one round of resident workgroups, at
+ *     the start of the gate/up launch (see MOE_MODE_LATE_ROUTING): in one
+ *     round, a routing at the end would leave the memory idle;
  *   MOE_MODE_TWO_LAUNCHES: the dense-in launch, then one persistent launch
  *     whose workgroups take the expert gate/up, shared-down, expert down and
  *     latent-up units from a queue in dependency order and wait on completion
@@ -231,7 +239,16 @@ moe_status moe_decode_last_dispatch(const moe_decode_ctx *ctx, moe_decode_dispat
  *     step stays capturable (fork and join are event record/wait pairs);
  *   MOE_MODE_FUSED: the whole step as one persistent launch of that kind
  *     (router, latent and shared units too), the single-launch design of
- *     [P-NV] "一个工程师、1.2万行代码、AI辅助开发".
+ *     [P-NV] "一个工程师、1.2万行代码、AI辅助开发";
+ *   MOE_MODE_LATE_ROUTING: the four launches, with the routing of up to 8
+ *     tokens (and at most 128 token-expert pairs) always at the start of the
+ *     gate/up launch instead of at the end of the dense-in launch: the
+ *     dense-in launch then only streams weights, and every gate/up workgroup
+ *     selects the experts itself from the scores and keys in memory, once,
+ *     then runs its units (other batches, and steps with a next-layer
+ *     prefetch, route in the dense-in launch);
+ *   MOE_MODE_DENSE_ROUTING: the four launches with the routing always in the
+ *     dense-in launch.
  * Shapes without a built persistent kernel (the f32 router, other expert
  * chunk shapes) run the four launches.  All modes compute the same values.
  * Returns MOE_ERR_INVALID_ARG for another mode.  Host-only. */
@@ -239,7 +256,9 @@ enum {
     MOE_MODE_FUSED = 0,
     MOE_MODE_FOUR_LAUNCHES = 1,
     MOE_MODE_TWO_LAUNCHES = 2,
-    MOE_MODE_SIDE_STREAM = 3
+    MOE_MODE_SIDE_STREAM = 3,
+    MOE_MODE_LATE_ROUTING = 4,
+    MOE_MODE_DENSE_ROUTING = 5
 };
 moe_status moe_decode_set_mode(moe_decode_ctx *ctx, int32_t mode);
 

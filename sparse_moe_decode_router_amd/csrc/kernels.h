@@ -356,7 +356,9 @@ enum { KIND_ROUTER = 0, KIND_LATENT = 1, KIND_SHARED = 2 };
 // that completes the router sets *s_last (LDS) for its workgroup.  Ends with
 // a workgroup barrier.  Coh: the z and shared-activation rows are read by
 // other units of the same launch (the fused step).
-template <bool Coh>
+// Route = false: the routing runs in a later launch; router tiles store their
+// scores and keys with plain stores and do not arrive on the counter.
+template <bool Coh, bool Route = true>
 __device__ __forceinline__ void dense_in_tile(const StepArgs &a, const Role &ro, int kind, int t,
                                               bool active, int cg, float *s_red, int *s_last) {
     const int lane = lane_id(), n = lane & 15, g = lane >> 4;
@@ -383,11 +385,18 @@ __device__ __forceinline__ void dense_in_tile(const StepArgs &a, const Role &ro,
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const float sv = sigmoidf_(acc[i]);
-                    store_agent(a.score + (size_t)b * kMaxExperts + e + i, sv);
-                    store_agent(a.key + (size_t)b * kMaxExperts + e + i, sv + bv[i]);
+                    float *ps = a.score + (size_t)b * kMaxExperts + e + i;
+                    float *pk = a.key + (size_t)b * kMaxExperts + e + i;
+                    if (Route) {
+                        store_agent(ps, sv);
+                        store_agent(pk, sv + bv[i]);
+                    } else {
+                        *ps = sv;
+                        *pk = sv + bv[i];
+                    }
                 }
             }
-            if (wave_publish(&a.gctr[G_ROUTER_DONE]) == (uint32_t)a.router_target - 1u &&
+            if (Route && wave_publish(&a.gctr[G_ROUTER_DONE]) == (uint32_t)a.router_target - 1u &&
                 lane == 0)
                 *s_last = 1;
         } else if (kind == KIND_LATENT) {
@@ -425,7 +434,7 @@ __device__ __forceinline__ const uint16_t *dense_in_row(const StepArgs &a, int k
 // wave that holds them: router scores and keys (then an arrival on the router
 // counter, *s_last set by the arrival that completes it), z or the shared
 // activation as hi/lo rows.
-template <bool Coh, int NCG>
+template <bool Coh, int NCG, bool Route = true>
 __device__ __forceinline__ void dense_in_epilogue(const StepArgs &a, int kind, int tt, int cg0,
                                                   const f32x4 (&acc)[NCG], int *s_last) {
     const int lane = lane_id(), n = lane & 15, g = lane >> 4;
@@ -441,12 +450,20 @@ __device__ __forceinline__ void dense_in_epilogue(const StepArgs &a, int kind, i
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const float sv = sigmoidf_(acc[c][i]);
-                    store_agent(a.score + (size_t)b * kMaxExperts + e + i, sv);
-                    store_agent(a.key + (size_t)b * kMaxExperts + e + i, sv + bv[i]);
+                    float *ps = a.score + (size_t)b * kMaxExperts + e + i;
+                    float *pk = a.key + (size_t)b * kMaxExperts + e + i;
+                    if (Route) {
+                        store_agent(ps, sv);
+                        store_agent(pk, sv + bv[i]);
+                    } else {
+                        *ps = sv;
+                        *pk = sv + bv[i];
+                    }
                 }
             }
         }
-        if (wave_publish(&a.gctr[G_ROUTER_DONE]) == (uint32_t)a.router_target - 1u && lane == 0)
+        if (Route && wave_publish(&a.gctr[G_ROUTER_DONE]) == (uint32_t)a.router_target - 1u &&
+            lane == 0)
             *s_last = 1;
     } else if (kind == KIND_LATENT) {
 #pragma unroll
@@ -477,7 +494,7 @@ __device__ __forceinline__ void dense_in_epilogue(const StepArgs &a, int kind, i
 
 // dense_in_tile for the NCG >= 2 column groups cg0 .. cg0 + NCG - 1 (s_red:
 // NCG reduction slices): every weight step is loaded once for all of them.
-template <bool Coh, int NCG>
+template <bool Coh, int NCG, bool Route = true>
 __device__ __forceinline__ void dense_in_tile_n(const StepArgs &a, const Role &ro, int kind, int t,
                                                 bool active, int cg0, float *s_red, int *s_last) {
     const int n = lane_id() & 15, g = lane_id() >> 4;
@@ -496,7 +513,7 @@ __device__ __forceinline__ void dense_in_tile_n(const StepArgs &a, const Role &r
     if (active)
         dense_chunk_xn<NCG>(A + 8 * g, X, valid, ro.kw * a.spc_in, (ro.kw + 1) * a.spc_in, acc);
     const bool leader = reduce_kn<NCG>(s_red, ro.wave, ro.kw, ro.KW, acc);
-    if (leader && active) dense_in_epilogue<Coh, NCG>(a, kind, tt, cg0, acc, s_last);
+    if (leader && active) dense_in_epilogue<Coh, NCG, Route>(a, kind, tt, cg0, acc, s_last);
     __syncthreads();
 }
 
@@ -679,18 +696,37 @@ __device__ __forceinline__ int read_record(const StepArgs &a, int c, int &e, int
 // by a wave (a barrier comes first).  CohIn: the record and z rows come from
 // units of the same launch; CohOut: the activation rows go to units of the
 // same launch (agent-scope stores).
+template <int S, bool CohIn, bool CohOut, int KS = 1>
+__device__ __forceinline__ void w13_unit_rec(const StepArgs &a, int recw, int tg, uint16_t *s_b,
+                                             bool &reuse);
+
 template <int S, bool CohIn, bool CohOut>
 __device__ __forceinline__ void w13_unit(const StepArgs &a, int c, int tg, uint16_t *s_b,
                                          bool &reuse) {
+    int e, nt, p0;
+    const int recw = read_record<CohIn>(a, c, e, nt, p0);
+    w13_unit_rec<S, CohIn, CohOut>(a, recw, tg, s_b, reuse);
+}
+
+// Gate/up unit with its record already read: lane l < 32 holds word l of the
+// record (lanes 32..63 a copy).  KS: waves per tile (8 / KS tiles per unit),
+// each taking S / KS steps of every chunk; their partial sums meet in LDS and
+// are added in wave order before the SwiGLU.
+template <int S, bool CohIn, bool CohOut, int KS>
+__device__ __forceinline__ void w13_unit_rec(const StepArgs &a, int recw, int tg, uint16_t *s_b,
+                                             bool &reuse) {
+    static_assert(S % KS == 0 && (KS == 1 || S >= 2), "steps per wave; LDS of the reduction");
+    constexpr int SW = S / KS;
     const int lane = lane_id(), n = lane & 15, g = lane >> 4, wave = wave_index();
     const int j = n >> 1, part = n & 1;
     const int OT = a.I >> 3;
     const int nchunk = a.L / (kKStep * S);
     const size_t qrow = a.L / 2, srow = a.L / 32;
-    const int t = tg * kWG + wave;
+    const int t = tg * (kWG / KS) + wave / KS, kh = wave % KS;
     const bool active = t < OT;
-    int e, nt, p0;
-    const int recw = read_record<CohIn>(a, c, e, nt, p0);
+    const int e = (int)readlane((uint32_t)recw, R_EXPERT);
+    const int nt = (int)readlane((uint32_t)recw, R_COUNT);
+    const int p0 = (int)readlane((uint32_t)recw, R_PAIR0);
     const int n_eff = j < nt ? n : part;
     const size_t r = (size_t)e * 2 * a.I + (n < 8 ? 0 : a.I) + 8 * (active ? t : 0) + (n & 7);
     const uint8_t *qp = a.w13_q + r * qrow + 16 * g;
@@ -704,24 +740,41 @@ __device__ __forceinline__ void w13_unit(const StepArgs &a, int c, int tg, uint1
         // for them alone.
         if (reuse) __syncthreads();  // every wave is done with s_b
         reuse = true;
-        Fp4Chunk<S> w;
-        if constexpr (S % 4 != 0) load_fp4_scales<S>(sp + (size_t)ch * S * 4, w);
+        Fp4Chunk<SW> w;
+        const size_t s0 = (size_t)ch * S + kh * SW;  // the wave's first step
+        if constexpr (SW % 4 != 0) load_fp4_scales<SW>(sp + s0 * 4, w);
         fence_schedule();
         stage_operand<S, CohIn>(s_b, a.zhl, a.L, ch * S * kKStep, nt,
                          [&](int jj) { return __shfl(recw, R_TOKEN + jj); });
         fence_schedule();
-        if constexpr (S % 4 == 0) load_fp4_scales<S>(sp + (size_t)ch * S * 4, w);
-        load_fp4_codes<S>(qp + (size_t)ch * S * 64, w);
+        if constexpr (SW % 4 == 0) load_fp4_scales<SW>(sp + s0 * 4, w);
+        load_fp4_codes<SW>(qp + s0 * 64, w);
         fence_schedule();
-        wait_staging<S>();
+        wait_staging<SW>();
         staged_barrier();
-        mfma_fp4_chunk<S>(w, s_b, n_eff, g, 0, acc);
+        mfma_fp4_chunk<SW, S>(w, s_b, n_eff, g, kh * SW, acc);
     }
     acc = add_pair_column(acc);
+    if constexpr (KS > 1) {
+        // The tile's KS partial sums, through LDS (the staged operand is no
+        // longer read once every wave has passed the barrier).
+        float *red = (float *)s_b;
+        __syncthreads();
+        stf4(red + (size_t)(wave * kWave + lane) * 4, acc);
+        __syncthreads();
+        if (kh == 0) {
+#pragma unroll
+            for (int q = 1; q < KS; ++q) {
+                const f32x4 o = ldf4(red + (size_t)((wave + q) * kWave + lane) * 4);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[i] += o[i];
+            }
+        }
+    }
     f32x4 up;
 #pragma unroll
     for (int i = 0; i < 4; ++i) up[i] = __shfl_xor(acc[i], 32);
-    if (active && j < nt && part == 0 && g < 2) {
+    if (kh == 0 && active && j < nt && part == 0 && g < 2) {
         f32x4 v;
 #pragma unroll
         for (int i = 0; i < 4; ++i) v[i] = silu_mul(acc[i], up[i]);
@@ -977,7 +1030,7 @@ __device__ __forceinline__ void routing_units(const StepArgs &a, int units, Rout
         wg_wait(a, &a.gctr[G_ROUTER_DONE], (uint32_t)a.router_target);
         const RouteArgs ra = route_args(a);
         const int b = kWG * r + wave_index();
-        if (b < a.B) topk_token(ra, b, s_route);
+        if (b < a.B) topk_token<true>(ra, b, s_route);
         wait_vm_all();
         __syncthreads();
         if (threadIdx.x == 0)
@@ -991,7 +1044,7 @@ __device__ __forceinline__ void routing_units(const StepArgs &a, int units, Rout
                 s_route.w[p] = load_agent(a.wsel + p);
             }
             __syncthreads();
-            build_meta(ra, s_route, kWG);
+            build_meta<false>(ra, s_route, kWG);
             if (threadIdx.x == 0) store_agent(&a.gctr[G_ROUTED], 0u);  // ready for the next step
         }
     }
@@ -1029,10 +1082,20 @@ __device__ __forceinline__ void prefetch_units(const StepArgs &a, int first) {
 // Kernel 1: dense-in units over tiles [dense_lo, dense_hi) of the list
 // [router | latent | shared]; each unit covers all NCG = ceil(B / 16) column
 // groups, so every weight tile is read once per step.
-template <int NCG>
+// The routing image of a dense-in launch that routes (none otherwise).
+template <bool Route>
+struct RouteShared {
+    RouteLds s;
+};
+template <>
+struct RouteShared<false> {};
+
+// Route = false: the routing runs at the start of the gate/up launch (at most
+// 8 tokens), so this launch holds no routing code and only streams weights.
+template <int NCG, bool Route>
 __global__ void __launch_bounds__(kWGThreads) __attribute__((amdgpu_waves_per_eu(4)))
 k_dense_in(const StepArgs a) {
-    __shared__ RouteLds s_route;
+    __shared__ RouteShared<Route> s_rs;
     __shared__ float s_red[NCG * kWG * kWave * 4];
     __shared__ int s_last;
     const Role ro = role_of(a.kw_in);
@@ -1053,17 +1116,21 @@ k_dense_in(const StepArgs a) {
         const int kind = t < n_rt ? KIND_ROUTER : t < n_rt + n_lt ? KIND_LATENT : KIND_SHARED;
         const int tl = kind == KIND_ROUTER ? t : kind == KIND_LATENT ? t - n_rt : t - n_rt - n_lt;
         if constexpr (NCG == 1)
-            dense_in_tile<false>(a, ro, kind, tl, active, cg, s_red, &s_last);
+            dense_in_tile<false, Route>(a, ro, kind, tl, active, cg, s_red, &s_last);
         else
-            dense_in_tile_n<false, NCG>(a, ro, kind, tl, active, 0, s_red, &s_last);
-        if (s_last && !a.route_units) {  // this workgroup completed the router: route the step
-            route_step(route_args(a), &s_route, kWG);
-            __syncthreads();
-            if (threadIdx.x == 0) s_last = 0;
+            dense_in_tile_n<false, NCG, Route>(a, ro, kind, tl, active, 0, s_red, &s_last);
+        if constexpr (Route) {
+            if (s_last && !a.route_units) {  // this workgroup completed the router: route the step
+                route_step(route_args(a), &s_rs.s, kWG);
+                __syncthreads();
+                if (threadIdx.x == 0) s_last = 0;
+            }
         }
     }
-    routing_units(a, units, s_route, &s_last);
-    prefetch_units(a, units + a.route_units);
+    if constexpr (Route) {
+        routing_units(a, units, s_rs.s, &s_last);
+        prefetch_units(a, units + a.route_units);
+    }
 }
 
 // Sum over the nsl slices of tile t's partials part[k][t][c][lane] (T tiles
@@ -1209,15 +1276,66 @@ k_dense_in_kx(const StepArgs a) {
     prefetch_units(a, units + a.route_units);
 }
 
-// Kernel 2: gate/up units.
-template <int S>
+// Kernel 2: gate/up units.  Late: the step's routing runs here first (at
+// most kLatePairs pairs; the dense-in launch only stored scores and keys):
+// every workgroup selects every token's experts and builds the unit records
+// in LDS once, keeps the records of its own units (units blockIdx.x,
+// blockIdx.x + gridDim.x, ..., at most kLateUnitsPerWG of them) in a small LDS
+// array outside the staging buffer, and runs them.  The routing goes to global
+// memory for the later launches: each column unit's record from the workgroup
+// that runs its first tile group, everything else from workgroup 0.
+constexpr int kLateUnitsPerWG = 16;
+template <int S, bool Late, int KS = 1>
 __global__ void __launch_bounds__(kWGThreads) __attribute__((amdgpu_waves_per_eu(4)))
 k_w13(const StepArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t s_b[8 * Stage<S>::kChunks];
-    const int NC = min(load_agent(a.meta + M_N_COLS), a.ncols_cap);  // never beyond the records
-    const int TG = ((a.I >> 3) + kWG - 1) / kWG;
+    constexpr int kStage = 8 * Stage<S>::kChunks * 2;
+    constexpr int kBytes = Late && (int)sizeof(LateRouteLds) > kStage ? (int)sizeof(LateRouteLds)
+                                                                       : kStage;
+    __shared__ __attribute__((aligned(16))) char s_mem[kBytes];
+    __shared__ int s_rec[Late ? kLateUnitsPerWG : 1][kRecWords];
+    uint16_t *s_b = (uint16_t *)s_mem;
+    constexpr int TW = kWG / KS;  // tiles per unit
+    const int TG = ((a.I >> 3) + TW - 1) / TW;
     bool reuse = false;
-    for (int u = blockIdx.x; u < NC * TG; u += gridDim.x) w13_unit<S, false, false>(a, u / TG, u % TG, s_b, reuse);
+    if constexpr (Late) {
+        LateRouteLds &lds = *(LateRouteLds *)s_mem;
+        const RouteArgs ra = route_args(a);
+        route_late(ra, lds, blockIdx.x == 0);
+        const int units = lds.ncols * TG;
+        const int mine = units > (int)blockIdx.x
+                             ? min(kLateUnitsPerWG, (units - (int)blockIdx.x + (int)gridDim.x - 1) /
+                                                        (int)gridDim.x)
+                             : 0;
+        // Wave r copies (and, for a column unit's first tile group, publishes)
+        // the record of the workgroup's unit r.
+        const int lane = lane_id();
+        for (int r = wave_index(); r < mine; r += kWG) {
+            const int u = (int)blockIdx.x + r * (int)gridDim.x;
+            const int c = u / TG;
+            if (lane < kRecWords) {
+                const int v = lds.rec[c][lane];
+                s_rec[r][lane] = v;
+                if (u % TG == 0) a.cu_rec[(size_t)c * kRecWords + lane] = v;
+            }
+        }
+        if (blockIdx.x == 0 && threadIdx.x == 0) {
+            a.meta[M_N_COLS] = lds.ncols;
+            a.meta[M_N_ACTIVE] = lds.n_active;
+        }
+        __syncthreads();  // the records are copied before the staging overwrites the image
+        for (int r = 0; r < mine; ++r) {
+            const int u = (int)blockIdx.x + r * (int)gridDim.x;
+            const int recw = s_rec[r][lane & 31];
+            w13_unit_rec<S, false, false, KS>(a, recw, u % TG, s_b, reuse);
+        }
+    } else {
+        const int NC = min(load_agent(a.meta + M_N_COLS), a.ncols_cap);  // never beyond the records
+        for (int u = blockIdx.x; u < NC * TG; u += gridDim.x) {
+            int e, nt, p0;
+            const int recw = read_record<false>(a, u / TG, e, nt, p0);
+            w13_unit_rec<S, false, false, KS>(a, recw, u % TG, s_b, reuse);
+        }
+    }
 }
 
 // Kernel 3: down units (KS waves per tile).

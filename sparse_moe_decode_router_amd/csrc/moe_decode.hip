@@ -56,7 +56,32 @@ StepKernel fused_kernel(const moe_decode_config &c, const Plan &p) {
 #define MOE_SPC_TABLE(K)                                                                      \
     {nullptr, K<1>, K<2>,  K<3>,  K<4>,  K<5>,  K<6>,  K<7>, K<8>,                                \
      K<9>,    K<10>, K<11>, K<12>, K<13>, K<14>, K<15>, K<16>}
-const StepKernel kW13[] = MOE_SPC_TABLE(k_w13);
+#define MOE_W13_TABLE(L)                                                                       \
+    {nullptr,        k_w13<1, L>,  k_w13<2, L>,  k_w13<3, L>,  k_w13<4, L>,  k_w13<5, L>,        \
+     k_w13<6, L>,    k_w13<7, L>,  k_w13<8, L>,  k_w13<9, L>,  k_w13<10, L>, k_w13<11, L>,       \
+     k_w13<12, L>,   k_w13<13, L>, k_w13<14, L>, k_w13<15, L>, k_w13<16, L>}
+const StepKernel kW13[] = MOE_W13_TABLE(false);
+// Gate/up kernels that run the routing first (batches up to 8).
+const StepKernel kW13Late[] = MOE_W13_TABLE(true);
+// Gate/up kernels with KS waves per tile (chunk shapes 2, 4, 8 and 16).
+struct W13Split {
+    int s, ks;
+    StepKernel k, k_late;
+};
+const W13Split kW13Split[] = {
+    {2, 2, k_w13<2, false, 2>, k_w13<2, true, 2>},    {4, 2, k_w13<4, false, 2>, k_w13<4, true, 2>},
+    {4, 4, k_w13<4, false, 4>, k_w13<4, true, 4>},    {8, 2, k_w13<8, false, 2>, k_w13<8, true, 2>},
+    {8, 4, k_w13<8, false, 4>, k_w13<8, true, 4>},    {8, 8, k_w13<8, false, 8>, k_w13<8, true, 8>},
+    {16, 2, k_w13<16, false, 2>, k_w13<16, true, 2>}, {16, 4, k_w13<16, false, 4>, k_w13<16, true, 4>},
+    {16, 8, k_w13<16, false, 8>, k_w13<16, true, 8>}};
+
+StepKernel w13_kernel(int s, int ks, bool late) {
+    if (ks == 1) return late ? kW13Late[s] : kW13[s];
+    for (const W13Split &w : kW13Split)
+        if (w.s == s && w.ks == ks) return late ? w.k_late : w.k;
+    return nullptr;
+}
+#undef MOE_W13_TABLE
 #undef MOE_SPC_TABLE
 #define MOE_W2_TABLE(KS)                                                                       \
     {nullptr,        k_w2<1, KS>,  k_w2<2, KS>,  k_w2<3, KS>,  k_w2<4, KS>,  k_w2<5, KS>,        \
@@ -272,6 +297,41 @@ moe_status moe_decode_step(moe_decode_ctx *ctx, const uint16_t *x, int32_t batch
     if (!fused) pl = make_plan(c, batch, top_k, false);
     const StepKernel tail = ctx->mode == MOE_MODE_TWO_LAUNCHES ? tail_kernel(c, pl) : nullptr;
     const bool side = ctx->mode == MOE_MODE_SIDE_STREAM && pl.sd.kw > 0 && pl.lu.kw > 0;
+    // The routing at the start of the gate/up launch instead of at the end of
+    // the dense-in launch (up to 8 tokens and kLatePairs pairs; not with a
+    // next-layer prefetch, whose units wait for the router in dense-in).
+    // Gate/up kernel of the multi-launch forms: when its units would fill less
+    // than the two resident workgroups per compute unit, KS waves share each
+    // tile (KS in {2, 4, 8}, the smallest that fills them, where a kernel of
+    // that shape exists).
+    int ks13 = 1;
+    if (!fused && !tail) {
+        const long long cols = ncols_cap(c.n_experts, batch, top_k);
+        for (int ks = 2; ks <= kWG && cols * pl.tg13 * ks13 < 2LL * ctx->n_cus; ks *= 2) {
+            if (!w13_kernel(pl.s13, ks, false)) break;
+            ks13 = ks;
+        }
+        pl.units_13 = cols * cdiv(c.expert_inter / 8, kWG / ks13);
+    }
+    const long long cap = 65528;  // workgroups (a multiple of the XCD count); more units loop
+    // The late gate/up launch is persistent: one workgroup per resident slot
+    // (two per compute unit), each routing once and running up to
+    // kLateUnitsPerWG units.
+    const long long late_grid = std::min<long long>(pl.units_13, 2LL * ctx->n_cus);
+    // Where the routing runs.  MOE_MODE_LATE_ROUTING: at the start of the
+    // gate/up launch wherever that form applies; MOE_MODE_DENSE_ROUTING:
+    // always in the dense-in launch; the default (MOE_MODE_FOUR_LAUNCHES and
+    // the side-stream form): late when the dense-in launch runs in one round
+    // of resident workgroups, where the routing at its end would be a tail
+    // with the memory idle (a launch of more rounds hides it under its last
+    // round, and the gate/up workgroups would only pay for it again).
+    const bool late_ok = c.router_dtype == MOE_ROUTER_BF16 && batch <= kWG &&
+                         batch * top_k <= kLatePairs && !ctx->next &&
+                         pl.units_13 <= (long long)kLateUnitsPerWG * late_grid;
+    const bool dense_one_round = pl.units_in <= 2LL * ctx->n_cus;
+    const bool late = late_ok && (ctx->mode == MOE_MODE_LATE_ROUTING ||
+                                  ((ctx->mode == MOE_MODE_FOUR_LAUNCHES ||
+                                    ctx->mode == MOE_MODE_SIDE_STREAM) && dense_one_round));
     StepArgs a = base_args(ctx);
     a.B = batch;
     a.k = top_k;
@@ -308,7 +368,6 @@ moe_status moe_decode_step(moe_decode_ctx *ctx, const uint16_t *x, int32_t batch
         a.pf_bytes1 = (uint64_t)nc.latent * nc.hidden * 2;
         a.pf_units = (int32_t)((a.pf_bytes0 + a.pf_bytes1 + kPfUnit - 1) / kPfUnit);
     }
-    const long long cap = 65528;  // workgroups (a multiple of the XCD count); more units loop
 
     moe_decode_dispatch_info &d = ctx->last;
     d.batch = batch;
@@ -316,7 +375,7 @@ moe_status moe_decode_step(moe_decode_ctx *ctx, const uint16_t *x, int32_t batch
     d.col_tiles = pl.ncg_in;
     d.split_in = pl.in.kw;
     d.split_out = pl.out.kw;
-    d.split_w13 = 1;
+    d.split_w13 = ks13;
     // Four-launch down kernel: when its units would fill less than the two
     // resident workgroups per compute unit, two waves share each tile (twice
     // the units, half the steps per wave).
@@ -325,11 +384,12 @@ moe_status moe_decode_step(moe_decode_ctx *ctx, const uint16_t *x, int32_t batch
                              cdiv(c.latent / 16, kWG / 2);
     d.split_w2 = split2 ? 2 : 1;
     d.grid_in = (int32_t)(pl.units_in + a.route_units);  // every unit its own workgroup
-    d.grid_w13 = grid_for(pl.units_13, cap);
+    d.grid_w13 = late ? (int32_t)late_grid : grid_for(pl.units_13, cap);
     d.grid_w2 = grid_for(pl.units_2, cap);
     d.grid_out = grid_for(pl.units_out, cap);
     d.router_f32 = c.router_dtype == MOE_ROUTER_F32;
     d.fused = fused ? 1 : tail ? 2 : side ? 3 : 0;
+    d.routing = d.router_f32 ? 3 : late ? 2 : a.route_units ? 1 : 0;
     d.n_kernels = fused ? 1 : tail ? 2 : side ? 6 + d.router_f32 : 4 + d.router_f32;
     d.grid_step = 0;
     d.out_staged = 0;
@@ -401,7 +461,8 @@ moe_status moe_decode_step(moe_decode_ctx *ctx, const uint16_t *x, int32_t batch
         const hipError_t e = hipGetLastError();
         return e == hipSuccess ? MOE_OK : hip_fail(ctx, e);
     }
-    const StepKernel dense_in[] = {k_dense_in<1>, k_dense_in<2>, k_dense_in<3>, k_dense_in<4>};
+    const StepKernel dense_in[] = {late ? k_dense_in<1, false> : k_dense_in<1, true>,
+                                   k_dense_in<2, true>, k_dense_in<3, true>, k_dense_in<4, true>};
     const StepKernel dense_in_kx[] = {nullptr, k_dense_in_kx<2>, k_dense_in_kx<3>,
                                       k_dense_in_kx<4>};
     // Above 16 tokens the dense-in launch stages x in LDS per row group of 8
@@ -445,7 +506,7 @@ moe_status moe_decode_step(moe_decode_ctx *ctx, const uint16_t *x, int32_t batch
         if (d.router_f32) launch(k_router_f32, cdiv(c.n_experts, kWavesPerBlock), kBlock);
         dense_launch(s, a);
         dense_launch(ctx->side, sa);
-        launch(kW13[pl.s13], d.grid_w13, kWGThreads);
+        launch(w13_kernel(pl.s13, ks13, late), d.grid_w13, kWGThreads);
         launch(split2 ? kW2Split[pl.s2] : kW2[pl.s2], d.grid_w2, kWGThreads);
         launch_on(ctx->side, k_out_part<OUT_SHARED>,
                   grid_for(dense_units_host(n_ot, kWG / pl.sd.kw, pl.ncg_out), cap), kWGThreads,
@@ -465,7 +526,7 @@ moe_status moe_decode_step(moe_decode_ctx *ctx, const uint16_t *x, int32_t batch
         const hipError_t e = hipGetLastError();
         return e == hipSuccess ? MOE_OK : hip_fail(ctx, e);
     }
-    launch(kW13[pl.s13], d.grid_w13, kWGThreads);
+    launch(w13_kernel(pl.s13, ks13, late), d.grid_w13, kWGThreads);
     launch(split2 ? kW2Split[pl.s2] : kW2[pl.s2], d.grid_w2, kWGThreads);
     if (pl.ncg_out >= 2) {
         // Above 8 tokens: the column operands staged in LDS per group of 8
@@ -598,7 +659,8 @@ moe_status moe_decode_set_next_layer(moe_decode_ctx *ctx, const moe_decode_ctx *
 
 moe_status moe_decode_set_mode(moe_decode_ctx *ctx, int32_t mode) {
     if (!ctx || (mode != MOE_MODE_FUSED && mode != MOE_MODE_FOUR_LAUNCHES &&
-                 mode != MOE_MODE_TWO_LAUNCHES && mode != MOE_MODE_SIDE_STREAM))
+                 mode != MOE_MODE_TWO_LAUNCHES && mode != MOE_MODE_SIDE_STREAM &&
+                 mode != MOE_MODE_LATE_ROUTING && mode != MOE_MODE_DENSE_ROUTING))
         return MOE_ERR_INVALID_ARG;
     ctx->mode = mode;
     return MOE_OK;

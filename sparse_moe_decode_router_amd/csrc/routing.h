@@ -109,16 +109,33 @@ __device__ __forceinline__ RouteArgs route_args(const StepArgs &a) {
     return r;
 }
 
-// LDS of the routing workgroup: the selections of every token, the token
-// masks of the experts, per-expert offsets and per-wave scan totals.
-struct RouteLds {
-    int16_t idx[kMaxBatch * kMaxTopK];
-    float w[kMaxBatch * kMaxTopK];
+// LDS of the routing: the selections of every token (MaxPairs = B k at
+// most), the token masks of the experts, per-expert offsets and per-wave scan
+// totals, the candidate lists of the threshold selection, and (MaxCols > 1)
+// the unit records when they are kept in LDS.
+template <int MaxPairs, int MaxCols>
+struct RouteLdsT {
+    int16_t idx[MaxPairs];
+    float w[MaxPairs];
     unsigned long long mask[kMaxExperts];
     int off[kMaxExperts];
     int unit[kMaxExperts];
     int wsum[kMaxRouteWaves][4];
+    // Per wave: the candidates of the threshold selection (key, expert,
+    // score), then the selection in key order (expert, score).
+    uint32_t cand_key[kMaxRouteWaves][kWave];
+    int cand_id[kMaxRouteWaves][kWave];
+    float cand_s[kMaxRouteWaves][kWave];
+    int rec[MaxCols][kRecWords];
+    int ncols, n_active;
 };
+// The routing of the dense-in launch (any batch up to kMaxBatch): records go
+// to global memory.
+typedef RouteLdsT<kMaxBatch * kMaxTopK, 1> RouteLds;
+// The routing at the start of the gate/up launch: at most kLatePairs (token,
+// expert) pairs, every unit record kept in LDS.
+constexpr int kLatePairs = 128;
+typedef RouteLdsT<kLatePairs, kLatePairs + kLatePairs / 8> LateRouteLds;
 
 // Best remaining experts of one lane, best first: orderable keys (0: none),
 // slots (expert = lane + 64 * slot) and scores.
@@ -161,41 +178,87 @@ __device__ __forceinline__ void fill_list(LaneList &L, const uint32_t (&ok)[kKey
     }
 }
 
-// Top-k of one token, by one wave.  Lane l owns experts l, l+64, ... and
-// keeps their keys and scores in registers and a short list of its best
-// remaining ones.  Each round takes the wave-wide largest list head (equal
-// keys: the lowest expert id); lane r keeps the id and score of round r's
-// winner, and the winning lane drops its head (and rebuilds its list after
-// kList drops).  The round does nothing else: ranks among the selected ids
-// and the sum of the selected scores (in selection order) follow the last
-// round, and the ids are written in ascending order with weights
-// s_e / sum(s).  Scores and keys are read with agent-scope loads, all in one
-// batch: they were published by other workgroups.
-__device__ __forceinline__ void topk_token(const RouteArgs &a, int b, RouteLds &lds) {
+// Number of set bits of m below the calling lane.
+__device__ __forceinline__ int lanes_below(unsigned long long m) {
+    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                          __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// Selection by threshold, one wave, without the k serial rounds:
+//  1. T = the k-th largest of the 64 lane maxima (a radix select over its 32
+//     bits, each bit one wave-wide count), so that at least k keys are >= T
+//     and every expert of the top k has a key >= T;
+//  2. the keys >= T are compacted into LDS in slot-major, lane-minor order,
+//     which is ascending expert id;
+//  3. each candidate's rank in selection order (larger key first, equal keys
+//     by lower id) is its count of candidates that come before it;
+//  4. the candidates of rank < k are written to LDS by rank, and lane r takes
+//     the rank-r expert and its score, as the round-based selection leaves
+//     them.
+// Returns false, having changed nothing the caller uses, when more than 64
+// keys are >= T (the caller then runs the rounds).
+__device__ __forceinline__ bool select_by_threshold(const uint32_t (&ok)[kKeysPerLane],
+                                                    const float (&sc)[kKeysPerLane], int k,
+                                                    uint32_t *cand_key, int *cand_id,
+                                                    float *cand_s, int &mine, float &s_mine) {
     const int lane = lane_id();
-    const int E = a.E, k = a.k;
-    const float *keyrow = a.key + (size_t)b * kMaxExperts;  // rows padded to kMaxExperts
-    const float *srow = a.score + (size_t)b * kMaxExperts;
-    const int nk = (E + kWave - 1) / kWave;
-    // All loads first, then their uses: the compiler keeps atomic loads in
-    // program order, so a use between two of them would serialise the round
-    // trips.
-    uint32_t ok[kKeysPerLane];
-    float sc[kKeysPerLane];
+    uint32_t lm = 0u;
 #pragma unroll
-    for (int i = 0; i < kKeysPerLane; ++i) ok[i] = __float_as_uint(load_agent(keyrow + lane + kWave * i));
+    for (int i = 0; i < kKeysPerLane; ++i) lm = max(lm, ok[i]);
+    uint32_t T = 0u;
 #pragma unroll
-    for (int i = 0; i < kKeysPerLane; ++i) sc[i] = load_agent(srow + lane + kWave * i);
+    for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t t = T | (1u << bit);
+        T = __popcll(__ballot(lm >= t)) >= k ? t : T;
+    }
+    int n = 0;
 #pragma unroll
     for (int i = 0; i < kKeysPerLane; ++i) {
-        const bool in = i < nk && lane + kWave * i < E;
-        ok[i] = in ? orderable(__uint_as_float(ok[i])) : 0u;
+        const bool c = ok[i] != 0u && ok[i] >= T;
+        const unsigned long long m = __ballot(c);
+        const int pos = n + lanes_below(m);
+        if (c && pos < kWave) {
+            cand_key[pos] = ok[i];
+            cand_id[pos] = lane + kWave * i;
+            cand_s[pos] = sc[i];
+        }
+        n += __popcll(m);
     }
+    if (n > kWave) return false;
+    wave_sync();
+    const bool have = lane < n;
+    const uint32_t ck = have ? cand_key[lane] : 0u;
+    const int cid = have ? cand_id[lane] : 0;
+    const float cs = have ? cand_s[lane] : 0.f;
+    int rank = 0;
+    for (int j = 0; j < n; ++j) {
+        const uint32_t kj = readlane(ck, j);
+        rank += (kj > ck || (kj == ck && j < lane)) ? 1 : 0;
+    }
+    wave_sync();
+    if (have && rank < k) {
+        cand_id[rank] = cid;
+        cand_s[rank] = cs;
+    }
+    wave_sync();
+    mine = lane < k ? cand_id[lane] : 0;
+    s_mine = lane < k ? cand_s[lane] : 0.f;
+    wave_sync();
+    return true;
+}
+
+// Selection by k rounds (any key distribution): lane l keeps a short list of
+// its best remaining experts; each round takes the wave-wide largest list
+// head (equal keys: the lowest expert id); lane r keeps the id and score of
+// round r's winner, and the winning lane drops its head (and rebuilds its list
+// after kList drops).
+__device__ __forceinline__ void select_by_rounds(const uint32_t (&ok)[kKeysPerLane],
+                                                 const float (&sc)[kKeysPerLane], int k,
+                                                 int &mine, float &s_mine) {
+    const int lane = lane_id();
     LaneList L;
     fill_list(L, ok, sc, 0xFFFFFFFFu, -1);
     int npop = 0;
-    int mine = 0;
-    float s_mine = 0.f;
     for (int r = 0; r < k; ++r) {
         const uint32_t ck = L.k[0];
         const int cid = lane + kWave * L.i[0];
@@ -230,6 +293,56 @@ __device__ __forceinline__ void topk_token(const RouteArgs &a, int b, RouteLds &
             }
         }
     }
+}
+
+// Top-k of one token, by one wave.  Lane l owns experts l, l+64, ... and
+// keeps their keys and scores in registers.  The selection (by threshold, or
+// by rounds when more than 64 keys pass the threshold) leaves lane r with the
+// id and score of the r-th expert in selection order; ranks among the
+// selected ids and the sum of the selected scores (in selection order) follow,
+// and the ids are written in ascending order with weights s_e / sum(s).
+// Scores and keys are read with agent-scope loads, all in one batch: they
+// were published by other workgroups.
+// Agent: the keys and scores come from other workgroups of the same launch
+// (agent-scope loads) and the selections go to them (agent-scope stores);
+// otherwise the keys come from an earlier launch and the selections are
+// written to global memory only when `global` (LDS always).
+template <bool Agent, typename Lds>
+__device__ __forceinline__ void topk_token(const RouteArgs &a, int b, Lds &lds, bool global = true) {
+    const int lane = lane_id();
+    const int E = a.E, k = a.k;
+    const float *keyrow = a.key + (size_t)b * kMaxExperts;  // rows padded to kMaxExperts
+    const float *srow = a.score + (size_t)b * kMaxExperts;
+    const int nk = (E + kWave - 1) / kWave;
+    // All loads first, then their uses: the compiler keeps atomic loads in
+    // program order, so a use between two of them would serialise the round
+    // trips.
+    uint32_t ok[kKeysPerLane];
+    float sc[kKeysPerLane];
+#pragma unroll
+    for (int i = 0; i < kKeysPerLane; ++i)
+        ok[i] = __float_as_uint(Agent ? load_agent(keyrow + lane + kWave * i)
+                                      : keyrow[lane + kWave * i]);
+#pragma unroll
+    for (int i = 0; i < kKeysPerLane; ++i)
+        sc[i] = Agent ? load_agent(srow + lane + kWave * i) : srow[lane + kWave * i];
+#pragma unroll
+    for (int i = 0; i < kKeysPerLane; ++i) {
+        const bool in = i < nk && lane + kWave * i < E;
+        ok[i] = in ? orderable(__uint_as_float(ok[i])) : 0u;
+    }
+    int mine = 0;
+    float s_mine = 0.f;
+    // The routing inside the dense-in launch takes the rounds: the threshold
+    // selection's registers would spill there, in a kernel whose other code
+    // needs them all.
+    bool done = false;
+    if constexpr (!Agent) {
+        const int wv = wave_index();
+        done = select_by_threshold(ok, sc, k, lds.cand_key[wv], lds.cand_id[wv], lds.cand_s[wv],
+                                   mine, s_mine);
+    }
+    if (!done) select_by_rounds(ok, sc, k, mine, s_mine);
     // Rank of each selection among the selected ids; sum of the selected
     // scores in selection order.
     int rank = 0;
@@ -244,12 +357,17 @@ __device__ __forceinline__ void topk_token(const RouteArgs &a, int b, RouteLds &
         const int o = b * k + rank;
         lds.idx[o] = (int16_t)mine;
         lds.w[o] = w;
-        // Agent-scope: with routing units, another workgroup of the launch
-        // builds the metadata from these.
-        store_agent(a.idx + o, mine);
-        store_agent(a.wsel + o, w);
-        if (a.user_idx) a.user_idx[o] = mine;
-        if (a.user_w) a.user_w[o] = w;
+        if (Agent) {
+            // With routing units, another workgroup of the launch builds the
+            // metadata from these.
+            store_agent(a.idx + o, mine);
+            store_agent(a.wsel + o, w);
+        } else if (global) {
+            a.idx[o] = mine;
+            a.wsel[o] = w;
+        }
+        if (global && a.user_idx) a.user_idx[o] = mine;
+        if (global && a.user_w) a.user_w[o] = w;
     }
 }
 
@@ -264,7 +382,10 @@ __device__ __forceinline__ void topk_token(const RouteArgs &a, int b, RouteLds &
 // parallel; expert offsets come from a two-level scan (lanes, then waves).
 // Everything is written with agent-scope stores: in the fused step the
 // expert units of other workgroups read it within the same launch.
-__device__ __forceinline__ void build_meta(const RouteArgs &a, RouteLds &lds, int nw) {
+// ToLds: the records go to lds.rec (and the unit count to lds.ncols) for the
+// workgroup's own use, and nothing is written to global memory.
+template <bool ToLds, typename Lds>
+__device__ __forceinline__ void build_meta(const RouteArgs &a, Lds &lds, int nw) {
     const int lane = lane_id(), wave = wave_index();
     const int tid = threadIdx.x, nt = nw * kWave;
     const int B = a.B, k = a.k, E = a.E, P = B * k;
@@ -306,13 +427,21 @@ __device__ __forceinline__ void build_meta(const RouteArgs &a, RouteLds &lds, in
         lds.off[e] = pi;
         lds.unit[e] = ci;
         if (!n) continue;
-        store_agent(a.act_expert + ai, e);
-        store_agent(a.act_off + ai, pi);
+        if (!ToLds) {
+            store_agent(a.act_expert + ai, e);
+            store_agent(a.act_off + ai, pi);
+        }
         for (int r = 0; r < n; r += 8, ++ci) {
-            int32_t *rec = a.cu_rec + (size_t)ci * kRecWords;
-            store_agent(rec + R_EXPERT, e);
-            store_agent(rec + R_COUNT, min(8, n - r));
-            store_agent(rec + R_PAIR0, pi + r);
+            if (ToLds) {
+                lds.rec[ci][R_EXPERT] = e;
+                lds.rec[ci][R_COUNT] = min(8, n - r);
+                lds.rec[ci][R_PAIR0] = pi + r;
+            } else {
+                int32_t *rec = a.cu_rec + (size_t)ci * kRecWords;
+                store_agent(rec + R_EXPERT, e);
+                store_agent(rec + R_COUNT, min(8, n - r));
+                store_agent(rec + R_PAIR0, pi + r);
+            }
         }
         ++ai;
         pi += n;
@@ -322,16 +451,27 @@ __device__ __forceinline__ void build_meta(const RouteArgs &a, RouteLds &lds, in
         const int e = lds.idx[p], b = p / k;
         const int r = __popcll(lds.mask[e] & ((1ull << b) - 1ull));
         const int pos = lds.off[e] + r;
-        store_agent(a.pair_slot + pos, p);
-        store_agent(a.pair_of_slot + p, pos);
-        int32_t *rec = a.cu_rec + (size_t)(lds.unit[e] + (r >> 3)) * kRecWords;
-        store_agent(rec + R_TOKEN + (r & 7), b);
-        store_agent(rec + R_WEIGHT + (r & 7), __float_as_int(lds.w[p]));
+        if (ToLds) {
+            int *rec = lds.rec[lds.unit[e] + (r >> 3)];
+            rec[R_TOKEN + (r & 7)] = b;
+            rec[R_WEIGHT + (r & 7)] = __float_as_int(lds.w[p]);
+        } else {
+            store_agent(a.pair_slot + pos, p);
+            store_agent(a.pair_of_slot + p, pos);
+            int32_t *rec = a.cu_rec + (size_t)(lds.unit[e] + (r >> 3)) * kRecWords;
+            store_agent(rec + R_TOKEN + (r & 7), b);
+            store_agent(rec + R_WEIGHT + (r & 7), __float_as_int(lds.w[p]));
+        }
     }
     if (tid == 0) {
-        store_agent(a.meta + M_N_ACTIVE, D);
-        store_agent(a.meta + M_N_COLS, NC);
-        store_agent(a.act_off + D, PT);
+        if (ToLds) {
+            lds.ncols = NC;
+            lds.n_active = D;
+        } else {
+            store_agent(a.meta + M_N_ACTIVE, D);
+            store_agent(a.meta + M_N_COLS, NC);
+            store_agent(a.act_off + D, PT);
+        }
     }
 }
 
@@ -339,9 +479,81 @@ __device__ __forceinline__ void build_meta(const RouteArgs &a, RouteLds &lds, in
 // arrival completed the router (all waves call it, after a workgroup
 // barrier).  Tokens are split across the waves; the selections meet in LDS.
 __device__ __forceinline__ void route_step(const RouteArgs &a, RouteLds *lds, int nwaves) {
-    for (int b = wave_index(); b < a.B; b += nwaves) topk_token(a, b, *lds);
+    for (int b = wave_index(); b < a.B; b += nwaves) topk_token<true>(a, b, *lds);
     __syncthreads();
-    build_meta(a, *lds, nwaves);
+    build_meta<false>(a, *lds, nwaves);
+}
+
+// The routing at the start of the gate/up launch (B k <= kLatePairs; the keys
+// and scores come from the dense-in launch before it): every workgroup
+// selects the experts of every token (a wave per token) and builds the unit
+// records in its own LDS.  The workgroup `lead` also writes the selections and
+// the per-pair lists to global memory for the later launches (the unit
+// records and the metadata header are written by the caller).  Ends with a
+// workgroup barrier.
+__device__ __forceinline__ void route_late(const RouteArgs &a, LateRouteLds &lds, bool lead) {
+    for (int b = wave_index(); b < a.B; b += kWG) topk_token<false>(a, b, lds, lead);
+    __syncthreads();
+    if (a.B == 1) {
+        // One token: every selected expert is one unit of one pair, in
+        // ascending id (the order of the selection in LDS).
+        const int tid = threadIdx.x, k = a.k;
+        for (int i = tid; i < k * kRecWords; i += kWGThreads) {
+            const int c = i / kRecWords, wd = i % kRecWords;
+            int v = 0;
+            if (wd == R_EXPERT) v = lds.idx[c];
+            else if (wd == R_COUNT) v = 1;
+            else if (wd == R_PAIR0) v = c;
+            else if (wd == R_WEIGHT) v = __float_as_int(lds.w[c]);
+            lds.rec[c][wd] = v;  // R_TOKEN: token 0
+        }
+        if (lead)
+            for (int c = tid; c <= k; c += kWGThreads) {
+                if (c < k) {
+                    a.act_expert[c] = lds.idx[c];
+                    a.pair_slot[c] = c;
+                    a.pair_of_slot[c] = c;
+                }
+                a.act_off[c] = c;
+            }
+        if (tid == 0) {
+            lds.ncols = k;
+            lds.n_active = k;
+        }
+        __syncthreads();
+        return;
+    }
+    build_meta<true>(a, lds, kWG);
+    __syncthreads();
+    if (lead) {
+        // The active experts in ascending id (those with a non-empty token
+        // mask) with the pair offsets that build_meta gave them, then the
+        // pair maps.
+        const int tid = threadIdx.x, P = a.B * a.k;
+        if (wave_index() == 0) {
+            int ai = 0;
+            for (int e0 = 0; e0 < a.E; e0 += kWave) {
+                const int e = e0 + lane_id();
+                const bool act = e < a.E && lds.mask[e] != 0ull;
+                const unsigned long long m = __ballot(act);
+                if (act) {
+                    const int i = ai + lanes_below(m);
+                    a.act_expert[i] = e;
+                    a.act_off[i] = lds.off[e];
+                }
+                ai += __popcll(m);
+            }
+            if (lane_id() == 0) a.act_off[ai] = P;
+        }
+        for (int p = tid; p < P; p += kWGThreads) {
+            const int e = lds.idx[p], b = p / a.k;
+            const int r = __popcll(lds.mask[e] & ((1ull << b) - 1ull));
+            const int pos = lds.off[e] + r;
+            a.pair_slot[pos] = p;
+            a.pair_of_slot[p] = pos;
+        }
+        __syncthreads();
+    }
 }
 
 }  // namespace moe

@@ -11,6 +11,9 @@ reading by the copy's ratio of counter to bytes, and writes
 ``profiles/traffic.json`` (per workload and kernel symbol: HBM bytes per
 launch, tied to the device sources by their digest).
 
+``busy``: per-kernel means of an SQ / GRBM counter run and the MFMA and
+VALU utilisation they imply.
+
     rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT/fetch -o run -- \\
         python3 -m sparse_moe_decode_router_amd.profile_step run --workload k3_b1
     rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT/write -o run -- \\
@@ -36,9 +39,13 @@ ROOT = os.path.dirname(HERE)
 WORKLOADS = {
     "k3_b1": ("k3", 1, 16, 0),
     "k3_zipf_b8": ("k3_zipf", 8, 16, 0),
+    "k3_flat_b64": ("k3_flat", 64, 16, 0),
     "k3_b64": ("k3", 64, 16, 0),
     "k3_tp8_b1": ("k3_tp8", 1, 16, 1000),
+    "k3_tp8_b8": ("k3_tp8", 8, 16, 1000),
+    "k3_tp8_b64": ("k3_tp8", 64, 16, 1000),
 }
+MODES = ("four_launches", "late_routing", "dense_routing", "side_stream", "two_launches", "fused")
 COPY_KERNEL = "elementwise"  # torch's kernel for the calibration copy
 
 
@@ -59,7 +66,12 @@ def run(args) -> None:
     torch.cuda.set_device(0)
     dev = binding.DeviceLayer(layer)
     ctx = binding.MoEDecode(dev, B, k)
-    ctx.set_mode(binding.MODE_FUSED if args.fused else binding.MODE_FOUR_LAUNCHES)
+    mode = "fused" if args.fused else args.mode
+    ctx.set_mode({"four_launches": binding.MODE_FOUR_LAUNCHES,
+                  "late_routing": binding.MODE_LATE_ROUTING,
+                  "dense_routing": binding.MODE_DENSE_ROUTING,
+                  "side_stream": binding.MODE_SIDE_STREAM,
+                  "two_launches": binding.MODE_TWO_LAUNCHES, "fused": binding.MODE_FUSED}[mode])
     xs = [torch.from_numpy(synth.make_tokens(layer.dims, seed, B, draw=r).view(np.int16)).cuda()
           for r in range(args.rotate)]
     out = torch.empty((B, layer.dims.hidden), dtype=torch.int16, device="cuda")
@@ -152,6 +164,46 @@ def summarize(args) -> None:
                       "kernels": {s: e["bytes_per_launch"] for s, e in entry.items()}}))
 
 
+def busy(args) -> None:
+    """Per-kernel means of the SQ / GRBM counters of one rocprofv3 --pmc run
+    (directory args.dir), with the utilisations they imply, by rocprofv3's
+    own derived-counter formulas (MfmaUtil, VALUBusy) on MI355X (8 XCDs, 256
+    compute units, 1024 SIMDs):
+      mfma_util = sum SQ_VALU_MFMA_BUSY_CYCLES / (GUI x 1024),
+      valu_busy = sum SQ_ACTIVE_INST_VALU / 256 / GUI,
+    where GUI is the busiest XCD's GRBM_GUI_ACTIVE (the CSV holds the sum over
+    the 8 XCDs, each active for the whole dispatch: GUI = sum / 8); printed as
+    one JSON line."""
+    files = glob.glob(os.path.join(args.dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {args.dir}")
+    per = defaultdict(lambda: defaultdict(lambda: defaultdict(float)))
+    for fn in files:
+        with open(fn, newline="") as f:
+            for row in csv.DictReader(f):
+                sym = symbol_of(row["Kernel_Name"])
+                if sym is None:
+                    continue
+                key = (fn, row.get("Dispatch_Id") or row.get("Correlation_Id"))
+                per[row["Kernel_Name"]][row["Counter_Name"]][key] += float(row["Counter_Value"])
+    out = {}
+    for name, counters in per.items():
+        mean = {c: sum(v.values()) / len(v) for c, v in counters.items()}
+        e = {"dispatches": max(len(v) for v in counters.values()), "mean": mean}
+        gui = mean.get("GRBM_GUI_ACTIVE")
+        if gui:
+            gui /= args.xcds
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in mean:
+                e["mfma_util"] = round(mean["SQ_VALU_MFMA_BUSY_CYCLES"] / (gui * args.cus * 4), 4)
+            if "SQ_ACTIVE_INST_VALU" in mean:
+                e["valu_busy"] = round(mean["SQ_ACTIVE_INST_VALU"] / args.cus / gui, 4)
+            if "SQ_INSTS_MFMA" in mean and "SQ_VALU_MFMA_BUSY_CYCLES" in mean:
+                e["mfma_cycles_per_inst"] = round(mean["SQ_VALU_MFMA_BUSY_CYCLES"] /
+                                                  max(1.0, mean["SQ_INSTS_MFMA"]), 2)
+        out[name] = e
+    print(json.dumps({"dir": args.dir, "kernels": out}))
+
+
 def main() -> None:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -159,7 +211,8 @@ def main() -> None:
     r.add_argument("--workload", default="k3_b1", choices=sorted(WORKLOADS))
     r.add_argument("--steps", type=int, default=16)
     r.add_argument("--rotate", type=int, default=8)
-    r.add_argument("--fused", action="store_true")
+    r.add_argument("--fused", action="store_true", help="the one-launch mode (same as --mode fused)")
+    r.add_argument("--mode", default="four_launches", choices=MODES)
     r.add_argument("--copy-mib", type=int, default=512)
     r.add_argument("--copies", type=int, default=3)
     s = sub.add_parser("summarize")
@@ -167,9 +220,15 @@ def main() -> None:
     s.add_argument("--fetch", required=True)
     s.add_argument("--write", required=True)
     s.add_argument("--copy-mib", type=int, default=512)
+    b = sub.add_parser("busy")
+    b.add_argument("--dir", required=True)
+    b.add_argument("--cus", type=int, default=256)
+    b.add_argument("--xcds", type=int, default=8)
     args = ap.parse_args()
     if args.cmd == "run":
         run(args)
+    elif args.cmd == "busy":
+        busy(args)
     else:
         summarize(args)
 

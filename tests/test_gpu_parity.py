@@ -106,11 +106,24 @@ def test_small_layer_batches(small_layer, small_ctx, B, k):
     x = synth.make_tokens(small_layer.dims, 100 + B, B)
     out, idx, w = run(small_ctx, x, k)
     assert small_ctx.last_dispatch()["out_staged"] == (1 if B <= 2 else 2 if B <= 8 else 0)
+    if B * k <= 8:  # few gate/up units: waves share each tile
+        assert small_ctx.last_dispatch()["split_w13"] >= 2
     r = check_step(small_layer, x, k, out, idx, w)
     if k == 1:
         assert np.all(w == 1.0)
     np.testing.assert_allclose(w.sum(axis=1), 1.0, atol=k * 2.0 ** -23)
     log("  ", r)
+
+
+@pytest.mark.parametrize("B", [1, 3, 8])
+def test_small_layer_dense_routing(small_layer, B):
+    """Up to 8 tokens with the routing at the end of the dense-in launch."""
+    ctx = make_ctx(small_layer, 8, 8)
+    ctx.set_mode(binding.MODE_DENSE_ROUTING)
+    x = synth.make_tokens(small_layer.dims, 120 + B, B)
+    out, idx, w = run(ctx, x, 8)
+    assert ctx.last_dispatch()["routing"] == 0
+    check_step(small_layer, x, 8, out, idx, w)
 
 
 def test_small_layer_without_bias():
@@ -149,10 +162,18 @@ def test_f32_router_layer_several_tokens():
     assert ctx.last_dispatch()["n_kernels"] == 5
 
 
-def test_zero_router_picks_lowest_ids_with_equal_weights():
+# Routing forms of up to 8 tokens: the default (this small layer's dense-in
+# launch is one round, so the gate/up launch routes, by threshold selection)
+# and the routing at the end of the dense-in launch (selection by rounds).
+ROUTING_FORMS = ["four_launches", "dense_routing"]
+
+
+@pytest.mark.parametrize("form", ROUTING_FORMS)
+def test_zero_router_picks_lowest_ids_with_equal_weights(form):
     layer = synth.make_layer(small_recipe(bias="none", k=5), 6)
     layer.router_w[:] = 0
     ctx = make_ctx(layer, 4)
+    ctx.set_mode(mode_const(form))
     x = synth.make_tokens(layer.dims, 6, 4)
     out, idx, w = run(ctx, x, 5)
     np.testing.assert_array_equal(idx, np.tile(np.arange(5), (4, 1)))
@@ -160,10 +181,11 @@ def test_zero_router_picks_lowest_ids_with_equal_weights():
     check_step(layer, x, 5, out, idx, w)
 
 
+@pytest.mark.parametrize("form", ROUTING_FORMS)
 @pytest.mark.parametrize("B", [4, 12])
 @pytest.mark.parametrize("k,want", [(5, [3, 7, 69, 130, 200]),
                                     (8, [3, 7, 69, 130, 131, 192, 200, 250])])
-def test_ties_at_the_threshold_go_to_the_lowest_ids(B, k, want):
+def test_ties_at_the_threshold_go_to_the_lowest_ids(B, k, want, form):
     """Keys equal at the k-th largest value, spread over several lane slots
     (expert e sits in slot e // 64): the selection takes the lowest ids among
     them, also when the cut falls between two ids of one slot (130 taken,
@@ -176,6 +198,7 @@ def test_ties_at_the_threshold_go_to_the_lowest_ids(B, k, want):
     layer.bias[[200, 3]] = 1.0
     layer.bias[[250, 7, 69, 130, 131, 192]] = 0.25
     ctx = make_ctx(layer, B, 8)
+    ctx.set_mode(mode_const(form))
     x = synth.make_tokens(layer.dims, 11, B)
     out, idx, w = run(ctx, x, k)
     np.testing.assert_array_equal(idx, np.tile(np.array(want), (B, 1)))
@@ -196,9 +219,11 @@ def test_hot_experts_serve_every_token():
     check_step(layer, x, 4, out, idx, w)
 
 
-def test_all_experts_selected():
+@pytest.mark.parametrize("form", ROUTING_FORMS)
+def test_all_experts_selected(form):
     layer = synth.make_layer(small_recipe(E=32, k=32), 9)
     ctx = make_ctx(layer, 3)
+    ctx.set_mode(mode_const(form))
     x = synth.make_tokens(layer.dims, 9, 3)
     out, idx, w = run(ctx, x, 32)
     np.testing.assert_array_equal(idx, np.tile(np.arange(32), (3, 1)))
@@ -338,7 +363,59 @@ PERSISTENT_MODES = [("fused", 1), ("two_launches", 2), ("side_stream", 3)]
 def mode_const(name):
     return {"fused": binding.MODE_FUSED, "two_launches": binding.MODE_TWO_LAUNCHES,
             "four_launches": binding.MODE_FOUR_LAUNCHES,
-            "side_stream": binding.MODE_SIDE_STREAM}[name]
+            "side_stream": binding.MODE_SIDE_STREAM,
+            "late_routing": binding.MODE_LATE_ROUTING,
+            "dense_routing": binding.MODE_DENSE_ROUTING}[name]
+
+
+@pytest.mark.parametrize("B,k", [(1, 1), (1, 6), (2, 8), (3, 6), (8, 8), (8, 1), (9, 6), (16, 8)])
+def test_late_routing_matches_four_launches(small_layer, B, k):
+    """The routing at the start of the gate/up launch (up to 8 tokens and 128
+    pairs; larger batches route in the dense-in launch as before) selects the
+    same experts with the same weights; outputs agree up to the order of the
+    latent combine; both against the oracle."""
+    late = make_ctx(small_layer, 64, 8)
+    late.set_mode(binding.MODE_LATE_ROUTING)
+    four = make_ctx(small_layer, 64, 8)
+    four.set_mode(binding.MODE_DENSE_ROUTING)
+    auto = make_ctx(small_layer, 64, 8)  # default: this layer's dense-in launch is one round
+    x = synth.make_tokens(small_layer.dims, 500 + B, B)
+    a = run(late, x, k)
+    b = run(four, x, k)
+    c = run(auto, x, k)
+    assert late.last_dispatch()["routing"] == (2 if B <= 8 else 1)
+    assert four.last_dispatch()["routing"] == (0 if B <= 8 else 1)
+    assert auto.last_dispatch()["routing"] == (2 if B <= 8 else 1)
+    assert_same_step(a, c)
+    assert_same_step(a, b)
+    check_step(small_layer, x, k, *a)
+
+
+def test_late_routing_repeated_steps_and_graph(small_layer):
+    """Steps of several batches in a row on one context, eager and replayed
+    from a graph: the gate/up launch's own routing leaves nothing stale."""
+    import torch
+    ctx = make_ctx(small_layer, 8, 8)
+    ctx.set_mode(binding.MODE_LATE_ROUTING)
+    for i, B in enumerate((8, 1, 5, 8, 2)):
+        x = synth.make_tokens(small_layer.dims, 600 + i, B)
+        check_step(small_layer, x, 6, *run(ctx, x, 6))
+    B, k = 4, 6
+    x = synth.make_tokens(small_layer.dims, 610, B)
+    xd = [to_dev_tokens(x)]
+    outs = [torch.empty((B, small_layer.dims.hidden), dtype=torch.int16, device="cuda")]
+    idxs = [torch.empty((B, k), dtype=torch.int32, device="cuda")]
+    ws = [torch.empty((B, k), dtype=torch.float32, device="cuda")]
+    g = binding.Graph([ctx], xd, B, k, outs, idxs, ws)
+    want = run(ctx, x, k)
+    stream = torch.cuda.Stream()
+    for _ in range(3):
+        g.launch(stream)
+        stream.synchronize()
+        got = (outs[0].cpu().numpy().view(np.uint16), idxs[0].cpu().numpy(), ws[0].cpu().numpy())
+        assert_same_step(got, want)
+        run(ctx, synth.make_tokens(small_layer.dims, 611, 7), 6)   # eager work between replays
+    g.close()
 
 
 @pytest.mark.parametrize("mode,kind", PERSISTENT_MODES)
@@ -462,6 +539,25 @@ def test_k3_persistent_step_matches_four_launches(k3_layer, k3_dev, bias_kind, B
     log(f"  K3 {mode} {bias_kind} B={B}:", r)
 
 
+@pytest.mark.parametrize("bias_kind,B", [("normal", 1), ("zipf", 8)])
+def test_k3_late_routing(k3_layer, k3_dev, bias_kind, B):
+    """The routing in the gate/up launch on the K3 layer: the four-launch
+    step's experts and weights, every token against the oracle."""
+    four, _ = k3_ctx(k3_dev, bias_kind, 8)
+    late, _ = k3_ctx(k3_dev, bias_kind, 8)
+    late.set_mode(binding.MODE_LATE_ROUTING)
+    x = synth.make_tokens(k3_dev.dims, 9, B)
+    a = run(four, x, 16)
+    b = run(late, x, 16)
+    # The K3 dense-in launch takes more than one round: by default the
+    # routing stays at its end.
+    assert four.last_dispatch()["routing"] == 0
+    assert late.last_dispatch()["routing"] == 2
+    assert_same_step(a, b)
+    r = check_step(layer_with_bias(k3_layer, bias_kind), x, 16, *b)
+    log(f"  K3 late routing {bias_kind} B={B}:", r)
+
+
 @pytest.mark.parametrize("users,drafts", [(1, 7), (8, 3)])
 def test_k3_spec_verify_batch(k3_layer, k3_dev, users, drafts):
     """Speculative-decoding verify batches (tokens of one user correlated):
@@ -482,6 +578,9 @@ def test_k3_tp8_share_layer():
         log(f"K3 TP8 share B={B}")
         x = synth.make_tokens(layer.dims, 1, B)
         out, idx, w = run(ctx, x, 16)
+        # Batch 1 leaves the gate/up kernel short of units (16 experts x 4
+        # tile groups): eight waves share each tile.
+        assert ctx.last_dispatch()["split_w13"] == (8 if B == 1 else 1)
         r = check_step(layer, x, 16, out, idx, w)
         log("  ", r)
 
@@ -584,7 +683,7 @@ def c4_graph_run(c4_layers, B, mode, replays=2):
 
 
 @pytest.mark.parametrize("mode", ["four_launches", "prefetch", "side_stream", "two_launches",
-                                  "fused"])
+                                  "fused", "late_routing", "dense_routing"])
 def test_c4_eight_layer_graph(c4_layers, mode):
     """Every execution mode: each layer's replayed result equals its eager
     step, and the replayed outputs of the first and last layers match the
