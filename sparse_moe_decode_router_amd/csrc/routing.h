@@ -113,7 +113,7 @@ __device__ __forceinline__ RouteArgs route_args(const StepArgs &a) {
 // most), the token masks of the experts, per-expert offsets and per-wave scan
 // totals, the candidate lists of the threshold selection, and (MaxCols > 1)
 // the unit records when they are kept in LDS.
-template <int MaxPairs, int MaxCols>
+template <int MaxPairs, int MaxCols, int CandRows>
 struct RouteLdsT {
     int16_t idx[MaxPairs];
     float w[MaxPairs];
@@ -123,19 +123,24 @@ struct RouteLdsT {
     int wsum[kMaxRouteWaves][4];
     // Per wave: the candidates of the threshold selection (key, expert,
     // score), then the selection in key order (expert, score).
-    uint32_t cand_key[kMaxRouteWaves][kWave];
-    int cand_id[kMaxRouteWaves][kWave];
-    float cand_s[kMaxRouteWaves][kWave];
+    uint32_t cand_key[CandRows][kWave];
+    int cand_id[CandRows][kWave];
+    float cand_s[CandRows][kWave];
     int rec[MaxCols][kRecWords];
     int ncols, n_active;
+    // Selection of one token by the whole workgroup: per-wave lane maxima,
+    // the threshold, per-wave candidate counts.
+    uint32_t wmax[kMaxRouteWaves][kWave];
+    uint32_t thr;
+    int wcnt[kMaxRouteWaves];
 };
 // The routing of the dense-in launch (any batch up to kMaxBatch): records go
 // to global memory.
-typedef RouteLdsT<kMaxBatch * kMaxTopK, 1> RouteLds;
+typedef RouteLdsT<kMaxBatch * kMaxTopK, 1, 2> RouteLds;
 // The routing at the start of the gate/up launch: at most kLatePairs (token,
 // expert) pairs, every unit record kept in LDS.
 constexpr int kLatePairs = 128;
-typedef RouteLdsT<kLatePairs, kLatePairs + kLatePairs / 8> LateRouteLds;
+typedef RouteLdsT<kLatePairs, kLatePairs + kLatePairs / 8, kMaxRouteWaves> LateRouteLds;
 
 // Best remaining experts of one lane, best first: orderable keys (0: none),
 // slots (expert = lane + 64 * slot) and scores.
@@ -371,6 +376,176 @@ __device__ __forceinline__ void topk_token(const RouteArgs &a, int b, Lds &lds, 
     }
 }
 
+// Top-k of one token by all kWG waves of a workgroup (every wave calls it;
+// workgroup barriers inside).  Wave w holds the keys and scores of the
+// experts lane + 64 (2w) and lane + 64 (2w + 1), so that the loads and the
+// scans are spread over the waves:
+//  1. every wave publishes its lanes' maxima; wave 0 takes per lane the
+//     maximum over the waves (the lane's maximum over all its experts) and
+//     finds T, the k-th largest of those 64 (a radix select over the bits
+//     below the lanes' common prefix), so that at least k keys are >= T and
+//     every expert of the top k has a key >= T;
+//  2. every wave counts its keys >= T; the candidates are compacted into LDS
+//     in (slot, lane) order, which is ascending expert id;
+//  3. wave 0 ranks the candidates in selection order (larger key first, equal
+//     keys by lower id), keeps those of rank < k, writes them in ascending id
+//     (the candidate order) with weights s / sum(s), the sum taken in
+//     selection order.
+// More than 64 candidates (ties over many experts): wave 0 loads every key of
+// the token and takes the rounds.  Agent: the keys come from other workgroups
+// of the same launch and the selections go to them; `global`: write the
+// selections to global memory (LDS always).
+template <bool Agent, typename Lds>
+__device__ void topk_token_wg(const RouteArgs &a, int b, Lds &lds, bool global = true) {
+    const int lane = lane_id(), wave = wave_index();
+    const int E = a.E, k = a.k;
+    const float *keyrow = a.key + (size_t)b * kMaxExperts;
+    const float *srow = a.score + (size_t)b * kMaxExperts;
+    uint32_t ok[2];
+    float sc[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int e = lane + kWave * (2 * wave + j);
+        const int ec = e < E ? e : 0;
+        ok[j] = __float_as_uint(Agent ? load_agent(keyrow + ec) : keyrow[ec]);
+        sc[j] = Agent ? load_agent(srow + ec) : srow[ec];
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int e = lane + kWave * (2 * wave + j);
+        ok[j] = e < E ? orderable(__uint_as_float(ok[j])) : 0u;
+    }
+    lds.wmax[wave][lane] = max(ok[0], ok[1]);
+    __syncthreads();
+    if (wave == 0) {
+        uint32_t lm = 0u;
+#pragma unroll
+        for (int w = 0; w < kWG; ++w) lm = max(lm, lds.wmax[w][lane]);
+        // Radix select of the k-th largest lane maximum, over the bits below
+        // the common prefix of the lanes' maxima (absent lanes, 0, excluded).
+        const uint32_t hi = wave_max_u32(lm);
+        const uint32_t lo = wave_min_u32(lm != 0u ? lm : hi);
+        const int top = 31 - __builtin_clz((hi ^ lo) | 1u);
+        uint32_t T = hi & ~((2u << top) - 1u);
+        for (int bit = top; bit >= 0; --bit) {
+            const uint32_t t = T | (1u << bit);
+            T = __popcll(__ballot(lm >= t)) >= k ? t : T;
+        }
+        if (lane == 0) lds.thr = T;
+    }
+    __syncthreads();
+    const uint32_t T = lds.thr;
+    const bool c0 = ok[0] != 0u && ok[0] >= T, c1 = ok[1] != 0u && ok[1] >= T;
+    const unsigned long long m0 = __ballot(c0), m1 = __ballot(c1);
+    if (lane == 0) lds.wcnt[wave] = __popcll(m0) + __popcll(m1);
+    __syncthreads();
+    int base = 0, n = 0;
+#pragma unroll
+    for (int w = 0; w < kWG; ++w) {
+        const int cw = lds.wcnt[w];
+        base += w < wave ? cw : 0;
+        n += cw;
+    }
+    if (n <= kWave) {
+        const int p0 = base + lanes_below(m0), p1 = base + __popcll(m0) + lanes_below(m1);
+        if (c0) {
+            lds.cand_key[0][p0] = ok[0];
+            lds.cand_id[0][p0] = lane + kWave * (2 * wave);
+            lds.cand_s[0][p0] = sc[0];
+        }
+        if (c1) {
+            lds.cand_key[0][p1] = ok[1];
+            lds.cand_id[0][p1] = lane + kWave * (2 * wave + 1);
+            lds.cand_s[0][p1] = sc[1];
+        }
+    }
+    if (n > kWave) {
+        // More than 64 keys >= T (ties over many experts): the keys and
+        // scores go to LDS (the token-mask area, free until the metadata)
+        // and wave 0 takes the exact k-th largest key Tk, then the experts
+        // with larger keys and the lowest-id ones equal to Tk, as the k
+        // candidates.
+        unsigned long long *kv = lds.mask;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int e = lane + kWave * (2 * wave + j);
+            if (e < E) kv[e] = (unsigned long long)ok[j] | ((unsigned long long)__float_as_uint(sc[j]) << 32);
+        }
+        __syncthreads();
+        if (wave == 0) {
+            const int nk = (E + kWave - 1) / kWave;
+            uint32_t Tk = 0u;
+            for (int bit = 31; bit >= 0; --bit) {
+                const uint32_t t = Tk | (1u << bit);
+                int cnt = 0;
+                for (int i = 0; i < nk; ++i) {
+                    const int e = lane + kWave * i;
+                    cnt += __popcll(__ballot(e < E && (uint32_t)kv[e] >= t));
+                }
+                Tk = cnt >= k ? t : Tk;
+            }
+            int gt = 0;
+            for (int i = 0; i < nk; ++i) {
+                const int e = lane + kWave * i;
+                gt += __popcll(__ballot(e < E && (uint32_t)kv[e] > Tk));
+            }
+            int eq_before = 0, sel_before = 0;
+            for (int i = 0; i < nk; ++i) {
+                const int e = lane + kWave * i;
+                const uint32_t key = e < E ? (uint32_t)kv[e] : 0u;
+                const bool eq = e < E && key == Tk;
+                const unsigned long long me = __ballot(eq);
+                const bool sel = (e < E && key > Tk) || (eq && eq_before + lanes_below(me) < k - gt);
+                const unsigned long long ms = __ballot(sel);
+                if (sel) {
+                    const int pos = sel_before + lanes_below(ms);
+                    lds.cand_key[0][pos] = key;
+                    lds.cand_id[0][pos] = e;
+                    lds.cand_s[0][pos] = __uint_as_float((uint32_t)(kv[e] >> 32));
+                }
+                eq_before += __popcll(me);
+                sel_before += __popcll(ms);
+            }
+        }
+        n = k;
+    }
+    __syncthreads();
+    if (wave != 0) return;
+    // Wave 0: lanes < n hold the candidates in ascending id; their ranks in
+    // selection order pick the k.
+    const bool have = lane < n;
+    const uint32_t ck = have ? lds.cand_key[0][lane] : 0u;
+    const int mine = have ? lds.cand_id[0][lane] : 0;
+    const float s_mine = have ? lds.cand_s[0][lane] : 0.f;
+    int rank = 0;
+    for (int j = 0; j < n; ++j) {
+        const uint32_t kj = readlane(ck, j);
+        rank += (kj > ck || (kj == ck && j < lane)) ? 1 : 0;
+    }
+    const bool selected = have && rank < k;
+    const int sel_pos = lanes_below(__ballot(selected));  // ascending id among the selected
+    wave_sync();
+    if (selected) lds.cand_s[1][rank] = s_mine;  // scores in selection order
+    wave_sync();
+    float total = 0.f;
+    for (int r = 0; r < k; ++r) total += lds.cand_s[1][r];
+    if (selected) {
+        const float w = s_mine / total;
+        const int o = b * k + sel_pos;
+        lds.idx[o] = (int16_t)mine;
+        lds.w[o] = w;
+        if (Agent) {
+            store_agent(a.idx + o, mine);
+            store_agent(a.wsel + o, w);
+        } else if (global) {
+            a.idx[o] = mine;
+            a.wsel[o] = w;
+        }
+        if (global && a.user_idx) a.user_idx[o] = mine;
+        if (global && a.user_w) a.user_w[o] = w;
+    }
+}
+
 // Routing metadata from the selections in LDS, by all nw waves of the routing
 // workgroup.  Active experts are listed in ascending id; the pairs of an
 // expert in ascending token; each expert's pairs are cut into column units of
@@ -479,7 +654,10 @@ __device__ __forceinline__ void build_meta(const RouteArgs &a, Lds &lds, int nw)
 // arrival completed the router (all waves call it, after a workgroup
 // barrier).  Tokens are split across the waves; the selections meet in LDS.
 __device__ __forceinline__ void route_step(const RouteArgs &a, RouteLds *lds, int nwaves) {
-    for (int b = wave_index(); b < a.B; b += nwaves) topk_token<true>(a, b, *lds);
+    if (a.B == 1 && nwaves == kWG)
+        topk_token_wg<true>(a, 0, *lds);
+    else
+        for (int b = wave_index(); b < a.B; b += nwaves) topk_token<true>(a, b, *lds);
     __syncthreads();
     build_meta<false>(a, *lds, nwaves);
 }
@@ -492,7 +670,10 @@ __device__ __forceinline__ void route_step(const RouteArgs &a, RouteLds *lds, in
 // records and the metadata header are written by the caller).  Ends with a
 // workgroup barrier.
 __device__ __forceinline__ void route_late(const RouteArgs &a, LateRouteLds &lds, bool lead) {
-    for (int b = wave_index(); b < a.B; b += kWG) topk_token<false>(a, b, lds, lead);
+    if (a.B == 1)
+        topk_token_wg<false>(a, 0, lds, lead);
+    else
+        for (int b = wave_index(); b < a.B; b += kWG) topk_token<false>(a, b, lds, lead);
     __syncthreads();
     if (a.B == 1) {
         // One token: every selected expert is one unit of one pair, in
