@@ -1170,7 +1170,10 @@ __device__ __forceinline__ void sum_slices(rsrc_t rpart, int nsl, int T, int t, 
 // group and step instead of once per tile and step.  A slice's partial sums
 // go to a.part; the last slice of a row group to arrive sums them in slice
 // order and runs the tile epilogues, so the results do not depend on the
-// order of arrival.
+// order of arrival.  The router's row groups come first, in slices of
+// a.kx_sps_r steps: shorter units, done early in the launch, so that the
+// routing that waits for the router runs while the other row groups still
+// stream their weights.
 constexpr int kXRows = 64;  // token rows of one staged step
 
 // Copies the x columns of step s into buf: row b (token b; rows past B copy
@@ -1209,12 +1212,16 @@ k_dense_in_kx(const StepArgs a) {
              i += gridDim.x * kWGThreads * 4)
             stf4(a.ylat + i, zero4());
     const int n_rt = a.n_rtiles, n_lt = a.L / a.latent_rows;
-    const int nsteps = a.H / kKStep, sps = a.kx_sps, nsl = (nsteps + sps - 1) / sps;
+    const int nsteps = a.H / kKStep;
+    const int nsl_r = (nsteps + a.kx_sps_r - 1) / a.kx_sps_r, nsl_o = (nsteps + a.kx_sps - 1) / a.kx_sps;
     const int nrg = (a.dense_hi - a.dense_lo + kWG - 1) / kWG;
-    const int units = nrg * nsl;
+    const int units_r = a.kx_rg_r * nsl_r, units = units_r + (nrg - a.kx_rg_r) * nsl_o;
     const rsrc_t rpart = buf_rsrc(a.part);
     for (int u = blockIdx.x; u < units; u += gridDim.x) {
-        const int rg = u / nsl, ks = u % nsl;
+        const bool short_sl = u < units_r;
+        const int nsl = short_sl ? nsl_r : nsl_o, sps = short_sl ? a.kx_sps_r : a.kx_sps;
+        const int v = short_sl ? u : u - units_r;
+        const int rg = (short_sl ? 0 : a.kx_rg_r) + v / nsl, ks = v % nsl;
         const int t = a.dense_lo + rg * kWG + wave;
         const bool active = t < a.dense_hi;
         const int kind = t < n_rt ? KIND_ROUTER : t < n_rt + n_lt ? KIND_LATENT : KIND_SHARED;
@@ -1525,9 +1532,10 @@ k_out(const StepArgs a) {
 // copies every token's column operand into LDS once: ylat as f32 at
 // latent-up steps (64 rows of 128 values; each lane splits its values into
 // the hi or lo half when it reads them) and the hi/lo rows of the shared
-// activation at shared-down steps (128 rows of 128 bf16).  The tile's last
-// slice adds the partial sums in slice order, then each token's hi and lo
-// columns, and rounds to bf16 once.
+// activation at shared-down steps (128 rows of 128 bf16).  Each slice adds
+// every token's hi and lo columns before it stores its partial sums (half the
+// partial bytes); the tile's last slice adds the partials in slice order and
+// rounds to bf16 once.
 constexpr int kOutStage = 32768;  // bytes of one staged step (both kinds)
 
 __device__ __forceinline__ void stage_out_step(char *buf, const StepArgs &a, int s, int Ls) {
@@ -1642,12 +1650,16 @@ k_out_kx(const StepArgs a) {
                         acc[c] = mfma(as_bf16x8(ra1[j]), out_operand(s_o[1], c, j), acc[c]);
             }
         }
-        // Partial sums of the slice, in MFMA layout: part[ks][t][c][lane].
+        // Partial sums of the slice with each token's hi and lo columns
+        // added, two column groups per store: lane (n, g) holds group 2c + (n
+        // & 1), token column n / 2: part[ks][t][c][lane], c < NCG / 2.
         if (active) {
 #pragma unroll
-            for (int c = 0; c < NCG; ++c)
-                buf_st16<true>(rpart, (uint32_t)(((((size_t)ks * n_ot + t) * NCG + c) * kWave + lane) * 16),
-                               __builtin_bit_cast(u32x4, acc[c]));
+            for (int c = 0; c < NCG / 2; ++c) {
+                const f32x4 v0 = add_pair_column(acc[2 * c]), v1 = add_pair_column(acc[2 * c + 1]);
+                buf_st16<true>(rpart, (uint32_t)(((((size_t)ks * n_ot + t) * (NCG / 2) + c) * kWave + lane) * 16),
+                               __builtin_bit_cast(u32x4, (n & 1) ? v1 : v0));
+            }
         }
         wait_vm_all();
         __syncthreads();
@@ -1658,14 +1670,13 @@ k_out_kx(const StepArgs a) {
         __syncthreads();
         if (s_arrive) {  // the tiles' last slice: sum the slices in order, round once
             if (active) {
-                const int col = n >> 1, part = n & 1;
-                f32x4 sums[NCG];
-                sum_slices<NCG>(rpart, nsl, n_ot, t, sums);
+                f32x4 sums[NCG / 2];
+                sum_slices<NCG / 2>(rpart, nsl, n_ot, t, sums);
 #pragma unroll
-                for (int c = 0; c < NCG; ++c) {
-                    const f32x4 v = add_pair_column(sums[c]);
-                    const int b = 8 * c + col;
-                    if (b < a.B && part == 0) {
+                for (int c = 0; c < NCG / 2; ++c) {
+                    const f32x4 v = sums[c];
+                    const int b = 8 * (2 * c + (n & 1)) + (n >> 1);
+                    if (b < a.B) {
                         const size_t o = (size_t)b * a.H + h0;
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {

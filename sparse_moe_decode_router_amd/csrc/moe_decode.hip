@@ -477,13 +477,21 @@ moe_status moe_decode_step(moe_decode_ctx *ctx, const uint16_t *x, int32_t batch
                       kWGThreads, args);
             return;
         }
+        // Router row groups (when this launch holds the router) in the
+        // shortest slices; the other row groups in as many slices as the
+        // compute units' remaining workgroup slots (two per unit) hold.
         const int nsteps = c.hidden / kKStep;
         const int nrg = cdiv(args.dense_hi - args.dense_lo, kWG);
-        int nsl = std::max(1, std::min({kMaxSlices, nsteps, (2 * ctx->n_cus + nrg / 2) / nrg}));
+        args.kx_rg_r = args.dense_lo == 0 && pl.n_rtiles > 0 ? std::min(nrg, cdiv(pl.n_rtiles, kWG)) : 0;
+        args.kx_sps_r = cdiv(nsteps, std::min(kMaxSlices, nsteps));
+        const int units_r = args.kx_rg_r * cdiv(nsteps, args.kx_sps_r);
+        const int nrg_o = nrg - args.kx_rg_r;
+        const int slots = 2 * ctx->n_cus - units_r - args.route_units - args.pf_units;
+        int nsl = nrg_o > 0 ? std::max(1, std::min({kMaxSlices, nsteps, slots / nrg_o})) : 1;
         args.kx_sps = cdiv(nsteps, nsl);
         nsl = cdiv(nsteps, args.kx_sps);
         launch_on(st, dense_in_kx[pl.ncg_in - 1],
-                  (unsigned)(nrg * nsl + args.route_units + args.pf_units), kWGThreads, args);
+                  (unsigned)(units_r + nrg_o * nsl + args.route_units + args.pf_units), kWGThreads, args);
     };
     if (side) {
         // The shared expert depends on x alone: its gate/up and down launches

@@ -41,6 +41,9 @@ struct StepArgs {
     // Dense-in above 16 tokens: steps per K slice, tiles and row groups of
     // the whole tile list (partial-buffer stride and counter offset).
     int32_t kx_sps, kx_tiles, kx_groups;
+    // ... row groups [0, kx_rg_r) (those holding router tiles) take shorter
+    // slices of kx_sps_r steps, so that the router completes early.
+    int32_t kx_rg_r, kx_sps_r;
     int32_t kx_sps_out;  // output kernel above 8 tokens: steps per K slice
     // Prefetch units of the dense-in launch (0: none): a following layer's
     // rows [pf0, pf0 + pf_bytes0) and [pf1, pf1 + pf_bytes1).
