@@ -71,6 +71,7 @@ def modes():
     allm = {"four_launches": binding.MODE_FOUR_LAUNCHES,
             "late_routing": binding.MODE_LATE_ROUTING,
             "dense_routing": binding.MODE_DENSE_ROUTING,
+            "ordered": binding.MODE_ORDERED,
             "side_stream": binding.MODE_SIDE_STREAM,
             "two_launches": binding.MODE_TWO_LAUNCHES, "fused": binding.MODE_FUSED}
     if MODE_FILTER is None:
@@ -592,7 +593,7 @@ def c4_summary(args, batches=(1, 8, 64), oracle_batches=(1, 64)):
             g.close()
         # The same graphs in the other multi-launch forms, for comparison.
         by_mode = {default_mode(): round(ms * 1e3 / n_layers, 2)}
-        for name in ("four_launches", "late_routing", "dense_routing"):
+        for name in ("four_launches", "late_routing", "dense_routing", "ordered"):
             if name == default_mode() or name not in modes():
                 continue
             for c in ctxs:

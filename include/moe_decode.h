@@ -216,6 +216,9 @@ typedef struct {
                               workgroup that completed the router), 1 in routing units
                               of the dense-in launch (above 8 tokens), 2 at the start
                               of the gate/up launch, 3 in the f32 router kernel */
+    int32_t ordered;       /* 1 when the latent combine ran in a fixed order
+                              (MOE_MODE_ORDERED): the step's outputs are the same bits
+                              from run to run */
 } moe_decode_dispatch_info;
 moe_status moe_decode_last_dispatch(const moe_decode_ctx *ctx, moe_decode_dispatch_info *info);
 
@@ -248,7 +251,17 @@ moe_status moe_decode_last_dispatch(const moe_decode_ctx *ctx, moe_decode_dispat
  *     then runs its units (other batches, and steps with a next-layer
  *     prefetch, route in the dense-in launch);
  *   MOE_MODE_DENSE_ROUTING: the four launches with the routing always in the
- *     dense-in launch.
+ *     dense-in launch;
+ *   MOE_MODE_ORDERED: the four launches (routing placed as by default) with
+ *     the latent combine in a fixed order: each pair's weighted down output
+ *     goes to the workspace, and the last of a token's k contributions to a
+ *     group of latent rows adds them in the order of the token's expert ids.
+ *     Every reduction of the step then has a fixed order, so a step's outputs
+ *     are the same bits from run to run (the other forms add the expert
+ *     outputs with f32 atomics, whose order varies).  The price: a store,
+ *     an arrival and, for the last arrival, a read of the k rows at the end
+ *     of each down unit (about 1.3 us at batch 1, 2-8 % of the step at
+ *     batch 8-64).
  * Shapes without a built persistent kernel (the f32 router, other expert
  * chunk shapes) run the four launches.  All modes compute the same values.
  * Returns MOE_ERR_INVALID_ARG for another mode.  Host-only. */
@@ -258,7 +271,8 @@ enum {
     MOE_MODE_TWO_LAUNCHES = 2,
     MOE_MODE_SIDE_STREAM = 3,
     MOE_MODE_LATE_ROUTING = 4,
-    MOE_MODE_DENSE_ROUTING = 5
+    MOE_MODE_DENSE_ROUTING = 5,
+    MOE_MODE_ORDERED = 6
 };
 moe_status moe_decode_set_mode(moe_decode_ctx *ctx, int32_t mode);
 

@@ -37,7 +37,7 @@ class DispatchInfo(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("batch", "top_k", "col_tiles", "split_in", "split_out", "split_w13",
                  "split_w2", "grid_in", "grid_w13", "grid_w2", "grid_out", "router_f32",
-                 "n_kernels", "fused", "grid_step", "out_staged", "routing")]
+                 "n_kernels", "fused", "grid_step", "out_staged", "routing", "ordered")]
 
 
 class Debug(ctypes.Structure):
@@ -46,7 +46,7 @@ class Debug(ctypes.Structure):
 
 
 MODE_FUSED, MODE_FOUR_LAUNCHES, MODE_TWO_LAUNCHES, MODE_SIDE_STREAM = 0, 1, 2, 3
-MODE_LATE_ROUTING, MODE_DENSE_ROUTING = 4, 5
+MODE_LATE_ROUTING, MODE_DENSE_ROUTING, MODE_ORDERED = 4, 5, 6
 DEFAULT_MODE = MODE_FOUR_LAUNCHES  # what moe_decode_init selects
 
 EXPORTED = ("moe_decode_validate_config", "moe_decode_workspace_size", "moe_decode_init",

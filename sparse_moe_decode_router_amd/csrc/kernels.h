@@ -783,12 +783,55 @@ __device__ __forceinline__ void w13_unit_rec(const StepArgs &a, int recw, int tg
     }
 }
 
+// Ordered latent combine, after a down unit's weighted outputs are in pout:
+// one arrival per pair of the unit on its token's counter for tile group tg
+// (k arrivals complete a token's group); the unit that completes a token
+// sums the token's k rows of pout over the group's latent rows [r0, r0 +
+// rows) in pair order, j = 0 .. k - 1 (ascending expert id), writes them to
+// ylat and clears the counter.  The sums therefore do not depend on the
+// order in which units run.  Starts after every wave's pout stores have
+// completed and a workgroup barrier; ends with a workgroup barrier.
+__device__ __forceinline__ void ordered_combine(const StepArgs &a, int recw, int nt, int tg,
+                                                int r0, int rows, int *s_done) {
+    const int lane = lane_id(), k = a.k;
+    if (wave_index() == 0) {
+        const int tok = __shfl(recw, R_TOKEN + (lane < nt ? lane : 0));
+        uint32_t *ctr = a.cctr + ((size_t)tok * kOrdGroups + tg) * kOrdStride;
+        uint32_t old = 0u;
+        if (lane < nt) old = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (lane < 8) s_done[lane] = lane < nt && old == (uint32_t)k - 1u ? tok : -1;
+        if (lane < nt && old == (uint32_t)k - 1u) store_agent(ctr, 0u);  // for the next step
+    }
+    __syncthreads();
+    const rsrc_t rp = buf_rsrc(a.pout);
+    const int q4 = rows / 4;  // 16-byte column chunks of one token
+    for (int it = threadIdx.x; it < 8 * q4; it += kWGThreads) {
+        const int b = s_done[it / q4];
+        if (b < 0) continue;
+        const int r = r0 + 4 * (it % q4);
+        f32x4 sum = zero4();
+        for (int j0 = 0; j0 < k; j0 += 16) {
+            u32x4 v[16];
+#pragma unroll
+            for (int q = 0; q < 16; ++q)
+                v[q] = buf_ld16<true>(rp, (uint32_t)((((size_t)b * k + min(j0 + q, k - 1)) * a.L + r) * 4));
+#pragma unroll
+            for (int q = 0; q < 16; ++q)
+                if (j0 + q < k) sum += __builtin_bit_cast(f32x4, v[q]);
+        }
+        stf4(a.ylat + (size_t)b * a.L + r, sum);
+    }
+    __syncthreads();
+}
+
 // Down unit: column unit c, tile group tg.  Tile t of expert e: latent rows
 // 16t .. 16t+15; the routing weight of each pair scales its column before the
 // f32 atomic add into ylat.  Coh: the record and activation rows come from
 // units of the same launch.  KS: waves per tile (8 / KS tiles per unit), each
-// taking S / KS steps of every chunk and adding its own partial sums.
-template <int S, bool Coh, int KS = 1>
+// taking S / KS steps of every chunk and adding its own partial sums.  Ord:
+// the weighted outputs go to pout instead (the KS partial sums added through
+// LDS first, in wave order) and ordered_combine forms ylat.
+template <int S, bool Coh, int KS = 1, bool Ord = false>
 __device__ __forceinline__ void w2_unit(const StepArgs &a, int c, int tg, uint16_t *s_b,
                                         bool &reuse) {
     static_assert(S % KS == 0, "steps per wave");
@@ -829,10 +872,37 @@ __device__ __forceinline__ void w2_unit(const StepArgs &a, int c, int tg, uint16
         mfma_fp4_chunk<SW, S>(w, s_b, n_eff, g, kh * SW, acc);
     }
     acc = add_pair_column(acc);
-    if (active && j < nt && part == 0) {
-        float *dst = a.ylat + (size_t)tok_j * a.L + 16 * t + 4 * g;
+    if constexpr (!Ord) {
+        if (active && j < nt && part == 0) {
+            float *dst = a.ylat + (size_t)tok_j * a.L + 16 * t + 4 * g;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) unsafeAtomicAdd(dst + i, w_j * acc[i]);
+            for (int i = 0; i < 4; ++i) unsafeAtomicAdd(dst + i, w_j * acc[i]);
+        }
+    } else {
+        if constexpr (KS > 1) {
+            float *red = (float *)s_b;
+            __syncthreads();  // every wave is done with the staged operand
+            stf4(red + (size_t)(wave * kWave + lane) * 4, acc);
+            __syncthreads();
+            if (kh == 0) {
+#pragma unroll
+                for (int q = 1; q < KS; ++q) acc += ldf4(red + (size_t)((wave + q) * kWave + lane) * 4);
+            }
+        }
+        // The pair's place in token order: b k + (its expert's rank among the
+        // token's experts).
+        const int pj = a.pair_slot[p0 + jc];
+        if (kh == 0 && active && j < nt && part == 0) {
+            f32x4 v;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] = w_j * acc[i];
+            buf_st16<true>(buf_rsrc(a.pout), (uint32_t)((((size_t)pj * a.L) + 16 * t + 4 * g) * 4),
+                           __builtin_bit_cast(u32x4, v));
+        }
+        wait_vm_all();    // this wave's pout stores have completed
+        __syncthreads();  // ... and every wave's; s_b is free
+        const int r0 = 16 * (kWG / KS) * tg;
+        ordered_combine(a, recw, nt, tg, r0, min(16 * (kWG / KS), a.L - r0), (int *)s_b);
     }
 }
 
@@ -1345,8 +1415,8 @@ k_w13(const StepArgs a) {
     }
 }
 
-// Kernel 3: down units (KS waves per tile).
-template <int S, int KS>
+// Kernel 3: down units (KS waves per tile; Ord: the ordered latent combine).
+template <int S, int KS, bool Ord = false>
 __global__ void __launch_bounds__(kWGThreads) __attribute__((amdgpu_waves_per_eu(4)))
 k_w2(const StepArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t s_b[8 * Stage<S>::kChunks];
@@ -1354,7 +1424,7 @@ k_w2(const StepArgs a) {
     const int TG = ((a.L >> 4) + kWG / KS - 1) / (kWG / KS);
     bool reuse = false;
     for (int u = blockIdx.x; u < NC * TG; u += gridDim.x)
-        w2_unit<S, false, KS>(a, u / TG, u % TG, s_b, reuse);
+        w2_unit<S, false, KS, Ord>(a, u / TG, u % TG, s_b, reuse);
 }
 
 // Kernel 4 up to 8 tokens with column operands staged in LDS once per

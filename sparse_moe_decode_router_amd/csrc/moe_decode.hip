@@ -89,12 +89,27 @@ StepKernel w13_kernel(int s, int ks, bool late) {
      k_w2<12, KS>,   k_w2<13, KS>, k_w2<14, KS>, k_w2<15, KS>, k_w2<16, KS>}
 const StepKernel kW2[] = MOE_W2_TABLE(1);
 #undef MOE_W2_TABLE
+#define MOE_W2_TABLE(KS)                                                                       \
+    {nullptr,              k_w2<1, KS, true>,  k_w2<2, KS, true>,  k_w2<3, KS, true>,          \
+     k_w2<4, KS, true>,    k_w2<5, KS, true>,  k_w2<6, KS, true>,  k_w2<7, KS, true>,          \
+     k_w2<8, KS, true>,    k_w2<9, KS, true>,  k_w2<10, KS, true>, k_w2<11, KS, true>,         \
+     k_w2<12, KS, true>,   k_w2<13, KS, true>, k_w2<14, KS, true>, k_w2<15, KS, true>,         \
+     k_w2<16, KS, true>}
+// Down kernels of the ordered latent combine.
+const StepKernel kW2Ord[] = MOE_W2_TABLE(1);
+#undef MOE_W2_TABLE
 // Down kernels with two waves per tile (even chunk shapes only).
 const StepKernel kW2Split[] = {nullptr,        nullptr,       k_w2<2, 2>,  nullptr,
                                k_w2<4, 2>,     nullptr,       k_w2<6, 2>,  nullptr,
                                k_w2<8, 2>,     nullptr,       k_w2<10, 2>, nullptr,
                                k_w2<12, 2>,    nullptr,       k_w2<14, 2>, nullptr,
                                k_w2<16, 2>};
+const StepKernel kW2SplitOrd[] = {nullptr,              nullptr,             k_w2<2, 2, true>,
+                                  nullptr,              k_w2<4, 2, true>,    nullptr,
+                                  k_w2<6, 2, true>,     nullptr,             k_w2<8, 2, true>,
+                                  nullptr,              k_w2<10, 2, true>,   nullptr,
+                                  k_w2<12, 2, true>,    nullptr,             k_w2<14, 2, true>,
+                                  nullptr,              k_w2<16, 2, true>};
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -180,6 +195,8 @@ StepArgs base_args(const moe_decode_ctx *ctx) {
     a.acthl = (uint16_t *)(ws + l.acthl);
     a.ylat = (float *)(ws + l.ylat);
     a.ysh = (float *)(ws + l.ysh);
+    a.pout = (float *)(ws + l.pout);
+    a.cctr = (uint32_t *)(ws + l.cctr);
     a.c13 = (uint32_t *)(ws + l.c13);
     a.part = (float *)(ws + l.part);
     a.rgc = (uint32_t *)(ws + l.rgc);
@@ -331,7 +348,8 @@ moe_status moe_decode_step(moe_decode_ctx *ctx, const uint16_t *x, int32_t batch
     const bool dense_one_round = pl.units_in <= 2LL * ctx->n_cus;
     const bool late = late_ok && (ctx->mode == MOE_MODE_LATE_ROUTING ||
                                   ((ctx->mode == MOE_MODE_FOUR_LAUNCHES ||
-                                    ctx->mode == MOE_MODE_SIDE_STREAM) && dense_one_round));
+                                    ctx->mode == MOE_MODE_SIDE_STREAM ||
+                                    ctx->mode == MOE_MODE_ORDERED) && dense_one_round));
     StepArgs a = base_args(ctx);
     a.B = batch;
     a.k = top_k;
@@ -383,6 +401,11 @@ moe_status moe_decode_step(moe_decode_ctx *ctx, const uint16_t *x, int32_t batch
     if (split2) pl.units_2 = (long long)ncols_cap(c.n_experts, batch, top_k) *
                              cdiv(c.latent / 16, kWG / 2);
     d.split_w2 = split2 ? 2 : 1;
+    // The latent combine in a fixed order (MOE_MODE_ORDERED).
+    const bool ordered = ctx->mode == MOE_MODE_ORDERED;
+    d.ordered = ordered ? 1 : 0;
+    const StepKernel w2_k = ordered ? (split2 ? kW2SplitOrd[pl.s2] : kW2Ord[pl.s2])
+                                    : (split2 ? kW2Split[pl.s2] : kW2[pl.s2]);
     d.grid_in = (int32_t)(pl.units_in + a.route_units);  // every unit its own workgroup
     d.grid_w13 = late ? (int32_t)late_grid : grid_for(pl.units_13, cap);
     d.grid_w2 = grid_for(pl.units_2, cap);
@@ -515,7 +538,7 @@ moe_status moe_decode_step(moe_decode_ctx *ctx, const uint16_t *x, int32_t batch
         dense_launch(s, a);
         dense_launch(ctx->side, sa);
         launch(w13_kernel(pl.s13, ks13, late), d.grid_w13, kWGThreads);
-        launch(split2 ? kW2Split[pl.s2] : kW2[pl.s2], d.grid_w2, kWGThreads);
+        launch(w2_k, d.grid_w2, kWGThreads);
         launch_on(ctx->side, k_out_part<OUT_SHARED>,
                   grid_for(dense_units_host(n_ot, kWG / pl.sd.kw, pl.ncg_out), cap), kWGThreads,
                   sa);
@@ -535,7 +558,7 @@ moe_status moe_decode_step(moe_decode_ctx *ctx, const uint16_t *x, int32_t batch
         return e == hipSuccess ? MOE_OK : hip_fail(ctx, e);
     }
     launch(w13_kernel(pl.s13, ks13, late), d.grid_w13, kWGThreads);
-    launch(split2 ? kW2Split[pl.s2] : kW2[pl.s2], d.grid_w2, kWGThreads);
+    launch(w2_k, d.grid_w2, kWGThreads);
     if (pl.ncg_out >= 2) {
         // Above 8 tokens: the column operands staged in LDS per group of 8
         // output tiles, K in slices (about two units per compute unit).
@@ -668,7 +691,8 @@ moe_status moe_decode_set_next_layer(moe_decode_ctx *ctx, const moe_decode_ctx *
 moe_status moe_decode_set_mode(moe_decode_ctx *ctx, int32_t mode) {
     if (!ctx || (mode != MOE_MODE_FUSED && mode != MOE_MODE_FOUR_LAUNCHES &&
                  mode != MOE_MODE_TWO_LAUNCHES && mode != MOE_MODE_SIDE_STREAM &&
-                 mode != MOE_MODE_LATE_ROUTING && mode != MOE_MODE_DENSE_ROUTING))
+                 mode != MOE_MODE_LATE_ROUTING && mode != MOE_MODE_DENSE_ROUTING &&
+                 mode != MOE_MODE_ORDERED))
         return MOE_ERR_INVALID_ARG;
     ctx->mode = mode;
     return MOE_OK;

@@ -45,4 +45,10 @@ enum { M_N_ACTIVE = 0, M_N_COLS = 1, M_COUNT = 16 };
 // then the token and the routing weight (f32 bits) of each pair.
 enum { R_EXPERT = 0, R_COUNT = 1, R_PAIR0 = 2, R_TOKEN = 8, R_WEIGHT = 16, kRecWords = 32 };
 
+// Ordered latent combine: one arrival counter per (token, tile group of the
+// down kernel), tile groups of at least 64 latent rows, counters 64 bytes
+// apart.
+constexpr int kOrdGroups = kMaxDenseK / 64;
+constexpr int kOrdStride = 16;
+
 }  // namespace moe

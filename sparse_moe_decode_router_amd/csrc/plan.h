@@ -145,8 +145,8 @@ constexpr int kMaxRowGroups = (kMaxExperts / 16 + kMaxDenseK / 16 + kMaxDenseK /
 static_assert(kMaxCols >= kMaxExperts && kMaxRowGroups >= kMaxDenseK / 16 / kWG, "limits");
 
 struct Layout {
-    size_t gctr, meta, c13, rgc, score, key, idx, wsel, act_expert, act_off, cu_rec, pair_slot,
-        pair_of_slot, zhl, ashhl, acthl, ylat, ysh, part, total;
+    size_t gctr, meta, c13, rgc, cctr, score, key, idx, wsel, act_expert, act_off, cu_rec,
+        pair_slot, pair_of_slot, zhl, ashhl, acthl, ylat, ysh, pout, part, total;
     size_t counters_end;  // [0, counters_end) holds every counter: cleared at init
 };
 
@@ -163,6 +163,7 @@ inline size_t counter_bytes() {
     o = align_up(o + M_COUNT * 4);
     o = align_up(o + (size_t)kMaxCols * kCtrStride * 4);
     o = align_up(o + (size_t)2 * kMaxRowGroups * kCtrStride * 4);
+    o = align_up(o + (size_t)kMaxBatch * kOrdGroups * kOrdStride * 4);
     return o;
 }
 
@@ -183,6 +184,7 @@ inline Layout make_layout(const moe_decode_config &c) {
     l.meta = take(M_COUNT * 4);
     l.c13 = take((size_t)kMaxCols * kCtrStride * 4);
     l.rgc = take((size_t)2 * kMaxRowGroups * kCtrStride * 4);  // caller's and side stream's launches
+    l.cctr = take((size_t)kMaxBatch * kOrdGroups * kOrdStride * 4);  // ordered latent combine
     l.counters_end = o;
     // Score and key rows are padded to kMaxExperts: the routing reads a whole
     // row with one base address (entries past E are never used).
@@ -201,14 +203,17 @@ inline Layout make_layout(const moe_decode_config &c) {
     l.ylat = take(Bm * L * 4);
     l.ysh = take(Bm * (size_t)c.hidden * 4);
     // Slice partials of the large-batch dense-in (above 16 tokens) and output
-    // (above 8 tokens) kernels; the two never run at the same time.
+    // (above 8 tokens) kernels, and the pair outputs of the ordered latent
+    // combine (down launch, between those two): no two of them are live at
+    // the same time (the ordered combine has no side stream).
     const size_t n_ot = (size_t)cdiv(c.hidden, out_tile_rows(c.hidden));
     const size_t ncg = (size_t)cdiv(c.max_batch, 16);
     const size_t part_in = ncg >= 2 ? (size_t)kMaxSlices * dense_tiles(c) * ncg * kWave * 16 : 0;
     // The output kernel's column groups per unit: 2, 4 or 8 (ceil(B / 8) rounded up).
     const size_t gout = c.max_batch <= 16 ? 2 : c.max_batch <= 32 ? 4 : kMaxGroupsOut;
     const size_t part_out = c.max_batch > 8 ? kMaxSlicesOut * n_ot * gout * kWave * 16 : 0;
-    l.part = take(std::max(part_in, part_out));
+    l.part = take(std::max({part_in, part_out, P * L * 4}));
+    l.pout = l.part;
     l.total = o;
     return l;
 }

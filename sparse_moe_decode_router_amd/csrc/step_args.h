@@ -75,6 +75,10 @@ struct StepArgs {
     uint16_t *zhl, *acthl, *ashhl;
     float *ylat;  // f32 latent combine (atomic adds)
     float *ysh;   // fused step: shared-down sums [B][H] f32
+    // Ordered latent combine: each pair's weighted down output [pair][L] f32
+    // (pairs in token order, b k + j) and the arrivals per (token, tile group).
+    float *pout;
+    uint32_t *cctr;
     float *part;    // dense-in above 16 tokens: slice partials [slice][tile][group][lane][4]
     uint32_t *rgc;  // ... arrivals per row group, 256 B apart (two sets: caller / side stream)
 };

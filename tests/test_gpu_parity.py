@@ -365,7 +365,8 @@ def mode_const(name):
             "four_launches": binding.MODE_FOUR_LAUNCHES,
             "side_stream": binding.MODE_SIDE_STREAM,
             "late_routing": binding.MODE_LATE_ROUTING,
-            "dense_routing": binding.MODE_DENSE_ROUTING}[name]
+            "dense_routing": binding.MODE_DENSE_ROUTING,
+            "ordered": binding.MODE_ORDERED}[name]
 
 
 @pytest.mark.parametrize("B,k", [(1, 1), (1, 6), (2, 8), (3, 6), (8, 8), (8, 1), (9, 6), (16, 8)])
@@ -389,6 +390,60 @@ def test_late_routing_matches_four_launches(small_layer, B, k):
     assert_same_step(a, c)
     assert_same_step(a, b)
     check_step(small_layer, x, k, *a)
+
+
+def assert_bits_equal(a, b):
+    for u, v in zip(a, b):
+        np.testing.assert_array_equal(np.asarray(u), np.asarray(v))
+
+
+@pytest.mark.parametrize("B,k", [(1, 1), (1, 8), (3, 6), (8, 8), (24, 6), (64, 8)])
+def test_ordered_combine_is_bit_reproducible(small_layer, B, k):
+    """MOE_MODE_ORDERED: repeated steps, on one context and on a fresh one,
+    give the same bits; the four-launch step's experts and weights, outputs
+    up to the order of the latent combine; every token against the oracle."""
+    ordered = make_ctx(small_layer, 64, 8)
+    ordered.set_mode(binding.MODE_ORDERED)
+    x = synth.make_tokens(small_layer.dims, 900 + B, B)
+    a = run(ordered, x, k)
+    for _ in range(3):
+        assert_bits_equal(a, run(ordered, x, k))
+    assert ordered.last_dispatch()["ordered"] == 1
+    fresh = make_ctx(small_layer, 64, 8)
+    fresh.set_mode(binding.MODE_ORDERED)
+    assert_bits_equal(a, run(fresh, x, k))
+    four = make_ctx(small_layer, 64, 8)
+    b = run(four, x, k)
+    assert four.last_dispatch()["ordered"] == 0
+    assert_same_step(a, b)
+    check_step(small_layer, x, k, *a)
+
+
+def test_ordered_combine_graph_replays_equal_eager_bits(small_layer):
+    """A captured two-layer graph of the ordered form replays the eager
+    step's bits, with eager steps of other batches between the replays."""
+    import torch
+    B, k = 8, 6
+    ctxs = [make_ctx(small_layer, 16, 6) for _ in range(2)]
+    for c in ctxs:
+        c.set_mode(binding.MODE_ORDERED)
+    x = synth.make_tokens(small_layer.dims, 14, B)
+    xd = [to_dev_tokens(x), to_dev_tokens(x)]
+    outs = [torch.empty((B, small_layer.dims.hidden), dtype=torch.int16, device="cuda")
+            for _ in range(2)]
+    idxs = [torch.empty((B, k), dtype=torch.int32, device="cuda") for _ in range(2)]
+    ws = [torch.empty((B, k), dtype=torch.float32, device="cuda") for _ in range(2)]
+    want = run(ctxs[0], x, k)
+    g = binding.Graph(ctxs, xd, B, k, outs, idxs, ws)
+    stream = torch.cuda.Stream()
+    for rep in range(3):
+        g.launch(stream)
+        stream.synchronize()
+        for li in range(2):
+            assert_bits_equal((outs[li].cpu().numpy().view(np.uint16), idxs[li].cpu().numpy(),
+                               ws[li].cpu().numpy()), want)
+        run(ctxs[1], synth.make_tokens(small_layer.dims, 15 + rep, 3), k)
+    g.close()
 
 
 def test_late_routing_repeated_steps_and_graph(small_layer):
@@ -539,6 +594,24 @@ def test_k3_persistent_step_matches_four_launches(k3_layer, k3_dev, bias_kind, B
     log(f"  K3 {mode} {bias_kind} B={B}:", r)
 
 
+@pytest.mark.parametrize("bias_kind,B", [("normal", 1), ("flat", 64)])
+def test_k3_ordered_combine(k3_layer, k3_dev, bias_kind, B):
+    """The ordered latent combine on the K3 layer (batch 1: two waves per
+    down tile, their sums added in LDS first): two runs give the same bits,
+    the four-launch step's experts and weights, every token against the
+    oracle."""
+    four, _ = k3_ctx(k3_dev, bias_kind, 64)
+    ordered, _ = k3_ctx(k3_dev, bias_kind, 64)
+    ordered.set_mode(binding.MODE_ORDERED)
+    x = synth.make_tokens(k3_dev.dims, 17, B)
+    a = run(ordered, x, 16)
+    assert_bits_equal(a, run(ordered, x, 16))
+    assert ordered.last_dispatch()["split_w2"] == (2 if B == 1 else 1)
+    assert_modes_agree(a, run(four, x, 16))
+    r = check_step(layer_with_bias(k3_layer, bias_kind), x, 16, *a)
+    log(f"  K3 ordered {bias_kind} B={B}:", r)
+
+
 @pytest.mark.parametrize("bias_kind,B", [("normal", 1), ("zipf", 8)])
 def test_k3_late_routing(k3_layer, k3_dev, bias_kind, B):
     """The routing in the gate/up launch on the K3 layer: the four-launch
@@ -683,7 +756,7 @@ def c4_graph_run(c4_layers, B, mode, replays=2):
 
 
 @pytest.mark.parametrize("mode", ["four_launches", "prefetch", "side_stream", "two_launches",
-                                  "fused", "late_routing", "dense_routing"])
+                                  "fused", "late_routing", "dense_routing", "ordered"])
 def test_c4_eight_layer_graph(c4_layers, mode):
     """Every execution mode: each layer's replayed result equals its eager
     step, and the replayed outputs of the first and last layers match the
