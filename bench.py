@@ -271,7 +271,12 @@ def kernel_durations(ctx, names, kb, xd, k, out, idx, wts, steps, stream, out_st
         avg_ms = sums[n] / steps
         avg_bytes = kbytes[n] / steps
         gbs = avg_bytes / (avg_ms * 1e-3) / 1e9
-        sym = "k_out_st" if n == "out" and out_staged else KERNEL_SYMBOLS[n]
+        sym = KERNEL_SYMBOLS[n]
+        B = ctx.last_dispatch()["batch"]
+        if n == "out":  # the output kernel's forms: K slices above 8 tokens, staged operands up to 8
+            sym = "k_out_kx" if B > 8 else "k_out_st" if out_staged else sym
+        elif n == "dense_in" and B > 16:  # x staged per row group, K slices
+            sym = "k_dense_in_kx"
         per_kernel[n] = {"symbol": sym, "us": round(avg_ms * 1e3, 2),
                          "bytes": int(avg_bytes), "gbs": round(gbs, 1),
                          "frac": round(gbs / HBM_PEAK_GBS, 4)}
@@ -628,7 +633,7 @@ def c4_summary(args, batches=(1, 8, 64), oracle_batches=(1, 64)):
                  "layer_kernels": per_kernel, "expert_path": expert_path(per_kernel),
                  "roofline": {"bound": "hbm", "kernel": pk["symbol"], "achieved": pk["gbs"],
                               "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": pk["frac"],
-                              "traffic": load_traffic(pk["symbol"], f"c4_b{B}")},
+                              "traffic": load_traffic(pk["symbol"], f"k3_tp8_b{B}")},
                  "timed": f"{args.steps} launches of the eight-layer graph"}
         if B in oracle_batches and not args.no_cpu_baseline:
             log(f"[bench] timing the CPU oracle on one C4 layer at batch {B}")
