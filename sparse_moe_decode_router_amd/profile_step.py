@@ -3,7 +3,8 @@
 ``run``: a short program for rocprofv3 to wrap: eager steps of one workload
 (rotating inputs), then a plain f32 copy of known size (``--copy-mib``), the
 calibration dispatch that says what FETCH_SIZE and WRITE_SIZE read for a
-known number of bytes moved.
+known number of bytes moved; with ``--read-mb``, read-only reference launches
+(torch's sum) of given sizes.
 
 ``summarize``: reads the counter CSVs of two rocprofv3 runs (one with
 FETCH_SIZE, one with WRITE_SIZE), scales each kernel's mean per-dispatch
@@ -45,7 +46,8 @@ WORKLOADS = {
     "k3_tp8_b8": ("k3_tp8", 8, 16, 1000),
     "k3_tp8_b64": ("k3_tp8", 64, 16, 1000),
 }
-MODES = ("four_launches", "late_routing", "dense_routing", "side_stream", "two_launches", "fused")
+MODES = ("four_launches", "late_routing", "dense_routing", "ordered", "side_stream", "two_launches",
+         "fused")
 COPY_KERNEL = "elementwise"  # torch's kernel for the calibration copy
 
 
@@ -70,6 +72,7 @@ def run(args) -> None:
     ctx.set_mode({"four_launches": binding.MODE_FOUR_LAUNCHES,
                   "late_routing": binding.MODE_LATE_ROUTING,
                   "dense_routing": binding.MODE_DENSE_ROUTING,
+                  "ordered": binding.MODE_ORDERED,
                   "side_stream": binding.MODE_SIDE_STREAM,
                   "two_launches": binding.MODE_TWO_LAUNCHES, "fused": binding.MODE_FUSED}[mode])
     xs = [torch.from_numpy(synth.make_tokens(layer.dims, seed, B, draw=r).view(np.int16)).cuda()
@@ -90,6 +93,17 @@ def run(args) -> None:
         torch.mul(src, 1.0, out=dst)  # reads and writes copy_mib MiB
     torch.cuda.synchronize()
     log(f"[profile] calibration copy: {args.copies} x {args.copy_mib} MiB")
+    # Read-only reference launches: torch's sum over buffers of the given
+    # sizes (MB), e.g. the bytes of one launch of the step, so that a
+    # kernel trace shows what one plain streaming launch of that size takes.
+    for mb in args.read_mb:
+        buf = torch.ones(int(mb * 1e6) // 4, dtype=torch.float32, device="cuda")
+        torch.cuda.synchronize()
+        for _ in range(args.copies):
+            buf.sum()
+        torch.cuda.synchronize()
+        log(f"[profile] read reference: {args.copies} x {mb} MB")
+        del buf
     ctx.close()
 
 
@@ -215,6 +229,8 @@ def main() -> None:
     r.add_argument("--mode", default="four_launches", choices=MODES)
     r.add_argument("--copy-mib", type=int, default=512)
     r.add_argument("--copies", type=int, default=3)
+    r.add_argument("--read-mb", type=float, nargs="*", default=[],
+                   help="sizes (MB) of read-only reference launches (torch sum)")
     s = sub.add_parser("summarize")
     s.add_argument("--workload", default="k3_b1", choices=sorted(WORKLOADS))
     s.add_argument("--fetch", required=True)
