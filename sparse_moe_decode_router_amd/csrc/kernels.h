@@ -1203,6 +1203,104 @@ k_dense_in(const StepArgs a) {
     }
 }
 
+// Kernel 1 up to 2 tokens: the tokens' x rows are staged in LDS by every
+// workgroup, so a wave's registers hold weights only and four of its K steps
+// stay in flight (a ring of four step buffers, each refilled with the step
+// four ahead as soon as its MFMAs have read it); a wave's chain of round
+// trips, not the bandwidth, sets the launch's time at these batches.  The
+// staging loads go out first, the four first weight steps behind them, and
+// only the staging loads are waited for before the LDS copy (vector loads
+// complete in issue order).  One unit per workgroup (no loop, so that no wait
+// carries over a loop edge); tiles, K split and epilogues as in k_dense_in.
+// Route: as in k_dense_in, the workgroup whose router arrival completes the
+// router then routes the step, in LDS that x no longer needs; prefetch units
+// follow the dense units.
+constexpr int kXlTokens = 2;
+constexpr int kXlRing = 4;
+constexpr int kXlPad = 8;  // elements after each staged row: the rows' equal columns on distinct banks
+template <bool Route>
+union XlShared {
+    uint16_t x[kXlTokens * (kMaxDenseK + kXlPad)];
+    RouteLds route;
+};
+template <>
+union XlShared<false> {
+    uint16_t x[kXlTokens * (kMaxDenseK + kXlPad)];
+};
+
+template <bool Route>
+__global__ void __launch_bounds__(kWGThreads) __attribute__((amdgpu_waves_per_eu(4)))
+k_dense_in_xl(const StepArgs a) {
+    __shared__ __attribute__((aligned(16))) XlShared<Route> s_u;
+    __shared__ float s_red[kWG * kWave * 4];
+    __shared__ int s_last;
+    uint16_t *s_x = s_u.x;
+    const Role ro = role_of(a.kw_in);
+    const int lane = lane_id(), n = lane & 15, g = lane >> 4;
+    if (threadIdx.x == 0) s_last = 0;
+    if (a.zero_ylat)
+        for (int i = (blockIdx.x * kWGThreads + threadIdx.x) * 4; i < a.B * a.L;
+             i += gridDim.x * kWGThreads * 4)
+            stf4(a.ylat + i, zero4());
+    const int units = dense_units(a.dense_hi - a.dense_lo, ro.RW, 1);
+    if ((int)blockIdx.x >= units) {
+        if constexpr (Route) prefetch_units(a, units + a.route_units);
+        return;
+    }
+    int cg, tg;
+    dense_unit(blockIdx.x, 1, cg, tg);
+    const int n_rt = a.n_rtiles, n_lt = a.L / a.latent_rows;
+    const int t0 = a.dense_lo + tg * ro.RW + ro.rg;
+    const bool active = t0 < a.dense_hi;
+    const int kind = t0 < n_rt ? KIND_ROUTER : t0 < n_rt + n_lt ? KIND_LATENT : KIND_SHARED;
+    const int tl = kind == KIND_ROUTER ? t0 : kind == KIND_LATENT ? t0 - n_rt : t0 - n_rt - n_lt;
+    const int tt = active ? tl : 0;
+    const uint16_t *A = dense_in_row(a, kind, tt) + 8 * g;
+    const int ns = a.spc_in, s0 = ro.kw * ns;  // kXlRing <= ns <= kMaxStepsPerChunk (host)
+    // x chunks of this thread (16 bytes each): c = threadIdx.x + kWGThreads q.
+    constexpr int kQx = kXlTokens * kMaxDenseK / 8 / kWGThreads;
+    const int nq = a.B * a.H / 8;
+    u32x4 xs[kQx];
+#pragma unroll
+    for (int q = 0; q < kQx; ++q) xs[q] = ld16(a.x + 8 * (size_t)min((int)threadIdx.x + kWGThreads * q, nq - 1));
+    fence_schedule();
+    u32x4 w[kXlRing][4];
+#pragma unroll
+    for (int i = 0; i < kXlRing; ++i) load_tile_bf16(A, s0 + i, w[i]);
+    fence_schedule();
+    // vmcnt(16): the x loads have landed (vmcnt in bits [3:0] and [15:14]).
+    constexpr int kWl = 4 * kXlRing;
+    __builtin_amdgcn_s_waitcnt((kWl & 15) | ((kWl >> 4) << 14) | 0x0F70);
+    const int rq = a.H / 8, xst = a.H + kXlPad;  // chunks per token row; staged row stride
+#pragma unroll
+    for (int q = 0; q < kQx; ++q) {
+        const int c = (int)threadIdx.x + kWGThreads * q;
+        if (c < nq) *(u32x4 *)(s_x + (size_t)(c / rq) * xst + 8 * (c % rq)) = xs[q];
+    }
+    lds_reuse_barrier();  // x is in LDS for every wave (weight loads still in flight)
+    const uint16_t *xr = s_x + (size_t)(n < a.B ? n : 0) * xst + 8 * g;
+    f32x4 acc = zero4();
+#pragma unroll
+    for (int i = 0; i < kMaxStepsPerChunk; ++i) {
+        if (i < ns) {
+            const uint16_t *xp = xr + (size_t)(s0 + i) * kKStep;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                acc = mfma(as_bf16x8(w[i % kXlRing][j]), as_bf16x8(*(const u32x4 *)(xp + 32 * j)), acc);
+            if (i + kXlRing < ns) load_tile_bf16(A, s0 + i + kXlRing, w[i % kXlRing]);
+        }
+    }
+    const bool leader = reduce_k1(s_red, ro.wave, ro.kw, ro.KW, acc);
+    if (leader && active) {
+        f32x4 sum[1] = {acc};
+        dense_in_epilogue<false, 1, Route>(a, kind, tt, 0, sum, &s_last);
+    }
+    if constexpr (Route) {
+        __syncthreads();  // s_last is set; every wave is done with x
+        if (s_last) route_step(route_args(a), &s_u.route, kWG);
+    }
+}
+
 // Sum over the nsl slices of tile t's partials part[k][t][c][lane] (T tiles
 // per slice), in slice order.  The loads of a batch of slices are all issued
 // before their sums (indices clamped to the last slice, the extra values

@@ -771,6 +771,23 @@ def test_c4_eight_layer_graph(c4_layers, mode):
         log(f"  C4 {mode} layer {l}:", r)
 
 
+@pytest.mark.parametrize("mode", ["prefetch", "dense_routing", "late_routing"])
+@pytest.mark.parametrize("B", [1, 2])
+def test_c4_graph_small_batch_forms(c4_layers, mode, B):
+    """Up to two tokens the dense-in launch stages x in LDS (with the routing
+    at its end, with prefetch units after it, or with the routing in the
+    gate/up launch): replays equal eager steps, and the first and last
+    layers match the oracle on every token."""
+    k = 16
+    ctxs, xs, reps = c4_graph_run(c4_layers, B, mode)
+    for rep in reps:
+        for l in range(len(xs)):
+            assert_same_step(rep[l], run(ctxs[l], xs[l], k))
+    for l in (0, len(xs) - 1):
+        r = check_step(c4_layers[0][l], xs[l], k, *reps[-1][l])
+        log(f"  C4 {mode} B={B} layer {l}:", r)
+
+
 @pytest.mark.parametrize("B", [1, 64])
 def test_c4_graph_replay_matches_oracle(c4_layers, B):
     """The default form at batch 1 and 64: the outputs of both replays of
