@@ -1602,11 +1602,15 @@ k_out_st(const StepArgs a) {
     ts.Ab = a.sh_w2 + h * a.Is + 8 * g;
     ts.Ls = a.L / kKStep;
     const int s0 = ro.kw * a.spc_out, s1 = s0 + a.spc_out;
-    u32x4 ra0[4], ra1[4];
-    load_out_w(ts, s0, ra0);
-    load_out_w(ts, s0 + 1 < s1 ? s0 + 1 : s0, ra1);
+    // Full: a ring of kXlRing weight steps in flight (every operand comes
+    // from LDS, so the registers hold weights only); otherwise two steps.
+    constexpr int kNw = Full ? kXlRing : 2;
+    u32x4 rw[kNw][4];
+#pragma unroll
+    for (int i = 0; i < kNw; ++i) load_out_w(ts, min(s0 + i, s1 - 1), rw[i]);
     fence_schedule();
-    __builtin_amdgcn_s_waitcnt(8 | 0x0F70);  // vmcnt(8): the staging loads have landed
+    // vmcnt(4 kNw): the staging loads have landed (vmcnt in bits [3:0] and [15:14]).
+    __builtin_amdgcn_s_waitcnt(((4 * kNw) & 15) | (((4 * kNw) >> 4) << 14) | 0x0F70);
 #pragma unroll
     for (int i = 0; i < kQ; ++i) {
         const int q = (int)threadIdx.x + kWGThreads * i;
@@ -1634,7 +1638,19 @@ k_out_st(const StepArgs a) {
     const rsrc_t rb_ash = buf_rsrc(a.ashhl);
     const uint32_t ob = (uint32_t)((((size_t)(valid ? col : 0) * 2 + part) * a.Is + 8 * g) * 2);
     f32x4 acc = zero4();
-    if (active) {
+    if constexpr (Full) {
+        if (active) {
+#pragma unroll
+            for (int i = 0; i < kMaxStepsPerChunk; ++i) {
+                if (i < a.spc_out) {
+                    mfma_tile_lds(rw[i % kNw], op, s0 + i, acc);
+                    if (i + kNw < a.spc_out) load_out_w(ts, s0 + i + kNw, rw[i % kNw]);
+                }
+            }
+        }
+    } else if (active) {
+        u32x4(&ra0)[4] = rw[0];
+        u32x4(&ra1)[4] = rw[1 % kNw];
 #pragma unroll 1
         for (int s = s0; s < s1; s += 2) {
             const bool two = s + 1 < s1;
@@ -1644,15 +1660,15 @@ k_out_st(const StepArgs a) {
                 load_out_w(ts, s2, ra1);
             }
             u32x4 rb0[4], rb1[4];
-            if (!Full && s >= ts.Ls) buf_cols_bf16<false>(rb_ash, ob, valid, s - ts.Ls, rb0);
-            if (!Full && s2 >= ts.Ls) buf_cols_bf16<false>(rb_ash, ob, valid, s2 - ts.Ls, rb1);
+            if (s >= ts.Ls) buf_cols_bf16<false>(rb_ash, ob, valid, s - ts.Ls, rb0);
+            if (s2 >= ts.Ls) buf_cols_bf16<false>(rb_ash, ob, valid, s2 - ts.Ls, rb1);
             fence_schedule();
-            if (Full || s < ts.Ls)
+            if (s < ts.Ls)
                 mfma_tile_lds(ra0, op, s, acc);
             else
                 mfma_tile(ra0, rb0, acc);
             if (two) {
-                if (Full || s2 < ts.Ls)
+                if (s2 < ts.Ls)
                     mfma_tile_lds(ra1, op, s2, acc);
                 else
                     mfma_tile(ra1, rb1, acc);
