@@ -1204,11 +1204,11 @@ k_dense_in(const StepArgs a) {
 }
 
 // Kernel 1 up to 2 tokens: the tokens' x rows are staged in LDS by every
-// workgroup, so a wave's registers hold weights only and four of its K steps
-// stay in flight (a ring of four step buffers, each refilled with the step
-// four ahead as soon as its MFMAs have read it); a wave's chain of round
+// workgroup, so a wave's registers hold weights only and six of its K steps
+// stay in flight (a ring of six step buffers, each refilled with the step six
+// ahead as soon as its MFMAs have read it); a wave's chain of round
 // trips, not the bandwidth, sets the launch's time at these batches.  The
-// staging loads go out first, the four first weight steps behind them, and
+// staging loads go out first, the six first weight steps behind them, and
 // only the staging loads are waited for before the LDS copy (vector loads
 // complete in issue order).  One unit per workgroup (no loop, so that no wait
 // carries over a loop edge); tiles, K split and epilogues as in k_dense_in.
@@ -1216,7 +1216,8 @@ k_dense_in(const StepArgs a) {
 // router then routes the step, in LDS that x no longer needs; prefetch units
 // follow the dense units.
 constexpr int kXlTokens = 2;
-constexpr int kXlRing = 4;
+constexpr int kXlRing = 4;       // weight steps in flight per wave (output kernel); the least spc
+constexpr int kXlDenseRing = 6;  // ... dense-in (K3 batch 1: 29.4 -> 28.5 us against 4)
 constexpr int kXlPad = 8;  // elements after each staged row: the rows' equal columns on distinct banks
 template <bool Route>
 union XlShared {
@@ -1264,12 +1265,12 @@ k_dense_in_xl(const StepArgs a) {
 #pragma unroll
     for (int q = 0; q < kQx; ++q) xs[q] = ld16(a.x + 8 * (size_t)min((int)threadIdx.x + kWGThreads * q, nq - 1));
     fence_schedule();
-    u32x4 w[kXlRing][4];
+    u32x4 w[kXlDenseRing][4];
 #pragma unroll
-    for (int i = 0; i < kXlRing; ++i) load_tile_bf16(A, s0 + i, w[i]);
+    for (int i = 0; i < kXlDenseRing; ++i) load_tile_bf16(A, min(s0 + i, s0 + ns - 1), w[i]);
     fence_schedule();
-    // vmcnt(16): the x loads have landed (vmcnt in bits [3:0] and [15:14]).
-    constexpr int kWl = 4 * kXlRing;
+    // vmcnt(24): the x loads have landed (vmcnt in bits [3:0] and [15:14]).
+    constexpr int kWl = 4 * kXlDenseRing;
     __builtin_amdgcn_s_waitcnt((kWl & 15) | ((kWl >> 4) << 14) | 0x0F70);
     const int rq = a.H / 8, xst = a.H + kXlPad;  // chunks per token row; staged row stride
 #pragma unroll
@@ -1286,8 +1287,8 @@ k_dense_in_xl(const StepArgs a) {
             const uint16_t *xp = xr + (size_t)(s0 + i) * kKStep;
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                acc = mfma(as_bf16x8(w[i % kXlRing][j]), as_bf16x8(*(const u32x4 *)(xp + 32 * j)), acc);
-            if (i + kXlRing < ns) load_tile_bf16(A, s0 + i + kXlRing, w[i % kXlRing]);
+                acc = mfma(as_bf16x8(w[i % kXlDenseRing][j]), as_bf16x8(*(const u32x4 *)(xp + 32 * j)), acc);
+            if (i + kXlDenseRing < ns) load_tile_bf16(A, s0 + i + kXlDenseRing, w[i % kXlDenseRing]);
         }
     }
     const bool leader = reduce_k1(s_red, ro.wave, ro.kw, ro.KW, acc);

@@ -491,8 +491,8 @@ moe_status moe_decode_step(moe_decode_ctx *ctx, const uint16_t *x, int32_t batch
     // Above 16 tokens the dense-in launch stages x in LDS per row group of 8
     // tiles and splits K into slices, about two units per compute unit.
     const bool kx = pl.ncg_in >= 2 && pl.latent_rows == 16 && pl.router_rows == 16;
-    // Up to 2 tokens: x staged in LDS, four weight steps in flight per wave
-    // (K3 batch 1: 32.0 -> 29.5 us).
+    // Up to 2 tokens: x staged in LDS, six weight steps in flight per wave
+    // (K3 batch 1: 32.0 -> 28.5 us).
     const bool xl = batch <= kXlTokens && pl.in.spc >= kXlRing && pl.in.spc <= kMaxStepsPerChunk &&
                     c.hidden <= kMaxDenseK && a.route_units == 0;
     auto dense_launch = [&](hipStream_t st, StepArgs &args) {
