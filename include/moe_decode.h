@@ -219,6 +219,8 @@ typedef struct {
     int32_t ordered;       /* 1 when the latent combine ran in a fixed order
                               (MOE_MODE_ORDERED): the step's outputs are the same bits
                               from run to run */
+    int32_t in_staged;     /* 1 when the dense-in launch staged x in LDS (at most two
+                              tokens), else 0 */
 } moe_decode_dispatch_info;
 moe_status moe_decode_last_dispatch(const moe_decode_ctx *ctx, moe_decode_dispatch_info *info);
 

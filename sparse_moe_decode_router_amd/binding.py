@@ -37,7 +37,8 @@ class DispatchInfo(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("batch", "top_k", "col_tiles", "split_in", "split_out", "split_w13",
                  "split_w2", "grid_in", "grid_w13", "grid_w2", "grid_out", "router_f32",
-                 "n_kernels", "fused", "grid_step", "out_staged", "routing", "ordered")]
+                 "n_kernels", "fused", "grid_step", "out_staged", "routing", "ordered",
+                  "in_staged")]
 
 
 class Debug(ctypes.Structure):

@@ -416,6 +416,7 @@ moe_status moe_decode_step(moe_decode_ctx *ctx, const uint16_t *x, int32_t batch
     d.n_kernels = fused ? 1 : tail ? 2 : side ? 6 + d.router_f32 : 4 + d.router_f32;
     d.grid_step = 0;
     d.out_staged = 0;
+    d.in_staged = 0;
     // One persistent workgroup per resident slot of `kernel` (the unit
     // queues do not rely on residency; this only sizes the grid).
     auto persistent_grid = [&](StepKernel kernel, long long units) {
@@ -493,8 +494,9 @@ moe_status moe_decode_step(moe_decode_ctx *ctx, const uint16_t *x, int32_t batch
     const bool kx = pl.ncg_in >= 2 && pl.latent_rows == 16 && pl.router_rows == 16;
     // Up to 2 tokens: x staged in LDS, six weight steps in flight per wave
     // (K3 batch 1: 32.0 -> 28.5 us).
-    const bool xl = batch <= kXlTokens && pl.in.spc >= kXlRing && pl.in.spc <= kMaxStepsPerChunk &&
-                    c.hidden <= kMaxDenseK && a.route_units == 0;
+    const bool xl = !fused && batch <= kXlTokens && pl.in.spc >= kXlRing &&
+                    pl.in.spc <= kMaxStepsPerChunk && c.hidden <= kMaxDenseK && a.route_units == 0;
+    d.in_staged = xl ? 1 : 0;
     auto dense_launch = [&](hipStream_t st, StepArgs &args) {
         if (xl) {
             const int rw_in = kWG / pl.in.kw;
