@@ -1109,9 +1109,29 @@ __device__ __forceinline__ void routing_units(const StepArgs &a, int units, Rout
                       (uint32_t)a.route_units - 1u;
         __syncthreads();
         if (*s_flag) {
-            for (int p = threadIdx.x; p < a.B * a.k; p += kWGThreads) {
-                s_route.idx[p] = (int16_t)load_agent(a.idx + p);
-                s_route.w[p] = load_agent(a.wsel + p);
+            // Every unit's selections into LDS: 16-byte coherent loads, all
+            // issued before the first use (one round trip).  The arrays are
+            // 256-byte aligned in the workspace, so the last chunk's bytes
+            // past B k are inside it; they are not used.
+            static_assert(kMaxBatch * kMaxTopK <= 2 * 4 * kWGThreads, "two chunks per thread");
+            const int P = a.B * a.k, nc = (P + 3) >> 2;
+            const rsrc_t ri = buf_rsrc(a.idx), rw = buf_rsrc(a.wsel);
+            u32x4 vi[2], vw[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int c = min((int)threadIdx.x + kWGThreads * h, nc - 1);
+                vi[h] = buf_ld16<true>(ri, (uint32_t)c * 16);
+                vw[h] = buf_ld16<true>(rw, (uint32_t)c * 16);
+            }
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int c = (int)threadIdx.x + kWGThreads * h;
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    if (4 * c + q < P) {
+                        s_route.idx[4 * c + q] = (int16_t)vi[h][q];
+                        s_route.w[4 * c + q] = __uint_as_float(vw[h][q]);
+                    }
             }
             __syncthreads();
             build_meta<false>(ra, s_route, kWG);

@@ -237,8 +237,10 @@ inline moe_status validate_config(const moe_decode_config *c) {
     const int ks[2] = {c->hidden, c->latent + c->shared_inter};
     for (int K : ks)
         if (choose_split(K / kKStep).kw == 0) return MOE_ERR_UNSUPPORTED;
-    // Offsets are formed in 32-bit ints where they index one token or pair.
-    if ((long long)c->hidden * c->shared_inter > (1LL << 31) ||
+    // Offsets are formed in 32-bit ints where they index one token or pair,
+    // and byte offsets into the shared gate/up matrix (2 Is rows of H bf16)
+    // in 32 bits.
+    if ((long long)c->hidden * c->shared_inter > (1LL << 29) ||
         (long long)c->n_experts * 2 * c->expert_inter > (1LL << 31))
         return MOE_ERR_UNSUPPORTED;
     if (row_groups(*c) > kMaxRowGroups) return MOE_ERR_UNSUPPORTED;  // implied by the above
