@@ -1086,7 +1086,37 @@ __global__ void __launch_bounds__(kBlock) k_router_f32(const StepArgs a) {
         if (lane == 0) s_last = last;
     }
     __syncthreads();
-    if (s_last) route_step(route_args(a), &s_route, kWavesPerBlock);
+    if (s_last) route_step<false>(route_args(a), &s_route, kWavesPerBlock);
+}
+
+// The last routing unit of a launch: every unit's selections into LDS
+// (16-byte coherent loads, all issued before the first use: one round trip;
+// the arrays are 256-byte aligned in the workspace, so the last chunk's bytes
+// past B k are inside it and unused), then the metadata.
+__device__ __forceinline__ void routed_meta(const StepArgs &a, const RouteArgs &ra, RouteLds &s_route) {
+    static_assert(kMaxBatch * kMaxTopK <= 2 * 4 * kWGThreads, "two chunks per thread");
+    const int P = a.B * a.k, nc = (P + 3) >> 2;
+    const rsrc_t ri = buf_rsrc(a.idx), rw = buf_rsrc(a.wsel);
+    u32x4 vi[2], vw[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int c = min((int)threadIdx.x + kWGThreads * h, nc - 1);
+        vi[h] = buf_ld16<true>(ri, (uint32_t)c * 16);
+        vw[h] = buf_ld16<true>(rw, (uint32_t)c * 16);
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int c = (int)threadIdx.x + kWGThreads * h;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            if (4 * c + q < P) {
+                s_route.idx[4 * c + q] = (int16_t)vi[h][q];
+                s_route.w[4 * c + q] = __uint_as_float(vw[h][q]);
+            }
+    }
+    __syncthreads();
+    build_meta<false, false>(ra, s_route, kWG);  // read by later launches only
+    if (threadIdx.x == 0) store_agent(&a.gctr[G_ROUTED], 0u);  // ready for the next step
 }
 
 // Routing units (large batches), after the `units` dense units of the
@@ -1108,35 +1138,73 @@ __device__ __forceinline__ void routing_units(const StepArgs &a, int units, Rout
                                              __HIP_MEMORY_SCOPE_AGENT) ==
                       (uint32_t)a.route_units - 1u;
         __syncthreads();
-        if (*s_flag) {
-            // Every unit's selections into LDS: 16-byte coherent loads, all
-            // issued before the first use (one round trip).  The arrays are
-            // 256-byte aligned in the workspace, so the last chunk's bytes
-            // past B k are inside it; they are not used.
-            static_assert(kMaxBatch * kMaxTopK <= 2 * 4 * kWGThreads, "two chunks per thread");
-            const int P = a.B * a.k, nc = (P + 3) >> 2;
-            const rsrc_t ri = buf_rsrc(a.idx), rw = buf_rsrc(a.wsel);
-            u32x4 vi[2], vw[2];
+        if (*s_flag) routed_meta(a, ra, s_route);
+    }
+}
+
+// Routing units of the large-batch dense-in launch when it holds the bf16
+// router (its router row groups store K-slice partial sums and never add
+// them): unit r routes tokens kRouteTokensTp r, ... once every router slice
+// has arrived.  Thread i takes token i / (4 n_rt), router tile t and lane
+// group g of the rest: it adds that token's partials of rows 4g .. 4g + 3 of
+// tile t over the slices in slice order (as the row groups' own slice sums
+// do), and writes scores and keys to global memory and, for the selection,
+// to LDS (kv: the x staging area, unused by routing units).  The workgroup
+// then selects each token's experts, and the last unit to finish builds the
+// metadata.  One round trip for the partials instead of a chain of slice
+// sums, router epilogues and key loads.
+__device__ __forceinline__ void routing_units_tp(const StepArgs &a, int units, RouteLds &s_route,
+                                                 float *kv, int *s_flag) {
+    static_assert(sizeof(s_route.cand_key) / sizeof(s_route.cand_key[0]) >= kRouteTokensTp,
+                  "a candidate row per selecting wave");
+    const int nsteps = a.H / kKStep, nsl = (nsteps + a.kx_sps_r - 1) / a.kx_sps_r;
+    const int n_rt = a.n_rtiles, ncg = (a.B + 15) >> 4, per = 4 * n_rt;
+    const rsrc_t rpart = buf_rsrc(a.part);
+    for (int r = (int)blockIdx.x - units; r >= 0 && r < a.route_units; r += gridDim.x) {
+        wg_wait(a, &a.gctr[G_ROUTER_DONE], (uint32_t)a.router_target);
+        const int i = threadIdx.x, j = i / per, t = (i % per) >> 2, g = i & 3;
+        const int b = kRouteTokensTp * r + j;
+        if (j < kRouteTokensTp && b < a.B) {
+            const int c = b >> 4, lane = (b & 15) + 16 * g;
+            u32x4 v[kMaxSlices];
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int c = min((int)threadIdx.x + kWGThreads * h, nc - 1);
-                vi[h] = buf_ld16<true>(ri, (uint32_t)c * 16);
-                vw[h] = buf_ld16<true>(rw, (uint32_t)c * 16);
+            for (int k = 0; k < kMaxSlices; ++k) {
+                const int kk = min(k, nsl - 1);
+                v[k] = buf_ld16<true>(rpart, (uint32_t)(((((size_t)kk * a.kx_tiles + t) * ncg + c) * kWave + lane) * 16));
             }
+            f32x4 sum = zero4();
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int c = (int)threadIdx.x + kWGThreads * h;
+            for (int k = 0; k < kMaxSlices; ++k)
+                if (k < nsl) sum += __builtin_bit_cast(f32x4, v[k]);
+            const int e = 16 * t + 4 * g;  // 16-row router tiles
+            const f32x4 bv = a.bias ? ldf4(a.bias + e) : zero4();
+            float *kr = kv + (size_t)j * 2 * kMaxExperts;
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    if (4 * c + q < P) {
-                        s_route.idx[4 * c + q] = (int16_t)vi[h][q];
-                        s_route.w[4 * c + q] = __uint_as_float(vw[h][q]);
-                    }
+            for (int q = 0; q < 4; ++q) {
+                const float sv = sigmoidf_(sum[q]), key = sv + bv[q];
+                a.score[(size_t)b * kMaxExperts + e + q] = sv;
+                a.key[(size_t)b * kMaxExperts + e + q] = key;
+                kr[e + q] = key;
+                kr[kMaxExperts + e + q] = sv;
             }
-            __syncthreads();
-            build_meta<false>(ra, s_route, kWG);
-            if (threadIdx.x == 0) store_agent(&a.gctr[G_ROUTED], 0u);  // ready for the next step
         }
+        __syncthreads();
+        // Wave j selects token kRouteTokensTp r + j (threshold selection, its
+        // own candidate row).
+        const RouteArgs ra = route_args(a);
+        const int jw = wave_index(), bb = kRouteTokensTp * r + jw;
+        if (jw < kRouteTokensTp && bb < a.B) {
+            const float *kr = kv + (size_t)jw * 2 * kMaxExperts;
+            topk_token<true, true>(ra, bb, s_route, true, kr, kr + kMaxExperts);
+        }
+        wait_vm_all();
+        __syncthreads();
+        if (threadIdx.x == 0)
+            *s_flag = __hip_atomic_fetch_add(&a.gctr[G_ROUTED], 1u, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT) ==
+                      (uint32_t)a.route_units - 1u;
+        __syncthreads();
+        if (*s_flag) routed_meta(a, ra, s_route);
     }
 }
 
@@ -1211,7 +1279,7 @@ k_dense_in(const StepArgs a) {
             dense_in_tile_n<false, NCG, Route>(a, ro, kind, tl, active, 0, s_red, &s_last);
         if constexpr (Route) {
             if (s_last && !a.route_units) {  // this workgroup completed the router: route the step
-                route_step(route_args(a), &s_rs.s, kWG);
+                route_step<false>(route_args(a), &s_rs.s, kWG);
                 __syncthreads();
                 if (threadIdx.x == 0) s_last = 0;
             }
@@ -1318,7 +1386,7 @@ k_dense_in_xl(const StepArgs a) {
     }
     if constexpr (Route) {
         __syncthreads();  // s_last is set; every wave is done with x
-        if (s_last) route_step(route_args(a), &s_u.route, kWG);
+        if (s_last) route_step<false>(route_args(a), &s_u.route, kWG);
     }
 }
 
@@ -1360,9 +1428,11 @@ __device__ __forceinline__ void sum_slices(rsrc_t rpart, int nsl, int T, int t, 
 // go to a.part; the last slice of a row group to arrive sums them in slice
 // order and runs the tile epilogues, so the results do not depend on the
 // order of arrival.  The router's row groups come first, in slices of
-// a.kx_sps_r steps: shorter units, done early in the launch, so that the
-// routing that waits for the router runs while the other row groups still
-// stream their weights.
+// a.kx_sps_r steps: shorter units, done early in the launch.  Their slices
+// only store partial sums and arrive on the router counter; the routing
+// units (routing_units_tp) add each token's router partials themselves, so
+// that the routing runs while the other row groups still stream their
+// weights.
 constexpr int kXRows = 64;  // token rows of one staged step
 
 // Copies the x columns of step s into buf: row b (token b; rows past B copy
@@ -1392,6 +1462,8 @@ template <int NCG>
 __global__ void __launch_bounds__(kWGThreads) __attribute__((amdgpu_waves_per_eu(4)))
 k_dense_in_kx(const StepArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t s_x[2][kXRows * kKStep];
+    static_assert(sizeof(s_x) >= kRouteTokensTp * 2 * kMaxExperts * sizeof(float),
+                  "routing units keep their tokens' keys and scores in the x staging area");
     __shared__ RouteLds s_route;
     __shared__ int s_last, s_arrive;
     const int lane = lane_id(), wave = wave_index(), g = lane >> 4;
@@ -1454,12 +1526,17 @@ k_dense_in_kx(const StepArgs a) {
         wait_vm_all();
         __syncthreads();
         uint32_t *rgc = a.rgc + (size_t)(a.dense_lo ? a.kx_groups : 0) * kCtrStride + (size_t)rg * kCtrStride;
-        if (threadIdx.x == 0)
+        if (threadIdx.x == 0) {
             s_arrive = __hip_atomic_fetch_add(rgc, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
                        (uint32_t)nsl - 1u;
+            // A router slice's partials are complete: the routing units add them.
+            if (short_sl)
+                __hip_atomic_fetch_add(&a.gctr[G_ROUTER_DONE], 1u, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+        }
         __syncthreads();
         if (s_arrive) {  // the row group's last slice: sum the slices in order
-            if (active) {
+            if (active && kind != KIND_ROUTER) {
                 f32x4 sum[NCG];
                 sum_slices<NCG>(rpart, nsl, a.kx_tiles, t, sum);
                 dense_in_epilogue<false, NCG>(a, kind, tt, 0, sum, &s_last);
@@ -1468,7 +1545,10 @@ k_dense_in_kx(const StepArgs a) {
         }
         __syncthreads();
     }
-    routing_units(a, units, s_route, &s_last);
+    if (a.kx_rg_r > 0)
+        routing_units_tp(a, units, s_route, (float *)&s_x[0][0], &s_last);
+    else
+        routing_units(a, units, s_route, &s_last);
     prefetch_units(a, units + a.route_units);
 }
 
@@ -1991,7 +2071,7 @@ k_step(const StepArgs a) {
                           &s_last);
             if (router) {
                 if (s_last) {  // this workgroup completed the router: route the step
-                    route_step(route_args(a), s_route, kWG);
+                    route_step<true>(route_args(a), s_route, kWG);
                     if (threadIdx.x == 0) s_last = 0;
                     wg_publish(&a.gctr[G_ROUTED]);
                 }

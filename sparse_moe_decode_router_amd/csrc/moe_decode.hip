@@ -520,11 +520,27 @@ moe_status moe_decode_step(moe_decode_ctx *ctx, const uint16_t *x, int32_t batch
         const int nsteps = c.hidden / kKStep;
         const int nrg = cdiv(args.dense_hi - args.dense_lo, kWG);
         args.kx_rg_r = args.dense_lo == 0 && pl.n_rtiles > 0 ? std::min(nrg, cdiv(pl.n_rtiles, kWG)) : 0;
-        args.kx_sps_r = cdiv(nsteps, std::min(kMaxSlices, nsteps));
-        const int units_r = args.kx_rg_r * cdiv(nsteps, args.kx_sps_r);
         const int nrg_o = nrg - args.kx_rg_r;
-        const int slots = 2 * ctx->n_cus - units_r - args.route_units - args.pf_units;
-        int nsl = nrg_o > 0 ? std::max(1, std::min({kMaxSlices, nsteps, slots / nrg_o})) : 1;
+        auto slices_o = [&](int units_r, int route) {
+            const int slots = 2 * ctx->n_cus - units_r - route - args.pf_units;
+            return nrg_o > 0 ? std::max(1, std::min({kMaxSlices, nsteps, slots / nrg_o})) : 1;
+        };
+        int sps_r = cdiv(nsteps, std::min(kMaxSlices, nsteps));
+        if (args.kx_rg_r > 0) {
+            // The routing units add the router's slices (kRouteTokensTp
+            // tokens each, one round trip): more of them than with keys in
+            // memory.  The router slices lengthen until the other row groups
+            // keep the slice count they would have next to cdiv(B, 8)
+            // routing units; the router counter counts router slices.
+            const int want = slices_o(args.kx_rg_r * cdiv(nsteps, sps_r), args.route_units);
+            args.route_units = cdiv(batch, kRouteTokensTp);
+            while (sps_r < nsteps && slices_o(args.kx_rg_r * cdiv(nsteps, sps_r), args.route_units) < want)
+                ++sps_r;
+            args.router_target = args.kx_rg_r * cdiv(nsteps, sps_r);
+        }
+        args.kx_sps_r = sps_r;
+        const int units_r = args.kx_rg_r * cdiv(nsteps, args.kx_sps_r);
+        int nsl = slices_o(units_r, args.route_units);
         args.kx_sps = cdiv(nsteps, nsl);
         nsl = cdiv(nsteps, args.kx_sps);
         launch_on(st, dense_in_kx[pl.ncg_in - 1],

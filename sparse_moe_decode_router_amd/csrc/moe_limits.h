@@ -45,6 +45,14 @@ enum { M_N_ACTIVE = 0, M_N_COLS = 1, M_COUNT = 16 };
 // then the token and the routing weight (f32 bits) of each pair.
 enum { R_EXPERT = 0, R_COUNT = 1, R_PAIR0 = 2, R_TOKEN = 8, R_WEIGHT = 16, kRecWords = 32 };
 
+constexpr int kMaxSlices = 16;     // K slices of the large-batch dense-in kernel
+constexpr int kMaxSlicesOut = 8;   // ... and of the large-batch output kernel
+
+// Tokens per routing unit of the large-batch dense-in launch when that
+// launch holds the bf16 router (the units add the router's K-slice partial
+// sums themselves).
+constexpr int kRouteTokensTp = 2;
+
 // Ordered latent combine: one arrival counter per (token, tile group of the
 // down kernel), tile groups of at least 64 latent rows, counters 64 bytes
 // apart.

@@ -130,8 +130,6 @@ inline int dense_tiles(const moe_decode_config &c) {
     return (c.router_dtype == MOE_ROUTER_BF16 ? c.n_experts / 16 : 0) + c.latent / 16 +
            c.shared_inter / 8;
 }
-constexpr int kMaxSlices = 16;     // K slices of the large-batch dense-in kernel
-constexpr int kMaxSlicesOut = 8;   // ... and of the large-batch output kernel
 constexpr int kMaxGroupsOut = 8;   // column groups of 8 tokens per output unit
 
 // The counter area has one size for every configuration, so that contexts of

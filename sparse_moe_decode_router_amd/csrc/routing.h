@@ -312,12 +312,16 @@ __device__ __forceinline__ void select_by_rounds(const uint32_t (&ok)[kKeysPerLa
 // (agent-scope loads) and the selections go to them (agent-scope stores);
 // otherwise the keys come from an earlier launch and the selections are
 // written to global memory only when `global` (LDS always).
-template <bool Agent, typename Lds>
-__device__ __forceinline__ void topk_token(const RouteArgs &a, int b, Lds &lds, bool global = true) {
+// FromLds: the keys and scores are read from kr and sr (LDS rows of
+// kMaxExperts entries written before a workgroup barrier), and the threshold
+// selection takes wave w's candidate row w of lds.
+template <bool Agent, bool FromLds = false, typename Lds>
+__device__ __forceinline__ void topk_token(const RouteArgs &a, int b, Lds &lds, bool global = true,
+                                           const float *kr = nullptr, const float *sr = nullptr) {
     const int lane = lane_id();
     const int E = a.E, k = a.k;
-    const float *keyrow = a.key + (size_t)b * kMaxExperts;  // rows padded to kMaxExperts
-    const float *srow = a.score + (size_t)b * kMaxExperts;
+    const float *keyrow = FromLds ? kr : a.key + (size_t)b * kMaxExperts;  // rows padded to kMaxExperts
+    const float *srow = FromLds ? sr : a.score + (size_t)b * kMaxExperts;
     const int nk = (E + kWave - 1) / kWave;
     // All loads first, then their uses: the compiler keeps atomic loads in
     // program order, so a use between two of them would serialise the round
@@ -326,11 +330,11 @@ __device__ __forceinline__ void topk_token(const RouteArgs &a, int b, Lds &lds, 
     float sc[kKeysPerLane];
 #pragma unroll
     for (int i = 0; i < kKeysPerLane; ++i)
-        ok[i] = __float_as_uint(Agent ? load_agent(keyrow + lane + kWave * i)
-                                      : keyrow[lane + kWave * i]);
+        ok[i] = __float_as_uint(Agent && !FromLds ? load_agent(keyrow + lane + kWave * i)
+                                                  : keyrow[lane + kWave * i]);
 #pragma unroll
     for (int i = 0; i < kKeysPerLane; ++i)
-        sc[i] = Agent ? load_agent(srow + lane + kWave * i) : srow[lane + kWave * i];
+        sc[i] = Agent && !FromLds ? load_agent(srow + lane + kWave * i) : srow[lane + kWave * i];
 #pragma unroll
     for (int i = 0; i < kKeysPerLane; ++i) {
         const bool in = i < nk && lane + kWave * i < E;
@@ -338,11 +342,11 @@ __device__ __forceinline__ void topk_token(const RouteArgs &a, int b, Lds &lds, 
     }
     int mine = 0;
     float s_mine = 0.f;
-    // The routing inside the dense-in launch takes the rounds: the threshold
-    // selection's registers would spill there, in a kernel whose other code
-    // needs them all.
+    // The routing inside the dense-in launch takes the rounds when it loads
+    // the keys from memory: the threshold selection's registers would spill
+    // there, in a kernel whose other code needs them all.
     bool done = false;
-    if constexpr (!Agent) {
+    if constexpr (!Agent || FromLds) {
         const int wv = wave_index();
         done = select_by_threshold(ok, sc, k, lds.cand_key[wv], lds.cand_id[wv], lds.cand_s[wv],
                                    mine, s_mine);
@@ -559,7 +563,20 @@ __device__ void topk_token_wg(const RouteArgs &a, int b, Lds &lds, bool global =
 // expert units of other workgroups read it within the same launch.
 // ToLds: the records go to lds.rec (and the unit count to lds.ncols) for the
 // workgroup's own use, and nothing is written to global memory.
-template <bool ToLds, typename Lds>
+// A store of the routing metadata: agent-scope (written through to the
+// device's coherent level) when workgroups of the same launch read it, plain
+// when only later launches do (the kernel boundary publishes it; a plain
+// store stays in the writer's L2 until then and costs the routing workgroup
+// far less under a full memory stream).
+template <bool Agent, typename T>
+__device__ __forceinline__ void meta_store(T *p, T v) {
+    if constexpr (Agent)
+        store_agent(p, v);
+    else
+        *p = v;
+}
+
+template <bool ToLds, bool Agent = true, typename Lds>
 __device__ __forceinline__ void build_meta(const RouteArgs &a, Lds &lds, int nw) {
     const int lane = lane_id(), wave = wave_index();
     const int tid = threadIdx.x, nt = nw * kWave;
@@ -603,8 +620,8 @@ __device__ __forceinline__ void build_meta(const RouteArgs &a, Lds &lds, int nw)
         lds.unit[e] = ci;
         if (!n) continue;
         if (!ToLds) {
-            store_agent(a.act_expert + ai, e);
-            store_agent(a.act_off + ai, pi);
+            meta_store<Agent>(a.act_expert + ai, e);
+            meta_store<Agent>(a.act_off + ai, pi);
         }
         for (int r = 0; r < n; r += 8, ++ci) {
             if (ToLds) {
@@ -613,9 +630,9 @@ __device__ __forceinline__ void build_meta(const RouteArgs &a, Lds &lds, int nw)
                 lds.rec[ci][R_PAIR0] = pi + r;
             } else {
                 int32_t *rec = a.cu_rec + (size_t)ci * kRecWords;
-                store_agent(rec + R_EXPERT, e);
-                store_agent(rec + R_COUNT, min(8, n - r));
-                store_agent(rec + R_PAIR0, pi + r);
+                meta_store<Agent>(rec + R_EXPERT, e);
+                meta_store<Agent>(rec + R_COUNT, min(8, n - r));
+                meta_store<Agent>(rec + R_PAIR0, pi + r);
             }
         }
         ++ai;
@@ -631,11 +648,11 @@ __device__ __forceinline__ void build_meta(const RouteArgs &a, Lds &lds, int nw)
             rec[R_TOKEN + (r & 7)] = b;
             rec[R_WEIGHT + (r & 7)] = __float_as_int(lds.w[p]);
         } else {
-            store_agent(a.pair_slot + pos, p);
-            store_agent(a.pair_of_slot + p, pos);
+            meta_store<Agent>(a.pair_slot + pos, p);
+            meta_store<Agent>(a.pair_of_slot + p, pos);
             int32_t *rec = a.cu_rec + (size_t)(lds.unit[e] + (r >> 3)) * kRecWords;
-            store_agent(rec + R_TOKEN + (r & 7), b);
-            store_agent(rec + R_WEIGHT + (r & 7), __float_as_int(lds.w[p]));
+            meta_store<Agent>(rec + R_TOKEN + (r & 7), b);
+            meta_store<Agent>(rec + R_WEIGHT + (r & 7), __float_as_int(lds.w[p]));
         }
     }
     if (tid == 0) {
@@ -643,9 +660,9 @@ __device__ __forceinline__ void build_meta(const RouteArgs &a, Lds &lds, int nw)
             lds.ncols = NC;
             lds.n_active = D;
         } else {
-            store_agent(a.meta + M_N_ACTIVE, D);
-            store_agent(a.meta + M_N_COLS, NC);
-            store_agent(a.act_off + D, PT);
+            meta_store<Agent>(a.meta + M_N_ACTIVE, D);
+            meta_store<Agent>(a.meta + M_N_COLS, NC);
+            meta_store<Agent>(a.act_off + D, PT);
         }
     }
 }
@@ -653,13 +670,16 @@ __device__ __forceinline__ void build_meta(const RouteArgs &a, Lds &lds, int nw)
 // The whole routing of the step, by every wave of the workgroup whose router
 // arrival completed the router (all waves call it, after a workgroup
 // barrier).  Tokens are split across the waves; the selections meet in LDS.
+// Agent: workgroups of the same launch read the metadata (the persistent
+// step); otherwise only later launches do.
+template <bool Agent>
 __device__ __forceinline__ void route_step(const RouteArgs &a, RouteLds *lds, int nwaves) {
     if (a.B == 1 && nwaves == kWG)
         topk_token_wg<true>(a, 0, *lds);
     else
         for (int b = wave_index(); b < a.B; b += nwaves) topk_token<true>(a, b, *lds);
     __syncthreads();
-    build_meta<false>(a, *lds, nwaves);
+    build_meta<false, Agent>(a, *lds, nwaves);
 }
 
 // The routing at the start of the gate/up launch (B k <= kLatePairs; the keys
