@@ -1148,10 +1148,10 @@ __device__ __forceinline__ void routing_units(const StepArgs &a, int units, Rout
 // has arrived.  Thread i takes token i / (4 n_rt), router tile t and lane
 // group g of the rest: it adds that token's partials of rows 4g .. 4g + 3 of
 // tile t over the slices in slice order (as the row groups' own slice sums
-// do), and writes scores and keys to global memory and, for the selection,
-// to LDS (kv: the x staging area, unused by routing units).  The workgroup
-// then selects each token's experts, and the last unit to finish builds the
-// metadata.  One round trip for the partials instead of a chain of slice
+// do) and keeps scores and keys in LDS (kv: the x staging area, unused by
+// routing units).  Waves 0 .. kRouteTokensTp - 1 then select one token's
+// experts each, the last unit to finish builds the metadata, and the scores
+// and keys go to global memory last.  One round trip for the partials instead of a chain of slice
 // sums, router epilogues and key loads.
 __device__ __forceinline__ void routing_units_tp(const StepArgs &a, int units, RouteLds &s_route,
                                                  float *kv, int *s_flag) {
@@ -1181,10 +1181,8 @@ __device__ __forceinline__ void routing_units_tp(const StepArgs &a, int units, R
             float *kr = kv + (size_t)j * 2 * kMaxExperts;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const float sv = sigmoidf_(sum[q]), key = sv + bv[q];
-                a.score[(size_t)b * kMaxExperts + e + q] = sv;
-                a.key[(size_t)b * kMaxExperts + e + q] = key;
-                kr[e + q] = key;
+                const float sv = sigmoidf_(sum[q]);
+                kr[e + q] = sv + bv[q];
                 kr[kMaxExperts + e + q] = sv;
             }
         }
@@ -1205,6 +1203,19 @@ __device__ __forceinline__ void routing_units_tp(const StepArgs &a, int units, R
                       (uint32_t)a.route_units - 1u;
         __syncthreads();
         if (*s_flag) routed_meta(a, ra, s_route);
+        // The units' scores and keys for later launches and the caller, from
+        // LDS with 16-byte stores once the selections are published: off
+        // the routing's chain of round trips.
+        const int q4n = a.E / 4;
+        for (int x = threadIdx.x; x < kRouteTokensTp * q4n; x += kWGThreads) {
+            const int jj = x / q4n, e4 = 4 * (x % q4n), bq = kRouteTokensTp * r + jj;
+            if (bq < a.B) {
+                const float *kr = kv + (size_t)jj * 2 * kMaxExperts;
+                stf4(a.key + (size_t)bq * kMaxExperts + e4, *(const f32x4 *)(kr + e4));
+                stf4(a.score + (size_t)bq * kMaxExperts + e4, *(const f32x4 *)(kr + kMaxExperts + e4));
+            }
+        }
+        __syncthreads();  // kv is read before a next unit of this workgroup writes it
     }
 }
 
