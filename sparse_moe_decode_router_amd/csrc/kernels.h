@@ -1830,8 +1830,8 @@ k_out(const StepArgs a) {
 // the hi or lo half when it reads them) and the hi/lo rows of the shared
 // activation at shared-down steps (128 rows of 128 bf16).  Each slice adds
 // every token's hi and lo columns before it stores its partial sums (half the
-// partial bytes); the tile's last slice adds the partials in slice order and
-// rounds to bf16 once.
+// partial bytes) and arrives on its row group's counter; sum units after the
+// slices in the grid add the partials in slice order and round to bf16 once.
 constexpr int kOutStage = 32768;  // bytes of one staged step (both kinds)
 
 __device__ __forceinline__ void stage_out_step(char *buf, const StepArgs &a, int s, int Ls) {
@@ -1900,7 +1900,6 @@ template <int NCG>
 __global__ void __launch_bounds__(kWGThreads) __attribute__((amdgpu_waves_per_eu(4)))
 k_out_kx(const StepArgs a) {
     __shared__ __attribute__((aligned(16))) char s_o[2][kOutStage];
-    __shared__ int s_arrive;
     // The router counter of the dense input kernel is cleared here, as in k_out.
     if (blockIdx.x == 0 && threadIdx.x == 0) a.gctr[G_ROUTER_DONE] = 0u;
     const int lane = lane_id(), wave = wave_index(), n = lane & 15, g = lane >> 4;
@@ -1959,32 +1958,60 @@ k_out_kx(const StepArgs a) {
         }
         wait_vm_all();
         __syncthreads();
-        uint32_t *rgc = a.rgc + (size_t)rg * kCtrStride;
         if (threadIdx.x == 0)
-            s_arrive = __hip_atomic_fetch_add(rgc, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                       (uint32_t)nsl - 1u;
-        __syncthreads();
-        if (s_arrive) {  // the tiles' last slice: sum the slices in order, round once
-            if (active) {
-                f32x4 sums[NCG / 2];
-                sum_slices<NCG / 2>(rpart, nsl, n_ot, t, sums);
+            __hip_atomic_fetch_add(a.rgc + (size_t)rg * kCtrStride, 1u, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+    }
+    // Sum units, after the slice units in the grid (so dispatched only once
+    // every slice unit has been): unit s adds, in slice order, the partial
+    // sums of tiles 8 rg + 4 h .. + 3 (rg = s / 2, h = s % 2) once all nsl
+    // slices of row group rg have arrived, and rounds to bf16 once.  Thread
+    // i takes chunks i and i + 512 of the half's 4 tiles x NCG / 2 groups x
+    // 64 lanes: every slice's load in one round trip (the slices' last
+    // arrival summing all 8 tiles took two).
+    constexpr int kSumChunks = 4 * (NCG / 2) * kWave;
+    constexpr int kSumPer = (kSumChunks + kWGThreads - 1) / kWGThreads;
+    const int nrg = (n_ot + kWG - 1) / kWG;
+    for (int su = (int)blockIdx.x - units; su >= 0 && su < 2 * nrg; su += gridDim.x) {
+        const int rg = su >> 1, hf = su & 1;
+        uint32_t *rgc = a.rgc + (size_t)rg * kCtrStride;
+        wg_wait(a, rgc, (uint32_t)nsl);
+        u32x4 v[kSumPer][kMaxSlicesOut];
 #pragma unroll
-                for (int c = 0; c < NCG / 2; ++c) {
-                    const f32x4 v = sums[c];
-                    const int b = 8 * (2 * c + (n & 1)) + (n >> 1);
-                    if (b < a.B) {
-                        const size_t o = (size_t)b * a.H + h0;
+        for (int q = 0; q < kSumPer; ++q) {
+            const int x = min((int)threadIdx.x + kWGThreads * q, kSumChunks - 1);
+            const int t = min(kWG * rg + 4 * hf + x / ((NCG / 2) * kWave), n_ot - 1);
+            const int c = (x / kWave) % (NCG / 2), l = x % kWave;
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const int r = 4 * g + i;
-                            if (r < RT && h0 + r < a.H) a.out[o + r] = (uint16_t)bf16_rne(v[i]);
-                        }
-                    }
+            for (int k = 0; k < kMaxSlicesOut; ++k) {
+                const int kk = min(k, nsl - 1);
+                v[q][k] = buf_ld16<true>(rpart, (uint32_t)(((((size_t)kk * n_ot + t) * (NCG / 2) + c) * kWave + l) * 16));
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < kSumPer; ++q) {
+            const int x = (int)threadIdx.x + kWGThreads * q;
+            const int t = kWG * rg + 4 * hf + x / ((NCG / 2) * kWave);
+            const int c = (x / kWave) % (NCG / 2), l = x % kWave, ln = l & 15, lg = l >> 4;
+            f32x4 sum = zero4();
+#pragma unroll
+            for (int k = 0; k < kMaxSlicesOut; ++k)
+                if (k < nsl) sum += __builtin_bit_cast(f32x4, v[q][k]);
+            const int b = 8 * (2 * c + (ln & 1)) + (ln >> 1), h0 = RT * t;
+            if (x < kSumChunks && t < n_ot && b < a.B) {
+                const size_t o = (size_t)b * a.H + h0;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = 4 * lg + i;
+                    if (r < RT && h0 + r < a.H) a.out[o + r] = (uint16_t)bf16_rne(sum[i]);
                 }
             }
-            if (threadIdx.x == 0) store_agent(rgc, 0u);  // ready for the next step
         }
-        __syncthreads();
+        // Each half arrives once more after its wait; the second resets the
+        // counter for the next step.
+        if (threadIdx.x == 0 &&
+            __hip_atomic_fetch_add(rgc, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)nsl + 1u)
+            store_agent(rgc, 0u);
     }
 }
 

@@ -599,7 +599,7 @@ moe_status moe_decode_step(moe_decode_ctx *ctx, const uint16_t *x, int32_t batch
         nsl = cdiv(nsteps, a.kx_sps_out);
         const StepKernel out_kx = pl.ncg_out <= 2 ? k_out_kx<2> : pl.ncg_out <= 4 ? k_out_kx<4>
                                                                                     : k_out_kx<8>;
-        launch(out_kx, (unsigned)(nrg * nsl), kWGThreads);
+        launch(out_kx, (unsigned)(nrg * nsl + 2 * nrg), kWGThreads);  // slice units, then sum units
     } else {
         // Up to two tokens the column operands of the whole reduction fit in
         // LDS, up to eight their ylat part: staged once per workgroup.
