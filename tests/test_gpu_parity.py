@@ -153,10 +153,15 @@ def test_intermediates_match_oracle(small_layer, small_ctx):
     assert dbg["n_active"][0] == len(np.unique(idx))
 
 
-def test_f32_router_layer_several_tokens():
+@pytest.mark.parametrize("B", [12, 33])
+def test_f32_router_layer_several_tokens(B):
+    """f32 router (its own launch first): routing units that load the keys
+    from memory, beside the dense-in kernel of up to 16 tokens and beside the
+    K-sliced one above 16."""
+    log(f"f32 router B={B}")
     layer = synth.make_layer(small_recipe(router_f32=True, bias="none", k=4), 5)
-    ctx = make_ctx(layer, 12)
-    x = synth.make_tokens(layer.dims, 5, 12)
+    ctx = make_ctx(layer, B)
+    x = synth.make_tokens(layer.dims, 5, B)
     out, idx, w = run(ctx, x, 4)
     check_step(layer, x, 4, out, idx, w)
     assert ctx.last_dispatch()["n_kernels"] == 5
@@ -182,7 +187,7 @@ def test_zero_router_picks_lowest_ids_with_equal_weights(form):
 
 
 @pytest.mark.parametrize("form", ROUTING_FORMS)
-@pytest.mark.parametrize("B", [4, 12])
+@pytest.mark.parametrize("B", [4, 12, 20])
 @pytest.mark.parametrize("k,want", [(5, [3, 7, 69, 130, 200]),
                                     (8, [3, 7, 69, 130, 131, 192, 200, 250])])
 def test_ties_at_the_threshold_go_to_the_lowest_ids(B, k, want, form):
@@ -191,7 +196,8 @@ def test_ties_at_the_threshold_go_to_the_lowest_ids(B, k, want, form):
     them, also when the cut falls between two ids of one slot (130 taken,
     131 not).  Zero router: every score is 0.5, so the keys are exactly
     1.5, 0.75 or 0.5 and the weights 1/k.  B = 12 routes through the routing
-    units."""
+    units, B = 20 through the ones that add the K-sliced router's partials
+    (with more than 64 keys at the threshold: the rounds)."""
     layer = synth.make_layer(small_recipe(E=256, bias="none", k=k), 11)
     layer.router_w[:] = 0
     layer.bias = np.zeros(256, np.float32)
@@ -220,13 +226,14 @@ def test_hot_experts_serve_every_token():
 
 
 @pytest.mark.parametrize("form", ROUTING_FORMS)
-def test_all_experts_selected(form):
+@pytest.mark.parametrize("B", [3, 20])
+def test_all_experts_selected(form, B):
     layer = synth.make_layer(small_recipe(E=32, k=32), 9)
-    ctx = make_ctx(layer, 3)
+    ctx = make_ctx(layer, B)
     ctx.set_mode(mode_const(form))
-    x = synth.make_tokens(layer.dims, 9, 3)
+    x = synth.make_tokens(layer.dims, 9, B)
     out, idx, w = run(ctx, x, 32)
-    np.testing.assert_array_equal(idx, np.tile(np.arange(32), (3, 1)))
+    np.testing.assert_array_equal(idx, np.tile(np.arange(32), (B, 1)))
     check_step(layer, x, 32, out, idx, w)
 
 
