@@ -275,9 +275,9 @@ def kernel_durations(ctx, names, kb, xd, k, out, idx, wts, steps, stream, out_st
         B = ctx.last_dispatch()["batch"]
         if n == "out":  # the output kernel's forms: K slices above 8 tokens, staged operands up to 8
             sym = "k_out_kx" if B > 8 else "k_out_st" if out_staged else sym
-        elif n == "dense_in" and B > 16:  # x staged per row group, K slices
+        elif n == "dense_in" and ctx.last_dispatch().get("in_staged") == 2:  # x per row group, K slices
             sym = "k_dense_in_kx"
-        elif n == "dense_in" and ctx.last_dispatch().get("in_staged"):  # x staged, up to 2 tokens
+        elif n == "dense_in" and ctx.last_dispatch().get("in_staged") == 1:  # x staged, up to 2 tokens
             sym = "k_dense_in_xl"
         per_kernel[n] = {"symbol": sym, "us": round(avg_ms * 1e3, 2),
                          "bytes": int(avg_bytes), "gbs": round(gbs, 1),

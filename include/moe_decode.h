@@ -219,8 +219,11 @@ typedef struct {
     int32_t ordered;       /* 1 when the latent combine ran in a fixed order
                               (MOE_MODE_ORDERED): the step's outputs are the same bits
                               from run to run */
-    int32_t in_staged;     /* 1 when the dense-in launch staged x in LDS (at most two
-                              tokens), else 0 */
+    int32_t in_staged;     /* how the dense-in launch read x: 0 through the caches per
+                              tile, 1 staged in LDS once per workgroup (at most two
+                              tokens), 2 staged in LDS per row group and step with K
+                              split into slices (above 16 tokens, and from 9 when
+                              the launch fits one round of resident workgroups) */
 } moe_decode_dispatch_info;
 moe_status moe_decode_last_dispatch(const moe_decode_ctx *ctx, moe_decode_dispatch_info *info);
 

@@ -342,6 +342,14 @@ moe_status moe_decode_step(moe_decode_ctx *ctx, const uint16_t *x, int32_t batch
     // of resident workgroups, where the routing at its end would be a tail
     // with the memory idle (a launch of more rounds hides it under its last
     // round, and the gate/up workgroups would only pay for it again).
+    // 9 to 16 tokens in a dense-in launch of one round of resident
+    // workgroups (the TP8 share): the K-sliced dense-in kernel, whose router
+    // slices finish early and whose routing units overlap the other row
+    // groups' stream, where the routing after a one-round launch is a tail
+    // (TP8 share batch 16: 91.2 -> 87.6 us; K3, 1.4 rounds, stays: 208 -> 212
+    // at batch 9).
+    const bool kx_small = !fused && !tail && !side && batch > kWG && pl.ncg_in == 1 &&
+                          c.router_dtype == MOE_ROUTER_BF16 && pl.units_in <= 2LL * ctx->n_cus;
     const bool late_ok = c.router_dtype == MOE_ROUTER_BF16 && batch <= kWG &&
                          batch * top_k <= kLatePairs && !ctx->next &&
                          pl.units_13 <= (long long)kLateUnitsPerWG * late_grid;
@@ -487,16 +495,17 @@ moe_status moe_decode_step(moe_decode_ctx *ctx, const uint16_t *x, int32_t batch
     }
     const StepKernel dense_in[] = {late ? k_dense_in<1, false> : k_dense_in<1, true>,
                                    k_dense_in<2, true>, k_dense_in<3, true>, k_dense_in<4, true>};
-    const StepKernel dense_in_kx[] = {nullptr, k_dense_in_kx<2>, k_dense_in_kx<3>,
+    const StepKernel dense_in_kx[] = {k_dense_in_kx<1>, k_dense_in_kx<2>, k_dense_in_kx<3>,
                                       k_dense_in_kx<4>};
-    // Above 16 tokens the dense-in launch stages x in LDS per row group of 8
-    // tiles and splits K into slices, about two units per compute unit.
-    const bool kx = pl.ncg_in >= 2 && pl.latent_rows == 16 && pl.router_rows == 16;
+    // Above 16 tokens (and kx_small) the dense-in launch stages x in LDS per
+    // row group of 8 tiles and splits K into slices, about two units per
+    // compute unit.
+    const bool kx = (pl.ncg_in >= 2 || kx_small) && pl.latent_rows == 16 && pl.router_rows == 16;
     // Up to 2 tokens: x staged in LDS, six weight steps in flight per wave
     // (K3 batch 1: 32.0 -> 28.5 us).
     const bool xl = !fused && batch <= kXlTokens && pl.in.spc >= kXlRing &&
                     pl.in.spc <= kMaxStepsPerChunk && c.hidden <= kMaxDenseK && a.route_units == 0;
-    d.in_staged = xl ? 1 : 0;
+    d.in_staged = kx ? 2 : xl ? 1 : 0;
     auto dense_launch = [&](hipStream_t st, StepArgs &args) {
         if (xl) {
             const int rw_in = kWG / pl.in.kw;

@@ -206,7 +206,9 @@ inline Layout make_layout(const moe_decode_config &c) {
     // the same time (the ordered combine has no side stream).
     const size_t n_ot = (size_t)cdiv(c.hidden, out_tile_rows(c.hidden));
     const size_t ncg = (size_t)cdiv(c.max_batch, 16);
-    const size_t part_in = ncg >= 2 ? (size_t)kMaxSlices * dense_tiles(c) * ncg * kWave * 16 : 0;
+    // K-sliced dense-in partials: above 16 tokens, and from 9 where that kernel
+    // also serves (a dense-in launch of one round).
+    const size_t part_in = c.max_batch > kWG ? (size_t)kMaxSlices * dense_tiles(c) * ncg * kWave * 16 : 0;
     // The output kernel's column groups per unit: 2, 4 or 8 (ceil(B / 8) rounded up).
     const size_t gout = c.max_batch <= 16 ? 2 : c.max_batch <= 32 ? 4 : kMaxGroupsOut;
     const size_t part_out = c.max_batch > 8 ? kMaxSlicesOut * n_ot * gout * kWave * 16 : 0;

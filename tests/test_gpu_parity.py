@@ -352,6 +352,9 @@ def test_dispatch_follows_the_batch(small_layer, small_ctx):
         # Up to two tokens the output launch stages its whole operand in LDS,
         # up to eight its latent part.
         assert d["out_staged"] == (1 if B <= 2 else 2 if B <= 8 else 0)
+        # Above 16 tokens the dense-in launch splits K into slices; this
+        # small layer's launch also fits one round at 16.
+        assert d["in_staged"] == (2 if B >= 9 else 0 if B > 2 else d["in_staged"])
     try:
         for mode, fused, n in ((binding.MODE_FUSED, 1, 1), (binding.MODE_TWO_LAUNCHES, 2, 2),
                                (binding.MODE_SIDE_STREAM, 3, 6)):
@@ -654,13 +657,17 @@ def test_k3_spec_verify_batch(k3_layer, k3_dev, users, drafts):
 def test_k3_tp8_share_layer():
     layer = synth.make_layer(synth.K3_TP8, synth.TP8_STACK_SEED0)
     ctx = make_ctx(layer, 64, 16)
-    for B in (1, 64):
+    for B in (1, 9, 16, 64):
         log(f"K3 TP8 share B={B}")
         x = synth.make_tokens(layer.dims, 1, B)
         out, idx, w = run(ctx, x, 16)
+        d = ctx.last_dispatch()
         # Batch 1 leaves the gate/up kernel short of units (16 experts x 4
         # tile groups): eight waves share each tile.
-        assert ctx.last_dispatch()["split_w13"] == (8 if B == 1 else 1)
+        assert d["split_w13"] == (8 if B == 1 else 1)
+        # x staged once per workgroup up to two tokens; from 9 tokens this
+        # one-round dense-in launch splits K into slices.
+        assert d["in_staged"] == (1 if B == 1 else 2)
         r = check_step(layer, x, 16, out, idx, w)
         log("  ", r)
 
