@@ -296,7 +296,8 @@ moe_status moe_decode_set_next_layer(moe_decode_ctx *ctx, const moe_decode_ctx *
  * the workspace; call after the steps completed).  Bit 0 is set when a bounded
  * wait of any step on this workspace ran out: a persistent step's wait on a
  * completion counter, or, in the multi-launch forms, the wait of a routing
- * unit (batches above 8) or a prefetch unit for the router to complete.  The
+ * unit (batches above 8) or a prefetch unit for the router to complete, or of
+ * an output sum unit (batches above 8) for its row group's K slices.  The
  * step then finished instead of hanging, and its outputs are invalid.  The
  * flag stays set for the life of the workspace.  A wait runs out
  * only when the GPU does not run the step's workgroups concurrently (e.g.
