@@ -156,5 +156,5 @@ def run(ctx: binding.MoEDecode, x: np.ndarray, top_k: int):
     xd = to_dev_tokens(x)
     out, idx, w = ctx.step(xd, top_k)
     torch.cuda.synchronize()
-    assert ctx.read_flags() == 0, "a bounded wait of the fused step ran out"
+    assert ctx.read_flags() == 0, "a bounded wait of the step ran out"
     return (out.cpu().numpy().view(np.uint16), idx.cpu().numpy(), w.cpu().numpy())
