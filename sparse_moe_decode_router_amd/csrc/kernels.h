@@ -1151,8 +1151,8 @@ __device__ __forceinline__ void routing_units(const StepArgs &a, int units, Rout
 // do) and keeps scores and keys in LDS (kv: the x staging area, unused by
 // routing units).  Waves 0 .. kRouteTokensTp - 1 then select one token's
 // experts each, the last unit to finish builds the metadata, and the scores
-// and keys go to global memory last.  One round trip for the partials instead of a chain of slice
-// sums, router epilogues and key loads.
+// and keys go to global memory last.  One round trip for the partials
+// instead of a chain of slice sums, router epilogues and key loads.
 __device__ __forceinline__ void routing_units_tp(const StepArgs &a, int units, RouteLds &s_route,
                                                  float *kv, int *s_flag) {
     static_assert(sizeof(s_route.cand_key) / sizeof(s_route.cand_key[0]) >= kRouteTokensTp,
