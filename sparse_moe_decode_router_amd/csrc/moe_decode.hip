@@ -415,8 +415,12 @@ moe_status moe_decode_step(moe_decode_ctx *ctx, const uint16_t *x, int32_t batch
     const StepKernel w2_k = ordered ? (split2 ? kW2SplitOrd[pl.s2] : kW2Ord[pl.s2])
                                     : (split2 ? kW2Split[pl.s2] : kW2[pl.s2]);
     d.grid_in = (int32_t)(pl.units_in + a.route_units);  // every unit its own workgroup
-    d.grid_w13 = late ? (int32_t)late_grid : grid_for(pl.units_13, cap);
-    d.grid_w2 = grid_for(pl.units_2, cap);
+    // Expert grids for the expected column units (ncols_grid); the kernels
+    // loop over the rest.
+    const long long cols_all = ncols_cap(c.n_experts, batch, top_k);
+    const long long cols_grid = ncols_grid(c.n_experts, batch, top_k);
+    d.grid_w13 = late ? (int32_t)late_grid : grid_for(pl.units_13 / cols_all * cols_grid, cap);
+    d.grid_w2 = grid_for(pl.units_2 / cols_all * cols_grid, cap);
     d.grid_out = grid_for(pl.units_out, cap);
     d.router_f32 = c.router_dtype == MOE_ROUTER_F32;
     d.fused = fused ? 1 : tail ? 2 : side ? 3 : 0;

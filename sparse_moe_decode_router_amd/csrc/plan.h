@@ -9,6 +9,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <cmath>
 
 #include "moe_limits.h"
 #include "moe_decode.h"
@@ -38,6 +39,18 @@ inline Split choose_split(int nsteps) {
 // each split into units of <= 8 tokens (B k pairs give at most B k / 8 extra
 // units).
 inline int ncols_cap(int E, int B, int k) { return std::min(E, B * k) + cdiv(B * k, 8); }
+
+// Column units to size the expert launches for: the distinct experts that
+// B k uniformly spread selections would touch, E (1 - (1 - 1/E)^(B k)), plus
+// 10 %, at most the capacity.  The kernels loop over units with the grid
+// stride, so more units are still all processed; fewer leave fewer
+// workgroups that only read the unit count and exit (at 64 tokens on the
+// K3 layer the capacity is 1,024 units against about 620 used).
+inline int ncols_grid(int E, int B, int k) {
+    const double e = E, pk = (double)B * k;
+    const double d = e * (1.0 - std::pow(1.0 - 1.0 / e, pk));
+    return std::min(ncols_cap(E, B, k), (int)std::ceil(1.1 * d) + 1);
+}
 
 // Steps per staged chunk of the expert kernels: the largest divisor of
 // K / 128 that is at most 16.
