@@ -1145,11 +1145,11 @@ __device__ __forceinline__ void routing_units(const StepArgs &a, int units, Rout
 // Routing units of the large-batch dense-in launch when it holds the bf16
 // router (its router row groups store K-slice partial sums and never add
 // them): unit r routes tokens kRouteTokensTp r, ... once every router slice
-// has arrived.  Thread i takes token i / (4 n_rt), router tile t and lane
-// group g of the rest: it adds that token's partials of rows 4g .. 4g + 3 of
-// tile t over the slices in slice order (as the row groups' own slice sums
-// do) and keeps scores and keys in LDS (kv: the x staging area, unused by
-// routing units).  Waves 0 .. kRouteTokensTp - 1 then select one token's
+// has arrived.  Thread i takes token i / (E / 4) and experts 4q .. 4q + 3
+// (q = i % (E / 4)): it adds that token's router partials of those experts
+// over the slices in slice order (the router slices store them token-major
+// for this, so a wave's loads are contiguous) and keeps scores and keys in
+// LDS (kv: the x staging area, unused by routing units).  Waves 0 .. kRouteTokensTp - 1 then select one token's
 // experts each, the last unit to finish builds the metadata, and the scores
 // and keys go to global memory last.  One round trip for the partials
 // instead of a chain of slice sums, router epilogues and key loads.
@@ -1158,25 +1158,24 @@ __device__ __forceinline__ void routing_units_tp(const StepArgs &a, int units, R
     static_assert(sizeof(s_route.cand_key) / sizeof(s_route.cand_key[0]) >= kRouteTokensTp,
                   "a candidate row per selecting wave");
     const int nsteps = a.H / kKStep, nsl = (nsteps + a.kx_sps_r - 1) / a.kx_sps_r;
-    const int n_rt = a.n_rtiles, ncg = (a.B + 15) >> 4, per = 4 * n_rt;
-    const rsrc_t rpart = buf_rsrc(a.part);
+    const int per = a.E / 4;  // 16-byte chunks of a token's router row
+    const rsrc_t rrpart = buf_rsrc(a.rpart);
     for (int r = (int)blockIdx.x - units; r >= 0 && r < a.route_units; r += gridDim.x) {
         wg_wait(a, &a.gctr[G_ROUTER_DONE], (uint32_t)a.router_target);
-        const int i = threadIdx.x, j = i / per, t = (i % per) >> 2, g = i & 3;
+        const int i = threadIdx.x, j = i / per, q = i % per;
         const int b = kRouteTokensTp * r + j;
         if (j < kRouteTokensTp && b < a.B) {
-            const int c = b >> 4, lane = (b & 15) + 16 * g;
             u32x4 v[kMaxSlices];
 #pragma unroll
             for (int k = 0; k < kMaxSlices; ++k) {
                 const int kk = min(k, nsl - 1);
-                v[k] = buf_ld16<true>(rpart, (uint32_t)(((((size_t)kk * a.kx_tiles + t) * ncg + c) * kWave + lane) * 16));
+                v[k] = buf_ld16<true>(rrpart, (uint32_t)((((size_t)kk * a.B + b) * kMaxExperts + 4 * q) * 4));
             }
             f32x4 sum = zero4();
 #pragma unroll
             for (int k = 0; k < kMaxSlices; ++k)
                 if (k < nsl) sum += __builtin_bit_cast(f32x4, v[k]);
-            const int e = 16 * t + 4 * g;  // 16-row router tiles
+            const int e = 4 * q;
             const f32x4 bv = a.bias ? ldf4(a.bias + e) : zero4();
             float *kr = kv + (size_t)j * 2 * kMaxExperts;
 #pragma unroll
@@ -1488,7 +1487,7 @@ k_dense_in_kx(const StepArgs a) {
     const int nsl_r = (nsteps + a.kx_sps_r - 1) / a.kx_sps_r, nsl_o = (nsteps + a.kx_sps - 1) / a.kx_sps;
     const int nrg = (a.dense_hi - a.dense_lo + kWG - 1) / kWG;
     const int units_r = a.kx_rg_r * nsl_r, units = units_r + (nrg - a.kx_rg_r) * nsl_o;
-    const rsrc_t rpart = buf_rsrc(a.part);
+    const rsrc_t rpart = buf_rsrc(a.part), rrpart = buf_rsrc(a.rpart);
     for (int u = blockIdx.x; u < units; u += gridDim.x) {
         const bool short_sl = u < units_r;
         const int nsl = short_sl ? nsl_r : nsl_o, sps = short_sl ? a.kx_sps_r : a.kx_sps;
@@ -1527,8 +1526,18 @@ k_dense_in_kx(const StepArgs a) {
                         acc[c] = mfma(as_bf16x8(ra1[j]), x_operand(s_x[1], c, j), acc[c]);
             }
         }
-        // Partial sums of the slice, in MFMA layout: part[ks][t][c][lane].
-        if (active) {
+        // Partial sums of the slice, in MFMA layout: part[ks][t][c][lane];
+        // router tiles token-major for the routing units: rpart[ks][b][e]
+        // (lane (n, g) holds experts 16 tt + 4g .. + 3 of token 16c + n).
+        if (active && kind == KIND_ROUTER) {
+#pragma unroll
+            for (int c = 0; c < NCG; ++c) {
+                const int b = 16 * c + (lane & 15);
+                if (b < a.B)
+                    buf_st16<true>(rrpart, (uint32_t)((((size_t)ks * a.B + b) * kMaxExperts + 16 * tt + 4 * g) * 4),
+                                   __builtin_bit_cast(u32x4, acc[c]));
+            }
+        } else if (active) {
 #pragma unroll
             for (int c = 0; c < NCG; ++c)
                 buf_st16<true>(rpart, (uint32_t)(((((size_t)ks * a.kx_tiles + t) * NCG + c) * kWave + lane) * 16),

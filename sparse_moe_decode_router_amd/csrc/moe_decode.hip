@@ -199,6 +199,7 @@ StepArgs base_args(const moe_decode_ctx *ctx) {
     a.cctr = (uint32_t *)(ws + l.cctr);
     a.c13 = (uint32_t *)(ws + l.c13);
     a.part = (float *)(ws + l.part);
+    a.rpart = (float *)(ws + l.rpart);
     a.rgc = (uint32_t *)(ws + l.rgc);
     a.kx_tiles = dense_tiles(ctx->cfg);
     a.kx_groups = cdiv(a.kx_tiles, kWG);

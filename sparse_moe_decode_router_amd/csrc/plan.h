@@ -157,7 +157,7 @@ static_assert(kMaxCols >= kMaxExperts && kMaxRowGroups >= kMaxDenseK / 16 / kWG,
 
 struct Layout {
     size_t gctr, meta, c13, rgc, cctr, score, key, idx, wsel, act_expert, act_off, cu_rec,
-        pair_slot, pair_of_slot, zhl, ashhl, acthl, ylat, ysh, pout, part, total;
+        pair_slot, pair_of_slot, zhl, ashhl, acthl, ylat, ysh, pout, part, rpart, total;
     size_t counters_end;  // [0, counters_end) holds every counter: cleared at init
 };
 
@@ -225,7 +225,12 @@ inline Layout make_layout(const moe_decode_config &c) {
     // The output kernel's column groups per unit: 2, 4 or 8 (ceil(B / 8) rounded up).
     const size_t gout = c.max_batch <= 16 ? 2 : c.max_batch <= 32 ? 4 : kMaxGroupsOut;
     const size_t part_out = c.max_batch > 8 ? kMaxSlicesOut * n_ot * gout * kWave * 16 : 0;
-    l.part = take(std::max({part_in, part_out, P * L * 4}));
+    // The router's K-slice partials of that dense-in kernel, token-major
+    // ([slice][token][kMaxExperts] f32, read by the routing units), after its
+    // other partials.
+    const size_t rpart = part_in ? (size_t)kMaxSlices * Bm * kMaxExperts * 4 : 0;
+    l.part = take(std::max({part_in + rpart, part_out, P * L * 4}));
+    l.rpart = l.part + part_in;
     l.pout = l.part;
     l.total = o;
     return l;

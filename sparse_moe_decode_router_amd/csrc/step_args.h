@@ -80,6 +80,7 @@ struct StepArgs {
     float *pout;
     uint32_t *cctr;
     float *part;    // dense-in above 16 tokens: slice partials [slice][tile][group][lane][4]
+    float *rpart;   // ... the router tiles' partials [slice][token][kMaxExperts]
     uint32_t *rgc;  // ... arrivals per row group, 256 B apart (two sets: caller / side stream)
 };
 
