@@ -873,10 +873,32 @@ __device__ __forceinline__ void w2_unit(const StepArgs &a, int c, int tg, uint16
     }
     acc = add_pair_column(acc);
     if constexpr (!Ord) {
+        // The unit's weighted sums meet in LDS as [KS][token][row] (rows of
+        // its 8 / KS tiles, the staged operand no longer read once every wave
+        // has passed the barrier); then each wave adds 64 consecutive rows of
+        // one token per atomic instruction, the KS partial sums added first.
+        constexpr int RW = 16 * (kWG / KS);  // latent rows of the unit
+        float *red = (float *)s_b;
+        static_assert(KS * 8 * RW * 4 <= 8 * Stage<1>::kChunks * 2, "reduction buffer");
+        __syncthreads();
         if (active && j < nt && part == 0) {
-            float *dst = a.ylat + (size_t)tok_j * a.L + 16 * t + 4 * g;
+            f32x4 v;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) unsafeAtomicAdd(dst + i, w_j * acc[i]);
+            for (int i = 0; i < 4; ++i) v[i] = w_j * acc[i];
+            stf4(red + (size_t)(kh * 8 + j) * RW + 16 * (wave / KS) + 4 * g, v);
+        }
+        __syncthreads();
+        const int r0 = 16 * tg * (kWG / KS);
+        const int rows = min(RW, a.L - r0);
+        for (int it = threadIdx.x; it < nt * RW; it += kWGThreads) {
+            const int jj = it / RW, rr = it % RW;
+            const int tok = __shfl(recw, R_TOKEN + jj);
+            if (rr < rows) {
+                float v = red[(size_t)jj * RW + rr];
+#pragma unroll
+                for (int q = 1; q < KS; ++q) v += red[(size_t)(q * 8 + jj) * RW + rr];
+                unsafeAtomicAdd(a.ylat + (size_t)tok * a.L + r0 + rr, v);
+            }
         }
     } else {
         if constexpr (KS > 1) {
