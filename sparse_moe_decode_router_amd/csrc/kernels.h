@@ -1657,8 +1657,13 @@ k_w13(const StepArgs a) {
 }
 
 // Kernel 3: down units (KS waves per tile; Ord: the ordered latent combine).
+// Units of at most two steps (short experts) are latency-bound chains of a
+// record read, the operand staging and the combine: four workgroups per
+// compute unit keep more of them in flight (64 registers, no spills; TP8
+// share batch 64: 140.7 -> 137.3 us per layer).
 template <int S, int KS, bool Ord = false>
-__global__ void __launch_bounds__(kWGThreads) __attribute__((amdgpu_waves_per_eu(4)))
+__global__ void __launch_bounds__(kWGThreads)
+__attribute__((amdgpu_waves_per_eu(S <= 2 && !Ord ? 8 : 4)))
 k_w2(const StepArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t s_b[8 * Stage<S>::kChunks];
     const int NC = min(load_agent(a.meta + M_N_COLS), a.ncols_cap);
