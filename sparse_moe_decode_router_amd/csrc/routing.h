@@ -205,7 +205,8 @@ __device__ __forceinline__ int lanes_below(unsigned long long m) {
 __device__ __forceinline__ bool select_by_threshold(const uint32_t (&ok)[kKeysPerLane],
                                                     const float (&sc)[kKeysPerLane], int k,
                                                     uint32_t *cand_key, int *cand_id,
-                                                    float *cand_s, int &mine, float &s_mine) {
+                                                    float *cand_s, int &mine, float &s_mine,
+                                                    bool &sel, int &pos, float &total) {
     const int lane = lane_id();
     uint32_t lm = 0u;
 #pragma unroll
@@ -240,14 +241,18 @@ __device__ __forceinline__ bool select_by_threshold(const uint32_t (&ok)[kKeysPe
         const uint32_t kj = readlane(ck, j);
         rank += (kj > ck || (kj == ck && j < lane)) ? 1 : 0;
     }
+    // The candidates are in ascending id, so a selection's place among the
+    // selected ids is its count of selected lanes below; the scores go to
+    // LDS in selection order for the sum.
+    sel = have && rank < k;
+    pos = lanes_below(__ballot(sel));
     wave_sync();
-    if (have && rank < k) {
-        cand_id[rank] = cid;
-        cand_s[rank] = cs;
-    }
+    if (sel) cand_s[rank] = cs;
     wave_sync();
-    mine = lane < k ? cand_id[lane] : 0;
-    s_mine = lane < k ? cand_s[lane] : 0.f;
+    total = 0.f;
+    for (int r = 0; r < k; ++r) total += cand_s[r];
+    mine = cid;
+    s_mine = cs;
     wave_sync();
     return true;
 }
@@ -345,25 +350,29 @@ __device__ __forceinline__ void topk_token(const RouteArgs &a, int b, Lds &lds, 
     // The routing inside the dense-in launch takes the rounds when it loads
     // the keys from memory: the threshold selection's registers would spill
     // there, in a kernel whose other code needs them all.
-    bool done = false;
+    // Each lane's selection (sel), its place among the selected ids (pos)
+    // and the sum of the selected scores in selection order (total).
+    bool done = false, sel = false;
+    int pos = 0;
+    float total = 0.f;
     if constexpr (!Agent || FromLds) {
         const int wv = wave_index();
         done = select_by_threshold(ok, sc, k, lds.cand_key[wv], lds.cand_id[wv], lds.cand_s[wv],
-                                   mine, s_mine);
+                                   mine, s_mine, sel, pos, total);
     }
-    if (!done) select_by_rounds(ok, sc, k, mine, s_mine);
-    // Rank of each selection among the selected ids; sum of the selected
-    // scores in selection order.
-    int rank = 0;
-    float total = 0.f;
-    for (int r = 0; r < k; ++r) {
-        const int other = (int)readlane((uint32_t)mine, r);
-        rank += other < mine ? 1 : 0;
-        total += __uint_as_float(readlane(__float_as_uint(s_mine), r));
+    if (!done) {
+        // Lane r holds the r-th selection.
+        select_by_rounds(ok, sc, k, mine, s_mine);
+        for (int r = 0; r < k; ++r) {
+            const int other = (int)readlane((uint32_t)mine, r);
+            pos += other < mine ? 1 : 0;
+            total += __uint_as_float(readlane(__float_as_uint(s_mine), r));
+        }
+        sel = lane < k;
     }
-    if (lane < k) {
+    if (sel) {
         const float w = s_mine / total;
-        const int o = b * k + rank;
+        const int o = b * k + pos;
         lds.idx[o] = (int16_t)mine;
         lds.w[o] = w;
         if (Agent) {
