@@ -279,6 +279,8 @@ def kernel_durations(ctx, names, kb, xd, k, out, idx, wts, steps, stream, out_st
             sym = "k_dense_in_kx"
         elif n == "dense_in" and ctx.last_dispatch().get("in_staged") == 1:  # x staged, up to 2 tokens
             sym = "k_dense_in_xl"
+        elif n == "dense_in" and ctx.last_dispatch().get("in_staged") == 3:  # x staged, 3 to 8 tokens
+            sym = "k_dense_in_xl8"
         per_kernel[n] = {"symbol": sym, "us": round(avg_ms * 1e3, 2),
                          "bytes": int(avg_bytes), "gbs": round(gbs, 1),
                          "frac": round(gbs / HBM_PEAK_GBS, 4)}

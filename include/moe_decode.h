@@ -223,7 +223,9 @@ typedef struct {
                               tile, 1 staged in LDS once per workgroup (at most two
                               tokens), 2 staged in LDS per row group and step with K
                               split into slices (above 16 tokens, and from 9 when
-                              the launch fits one round of resident workgroups) */
+                              the launch fits one round of resident workgroups), 3
+                              staged in LDS once per workgroup, 3 to 8 tokens when
+                              the launch fits one workgroup per compute unit */
 } moe_decode_dispatch_info;
 moe_status moe_decode_last_dispatch(const moe_decode_ctx *ctx, moe_decode_dispatch_info *info);
 

@@ -1336,25 +1336,28 @@ k_dense_in(const StepArgs a) {
 // router then routes the step, in LDS that x no longer needs; prefetch units
 // follow the dense units.
 constexpr int kXlTokens = 2;
+// 3 to 8 tokens: the same kernel with all 8 rows staged (131 KB of LDS, one
+// workgroup per compute unit, whose waves may hold twice the registers: the
+// staged x and the weight ring together).  Instead of two weight steps in
+// flight per wave with the columns loaded from memory by every wave.
+constexpr int kXlTokensWide = 8;
 constexpr int kXlRing = 4;       // weight steps in flight per wave (output kernel); the least spc
 constexpr int kXlDenseRing = 6;  // ... dense-in (K3 batch 1: 29.4 -> 28.5 us against 4)
 constexpr int kXlPad = 8;  // elements after each staged row: the rows' equal columns on distinct banks
-template <bool Route>
+template <bool Route, int NT>
 union XlShared {
-    uint16_t x[kXlTokens * (kMaxDenseK + kXlPad)];
+    uint16_t x[NT * (kMaxDenseK + kXlPad)];
     RouteLds route;
 };
-template <>
-union XlShared<false> {
-    uint16_t x[kXlTokens * (kMaxDenseK + kXlPad)];
+template <int NT>
+union XlShared<false, NT> {
+    uint16_t x[NT * (kMaxDenseK + kXlPad)];
 };
 
-template <bool Route>
-__global__ void __launch_bounds__(kWGThreads) __attribute__((amdgpu_waves_per_eu(4)))
-k_dense_in_xl(const StepArgs a) {
-    __shared__ __attribute__((aligned(16))) XlShared<Route> s_u;
-    __shared__ float s_red[kWG * kWave * 4];
-    __shared__ int s_last;
+// The dense-in tile of the workgroup with NT token rows of x staged in LDS.
+template <bool Route, int NT>
+__device__ __forceinline__ void dense_in_xl_body(const StepArgs &a, XlShared<Route, NT> &s_u,
+                                                 float *s_red, int &s_last) {
     uint16_t *s_x = s_u.x;
     const Role ro = role_of(a.kw_in);
     const int lane = lane_id(), n = lane & 15, g = lane >> 4;
@@ -1379,7 +1382,7 @@ k_dense_in_xl(const StepArgs a) {
     const uint16_t *A = dense_in_row(a, kind, tt) + 8 * g;
     const int ns = a.spc_in, s0 = ro.kw * ns;  // kXlRing <= ns <= kMaxStepsPerChunk (host)
     // x chunks of this thread (16 bytes each): c = threadIdx.x + kWGThreads q.
-    constexpr int kQx = kXlTokens * kMaxDenseK / 8 / kWGThreads;
+    constexpr int kQx = NT * kMaxDenseK / 8 / kWGThreads;
     const int nq = a.B * a.H / 8;
     u32x4 xs[kQx];
 #pragma unroll
@@ -1420,6 +1423,24 @@ k_dense_in_xl(const StepArgs a) {
         __syncthreads();  // s_last is set; every wave is done with x
         if (s_last) route_step<false>(route_args(a), &s_u.route, kWG);
     }
+}
+
+template <bool Route>
+__global__ void __launch_bounds__(kWGThreads) __attribute__((amdgpu_waves_per_eu(4)))
+k_dense_in_xl(const StepArgs a) {
+    __shared__ __attribute__((aligned(16))) XlShared<Route, kXlTokens> s_u;
+    __shared__ float s_red[kWG * kWave * 4];
+    __shared__ int s_last;
+    dense_in_xl_body<Route, kXlTokens>(a, s_u, s_red, s_last);
+}
+
+template <bool Route>
+__global__ void __launch_bounds__(kWGThreads) __attribute__((amdgpu_waves_per_eu(2)))
+k_dense_in_xl8(const StepArgs a) {
+    __shared__ __attribute__((aligned(16))) XlShared<Route, kXlTokensWide> s_u;
+    __shared__ float s_red[kWG * kWave * 4];
+    __shared__ int s_last;
+    dense_in_xl_body<Route, kXlTokensWide>(a, s_u, s_red, s_last);
 }
 
 // Sum over the nsl slices of tile t's partials part[k][t][c][lane] (T tiles

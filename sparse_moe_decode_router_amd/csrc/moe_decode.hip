@@ -507,14 +507,22 @@ moe_status moe_decode_step(moe_decode_ctx *ctx, const uint16_t *x, int32_t batch
     // compute unit.
     const bool kx = (pl.ncg_in >= 2 || kx_small) && pl.latent_rows == 16 && pl.router_rows == 16;
     // Up to 2 tokens: x staged in LDS, six weight steps in flight per wave
-    // (K3 batch 1: 32.0 -> 28.5 us).
-    const bool xl = !fused && batch <= kXlTokens && pl.in.spc >= kXlRing &&
-                    pl.in.spc <= kMaxStepsPerChunk && c.hidden <= kMaxDenseK && a.route_units == 0;
-    d.in_staged = kx ? 2 : xl ? 1 : 0;
+    // (K3 batch 1: 32.0 -> 28.5 us).  3 to 8 tokens, where the launch fits
+    // one workgroup per compute unit: all 8 rows staged, once per compute
+    // unit (TP8 share batch 3 / 4 / 8: -0.3 / -0.4 / -0.9 us per layer; K3,
+    // whose 696 tiles would re-stage them 2.7 times per compute unit, keeps
+    // the unstaged kernel: batch 3-5 +1 us with it).
+    const bool xl_wide = batch > kXlTokens && pl.units_in <= ctx->n_cus;
+    const bool xl = !fused && (batch <= kXlTokens || (batch <= kXlTokensWide && xl_wide)) &&
+                    pl.in.spc >= kXlRing && pl.in.spc <= kMaxStepsPerChunk &&
+                    c.hidden <= kMaxDenseK && a.route_units == 0;
+    d.in_staged = kx ? 2 : xl && xl_wide ? 3 : xl ? 1 : 0;
     auto dense_launch = [&](hipStream_t st, StepArgs &args) {
         if (xl) {
             const int rw_in = kWG / pl.in.kw;
-            launch_on(st, late ? k_dense_in_xl<false> : k_dense_in_xl<true>,
+            launch_on(st,
+                      xl_wide ? (late ? k_dense_in_xl8<false> : k_dense_in_xl8<true>)
+                              : (late ? k_dense_in_xl<false> : k_dense_in_xl<true>),
                       (unsigned)(dense_units_host(args.dense_hi - args.dense_lo, rw_in, 1) +
                                  args.route_units + args.pf_units),
                       kWGThreads, args);

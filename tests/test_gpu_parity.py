@@ -237,6 +237,29 @@ def test_all_experts_selected(form, B):
     check_step(layer, x, 32, out, idx, w)
 
 
+# Hidden 4096: four 128-element steps per wave, so the dense-in launch stages
+# x in LDS (up to 8 tokens).
+STAGED_MID = small_recipe(H=4096, L=512, E=96, I=384, Is=384, k=6)
+
+
+@pytest.mark.parametrize("form", ["four_launches", "dense_routing"])
+def test_staged_dense_in_up_to_8_tokens(form):
+    """The dense-in launch with x staged in LDS: 2 rows up to 2 tokens, all 8
+    rows (one workgroup per compute unit, this layer's 86 tiles fitting one
+    round) from 3 to 8; every token's output against the oracle, with the
+    routing after it (dense routing) or at the start of the gate/up launch."""
+    layer = synth.make_layer(STAGED_MID, 21)
+    ctx = make_ctx(layer, 8)
+    ctx.set_mode(mode_const(form))
+    for B in (1, 2, 3, 5, 8):
+        log(f"staged dense-in, {form}, B={B}")
+        x = synth.make_tokens(layer.dims, 30 + B, B)
+        out, idx, w = run(ctx, x, 6)
+        assert ctx.last_dispatch()["in_staged"] == (1 if B <= 2 else 3)
+        check_step(layer, x, 6, out, idx, w)
+    ctx.close()
+
+
 def assert_same_step(a, b):
     """Two runs of one step: identical expert ids and weights; outputs equal
     up to the order of the f32 atomic adds of the expert combine.  A different
@@ -583,6 +606,9 @@ def test_k3_layer(k3_layer, k3_dev, bias_kind, B):
     # output launch stages its operands in LDS.
     assert ctx.last_dispatch()["split_w2"] == (2 if B == 1 else 1)
     assert ctx.last_dispatch()["out_staged"] == (1 if B == 1 else 2 if B == 8 else 0)
+    # x staged in LDS at batch 1; at batch 8 the 1.4-round launch reads it
+    # through the caches; K slices at 64.
+    assert ctx.last_dispatch()["in_staged"] == {1: 1, 8: 0, 64: 2}[B]
     r = check_step(layer, x, 16, out, idx, w)
     log("  ", r, "distinct experts", len(np.unique(idx)))
 
@@ -657,7 +683,7 @@ def test_k3_spec_verify_batch(k3_layer, k3_dev, users, drafts):
 def test_k3_tp8_share_layer():
     layer = synth.make_layer(synth.K3_TP8, synth.TP8_STACK_SEED0)
     ctx = make_ctx(layer, 64, 16)
-    for B in (1, 9, 16, 64):
+    for B in (1, 8, 9, 16, 64):
         log(f"K3 TP8 share B={B}")
         x = synth.make_tokens(layer.dims, 1, B)
         out, idx, w = run(ctx, x, 16)
@@ -665,9 +691,9 @@ def test_k3_tp8_share_layer():
         # Batch 1 leaves the gate/up kernel short of units (16 experts x 4
         # tile groups): eight waves share each tile.
         assert d["split_w13"] == (8 if B == 1 else 1)
-        # x staged once per workgroup up to two tokens; from 9 tokens this
-        # one-round dense-in launch splits K into slices.
-        assert d["in_staged"] == (1 if B == 1 else 2)
+        # x staged once per workgroup up to 8 tokens (all 8 rows from 3);
+        # from 9 tokens this one-round dense-in launch splits K into slices.
+        assert d["in_staged"] == (1 if B == 1 else 3 if B == 8 else 2)
         r = check_step(layer, x, 16, out, idx, w)
         log("  ", r)
 
