@@ -828,9 +828,9 @@ __device__ __forceinline__ void ordered_combine(const StepArgs &a, int recw, int
 // 16t .. 16t+15; the routing weight of each pair scales its column before the
 // f32 atomic add into ylat.  Coh: the record and activation rows come from
 // units of the same launch.  KS: waves per tile (8 / KS tiles per unit), each
-// taking S / KS steps of every chunk and adding its own partial sums.  Ord:
-// the weighted outputs go to pout instead (the KS partial sums added through
-// LDS first, in wave order) and ordered_combine forms ylat.
+// taking S / KS steps of every chunk; the KS partial sums are added through
+// LDS, in wave order.  Ord: the weighted outputs go to pout instead and
+// ordered_combine forms ylat.
 template <int S, bool Coh, int KS = 1, bool Ord = false>
 __device__ __forceinline__ void w2_unit(const StepArgs &a, int c, int tg, uint16_t *s_b,
                                         bool &reuse) {

@@ -197,9 +197,11 @@ __device__ __forceinline__ int lanes_below(unsigned long long m) {
 //     which is ascending expert id;
 //  3. each candidate's rank in selection order (larger key first, equal keys
 //     by lower id) is its count of candidates that come before it;
-//  4. the candidates of rank < k are written to LDS by rank, and lane r takes
-//     the rank-r expert and its score, as the round-based selection leaves
-//     them.
+//  4. the candidates of rank < k are selected: sel on their lanes (mine and
+//     s_mine: expert and score), pos = their place among the selected ids
+//     (the selected lanes below, the candidates being in ascending id), and
+//     total = the sum of the selected scores in selection order (the scores
+//     written to LDS by rank, then added in rank order).
 // Returns false, having changed nothing the caller uses, when more than 64
 // keys are >= T (the caller then runs the rounds).
 __device__ __forceinline__ bool select_by_threshold(const uint32_t (&ok)[kKeysPerLane],
