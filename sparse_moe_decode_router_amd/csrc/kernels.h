@@ -1624,8 +1624,13 @@ k_dense_in_kx(const StepArgs a) {
 // memory for the later launches: each column unit's record from the workgroup
 // that runs its first tile group, everything else from workgroup 0.
 constexpr int kLateUnitsPerWG = 16;
+// Chunks of 8 steps (K split 1, not late) are compiled for three workgroups
+// per compute unit (80 registers, 32 KB of LDS): with units of one workgroup
+// each, more units in flight beat the longer weight burst of 16-step chunks
+// that leave room for two (K3 batch 2 / 8 / 64 step: -3 / -3.4 / -3.2 %).
 template <int S, bool Late, int KS = 1>
-__global__ void __launch_bounds__(kWGThreads) __attribute__((amdgpu_waves_per_eu(4)))
+__global__ void __launch_bounds__(kWGThreads)
+__attribute__((amdgpu_waves_per_eu(S == 8 && !Late && KS == 1 ? 6 : 4)))
 k_w13(const StepArgs a) {
     constexpr int kStage = 8 * Stage<S>::kChunks * 2;
     constexpr int kBytes = Late && (int)sizeof(LateRouteLds) > kStage ? (int)sizeof(LateRouteLds)
@@ -1681,10 +1686,11 @@ k_w13(const StepArgs a) {
 // Units of at most two steps (short experts) are latency-bound chains of a
 // record read, the operand staging and the combine: four workgroups per
 // compute unit keep more of them in flight (64 registers, no spills; TP8
-// share batch 64: 140.7 -> 137.3 us per layer).
+// share batch 64: 140.7 -> 137.3 us per layer).  Chunks of 8 steps (K split
+// 1) take three workgroups, as in k_w13 (80 registers).
 template <int S, int KS, bool Ord = false>
 __global__ void __launch_bounds__(kWGThreads)
-__attribute__((amdgpu_waves_per_eu(S <= 2 && !Ord ? 8 : 4)))
+__attribute__((amdgpu_waves_per_eu(S <= 2 && !Ord ? 8 : S == 8 && KS == 1 && !Ord ? 6 : 4)))
 k_w2(const StepArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t s_b[8 * Stage<S>::kChunks];
     const int NC = min(load_agent(a.meta + M_N_COLS), a.ncols_cap);

@@ -403,6 +403,13 @@ moe_status moe_decode_step(moe_decode_ctx *ctx, const uint16_t *x, int32_t batch
     d.split_in = pl.in.kw;
     d.split_out = pl.out.kw;
     d.split_w13 = ks13;
+    // Expert chunks: from 2 tokens the gate/up kernel, and above 8 the down
+    // kernel, take 8 of the 16 steps per chunk where that would be 16 (K
+    // split 1): half the LDS, three resident workgroups instead of two (K3
+    // batch 2 / 8 / 64 step: 103.5 / 199.0 / 515.6 -> 100.3 / 192.3 / 493.3
+    // us; the down kernel from 2 tokens lost 1-2 us).
+    const int s13 = batch > 1 && ks13 == 1 && pl.s13 == 16 ? 8 : pl.s13;
+    const int s2_one = batch > 8 && pl.s2 == 16 ? 8 : pl.s2;
     // Four-launch down kernel: when its units would fill less than the two
     // resident workgroups per compute unit, two waves share each tile (twice
     // the units, half the steps per wave).
@@ -414,7 +421,7 @@ moe_status moe_decode_step(moe_decode_ctx *ctx, const uint16_t *x, int32_t batch
     const bool ordered = ctx->mode == MOE_MODE_ORDERED;
     d.ordered = ordered ? 1 : 0;
     const StepKernel w2_k = ordered ? (split2 ? kW2SplitOrd[pl.s2] : kW2Ord[pl.s2])
-                                    : (split2 ? kW2Split[pl.s2] : kW2[pl.s2]);
+                                    : (split2 ? kW2Split[pl.s2] : kW2[s2_one]);
     d.grid_in = (int32_t)(pl.units_in + a.route_units);  // every unit its own workgroup
     // Expert grids for the expected column units (ncols_grid); the kernels
     // loop over the rest.
@@ -589,7 +596,7 @@ moe_status moe_decode_step(moe_decode_ctx *ctx, const uint16_t *x, int32_t batch
         if (d.router_f32) launch(k_router_f32, cdiv(c.n_experts, kWavesPerBlock), kBlock);
         dense_launch(s, a);
         dense_launch(ctx->side, sa);
-        launch(w13_kernel(pl.s13, ks13, late), d.grid_w13, kWGThreads);
+        launch(w13_kernel(s13, ks13, late), d.grid_w13, kWGThreads);
         launch(w2_k, d.grid_w2, kWGThreads);
         launch_on(ctx->side, k_out_part<OUT_SHARED>,
                   grid_for(dense_units_host(n_ot, kWG / pl.sd.kw, pl.ncg_out), cap), kWGThreads,
@@ -609,7 +616,7 @@ moe_status moe_decode_step(moe_decode_ctx *ctx, const uint16_t *x, int32_t batch
         const hipError_t e = hipGetLastError();
         return e == hipSuccess ? MOE_OK : hip_fail(ctx, e);
     }
-    launch(w13_kernel(pl.s13, ks13, late), d.grid_w13, kWGThreads);
+    launch(w13_kernel(s13, ks13, late), d.grid_w13, kWGThreads);
     launch(w2_k, d.grid_w2, kWGThreads);
     if (pl.ncg_out >= 2) {
         // Above 8 tokens: the column operands staged in LDS per group of 8
