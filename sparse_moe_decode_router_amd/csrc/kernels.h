@@ -1686,11 +1686,16 @@ k_w13(const StepArgs a) {
 // Units of at most two steps (short experts) are latency-bound chains of a
 // record read, the operand staging and the combine: four workgroups per
 // compute unit keep more of them in flight (64 registers, no spills; TP8
-// share batch 64: 140.7 -> 137.3 us per layer).  Chunks of 8 steps (K split
-// 1) take three workgroups, as in k_w13 (80 registers).
+// share batch 64: 140.7 -> 137.3 us per layer; the ordered form, whose
+// pair stores need more registers, three).  Chunks of 8 steps (K split 1)
+// take three workgroups, as in k_w13 (80 registers; the ordered form would
+// spill).
 template <int S, int KS, bool Ord = false>
 __global__ void __launch_bounds__(kWGThreads)
-__attribute__((amdgpu_waves_per_eu(S <= 2 && !Ord ? 8 : S == 8 && KS == 1 && !Ord ? 6 : 4)))
+__attribute__((amdgpu_waves_per_eu(S <= 2 && !Ord   ? 8
+                                   : S <= 2 && KS == 1 ? 6
+                                   : S == 8 && KS == 1 && !Ord ? 6
+                                                              : 4)))
 k_w2(const StepArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t s_b[8 * Stage<S>::kChunks];
     const int NC = min(load_agent(a.meta + M_N_COLS), a.ncols_cap);
